@@ -1,0 +1,156 @@
+"""CPU oracle for MXFP8 block quantisation -- TEST INFRASTRUCTURE ONLY.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
+``bench.py`` may import this module; the product path never does.
+
+MXFP8 is the reduced-precision format the pages report for the expert
+feed-forward compute and for moving data between experts (unite.ai, "Ai2
+κυκλοφορεί το Olmo-Core 3…", section "Παραλληλισμός, Ακρίβεια και Τεχνικές
+Μνήμης"; ettayeb.fr, "Olmo-core 3 ouvre l'entraînement des MoE…", section
+"Trois parallélismes, trois optimisations de routage", where it is described as
+storing some values in fewer bits).  The pages give no bit layout; the reading
+taken is the OCP microscaling one: blocks of 32 consecutive elements along the
+GEMM's reduction axis share one power-of-two scale stored as an E8M0 byte, and
+each element is an FP8 E4M3 code.
+
+Definitions written out here:
+  E4M3  sign | 4-bit exponent (bias 7) | 3-bit mantissa; exponent field 0 is
+        subnormal (m/8 * 2^-6); codes 0x7F and 0xFF are NaN; no infinities;
+        largest finite magnitude 1.75 * 2^8 = 448.
+  E8M0  byte b encodes 2^(b-127); b = 255 is NaN (never produced here).
+  block scale   s = the smallest integer with amax * 2^-s <= 448, clamped to
+                [-127, 127]; amax = 0 -> -127.  Computed exactly as
+                s0 = floor(log2(amax)) - 8 (8 = exponent of E4M3's largest
+                normal), plus one when amax * 2^-s0 > 448.  No element of a block
+                saturates, so amax * 2^-s lies in (224, 448].  (The other common
+                reading, s0 alone with saturation at 448, clips up to 12.5% off
+                the largest element of about a fifth of all blocks.)
+  element       code = RNE(v * 2^-s) on the E4M3 grid; the encoder still
+                saturates at 448 as a guard.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+E4M3_MAX = 448.0
+BLOCK = 32
+
+
+def e4m3_decode(codes) -> np.ndarray:
+    """Value of every E4M3 code (float64; NaN for 0x7F / 0xFF)."""
+    c = np.asarray(codes).astype(np.int64) & 0xFF
+    s = (c >> 7) & 1
+    e = (c >> 3) & 0xF
+    m = c & 0x7
+    mag = np.where(e == 0, (m / 8.0) * 2.0 ** -6, (1.0 + m / 8.0) * np.exp2(e - 7.0))
+    v = np.where(s == 1, -mag, mag)
+    return np.where((c & 0x7F) == 0x7F, np.nan, v)
+
+
+def _positive_grid():
+    codes = np.arange(0x7F, dtype=np.int64)      # 0x00 .. 0x7E: the finite non-negative codes
+    return codes, e4m3_decode(codes)              # ascending in value
+
+
+def e4m3_encode(v) -> np.ndarray:
+    """Round-to-nearest-even onto the E4M3 grid, saturating at +-448.
+
+    Nearest grid point by magnitude; on an exact tie the code with an even
+    mantissa (even code) wins.  The sign bit follows the input's sign bit, so
+    -0.0 and negative values that round to zero give 0x80.
+    """
+    x = np.asarray(v, dtype=np.float64)
+    assert not np.isnan(x).any()
+    codes, grid = _positive_grid()
+    mag = np.minimum(np.abs(x), E4M3_MAX)
+    hi = np.searchsorted(grid, mag, side="left")          # grid[hi] >= mag
+    hi = np.minimum(hi, len(grid) - 1)
+    lo = np.maximum(hi - 1, 0)
+    dlo = mag - grid[lo]
+    dhi = grid[hi] - mag
+    pick_hi = (dhi < dlo) | ((dhi == dlo) & (codes[hi] % 2 == 0))
+    out = np.where(pick_hi, codes[hi], codes[lo])
+    out = np.where(grid[hi] == mag, codes[hi], out)        # exact grid hit
+    sign = np.signbit(x).astype(np.int64) << 7
+    return (out | sign).astype(np.uint8)
+
+
+def block_scale_exponent(amax) -> np.ndarray:
+    """Shared exponent s of a block with largest magnitude amax (exact, via frexp)."""
+    a = np.asarray(amax, dtype=np.float64)
+    mant, ex = np.frexp(a)                 # a = mant * 2^ex, mant in [0.5, 1)
+    fl = ex.astype(np.int64) - 1           # floor(log2 a) for a > 0
+    s = fl - 8
+    s = s + (a * np.exp2(-s.astype(np.float64)) > E4M3_MAX)   # exact: power-of-two scaling
+    s = np.clip(s, -127, 127)
+    return np.where(a == 0, -127, s).astype(np.int64)
+
+
+def quantize_rows(v, block: int = BLOCK):
+    """Quantise a [R, K] matrix in blocks of ``block`` consecutive elements along
+    each row (the reduction axis when rows are contiguous in K).  A partial last
+    block is zero-padded (zeros do not change amax).
+    Returns codes uint8 [R, K] and scale bytes uint8 [R, ceil(K / block)]."""
+    x = np.asarray(v, dtype=np.float64)
+    R, K = x.shape
+    nb = -(-K // block)
+    pad = np.zeros((R, nb * block))
+    pad[:, :K] = x
+    blocks = pad.reshape(R, nb, block)
+    amax = np.abs(blocks).max(axis=2)
+    s = block_scale_exponent(amax)                         # [R, nb]
+    scaled = blocks * np.exp2(-s.astype(np.float64))[:, :, None]
+    codes = e4m3_encode(scaled).reshape(R, nb * block)[:, :K]
+    return codes, (s + 127).astype(np.uint8)
+
+
+def quantize_segment_cols(v, offsets, block: int = BLOCK):
+    """Quantise a [R, K] matrix in blocks of ``block`` consecutive ROWS, restarting
+    at every segment start offsets[e] (rows of one expert form one segment; the
+    reduction of a weight-gradient GEMM runs over them).  A segment's last block
+    is zero-padded.
+    Returns codes uint8 [R, K] (in place of the values) and a list, one entry per
+    segment, of scale bytes uint8 [ceil(count_e / block), K]."""
+    x = np.asarray(v, dtype=np.float64)
+    off = np.asarray(offsets).astype(np.int64)
+    R, K = x.shape
+    codes = np.zeros((R, K), dtype=np.uint8)
+    scales = []
+    for e in range(len(off) - 1):
+        lo, hi = off[e], off[e + 1]
+        n = hi - lo
+        nb = -(-n // block)
+        if n == 0:
+            scales.append(np.zeros((0, K), dtype=np.uint8))
+            continue
+        pad = np.zeros((nb * block, K))
+        pad[:n] = x[lo:hi]
+        blocks = pad.reshape(nb, block, K)
+        amax = np.abs(blocks).max(axis=1)                  # [nb, K]
+        s = block_scale_exponent(amax)
+        scaled = blocks * np.exp2(-s.astype(np.float64))[:, None, :]
+        codes[lo:hi] = e4m3_encode(scaled).reshape(nb * block, K)[:n]
+        scales.append((s + 127).astype(np.uint8))
+    return codes, scales
+
+
+def dequantize_rows(codes, scales, block: int = BLOCK) -> np.ndarray:
+    c = np.asarray(codes)
+    R, K = c.shape
+    s = np.asarray(scales).astype(np.float64) - 127.0
+    rep = np.repeat(s, block, axis=1)[:, :K]
+    return e4m3_decode(c) * np.exp2(rep)
+
+
+def dequantize_segment_cols(codes, scales, offsets, block: int = BLOCK) -> np.ndarray:
+    c = np.asarray(codes)
+    off = np.asarray(offsets).astype(np.int64)
+    out = np.zeros(c.shape)
+    for e in range(len(off) - 1):
+        lo, hi = off[e], off[e + 1]
+        if hi == lo:
+            continue
+        s = np.asarray(scales[e]).astype(np.float64) - 127.0
+        rep = np.repeat(s, block, axis=0)[: hi - lo]
+        out[lo:hi] = e4m3_decode(c[lo:hi]) * np.exp2(rep)
+    return out
