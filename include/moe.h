@@ -1,0 +1,211 @@
+/*
+ * moe.h -- C-ABI of the MI355X (gfx950) MoE expert-layer library (libmoe_mi355x.so).
+ *
+ * The library computes one mixture-of-experts expert layer on the experts resident on
+ * one GPU: router scores, top-k gating, a stable rowwise permutation that writes routed
+ * tokens straight into per-expert input buffers, grouped SwiGLU expert GEMMs, and the
+ * weighted combine, forward and backward.  The structure follows the pages' statement
+ * of the problem: E experts with k chosen per token (unite.ai, "Ai2 κυκλοφορεί το
+ * Olmo-Core 3…", opening section; ettayeb.fr, "Olmo-core 3 ouvre l'entraînement des
+ * MoE…", section "Le problème que les MoE n'ont jamais tout à fait résolu"); routed data
+ * placed directly into expert input buffers, routing metadata kept on the GPU so the
+ * host never waits for a copy-back, and a grouped GEMM over the many small expert
+ * computations (unite.ai, section "Παραλληλισμός, Ακρίβεια και Τεχνικές Μνήμης";
+ * ettayeb.fr, section "Trois parallélismes, trois optimisations de routage").
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Every tensor argument is a DEVICE pointer owned by the caller.  The library never
+ *    allocates, frees, synchronises, or reads device memory from the host.  All work is
+ *    enqueued on `stream` (a hipStream_t; NULL = the default stream).  No call copies
+ *    anything back to the host, so expert counts and offsets never leave the GPU.
+ *  - Notation: T tokens, d model width, f expert hidden width, E experts, k experts per
+ *    token, R = T*k routed rows.  All matrices are row-major.  Weights are stored
+ *    [out, in] per expert: Wr [E, d], W1 and W3 [E, f, d], W2 [E, d, f].
+ *  - `act` dtype (moe_shape.act) is the element type of x, weights, y, every [R, *]
+ *    activation buffer and every gradient except those documented as float.
+ *    MOE_F32 -> float, MOE_BF16 -> bf16 (bit pattern in uint16).  Scores, gates and
+ *    their gradients are always float.
+ *  - Return value: MOE_OK, or a negative moe_status for an error detected on the host
+ *    before anything was enqueued (bad shape, null pointer, misalignment, workspace too
+ *    small).  MOE_ELAUNCH means a kernel launch failed (the stream state is then
+ *    unspecified).  Data errors that only the device can see (an invalid pre-routed
+ *    expert id) are reported by OR-ing bits into a caller-provided device word.
+ *  - Determinism: every output is bitwise reproducible run to run (no float atomics,
+ *    fixed reduction orders).
+ *  - Re-entrancy: the library holds no state; calls on different streams with disjoint
+ *    buffers may run concurrently.  Calls that share a workspace must be ordered.
+ *  - Limits: 1 <= k <= E <= 1024, T*k < 2^31, d and f multiples of 64; with MOE_MXFP8
+ *    GEMMs d and f must be multiples of 128.  bf16 buffers need 16-byte alignment.
+ */
+#ifndef MOE_MI355X_H
+#define MOE_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_EINVAL = -1,        /* shape or argument out of the supported range */
+  MOE_ENULL = -2,         /* a required pointer is NULL */
+  MOE_EALIGN = -3,        /* a pointer is not aligned as required */
+  MOE_EWORKSPACE = -4,    /* workspace smaller than moe_workspace_size() */
+  MOE_EUNSUPPORTED = -5,  /* dtype combination not implemented */
+  MOE_ELAUNCH = -6        /* a kernel launch failed */
+} moe_status;
+
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_MXFP8 = 2 } moe_dtype;
+
+/* All sizes are known on the host; nothing about the routing is. */
+typedef struct {
+  int32_t T, d, f, E, k;
+  int32_t act;   /* MOE_F32 or MOE_BF16 */
+  int32_t gemm;  /* grouped-GEMM arithmetic: MOE_F32 (act F32), MOE_BF16 or MOE_MXFP8 (act BF16) */
+} moe_shape;
+
+/* Bits OR-ed into *dev_err by moe_route_given. */
+#define MOE_DEVERR_EXPERT_RANGE 1  /* an expert id outside [0, E) (clamped before use) */
+#define MOE_DEVERR_DUPLICATE 2     /* one token lists the same expert twice */
+
+const char* moe_status_str(int status);
+
+/* Bytes of device workspace any call below may need for this shape (pure host
+ * function; no HIP call).  Calls taking (ws, ws_bytes) use it as scratch only: its
+ * contents on entry are ignored and on exit are unspecified. */
+size_t moe_workspace_size(const moe_shape* s);
+
+/* ---------------------------------------------------------------- forward */
+
+/* Router scores: logits[t, e] = sum_i x[t, i] * Wr[e, i] (+ bias[e]).
+ * x [T, d] act, Wr [E, d] act, bias [E] float or NULL, logits [T, E] float (written).
+ * Router of the learned-routing rows (bigchange.ai, "Olmo-core 3 открывает стек
+ * обучения MoE от Ai2…", section "Что инженер может попробовать на практике"). */
+moe_status moe_router_fwd(const moe_shape* s, const void* x, const void* Wr, const float* bias,
+                          float* logits, void* stream);
+
+/* Top-k gating and dispatch metadata, all on the device.
+ * In:  logits [T, E] float (finite).
+ * Out: topk_idx [T, k] int32, the k largest scores per token in value-descending order,
+ *      equal scores broken toward the lower expert index;
+ *      gates [T, k] float, softmax over the k selected scores;
+ *      counts [E] int32 rows routed to each expert;
+ *      offsets [E + 1] int32 exclusive prefix sum of counts (offsets[E] = T*k);
+ *      slot_row [T, k] int32, packed row of routed slot (t, j): rows of one expert keep
+ *      ascending slot order t*k + j (a stable counting sort).
+ * ws: scratch of at least moe_workspace_size(s) bytes. */
+moe_status moe_route(const moe_shape* s, const float* logits, int32_t* topk_idx, float* gates,
+                     int32_t* counts, int32_t* offsets, int32_t* slot_row, void* ws, size_t ws_bytes,
+                     void* stream);
+
+/* Dispatch metadata for tokens that arrive already routed (random routing of the large
+ * benchmark rows: bigchange.ai, section "Три числа, три знаменателя"; unite.ai, section
+ * "Δοκιμές τρισεκατομμυρίων παραμέτρων").  topk_idx [T, k] int32 is the input; counts,
+ * offsets and slot_row are written as in moe_route.  Invalid ids set bits in *dev_err
+ * (a device int32 the caller zeroes and reads at its own sync point) and are clamped
+ * into [0, E) so every later kernel stays in bounds. */
+moe_status moe_route_given(const moe_shape* s, const int32_t* topk_idx, int32_t* counts,
+                           int32_t* offsets, int32_t* slot_row, int32_t* dev_err, void* ws,
+                           size_t ws_bytes, void* stream);
+
+/* Rowwise dispatch into per-expert input buffers: x_perm[slot_row[t, j]] = x[t] and
+ * row_src[slot_row[t, j]] = t.  x [T, d] act, slot_row [T, k], row_src [R] int32 (written,
+ * may be NULL), x_perm [R, d] act (written). */
+moe_status moe_permute(const moe_shape* s, const void* x, const int32_t* slot_row, int32_t* row_src,
+                       void* x_perm, void* stream);
+
+/* Grouped SwiGLU expert FFN over the packed buffers (one group per expert, rows
+ * [offsets[e], offsets[e+1])):  a = X_e W1_e^T, b = X_e W3_e^T, h = silu(a) * b,
+ * y_e = h W2_e^T.  Equivalent to moe_ffn_gemm1_fwd followed by moe_ffn_gemm2_fwd.
+ * x_perm [R, d] act; ab [R, 2f] act written (a in columns [0, f), b in [f, 2f), kept for
+ * the backward); h [R, f] act written; y_perm [R, d] act written.  Accumulation is
+ * float; with MOE_MXFP8 both GEMMs take E4M3 operands with one E8M0 scale per 32
+ * elements along K (MXFP8 for the expert FFN: unite.ai, section "Παραλληλισμός,
+ * Ακρίβεια και Τεχνικές Μνήμης"). */
+moe_status moe_grouped_ffn_fwd(const moe_shape* s, const void* x_perm, const void* W1, const void* W3,
+                               const void* W2, const int32_t* offsets, void* ab, void* h, void* y_perm,
+                               void* ws, size_t ws_bytes, void* stream);
+
+moe_status moe_ffn_gemm1_fwd(const moe_shape* s, const void* x_perm, const void* W1, const void* W3,
+                             const int32_t* offsets, void* ab, void* h, void* ws, size_t ws_bytes,
+                             void* stream);
+moe_status moe_ffn_gemm2_fwd(const moe_shape* s, const void* h, const void* W2, const int32_t* offsets,
+                             void* y_perm, void* ws, size_t ws_bytes, void* stream);
+
+/* Weighted combine: y[t] = sum_j gates[t, j] * y_perm[slot_row[t, j]] (float accumulation
+ * in j order).  y_perm [R, d] act, gates [T, k] float, y [T, d] act (written). */
+moe_status moe_combine(const moe_shape* s, const void* y_perm, const float* gates, const int32_t* slot_row,
+                       void* y, void* stream);
+
+/* ---------------------------------------------------------------- backward */
+
+/* dy_perm[slot_row[t, j]] = gates[t, j] * dy[t];  dgates[t, j] = <dy[t], y_perm[slot_row[t, j]]>.
+ * dy [T, d] act, y_perm [R, d] act, gates [T, k] float; dy_perm [R, d] act and
+ * dgates [T, k] float written. */
+moe_status moe_combine_bwd(const moe_shape* s, const void* dy, const void* y_perm, const float* gates,
+                           const int32_t* slot_row, void* dy_perm, float* dgates, void* stream);
+
+/* Backward of the grouped FFN (equivalent to moe_ffn_dgrad2, moe_ffn_wgrad2,
+ * moe_ffn_dgrad1, moe_ffn_wgrad1 in that order).
+ *   dh = dy_e W2_e;  da = dh * b * s * (1 + a (1 - s)), db = dh * silu(a), s = sigmoid(a)
+ *   dW2_e = dy_e^T h_e;  dx_e = da W1_e + db W3_e;  dW1_e = da^T X_e;  dW3_e = db^T X_e
+ * dy_perm [R, d], x_perm [R, d], ab [R, 2f], h [R, f]: act inputs.  dab [R, 2f] act written
+ * (da | db), dx_perm [R, d] act written, dW1 dW3 [E, f, d] and dW2 [E, d, f] act written;
+ * an expert with no rows gets exactly zero weight gradients. */
+moe_status moe_grouped_ffn_bwd(const moe_shape* s, const void* dy_perm, const void* x_perm, const void* ab,
+                               const void* h, const void* W1, const void* W3, const void* W2,
+                               const int32_t* offsets, void* dab, void* dx_perm, void* dW1, void* dW3,
+                               void* dW2, void* ws, size_t ws_bytes, void* stream);
+
+moe_status moe_ffn_dgrad2(const moe_shape* s, const void* dy_perm, const void* W2, const void* ab,
+                          const int32_t* offsets, void* dab, void* ws, size_t ws_bytes, void* stream);
+moe_status moe_ffn_wgrad2(const moe_shape* s, const void* h, const void* dy_perm, const int32_t* offsets,
+                          void* dW2, void* ws, size_t ws_bytes, void* stream);
+moe_status moe_ffn_dgrad1(const moe_shape* s, const void* dab, const void* W1, const void* W3,
+                          const int32_t* offsets, void* dx_perm, void* ws, size_t ws_bytes, void* stream);
+moe_status moe_ffn_wgrad1(const moe_shape* s, const void* x_perm, const void* dab, const int32_t* offsets,
+                          void* dW1, void* dW3, void* ws, size_t ws_bytes, void* stream);
+
+/* Gradient of the gates w.r.t. the scores: dlogits[t, e] = g_e (dg_e - sum_i g_i dg_i) for
+ * the k chosen experts, 0 for the others.  dgates, gates [T, k] float, topk_idx [T, k],
+ * dlogits [T, E] float (written in full). */
+moe_status moe_route_bwd(const moe_shape* s, const float* dgates, const float* gates,
+                         const int32_t* topk_idx, float* dlogits, void* stream);
+
+/* Router backward: dx_r = dlogits Wr ([T, d] act, written), dWr = dlogits^T x ([E, d]
+ * float, written). */
+moe_status moe_router_bwd(const moe_shape* s, const void* x, const void* Wr, const float* dlogits,
+                          void* dx_r, float* dWr, void* stream);
+
+/* Un-permute and sum: dx[t] = dx_r[t] + sum_j dx_perm[slot_row[t, j]] (float accumulation,
+ * dx_r may be NULL).  dx_perm [R, d], dx_r [T, d], dx [T, d] act. */
+moe_status moe_permute_bwd(const moe_shape* s, const void* dx_perm, const int32_t* slot_row,
+                           const void* dx_r, void* dx, void* stream);
+
+/* ---------------------------------------------------------------- MXFP8 */
+
+/* Block quantisation bf16 -> E4M3 codes + E8M0 scales, 32 elements per block.
+ * src [rows, cols] bf16.  The scale of a block is the smallest power of two 2^s with
+ * amax * 2^-s <= 448 (s clamped to [-127, 127]; an all-zero block gets s = -127); each
+ * element is rounded to nearest-even on the E4M3 grid.
+ * axis 0: blocks run along each row (32 consecutive columns); q [rows, cols] u8 and
+ *         scales [rows, cols/32] u8; cols must be a multiple of 32.
+ * axis 1: blocks run down the columns, restarting at every segment start
+ *         seg_offsets[e] (e < nseg; seg_offsets has nseg + 1 entries, seg_offsets[nseg] =
+ *         rows); the output is TRANSPOSED into the padded layout the weight-gradient GEMM
+ *         reads: segment e occupies columns [P_e, P_e + roundup(n_e, 128)) of
+ *         q [cols, rows_pad] with P_e = sum_{e'<e} roundup(n_e', 128), rows_pad = rows +
+ *         128 * nseg, and scales [cols, rows_pad / 32]; padding is written as zero codes
+ *         and zero-block scales.
+ * MXFP8 for the expert FFN: unite.ai, section "Παραλληλισμός, Ακρίβεια και Τεχνικές
+ * Μνήμης"; ettayeb.fr, section "Trois parallélismes, trois optimisations de routage". */
+moe_status moe_mx_quantize(int32_t rows, int32_t cols, int32_t axis, const int32_t* seg_offsets,
+                           int32_t nseg, const void* src, uint8_t* q, uint8_t* scales, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_MI355X_H */

@@ -1,0 +1,215 @@
+"""Python binding of libmoe_mi355x.so (the MI355X MoE expert-layer library).
+
+Argument marshalling only: every function here takes torch tensors that live on the
+GPU, checks dtypes/shapes cheaply, and calls the C-ABI entry point of the same name
+(declared in include/moe.h) on the current HIP stream.  Every step of the layer runs in
+the library's HIP kernels; there is no CPU or PyTorch fallback, and importing this
+package fails loudly if the library has not been built.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmoe_mi355x.so")
+
+MOE_F32, MOE_BF16, MOE_MXFP8 = 0, 1, 2
+MOE_DEVERR_EXPERT_RANGE, MOE_DEVERR_DUPLICATE = 1, 2
+
+
+class MoeError(RuntimeError):
+    def __init__(self, fn: str, status: int, msg: str):
+        super().__init__(f"{fn} failed: {msg} (status {status})")
+        self.status = status
+
+
+class moe_shape(ctypes.Structure):
+    _fields_ = [("T", ctypes.c_int32), ("d", ctypes.c_int32), ("f", ctypes.c_int32),
+                ("E", ctypes.c_int32), ("k", ctypes.c_int32), ("act", ctypes.c_int32),
+                ("gemm", ctypes.c_int32)]
+
+    def __repr__(self):
+        return (f"moe_shape(T={self.T}, d={self.d}, f={self.f}, E={self.E}, k={self.k}, "
+                f"act={self.act}, gemm={self.gemm})")
+
+
+def make_shape(T, d, f, E, k, act=MOE_BF16, gemm=None) -> moe_shape:
+    if gemm is None:
+        gemm = MOE_F32 if act == MOE_F32 else MOE_BF16
+    return moe_shape(T, d, f, E, k, act, gemm)
+
+
+_VP = ctypes.c_void_p
+_SZ = ctypes.c_size_t
+_SHP = ctypes.POINTER(moe_shape)
+
+# entry point -> argument types after the shape pointer (None = no shape argument)
+_SIGS = {
+    "moe_router_fwd": [_VP, _VP, _VP, _VP, _VP],
+    "moe_route": [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _SZ, _VP],
+    "moe_route_given": [_VP, _VP, _VP, _VP, _VP, _VP, _SZ, _VP],
+    "moe_permute": [_VP, _VP, _VP, _VP, _VP],
+    "moe_grouped_ffn_fwd": [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _SZ, _VP],
+    "moe_ffn_gemm1_fwd": [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _SZ, _VP],
+    "moe_ffn_gemm2_fwd": [_VP, _VP, _VP, _VP, _VP, _SZ, _VP],
+    "moe_combine": [_VP, _VP, _VP, _VP, _VP],
+    "moe_combine_bwd": [_VP, _VP, _VP, _VP, _VP, _VP, _VP],
+    "moe_grouped_ffn_bwd": [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _SZ, _VP],
+    "moe_ffn_dgrad2": [_VP, _VP, _VP, _VP, _VP, _VP, _SZ, _VP],
+    "moe_ffn_wgrad2": [_VP, _VP, _VP, _VP, _VP, _SZ, _VP],
+    "moe_ffn_dgrad1": [_VP, _VP, _VP, _VP, _VP, _VP, _SZ, _VP],
+    "moe_ffn_wgrad1": [_VP, _VP, _VP, _VP, _VP, _VP, _SZ, _VP],
+    "moe_route_bwd": [_VP, _VP, _VP, _VP, _VP],
+    "moe_router_bwd": [_VP, _VP, _VP, _VP, _VP, _VP],
+    "moe_permute_bwd": [_VP, _VP, _VP, _VP, _VP],
+}
+EXPORTED = sorted(list(_SIGS) + ["moe_mx_quantize", "moe_workspace_size", "moe_status_str"])
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load the built library (raises if it is missing: there is no fallback)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is missing: build it with `python -m mixture_experts_layer_logits_amd.build`")
+    lib = ctypes.CDLL(path)
+    for name, args in _SIGS.items():
+        fn = getattr(lib, name)
+        fn.argtypes = [_SHP] + args
+        fn.restype = ctypes.c_int
+    lib.moe_mx_quantize.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, _VP, ctypes.c_int32, _VP, _VP,
+                                    _VP, _VP]
+    lib.moe_mx_quantize.restype = ctypes.c_int
+    lib.moe_workspace_size.argtypes = [_SHP]
+    lib.moe_workspace_size.restype = ctypes.c_size_t
+    lib.moe_status_str.argtypes = [ctypes.c_int]
+    lib.moe_status_str.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def _p(t):
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    if not t.is_cuda:
+        raise ValueError("tensor arguments must live on the GPU")
+    if not t.is_contiguous():
+        raise ValueError("tensor arguments must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(stream=None):
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else stream
+
+
+def _call(name, shape, *args, stream=None):
+    lib = load_library()
+    st = getattr(lib, name)(ctypes.byref(shape), *[_p(a) if not isinstance(a, ctypes.c_size_t) else a for a in args],
+                            _stream(stream))
+    if st != 0:
+        raise MoeError(name, st, lib.moe_status_str(st).decode())
+
+
+def moe_workspace_size(shape: moe_shape) -> int:
+    return int(load_library().moe_workspace_size(ctypes.byref(shape)))
+
+
+def moe_status_str(status: int) -> str:
+    return load_library().moe_status_str(status).decode()
+
+
+def _ws(ws):
+    return ctypes.c_size_t(ws.numel() * ws.element_size())
+
+
+# ------------------------------------------------------------------ forward
+def moe_router_fwd(shape, x, Wr, bias, logits, stream=None):
+    _call("moe_router_fwd", shape, x, Wr, bias, logits, stream=stream)
+
+
+def moe_route(shape, logits, topk_idx, gates, counts, offsets, slot_row, ws, stream=None):
+    _call("moe_route", shape, logits, topk_idx, gates, counts, offsets, slot_row, ws, _ws(ws), stream=stream)
+
+
+def moe_route_given(shape, topk_idx, counts, offsets, slot_row, dev_err, ws, stream=None):
+    _call("moe_route_given", shape, topk_idx, counts, offsets, slot_row, dev_err, ws, _ws(ws), stream=stream)
+
+
+def moe_permute(shape, x, slot_row, row_src, x_perm, stream=None):
+    _call("moe_permute", shape, x, slot_row, row_src, x_perm, stream=stream)
+
+
+def moe_grouped_ffn_fwd(shape, x_perm, W1, W3, W2, offsets, ab, h, y_perm, ws, stream=None):
+    _call("moe_grouped_ffn_fwd", shape, x_perm, W1, W3, W2, offsets, ab, h, y_perm, ws, _ws(ws), stream=stream)
+
+
+def moe_ffn_gemm1_fwd(shape, x_perm, W1, W3, offsets, ab, h, ws, stream=None):
+    _call("moe_ffn_gemm1_fwd", shape, x_perm, W1, W3, offsets, ab, h, ws, _ws(ws), stream=stream)
+
+
+def moe_ffn_gemm2_fwd(shape, h, W2, offsets, y_perm, ws, stream=None):
+    _call("moe_ffn_gemm2_fwd", shape, h, W2, offsets, y_perm, ws, _ws(ws), stream=stream)
+
+
+def moe_combine(shape, y_perm, gates, slot_row, y, stream=None):
+    _call("moe_combine", shape, y_perm, gates, slot_row, y, stream=stream)
+
+
+# ------------------------------------------------------------------ backward
+def moe_combine_bwd(shape, dy, y_perm, gates, slot_row, dy_perm, dgates, stream=None):
+    _call("moe_combine_bwd", shape, dy, y_perm, gates, slot_row, dy_perm, dgates, stream=stream)
+
+
+def moe_grouped_ffn_bwd(shape, dy_perm, x_perm, ab, h, W1, W3, W2, offsets, dab, dx_perm, dW1, dW3, dW2, ws,
+                        stream=None):
+    _call("moe_grouped_ffn_bwd", shape, dy_perm, x_perm, ab, h, W1, W3, W2, offsets, dab, dx_perm, dW1, dW3, dW2,
+          ws, _ws(ws), stream=stream)
+
+
+def moe_ffn_dgrad2(shape, dy_perm, W2, ab, offsets, dab, ws, stream=None):
+    _call("moe_ffn_dgrad2", shape, dy_perm, W2, ab, offsets, dab, ws, _ws(ws), stream=stream)
+
+
+def moe_ffn_wgrad2(shape, h, dy_perm, offsets, dW2, ws, stream=None):
+    _call("moe_ffn_wgrad2", shape, h, dy_perm, offsets, dW2, ws, _ws(ws), stream=stream)
+
+
+def moe_ffn_dgrad1(shape, dab, W1, W3, offsets, dx_perm, ws, stream=None):
+    _call("moe_ffn_dgrad1", shape, dab, W1, W3, offsets, dx_perm, ws, _ws(ws), stream=stream)
+
+
+def moe_ffn_wgrad1(shape, x_perm, dab, offsets, dW1, dW3, ws, stream=None):
+    _call("moe_ffn_wgrad1", shape, x_perm, dab, offsets, dW1, dW3, ws, _ws(ws), stream=stream)
+
+
+def moe_route_bwd(shape, dgates, gates, topk_idx, dlogits, stream=None):
+    _call("moe_route_bwd", shape, dgates, gates, topk_idx, dlogits, stream=stream)
+
+
+def moe_router_bwd(shape, x, Wr, dlogits, dx_r, dWr, stream=None):
+    _call("moe_router_bwd", shape, x, Wr, dlogits, dx_r, dWr, stream=stream)
+
+
+def moe_permute_bwd(shape, dx_perm, slot_row, dx_r, dx, stream=None):
+    _call("moe_permute_bwd", shape, dx_perm, slot_row, dx_r, dx, stream=stream)
+
+
+# ------------------------------------------------------------------ MXFP8
+def moe_mx_quantize(rows, cols, axis, seg_offsets, nseg, src, q, scales, stream=None):
+    lib = load_library()
+    st = lib.moe_mx_quantize(rows, cols, axis, _p(seg_offsets), nseg, _p(src), _p(q), _p(scales), _stream(stream))
+    if st != 0:
+        raise MoeError("moe_mx_quantize", st, lib.moe_status_str(st).decode())
+
+
+from .layer import MoEExpertLayer  # noqa: E402  (re-export)

@@ -1,0 +1,35 @@
+// Internal declarations: MXFP8 (E4M3 elements, E8M0 scale per 32) quantisers and the
+// scaled-MFMA expert GEMMs.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+#include "gemm.h"
+
+namespace moe {
+
+constexpr int kMxBlock = 32;     // elements per shared scale
+constexpr int kMxSegPad = 128;   // expert segments are padded to this many rows in K-major copies
+
+size_t mx_workspace_bytes(int R, int d, int f, int E);
+
+// axis 0: blocks along rows; q [rows, cols], scales [rows, cols/32]
+hipError_t mx_quantize_rows(int rows, int cols, const bf16_t* src, uint8_t* q, uint8_t* scales, hipStream_t st);
+// axis 1: blocks down columns restarting at segment starts; transposed padded output
+hipError_t mx_quantize_cols_seg(int rows, int cols, const int32_t* seg_offsets, int nseg, const bf16_t* src,
+                                uint8_t* q, uint8_t* scales, hipStream_t st);
+
+hipError_t gemm1_fwd_mx(const GemmShape& s, const int* offsets, const bf16_t* X, const bf16_t* W1, const bf16_t* W3,
+                        bf16_t* ab, bf16_t* h, void* ws, hipStream_t st);
+hipError_t gemm2_fwd_mx(const GemmShape& s, const int* offsets, const bf16_t* H, const bf16_t* W2, bf16_t* Y,
+                        void* ws, hipStream_t st);
+hipError_t dgrad2_mx(const GemmShape& s, const int* offsets, const bf16_t* dY, const bf16_t* W2, const bf16_t* ab,
+                     bf16_t* dab, void* ws, hipStream_t st);
+hipError_t wgrad2_mx(const GemmShape& s, const int* offsets, const bf16_t* H, const bf16_t* dY, bf16_t* dW2,
+                     void* ws, hipStream_t st);
+hipError_t dgrad1_mx(const GemmShape& s, const int* offsets, const bf16_t* dab, const bf16_t* W1, const bf16_t* W3,
+                     bf16_t* dX, void* ws, hipStream_t st);
+hipError_t wgrad1_mx(const GemmShape& s, const int* offsets, const bf16_t* X, const bf16_t* dab, bf16_t* dW1,
+                     bf16_t* dW3, void* ws, hipStream_t st);
+
+}  // namespace moe

@@ -1,0 +1,33 @@
+// Internal declarations: routing, dispatch and row-movement launchers.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace moe {
+
+constexpr int kRouteChunk = 32;   // tokens per routing workgroup (stable-rank chunk)
+constexpr int kMaxTopK = 32;      // largest supported k
+constexpr int MOE_DEVERR_EXPERT_RANGE_BIT = 1;
+constexpr int MOE_DEVERR_DUPLICATE_BIT = 2;
+
+size_t route_workspace_bytes(int T, int E, int k);
+hipError_t route_topk(int T, int E, int k, const float* logits, int32_t* idx, float* gates, int32_t* counts,
+                      int32_t* offsets, int32_t* slot_row, void* ws, hipStream_t st);
+hipError_t route_given(int T, int E, int k, const int32_t* idx, int32_t* counts, int32_t* offsets,
+                       int32_t* slot_row, int32_t* dev_err, void* ws, hipStream_t st);
+hipError_t route_backward(int T, int E, int k, const float* dgates, const float* gates, const int32_t* idx,
+                          float* dlogits, hipStream_t st);
+
+// elem_bytes: 2 (bf16) or 4 (float)
+hipError_t permute_rows(int elem_bytes, int T, int d, int k, const void* x, const int32_t* slot_row,
+                        int32_t* row_src, void* x_perm, hipStream_t st);
+hipError_t combine_rows(int elem_bytes, int T, int d, int k, const void* y_perm, const float* gates,
+                        const int32_t* slot_row, void* y, hipStream_t st);
+hipError_t combine_rows_bwd(int elem_bytes, int T, int d, int k, const void* dy, const void* y_perm,
+                            const float* gates, const int32_t* slot_row, void* dy_perm, float* dgates,
+                            hipStream_t st);
+hipError_t unpermute_sum_rows(int elem_bytes, int T, int d, int k, const void* dx_perm, const int32_t* slot_row,
+                              const void* dx_r, void* dx, hipStream_t st);
+
+}  // namespace moe

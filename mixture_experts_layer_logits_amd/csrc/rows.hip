@@ -1,0 +1,170 @@
+// Row movement between token order and the packed per-expert buffers.
+//
+// Dispatch writes every routed token row straight into its expert's input buffer
+// (rowwise dispatch: unite.ai, "Ai2 κυκλοφορεί το Olmo-Core 3…", section
+// "Παραλληλισμός, Ακρίβεια και Τεχνικές Μνήμης"; ettayeb.fr, "Olmo-core 3 ouvre
+// l'entraînement des MoE…", section "Trois parallélismes, trois optimisations de
+// routage"); combine gathers the expert outputs back per token, weighted by the gates.
+// All four kernels are HBM-bound row copies: one wavefront per token, 16-byte accesses,
+// consecutive lanes on consecutive 16-byte chunks of a row, float accumulation in a
+// fixed order (j = 0..k-1), no atomics.
+#include "common.h"
+#include "route.h"
+
+namespace moe {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kTokPerBlock = kThreads / kWave;
+
+// x_perm[slot_row[t, j]] = x[t]; row_src[slot_row[t, j]] = t
+template <typename T>
+__global__ void __launch_bounds__(kThreads) permute_kernel(int ntok, int d, int k, const T* __restrict__ x,
+                                                           const int32_t* __restrict__ slot_row,
+                                                           int32_t* __restrict__ row_src, T* __restrict__ x_perm) {
+  const int t = blockIdx.x * kTokPerBlock + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (t >= ntok) return;
+  constexpr int V = 16 / sizeof(T);
+  const int nchunk = d / V;
+  const uint4* src = reinterpret_cast<const uint4*>(x + (int64_t)t * d);
+  for (int c = lane; c < nchunk; c += kWave) {
+    const uint4 v = src[c];
+    for (int j = 0; j < k; j++) {
+      const int r = slot_row[(int64_t)t * k + j];
+      reinterpret_cast<uint4*>(x_perm + (int64_t)r * d)[c] = v;
+    }
+  }
+  if (row_src && lane < k) row_src[slot_row[(int64_t)t * k + lane]] = t;
+}
+
+// y[t] = sum_j gates[t, j] * y_perm[slot_row[t, j]]
+template <typename T>
+__global__ void __launch_bounds__(kThreads) combine_kernel(int ntok, int d, int k, const T* __restrict__ y_perm,
+                                                           const float* __restrict__ gates,
+                                                           const int32_t* __restrict__ slot_row, T* __restrict__ y) {
+  const int t = blockIdx.x * kTokPerBlock + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (t >= ntok) return;
+  const int nchunk = d / 8;
+  for (int c = lane; c < nchunk; c += kWave) {
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < k; j++) {
+      const int r = slot_row[(int64_t)t * k + j];
+      const float g = gates[(int64_t)t * k + j];
+      float v[8];
+      load8<T>(y_perm + (int64_t)r * d + c * 8, v);
+#pragma unroll
+      for (int i = 0; i < 8; i++) acc[i] = fmaf(g, v[i], acc[i]);
+    }
+    store8<T>(y + (int64_t)t * d + c * 8, acc);
+  }
+}
+
+// dy_perm[slot_row[t, j]] = gates[t, j] * dy[t];  dgates[t, j] = <dy[t], y_perm[slot_row[t, j]]>
+template <typename T>
+__global__ void __launch_bounds__(kThreads) combine_bwd_kernel(int ntok, int d, int k, const T* __restrict__ dy,
+                                                               const T* __restrict__ y_perm,
+                                                               const float* __restrict__ gates,
+                                                               const int32_t* __restrict__ slot_row,
+                                                               T* __restrict__ dy_perm, float* __restrict__ dgates) {
+  const int t = blockIdx.x * kTokPerBlock + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (t >= ntok) return;
+  const int nchunk = d / 8;
+  for (int j = 0; j < k; j++) {
+    const int r = slot_row[(int64_t)t * k + j];
+    const float g = gates[(int64_t)t * k + j];
+    float dot = 0.f;
+    for (int c = lane; c < nchunk; c += kWave) {
+      float u[8], v[8], o[8];
+      load8<T>(dy + (int64_t)t * d + c * 8, u);
+      load8<T>(y_perm + (int64_t)r * d + c * 8, v);
+#pragma unroll
+      for (int i = 0; i < 8; i++) {
+        dot = fmaf(u[i], v[i], dot);
+        o[i] = g * u[i];
+      }
+      store8<T>(dy_perm + (int64_t)r * d + c * 8, o);
+    }
+    dot = wave_sum(dot);
+    if (lane == 0) dgates[(int64_t)t * k + j] = dot;
+  }
+}
+
+// dx[t] = dx_r[t] + sum_j dx_perm[slot_row[t, j]]
+template <typename T>
+__global__ void __launch_bounds__(kThreads) unpermute_sum_kernel(int ntok, int d, int k, const T* __restrict__ dx_perm,
+                                                                 const int32_t* __restrict__ slot_row,
+                                                                 const T* __restrict__ dx_r, T* __restrict__ dx) {
+  const int t = blockIdx.x * kTokPerBlock + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (t >= ntok) return;
+  const int nchunk = d / 8;
+  for (int c = lane; c < nchunk; c += kWave) {
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    if (dx_r) load8<T>(dx_r + (int64_t)t * d + c * 8, acc);
+    for (int j = 0; j < k; j++) {
+      const int r = slot_row[(int64_t)t * k + j];
+      float v[8];
+      load8<T>(dx_perm + (int64_t)r * d + c * 8, v);
+#pragma unroll
+      for (int i = 0; i < 8; i++) acc[i] += v[i];
+    }
+    store8<T>(dx + (int64_t)t * d + c * 8, acc);
+  }
+}
+
+inline dim3 tok_grid(int T) { return dim3((unsigned)((T + kTokPerBlock - 1) / kTokPerBlock)); }
+
+}  // namespace
+
+hipError_t permute_rows(int eb, int T, int d, int k, const void* x, const int32_t* slot_row, int32_t* row_src,
+                        void* x_perm, hipStream_t st) {
+  if (T == 0) return hipSuccess;
+  if (eb == 2)
+    hipLaunchKernelGGL(permute_kernel<bf16_t>, tok_grid(T), dim3(kThreads), 0, st, T, d, k, (const bf16_t*)x, slot_row,
+                       row_src, (bf16_t*)x_perm);
+  else
+    hipLaunchKernelGGL(permute_kernel<float>, tok_grid(T), dim3(kThreads), 0, st, T, d, k, (const float*)x, slot_row,
+                       row_src, (float*)x_perm);
+  return hipGetLastError();
+}
+
+hipError_t combine_rows(int eb, int T, int d, int k, const void* y_perm, const float* gates, const int32_t* slot_row,
+                        void* y, hipStream_t st) {
+  if (T == 0) return hipSuccess;
+  if (eb == 2)
+    hipLaunchKernelGGL(combine_kernel<bf16_t>, tok_grid(T), dim3(kThreads), 0, st, T, d, k, (const bf16_t*)y_perm,
+                       gates, slot_row, (bf16_t*)y);
+  else
+    hipLaunchKernelGGL(combine_kernel<float>, tok_grid(T), dim3(kThreads), 0, st, T, d, k, (const float*)y_perm, gates,
+                       slot_row, (float*)y);
+  return hipGetLastError();
+}
+
+hipError_t combine_rows_bwd(int eb, int T, int d, int k, const void* dy, const void* y_perm, const float* gates,
+                            const int32_t* slot_row, void* dy_perm, float* dgates, hipStream_t st) {
+  if (T == 0) return hipSuccess;
+  if (eb == 2)
+    hipLaunchKernelGGL(combine_bwd_kernel<bf16_t>, tok_grid(T), dim3(kThreads), 0, st, T, d, k, (const bf16_t*)dy,
+                       (const bf16_t*)y_perm, gates, slot_row, (bf16_t*)dy_perm, dgates);
+  else
+    hipLaunchKernelGGL(combine_bwd_kernel<float>, tok_grid(T), dim3(kThreads), 0, st, T, d, k, (const float*)dy,
+                       (const float*)y_perm, gates, slot_row, (float*)dy_perm, dgates);
+  return hipGetLastError();
+}
+
+hipError_t unpermute_sum_rows(int eb, int T, int d, int k, const void* dx_perm, const int32_t* slot_row,
+                              const void* dx_r, void* dx, hipStream_t st) {
+  if (T == 0) return hipSuccess;
+  if (eb == 2)
+    hipLaunchKernelGGL(unpermute_sum_kernel<bf16_t>, tok_grid(T), dim3(kThreads), 0, st, T, d, k,
+                       (const bf16_t*)dx_perm, slot_row, (const bf16_t*)dx_r, (bf16_t*)dx);
+  else
+    hipLaunchKernelGGL(unpermute_sum_kernel<float>, tok_grid(T), dim3(kThreads), 0, st, T, d, k,
+                       (const float*)dx_perm, slot_row, (const float*)dx_r, (float*)dx);
+  return hipGetLastError();
+}
+
+}  // namespace moe

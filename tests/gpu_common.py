@@ -1,0 +1,77 @@
+"""Helpers shared by the GPU parity tests: run the HIP path through the C-ABI binding
+and compare with the CPU oracle under the tolerances of the method.
+
+Tolerances (normwise: max|got - ref| / max|ref|, per tensor):
+  bf16 path   2e-2   (values and gradients against the fp64 oracle)
+  fp32 path   1e-4
+  MXFP8 path  6e-2
+Integers (expert ids, counts, offsets, packed rows, row sources, E4M3/E8M0 bytes) must
+match bit for bit.
+"""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import torch
+
+TOL = {"bf16": 2e-2, "f32": 1e-4, "mxfp8": 6e-2}
+
+
+def normwise_err(got, ref) -> float:
+    g = np.asarray(got, dtype=np.float64)
+    r = np.asarray(ref, dtype=np.float64)
+    den = np.abs(r).max()
+    if den == 0:
+        return float(np.abs(g).max())
+    return float(np.abs(g - r).max() / den)
+
+
+def host(t) -> np.ndarray:
+    t = t.detach().cpu()
+    if t.dtype in (torch.bfloat16, torch.float16):
+        t = t.float()
+    return t.numpy()
+
+
+def to_dev(inp: dict) -> dict:
+    return {k: (v.cuda() if isinstance(v, torch.Tensor) else v) for k, v in inp.items()}
+
+
+def say(msg: str):
+    """Name the case before each GPU step (flushed, so a failing run still shows it)."""
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def run_layer(w, inp: dict, layer=None):
+    """Forward + backward of the whole layer on the GPU; returns the layer object."""
+    import mixture_experts_layer_logits_amd as m
+    act = m.MOE_F32 if w.dtype == "f32" else m.MOE_BF16
+    gemm = {"f32": m.MOE_F32, "bf16": m.MOE_BF16, "mxfp8": m.MOE_MXFP8}[w.gemm]
+    if layer is None:
+        layer = m.MoEExpertLayer(w.T, w.d, w.f, w.E, w.k, act=act, gemm=gemm)
+    d = to_dev(inp)
+    if w.routing == "given_uniform":
+        layer.forward(d["x"], d["W1"], d["W3"], d["W2"], topk_idx=d["topk_idx"], gates=d["gates"])
+    else:
+        layer.forward(d["x"], d["W1"], d["W3"], d["W2"], Wr=d["Wr"], bias=d["router_bias"])
+    layer.backward(d["dy"])
+    torch.cuda.synchronize()
+    return layer
+
+
+def oracle_for(w, inp: dict, gpu_logits=None):
+    """Oracle forward+backward on the same inputs; learned routing selects on the GPU's
+    fp32 scores (the selection is an integer decision taken in fp32 on both sides)."""
+    from oracle import moe_ref as ref
+    learned = w.routing != "given_uniform"
+    if learned:
+        fw = ref.layer_forward(inp["x"], inp["W1"], inp["W3"], inp["W2"], w.k, Wr=inp["Wr"],
+                               bias=inp["router_bias"], select_logits=gpu_logits)
+    else:
+        fw = ref.layer_forward(inp["x"], inp["W1"], inp["W3"], inp["W2"], w.k,
+                               topk_idx=inp["topk_idx"].numpy(), gates=inp["gates"])
+    bw = ref.layer_backward(fw, inp["dy"], inp["x"], inp["W1"], inp["W3"], inp["W2"], Wr=inp["Wr"],
+                            learned=learned)
+    return fw, bw

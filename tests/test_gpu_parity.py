@@ -1,0 +1,161 @@
+"""GPU parity of the HIP path (through the C-ABI) against the CPU oracle.
+
+Sizes here are ones the oracle finishes in seconds but that still span several GEMM
+tiles, ragged expert segments, empty experts and partial routing chunks.  Integer
+outputs must match bit for bit; values within the method's tolerances.
+"""
+import numpy as np
+import pytest
+import torch
+
+import workloads
+from gpu_common import TOL, host, normwise_err, oracle_for, run_layer, say, to_dev
+
+pytestmark = pytest.mark.gpu
+
+W = workloads.WORKLOADS
+
+# (workload, overrides) -- scaled copies keep dtype and routing mode
+CASES = [
+    ("tiny_fp32", {}),
+    ("e8_k4_t8192", dict(T=512, d=256, f=128)),
+    ("e128_k4_t8192", dict(T=512, d=256, f=192)),
+    ("e128_k4_t16384_zipf", dict(T=600, d=128, f=128)),
+    ("e128_k4_t16384_random", dict(T=333, d=192, f=128)),
+    ("e8_k4_t8192", dict(T=77, d=64, f=64, E=1, k=1, name="single_expert")),
+    ("e8_k4_t8192", dict(T=130, d=128, f=64, E=4, k=4, name="k_equals_E")),
+]
+
+
+def _case(name, over):
+    w = W[name]
+    return workloads.scaled(w, **over) if over else w
+
+
+def _check_layer(w, inp, layer):
+    tol = TOL[w.gemm]
+    learned = w.routing != "given_uniform"
+    gl = host(layer.logits) if learned else None
+    fw, bw = oracle_for(w, inp, gpu_logits=gl)
+    # integers: bit-exact
+    assert np.array_equal(host(layer.topk_idx), fw["topk_idx"]) if learned else True
+    assert np.array_equal(host(layer.counts), fw["counts"])
+    assert np.array_equal(host(layer.offsets), fw["offsets"])
+    assert np.array_equal(host(layer.slot_row), fw["slot_row"])
+    assert np.array_equal(host(layer.row_src), fw["row_src"])
+    # permute is a pure copy: bit-exact
+    assert np.array_equal(host(layer.x_perm), np.asarray(fw["x_perm"], dtype=np.float64))
+    errs = {}
+    if learned:
+        errs["logits"] = normwise_err(gl, fw["logits"])
+        errs["gates"] = normwise_err(host(layer.gates), fw["gates"])
+    errs["h"] = normwise_err(host(layer.h), fw["h"])
+    errs["y_perm"] = normwise_err(host(layer.y_perm), fw["y_perm"])
+    errs["y"] = normwise_err(host(layer.y), fw["y"])
+    errs["dgates"] = normwise_err(host(layer.dgates), bw["dgates"])
+    errs["dx_perm"] = normwise_err(host(layer.dx_perm), bw["dx_perm"])
+    errs["dW1"] = normwise_err(host(layer.dW1), bw["dW1"])
+    errs["dW3"] = normwise_err(host(layer.dW3), bw["dW3"])
+    errs["dW2"] = normwise_err(host(layer.dW2), bw["dW2"])
+    errs["dx"] = normwise_err(host(layer.dx), bw["dx"])
+    if learned:
+        errs["dlogits"] = normwise_err(host(layer.dlogits), bw["dlogits"])
+        errs["dWr"] = normwise_err(host(layer.dWr), bw["dWr"])
+    print(w.name, {k: f"{v:.2e}" for k, v in errs.items()})
+    bad = {k: v for k, v in errs.items() if v > tol}
+    assert not bad, (w.name, bad)
+    # experts without rows get exactly zero weight gradients
+    empty = np.nonzero(fw["counts"] == 0)[0]
+    for e in empty:
+        assert not host(layer.dW1[e]).any() and not host(layer.dW2[e]).any()
+
+
+@pytest.mark.parametrize("name,over", CASES, ids=[c[1].get("name", c[0]) for c in CASES])
+def test_layer_parity(name, over):
+    w = _case(name, over)
+    inp = workloads.make_inputs(w)
+    say(f"[gpu] layer parity {w}")
+    layer = run_layer(w, inp)
+    _check_layer(w, inp, layer)
+
+
+def test_layer_deterministic():
+    w = workloads.scaled(W["e128_k4_t8192"], T=512, d=256, f=128)
+    inp = workloads.make_inputs(w)
+    say("[gpu] determinism")
+    a = run_layer(w, inp)
+    outs = [t.clone() for t in (a.y, a.dx, a.dW1, a.dW2, a.dW3, a.dWr, a.slot_row)]
+    b = run_layer(w, inp, layer=a)
+    for t0, t1 in zip(outs, (b.y, b.dx, b.dW1, b.dW2, b.dW3, b.dWr, b.slot_row)):
+        assert torch.equal(t0, t1)
+
+
+def test_empty_batch():
+    import mixture_experts_layer_logits_amd as m
+    w = workloads.scaled(W["e8_k4_t8192"], T=0, d=64, f=64)
+    say("[gpu] T = 0")
+    L = m.MoEExpertLayer(0, 64, 64, 8, 4)
+    inp = workloads.make_inputs(workloads.scaled(W["e8_k4_t8192"], T=1, d=64, f=64))
+    d = to_dev(inp)
+    x = torch.empty(0, 64, dtype=torch.bfloat16, device="cuda")
+    L.forward(x, d["W1"], d["W3"], d["W2"], Wr=d["Wr"])
+    L.backward(x)
+    torch.cuda.synchronize()
+    assert not host(L.counts).any() and not host(L.offsets).any()
+    assert not host(L.dW1).any() and not host(L.dW2).any() and not host(L.dWr).any()
+
+
+def test_route_ties_and_limits():
+    """Constructed ties (equal scores, +-0), the largest E and k the kernels support."""
+    import mixture_experts_layer_logits_amd as m
+    from oracle import moe_ref as ref
+    for (T, E, k) in [(96, 16, 4), (64, 1024, 8), (70, 64, 32), (33, 1, 1)]:
+        say(f"[gpu] route ties T={T} E={E} k={k}")
+        g = torch.Generator().manual_seed(T * E + k)
+        L = torch.randint(-2, 3, (T, E), generator=g).float()
+        L[0] = 0.0
+        L[1, ::2] = -0.0
+        s = m.make_shape(T, 64, 64, E, k)
+        out = dict(idx=torch.empty(T, k, dtype=torch.int32, device="cuda"),
+                   gates=torch.empty(T, k, device="cuda"),
+                   counts=torch.empty(E, dtype=torch.int32, device="cuda"),
+                   offsets=torch.empty(E + 1, dtype=torch.int32, device="cuda"),
+                   slot=torch.empty(T, k, dtype=torch.int32, device="cuda"))
+        ws = torch.empty(m.moe_workspace_size(s), dtype=torch.uint8, device="cuda")
+        m.moe_route(s, L.cuda(), out["idx"], out["gates"], out["counts"], out["offsets"], out["slot"], ws)
+        torch.cuda.synchronize()
+        idx, gates = ref.topk_gates(L.numpy(), k)
+        counts, offsets, slot_row, _ = ref.dispatch(idx, E)
+        assert np.array_equal(host(out["idx"]), idx)
+        assert np.array_equal(host(out["counts"]), counts)
+        assert np.array_equal(host(out["offsets"]), offsets)
+        assert np.array_equal(host(out["slot"]), slot_row)
+        assert normwise_err(host(out["gates"]), gates) < 1e-6
+        assert np.abs(host(out["gates"]).sum(axis=1) - 1).max() < 1e-6
+
+
+def test_route_given_errors():
+    """Out-of-range and duplicate pre-routed ids set the device error word and are
+    clamped, so the dispatch stays a bijection."""
+    import mixture_experts_layer_logits_amd as m
+    from oracle import moe_ref as ref
+    T, E, k = 40, 8, 2
+    idx = torch.stack([torch.randperm(E)[:k] for _ in range(T)]).int()
+    idx[3, 1] = 9
+    idx[5, 0] = -2
+    idx[7] = torch.tensor([4, 4])
+    s = m.make_shape(T, 64, 64, E, k)
+    say("[gpu] route_given errors")
+    counts = torch.empty(E, dtype=torch.int32, device="cuda")
+    offsets = torch.empty(E + 1, dtype=torch.int32, device="cuda")
+    slot = torch.empty(T, k, dtype=torch.int32, device="cuda")
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    ws = torch.empty(m.moe_workspace_size(s), dtype=torch.uint8, device="cuda")
+    m.moe_route_given(s, idx.cuda(), counts, offsets, slot, err, ws)
+    torch.cuda.synchronize()
+    assert int(err.item()) == (m.MOE_DEVERR_EXPERT_RANGE | m.MOE_DEVERR_DUPLICATE)
+    flags = ref.validate_given_routing(idx.numpy(), E)
+    assert flags[3] & 1 and flags[5] & 1 and flags[7] & 2
+    clamped = idx.clamp(0, E - 1).numpy()
+    c, o, sr, _ = ref.dispatch(clamped, E)
+    assert np.array_equal(host(counts), c) and np.array_equal(host(offsets), o) and np.array_equal(host(slot), sr)
