@@ -1,0 +1,230 @@
+"""Throughput of the MoE expert layer (forward + backward) on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+
+A step is one pass of the whole layer over one batch of synthetic, seeded input that is
+already resident in HBM: router scores, top-k routing, dispatch into per-expert buffers,
+the two grouped SwiGLU GEMMs, combine, and the full backward (combine, four grouped
+GEMMs, gate and router gradients, un-permute).  Every step runs through the C-ABI of
+libmoe_mi355x.so on one stream.  Prints ONE JSON line on stdout; per-kernel detail goes to
+stderr.
+
+The default workload is the expert pool of 128 with top-4 routing at 8192 tokens
+(d=2048, f=1024, bf16), the layer-level counterpart of the pages' 8 -> 128 expert-pool
+comparison (bigchange.ai, "Olmo-core 3 открывает стек обучения MoE от Ai2…", section
+"Три числа, три знаменателя").
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MoE layer tokens/s fwd+bwd at E=128,k=4 on 1 GPU; grouped-GEMM MFMA % of peak"
+PEAK_TFLOPS = {"bf16": 2500.0, "mxfp8": 5000.0, "f32": 157.3}
+PEAK_HBM_GBS = 8000.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.json")
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="e128_k4_t8192")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample-tokens", type=int, default=1024)
+    return ap.parse_args()
+
+
+def kernel_sources_digest(files):
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(ROOT, "mixture_experts_layer_logits_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def step_calls(m, L, d_inp, learned):
+    """The layer as (name, callable) pairs, in execution order."""
+    s = L.shape
+    x, W1, W3, W2 = d_inp["x"], d_inp["W1"], d_inp["W3"], d_inp["W2"]
+    Wr, bias, dy = d_inp["Wr"], d_inp["router_bias"], d_inp["dy"]
+    g = L.gates if learned else d_inp["gates"]
+    calls = []
+    if learned:
+        calls += [("router_fwd", lambda: m.moe_router_fwd(s, x, Wr, bias, L.logits)),
+                  ("route", lambda: m.moe_route(s, L.logits, L.topk_idx, L.gates, L.counts, L.offsets, L.slot_row,
+                                                L.ws))]
+    else:
+        calls += [("route_given", lambda: m.moe_route_given(s, d_inp["topk_idx"], L.counts, L.offsets, L.slot_row,
+                                                            L.dev_err, L.ws))]
+    calls += [
+        ("permute", lambda: m.moe_permute(s, x, L.slot_row, L.row_src, L.x_perm)),
+        ("gemm1_fwd", lambda: m.moe_ffn_gemm1_fwd(s, L.x_perm, W1, W3, L.offsets, L.ab, L.h, L.ws)),
+        ("gemm2_fwd", lambda: m.moe_ffn_gemm2_fwd(s, L.h, W2, L.offsets, L.y_perm, L.ws)),
+        ("combine", lambda: m.moe_combine(s, L.y_perm, g, L.slot_row, L.y)),
+        ("combine_bwd", lambda: m.moe_combine_bwd(s, dy, L.y_perm, g, L.slot_row, L.dy_perm, L.dgates)),
+        ("dgrad2", lambda: m.moe_ffn_dgrad2(s, L.dy_perm, W2, L.ab, L.offsets, L.dab, L.ws)),
+        ("wgrad2", lambda: m.moe_ffn_wgrad2(s, L.h, L.dy_perm, L.offsets, L.dW2, L.ws)),
+        ("dgrad1", lambda: m.moe_ffn_dgrad1(s, L.dab, W1, W3, L.offsets, L.dx_perm, L.ws)),
+        ("wgrad1", lambda: m.moe_ffn_wgrad1(s, L.x_perm, L.dab, L.offsets, L.dW1, L.dW3, L.ws)),
+    ]
+    if learned:
+        calls += [("route_bwd", lambda: m.moe_route_bwd(s, L.dgates, g, L.topk_idx, L.dlogits)),
+                  ("router_bwd", lambda: m.moe_router_bwd(s, x, Wr, L.dlogits, L.dx_r, L.dWr, L.ws))]
+    calls += [("permute_bwd", lambda: m.moe_permute_bwd(s, L.dx_perm, L.slot_row, L.dx_r if learned else None,
+                                                        L.dx))]
+    return calls
+
+
+def algorithmic_work(w, eb):
+    """Per-launch algorithmic flops (GEMMs) and HBM bytes (everything) of each call."""
+    T, d, f, E, k = w.T, w.d, w.f, w.E, w.k
+    R = T * k
+    gem = {"gemm1_fwd": 2.0 * R * d * 2 * f, "gemm2_fwd": 2.0 * R * f * d, "dgrad2": 2.0 * R * d * f,
+           "wgrad2": 2.0 * R * d * f, "dgrad1": 2.0 * R * 2 * f * d, "wgrad1": 2.0 * R * 2 * f * d}
+    wbytes = E * f * d * eb
+    byt = {
+        "router_fwd": T * d * eb + E * d * eb + T * E * 4,
+        "route": T * E * 4 + R * 12,
+        "route_given": R * 8,
+        "permute": T * d * eb + R * d * eb + R * 8,
+        "gemm1_fwd": R * d * eb + 2 * wbytes + R * 3 * f * eb,
+        "gemm2_fwd": R * f * eb + wbytes + R * d * eb,
+        "combine": R * d * eb + T * d * eb + R * 8,
+        "combine_bwd": T * d * eb + 2 * R * d * eb + R * 12,
+        "dgrad2": R * d * eb + wbytes + R * 2 * f * eb * 2,
+        "wgrad2": R * d * eb + R * f * eb + wbytes,
+        "dgrad1": R * 2 * f * eb + 2 * wbytes + R * d * eb,
+        "wgrad1": R * 2 * f * eb + R * d * eb + 2 * wbytes,
+        "route_bwd": R * 12 + T * E * 4,
+        "router_bwd": 2 * T * E * 4 + E * d * eb + 2 * T * d * eb + E * d * 4,
+        "permute_bwd": R * d * eb + 2 * T * d * eb + R * 4,
+    }
+    return gem, byt
+
+
+def cpu_baseline(w, inp, ntok):
+    """The oracle as it stands, timed on the host cores on the first `ntok` tokens of the
+    same batch (all experts' weights), forward + backward."""
+    import numpy as np
+    from oracle import moe_ref as ref
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count() or 1
+    sub = {}
+    for key in ("x", "dy"):
+        sub[key] = inp[key][:ntok]
+    learned = w.routing != "given_uniform"
+    t0 = time.perf_counter()
+    if learned:
+        fw = ref.layer_forward(sub["x"], inp["W1"], inp["W3"], inp["W2"], w.k, Wr=inp["Wr"], bias=inp["router_bias"])
+    else:
+        fw = ref.layer_forward(sub["x"], inp["W1"], inp["W3"], inp["W2"], w.k, topk_idx=inp["topk_idx"][:ntok].numpy(),
+                               gates=inp["gates"][:ntok])
+    ref.layer_backward(fw, sub["dy"], sub["x"], inp["W1"], inp["W3"], inp["W2"], Wr=inp["Wr"], learned=learned)
+    dt = time.perf_counter() - t0
+    return {"value": ntok / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"first {ntok} of {w.T} tokens, all {w.E} experts' weights, fwd+bwd in fp64 NumPy "
+                      f"({dt:.1f} s)"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only: the layer runs on one GPU's resident experts and this build has no "
+              f"multi-GPU path (asked for --gpus {args.gpus})", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import mixture_experts_layer_logits_amd as m
+    import workloads
+
+    w = workloads.WORKLOADS[args.workload]
+    inp = workloads.make_inputs(w)
+    learned = w.routing != "given_uniform"
+    act = m.MOE_F32 if w.dtype == "f32" else m.MOE_BF16
+    gemm = {"f32": m.MOE_F32, "bf16": m.MOE_BF16, "mxfp8": m.MOE_MXFP8}[w.gemm]
+    torch.cuda.set_device(0)
+    L = m.MoEExpertLayer(w.T, w.d, w.f, w.E, w.k, act=act, gemm=gemm)
+    d_inp = {k: (v.cuda() if isinstance(v, torch.Tensor) else v) for k, v in inp.items()}
+    L.forward(d_inp["x"], d_inp["W1"], d_inp["W3"], d_inp["W2"], Wr=d_inp["Wr"], bias=d_inp["router_bias"],
+              topk_idx=d_inp["topk_idx"], gates=d_inp["gates"])
+    calls = step_calls(m, L, d_inp, learned)
+
+    for _ in range(args.warmup):
+        for _, fn in calls:
+            fn()
+    torch.cuda.synchronize()
+
+    ev = {name: [] for name, _ in calls}
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        for name, fn in calls:
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record()
+            fn()
+            b.record()
+            ev[name].append((a, b))
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+
+    per_call_ms = {name: sum(a.elapsed_time(b) for a, b in pairs) / len(pairs) for name, pairs in ev.items()}
+    ms_per_step = elapsed * 1e3 / args.steps
+    tokens_per_s = w.T * args.steps / elapsed
+
+    eb = 4 if w.dtype == "f32" else 2
+    gem, byt = algorithmic_work(w, eb)
+    kernels = {}
+    for name, ms in per_call_ms.items():
+        e = {"ms": round(ms, 4)}
+        if name in gem:
+            e["tflops"] = round(gem[name] / (ms * 1e-3) / 1e12, 1)
+        if name in byt:
+            e["gbs"] = round(byt[name] / (ms * 1e-3) / 1e9, 1)
+        kernels[name] = e
+    dom = max(gem, key=lambda n: per_call_ms[n])
+    achieved = gem[dom] / (per_call_ms[dom] * 1e-3) / 1e12
+    peak = PEAK_TFLOPS[w.gemm]
+    traffic = None
+    digest = kernel_sources_digest(["gemm_bf16.hip", "gemm.h", "common.h"])
+    if os.path.exists(TRAFFIC_FILE):
+        try:
+            rec = json.load(open(TRAFFIC_FILE)).get(f"{w.name}:{dom}")
+            if rec and rec.get("source_digest") == digest:
+                traffic = rec["bytes_per_launch"]
+        except Exception:
+            traffic = None
+    roofline = {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 1), "peak": peak, "unit": "TFLOP/s",
+                "frac": round(achieved / peak, 4), "traffic": traffic,
+                "algorithmic_flops_per_launch": gem[dom]}
+    gemm_ms = sum(per_call_ms[n] for n in gem)
+    out = {
+        "metric": METRIC, "value": round(tokens_per_s, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16" if w.dtype == "bf16" else "f32", "data": "synthetic",
+        "config": {"workload": w.name, "T": w.T, "d": w.d, "f": w.f, "E": w.E, "k": w.k, "routing": w.routing,
+                   "gemm": w.gemm},
+        "roofline": roofline,
+        "grouped_gemm_mfma_frac_all6": round(sum(gem.values()) / (gemm_ms * 1e-3) / 1e12 / peak, 4),
+        "kernels": kernels,
+        "expert_load": {"max": int(L.counts.max().item()), "mean": w.T * w.k / w.E,
+                        "empty": int((L.counts == 0).sum().item())},
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w, inp, min(args.cpu_sample_tokens, w.T))
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

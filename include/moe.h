@@ -176,9 +176,10 @@ moe_status moe_route_bwd(const moe_shape* s, const float* dgates, const float* g
                          const int32_t* topk_idx, float* dlogits, void* stream);
 
 /* Router backward: dx_r = dlogits Wr ([T, d] act, written), dWr = dlogits^T x ([E, d]
- * float, written). */
+ * float, written).  The reduction over T is split into partial sums held in ws and added
+ * in a fixed order (deterministic). */
 moe_status moe_router_bwd(const moe_shape* s, const void* x, const void* Wr, const float* dlogits,
-                          void* dx_r, float* dWr, void* stream);
+                          void* dx_r, float* dWr, void* ws, size_t ws_bytes, void* stream);
 
 /* Un-permute and sum: dx[t] = dx_r[t] + sum_j dx_perm[slot_row[t, j]] (float accumulation,
  * dx_r may be NULL).  dx_perm [R, d], dx_r [T, d], dx [T, d] act. */

@@ -63,7 +63,7 @@ _SIGS = {
     "moe_ffn_dgrad1": [_VP, _VP, _VP, _VP, _VP, _VP, _SZ, _VP],
     "moe_ffn_wgrad1": [_VP, _VP, _VP, _VP, _VP, _VP, _SZ, _VP],
     "moe_route_bwd": [_VP, _VP, _VP, _VP, _VP],
-    "moe_router_bwd": [_VP, _VP, _VP, _VP, _VP, _VP],
+    "moe_router_bwd": [_VP, _VP, _VP, _VP, _VP, _VP, _SZ, _VP],
     "moe_permute_bwd": [_VP, _VP, _VP, _VP, _VP],
 }
 EXPORTED = sorted(list(_SIGS) + ["moe_mx_quantize", "moe_workspace_size", "moe_status_str"])
@@ -196,8 +196,8 @@ def moe_route_bwd(shape, dgates, gates, topk_idx, dlogits, stream=None):
     _call("moe_route_bwd", shape, dgates, gates, topk_idx, dlogits, stream=stream)
 
 
-def moe_router_bwd(shape, x, Wr, dlogits, dx_r, dWr, stream=None):
-    _call("moe_router_bwd", shape, x, Wr, dlogits, dx_r, dWr, stream=stream)
+def moe_router_bwd(shape, x, Wr, dlogits, dx_r, dWr, ws, stream=None):
+    _call("moe_router_bwd", shape, x, Wr, dlogits, dx_r, dWr, ws, _ws(ws), stream=stream)
 
 
 def moe_permute_bwd(shape, dx_perm, slot_row, dx_r, dx, stream=None):

@@ -104,6 +104,10 @@ const char* moe_status_str(int status) {
 size_t moe_workspace_size(const moe_shape* s) {
   if (check_shape(s) != MOE_OK) return 0;
   size_t b = route_workspace_bytes(s->T, s->E, s->k);
+  if (s->act == MOE_BF16) {
+    const size_t r = router_dw_workspace_bytes(s->T, s->d, s->E);
+    if (r > b) b = r;
+  }
   if (s->gemm == MOE_MXFP8) {
     const size_t m = mx_workspace_bytes(s->T * s->k, s->d, s->f, s->E);
     if (m > b) b = m;
@@ -317,7 +321,7 @@ moe_status moe_route_bwd(const moe_shape* s, const float* dgates, const float* g
 }
 
 moe_status moe_router_bwd(const moe_shape* s, const void* x, const void* Wr, const float* dlogits, void* dx_r,
-                          float* dWr, void* st) {
+                          float* dWr, void* ws, size_t ws_bytes, void* st) {
   MOE_TRY(check_shape(s));
   MOE_TRY(check_ptrs({Wr, dWr}));
   MOE_TRY(check_rows(s, {x, dx_r}));
@@ -327,9 +331,11 @@ moe_status moe_router_bwd(const moe_shape* s, const void* x, const void* Wr, con
       return MOE_ELAUNCH;
     return launched(router_dw_f32(s->T, s->d, s->E, dlogits, (const float*)x, dWr, S(st)));
   }
+  if (!ws) return MOE_ENULL;
+  if (ws_bytes < router_dw_workspace_bytes(s->T, s->d, s->E)) return MOE_EWORKSPACE;
   if (s->T > 0 && router_dx_bf16(s->T, s->d, s->E, dlogits, (const bf16_t*)Wr, (bf16_t*)dx_r, S(st)) != hipSuccess)
     return MOE_ELAUNCH;
-  return launched(router_dw_bf16(s->T, s->d, s->E, dlogits, (const bf16_t*)x, dWr, S(st)));
+  return launched(router_dw_bf16(s->T, s->d, s->E, dlogits, (const bf16_t*)x, dWr, ws, S(st)));
 }
 
 moe_status moe_permute_bwd(const moe_shape* s, const void* dx_perm, const int32_t* slot_row, const void* dx_r,

@@ -19,6 +19,10 @@
 // as loaded and read with the gfx950 transpose read ds_read_b64_tr_b16, so no operand
 // is ever transposed in HBM.  MFMA: v_mfma_f32_32x32x16_bf16 (lane l holds row l%32,
 // k = 8*(l/32)..+7 of A; column l%32 of B; accumulator row 8*(i/4)+4*(l/32)+i%4).
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+
 #include "common.h"
 #include "gemm.h"
 
@@ -147,9 +151,8 @@ __global__ void __launch_bounds__(Cfg::NT) grouped_gemm_kernel(const Prob p) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wave_m = wave / Cfg::WAVES_N, wave_n = wave % Cfg::WAVES_N;
   const int E = p.E;
-  // segment e spans [seg(e), seg(e+1)); without offsets there is one segment over all rows
-  const int total_rows = Prob::GROUP == Group::M ? p.M : p.K;
-  auto seg = [&](int e) { return p.offsets ? p.offsets[e] : (e == 0 ? 0 : total_rows); };
+  // segment e spans [seg(e), seg(e+1)) rows of the grouped dimension
+  auto seg = [&](int e) { return p.seg(e); };
 
   // ---- tile map
   int total_tiles;
@@ -295,19 +298,31 @@ __global__ void __launch_bounds__(Cfg::NT) grouped_gemm_kernel(const Prob p) {
 }
 
 // ---------------------------------------------------------------------------------------
-// Problem descriptions (operand addressing + epilogue) for each GEMM of the layer
+// Problem descriptions (operand addressing + epilogue) for each GEMM of the layer.
+// seg(e): start row of group e -- from the routing offsets, or uniform splits of
+// seg_len rows (single-group GEMMs and split reductions).
 // ---------------------------------------------------------------------------------------
+struct ProbBase {
+  int M = 0, N = 0, K = 0, E = 1;
+  const int* offsets = nullptr;
+  int seg_len = 0, seg_total = 0;
+  __device__ int seg(int e) const {
+    if (offsets) return offsets[e];
+    const int64_t v = (int64_t)e * seg_len;
+    return v < seg_total ? (int)v : seg_total;
+  }
+};
+
 // Forward GEMM1 with the SwiGLU epilogue: [a | b] = X_e [W1_e | W3_e]^T, the B tile's
 // 32-column blocks alternate W1 / W3 rows so each wave holds a and b of the same column.
-struct ProbGemm1 {
+struct ProbGemm1 : ProbBase {
   using TA = bf16_t;
   static constexpr Group GROUP = Group::M;
   static constexpr bool A_KC = true, B_KC = true;
   static constexpr Epi EPI = Epi::SwiGLU;
-  int M, N, K, E, f;
-  const int* offsets;
-  const bf16_t* X; const bf16_t* W1; const bf16_t* W3;
-  bf16_t* ab; bf16_t* h;
+  int f = 0;
+  const bf16_t* X = nullptr; const bf16_t* W1 = nullptr; const bf16_t* W3 = nullptr;
+  bf16_t* ab = nullptr; bf16_t* h = nullptr;
   __device__ const bf16_t* a_row(int, int m) const { return X + (int64_t)m * K; }
   __device__ const bf16_t* b_row(int e, int n) const {
     const int blk = n >> 5, col = (blk >> 1) * 32 + (n & 31);
@@ -324,30 +339,26 @@ struct ProbGemm1 {
 };
 
 // y_perm = h W2_e^T
-struct ProbGemm2 {
+struct ProbGemm2 : ProbBase {
   using TA = bf16_t;
   static constexpr Group GROUP = Group::M;
   static constexpr bool A_KC = true, B_KC = true;
   static constexpr Epi EPI = Epi::Store;
-  int M, N, K, E;
-  const int* offsets;
-  const bf16_t* Hm; const bf16_t* W2;
-  bf16_t* Y;
+  const bf16_t* Hm = nullptr; const bf16_t* W2 = nullptr;
+  bf16_t* Y = nullptr;
   __device__ const bf16_t* a_row(int, int m) const { return Hm + (int64_t)m * K; }
   __device__ const bf16_t* b_row(int e, int n) const { return W2 + ((int64_t)e * N + n) * K; }
   __device__ void epilogue(int, int m, int n, float v) const { Y[(int64_t)m * N + n] = f2bf(v); }
 };
 
 // dh = dy_e W2_e (B = W2_e read [k=d][n=f]) with the SwiGLU-gradient epilogue
-struct ProbDgrad2 {
+struct ProbDgrad2 : ProbBase {
   using TA = bf16_t;
   static constexpr Group GROUP = Group::M;
   static constexpr bool A_KC = true, B_KC = false;
   static constexpr Epi EPI = Epi::DSwiGLU;
-  int M, N, K, E;  // N = f, K = d
-  const int* offsets;
-  const bf16_t* dY; const bf16_t* W2; const bf16_t* ab;
-  bf16_t* dab;
+  const bf16_t* dY = nullptr; const bf16_t* W2 = nullptr; const bf16_t* ab = nullptr;
+  bf16_t* dab = nullptr;
   __device__ const bf16_t* a_row(int, int m) const { return dY + (int64_t)m * K; }
   __device__ const bf16_t* b_row(int e, int k) const { return W2 + ((int64_t)e * K + k) * N; }
   __device__ void epilogue(int, int m, int n, float dh) const {
@@ -361,30 +372,27 @@ struct ProbDgrad2 {
 };
 
 // dW2_e[d, f] = dy_e^T h_e: A[m=d][k=r] = dy[r][d], B[k=r][n=f] = h[r][f]
-struct ProbWgrad2 {
+struct ProbWgrad2 : ProbBase {
   using TA = bf16_t;
   static constexpr Group GROUP = Group::K;
   static constexpr bool A_KC = false, B_KC = false;
   static constexpr Epi EPI = Epi::Store;
-  int M, N, K, E;  // M = d, N = f
-  const int* offsets;
-  const bf16_t* dY; const bf16_t* Hm;
-  bf16_t* dW2;
+  const bf16_t* dY = nullptr; const bf16_t* Hm = nullptr;
+  bf16_t* dW2 = nullptr;
   __device__ const bf16_t* a_row(int, int r) const { return dY + (int64_t)r * M; }
   __device__ const bf16_t* b_row(int, int r) const { return Hm + (int64_t)r * N; }
   __device__ void epilogue(int e, int m, int n, float v) const { dW2[((int64_t)e * M + m) * N + n] = f2bf(v); }
 };
 
 // dx_e = [da | db] [W1_e ; W3_e]: K = 2f, B rows k < f from W1, else W3 (read [k][n=d])
-struct ProbDgrad1 {
+struct ProbDgrad1 : ProbBase {
   using TA = bf16_t;
   static constexpr Group GROUP = Group::M;
   static constexpr bool A_KC = true, B_KC = false;
   static constexpr Epi EPI = Epi::Store;
-  int M, N, K, E, f;  // N = d, K = 2f
-  const int* offsets;
-  const bf16_t* dab; const bf16_t* W1; const bf16_t* W3;
-  bf16_t* dX;
+  int f = 0;
+  const bf16_t* dab = nullptr; const bf16_t* W1 = nullptr; const bf16_t* W3 = nullptr;
+  bf16_t* dX = nullptr;
   __device__ const bf16_t* a_row(int, int m) const { return dab + (int64_t)m * K; }
   __device__ const bf16_t* b_row(int e, int k) const {
     return k < f ? W1 + ((int64_t)e * f + k) * N : W3 + ((int64_t)e * f + (k - f)) * N;
@@ -393,15 +401,14 @@ struct ProbDgrad1 {
 };
 
 // [dW1_e ; dW3_e] [2f, d] = [da | db]_e^T X_e: A[m][k=r] = dab[r][m], B[k=r][n] = x_perm[r][n]
-struct ProbWgrad1 {
+struct ProbWgrad1 : ProbBase {
   using TA = bf16_t;
   static constexpr Group GROUP = Group::K;
   static constexpr bool A_KC = false, B_KC = false;
   static constexpr Epi EPI = Epi::Store;
-  int M, N, K, E, f;  // M = 2f, N = d
-  const int* offsets;
-  const bf16_t* dab; const bf16_t* X;
-  bf16_t* dW1; bf16_t* dW3;
+  int f = 0;
+  const bf16_t* dab = nullptr; const bf16_t* X = nullptr;
+  bf16_t* dW1 = nullptr; bf16_t* dW3 = nullptr;
   __device__ const bf16_t* a_row(int, int r) const { return dab + (int64_t)r * M; }
   __device__ const bf16_t* b_row(int, int r) const { return X + (int64_t)r * N; }
   __device__ void epilogue(int e, int m, int n, float v) const {
@@ -411,115 +418,194 @@ struct ProbWgrad1 {
 };
 
 // Router scores: logits[t, e] = x[t] . Wr[e] + bias[e]  (single group over T rows)
-struct ProbRouterFwd {
+struct ProbRouterFwd : ProbBase {
   using TA = bf16_t;
   static constexpr Group GROUP = Group::M;
   static constexpr bool A_KC = true, B_KC = true;
   static constexpr Epi EPI = Epi::Store;
-  int M, N, K, E;  // M = T, N = experts, K = d; E = 1 group
-  const int* offsets;
-  const bf16_t* X; const bf16_t* Wr; const float* bias;
-  float* L;
+  const bf16_t* X = nullptr; const bf16_t* Wr = nullptr; const float* bias = nullptr;
+  float* L = nullptr;
   __device__ const bf16_t* a_row(int, int m) const { return X + (int64_t)m * K; }
   __device__ const bf16_t* b_row(int, int n) const { return Wr + (int64_t)n * K; }
   __device__ void epilogue(int, int m, int n, float v) const { L[(int64_t)m * N + n] = v + (bias ? bias[n] : 0.f); }
 };
 
 // dx_r = dlogits Wr: A = dlogits [T][E] float (rounded to bf16 on staging), B[k=e][n] = Wr[e][n]
-struct ProbRouterDx {
+struct ProbRouterDx : ProbBase {
   using TA = float;
   static constexpr Group GROUP = Group::M;
   static constexpr bool A_KC = true, B_KC = false;
   static constexpr Epi EPI = Epi::Store;
-  int M, N, K, E;  // M = T, N = d, K = experts
-  const int* offsets;
-  const float* dL; const bf16_t* Wr;
-  bf16_t* dX;
+  const float* dL = nullptr; const bf16_t* Wr = nullptr;
+  bf16_t* dX = nullptr;
   __device__ const float* a_row(int, int m) const { return dL + (int64_t)m * K; }
   __device__ const bf16_t* b_row(int, int k) const { return Wr + (int64_t)k * N; }
   __device__ void epilogue(int, int m, int n, float v) const { dX[(int64_t)m * N + n] = f2bf(v); }
 };
 
-// dWr[e, i] = sum_t dlogits[t, e] x[t, i]: one group spanning all T rows
-struct ProbRouterDw {
+// Partial router weight gradients: split s of the T rows writes
+// part[s][e][i] = sum_{t in split s} dlogits[t, e] x[t, i]; a second kernel sums splits.
+struct ProbRouterDwSplit : ProbBase {
   using TA = float;
   static constexpr Group GROUP = Group::K;
   static constexpr bool A_KC = false, B_KC = false;
   static constexpr Epi EPI = Epi::Store;
-  int M, N, K, E;  // M = experts, N = d
-  const int* offsets;
-  const float* dL; const bf16_t* X;
-  float* dW;
+  const float* dL = nullptr; const bf16_t* X = nullptr;
+  float* part = nullptr;
   __device__ const float* a_row(int, int r) const { return dL + (int64_t)r * M; }
   __device__ const bf16_t* b_row(int, int r) const { return X + (int64_t)r * N; }
-  __device__ void epilogue(int, int m, int n, float v) const { dW[(int64_t)m * N + n] = v; }
+  __device__ void epilogue(int e, int m, int n, float v) const { part[((int64_t)e * M + m) * N + n] = v; }
 };
 
+namespace {
+// dW[i] = sum over splits s (in order) of part[s][i]
+__global__ void sum_splits_kernel(int64_t n, int nsplit, const float* __restrict__ part, float* __restrict__ out) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n) return;
+  float acc = 0.f;
+  for (int s = 0; s < nsplit; s++) acc += part[(int64_t)s * n + i];
+  out[i] = acc;
+}
+}  // namespace
+
 // ---------------------------------------------------------------------------------------
-// Launchers
+// Launchers: tile shape per GEMM (MOE_TILE_<GEMM>=128x256 etc. overrides the default)
 // ---------------------------------------------------------------------------------------
-using Cfg128 = TileCfg<128, 128, 2, 2>;
+enum class Tile { t128x128, t128x256, t256x128, t256x256, t64x128, t32x128 };
+
+static bool parse_tile(const char* v, Tile* t) {
+  if (!v) return false;
+  const struct { const char* s; Tile t; } tab[] = {{"128x128", Tile::t128x128}, {"128x256", Tile::t128x256},
+                                                  {"256x128", Tile::t256x128}, {"256x256", Tile::t256x256},
+                                                  {"64x128", Tile::t64x128},   {"32x128", Tile::t32x128}};
+  for (const auto& e : tab)
+    if (strcmp(v, e.s) == 0) { *t = e.t; return true; }
+  return false;
+}
+
+static Tile tile_for(const char* name, Tile dflt) {
+  char key[64];
+  snprintf(key, sizeof key, "MOE_TILE_%s", name);
+  Tile t = dflt;
+  if (!parse_tile(getenv(key), &t)) parse_tile(getenv("MOE_TILE"), &t);
+  return t;
+}
 
 template <class Cfg, class Prob>
-static hipError_t launch(const Prob& p, int tile_bound, hipStream_t st) {
-  int G = device_cu_count() * 2;
-  if (tile_bound < G) G = tile_bound;
+static hipError_t launch_cfg(const Prob& p, hipStream_t st) {
+  const auto kern = grouped_gemm_kernel<Cfg, Prob>;
+  static int occ = 0;  // resident workgroups per CU for this instantiation
+  if (occ == 0) {
+    int o = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&o, kern, Cfg::NT, 0) != hipSuccess || o < 1) o = 1;
+    occ = o;
+  }
+  int64_t bound;
+  const int64_t ntn = (p.N + Cfg::BN - 1) / Cfg::BN;
+  if constexpr (Prob::GROUP == Group::M) bound = ((int64_t)p.M / Cfg::BM + p.E) * ntn;
+  else bound = (int64_t)p.E * ((p.M + Cfg::BM - 1) / Cfg::BM) * ntn;
+  int64_t G = (int64_t)device_cu_count() * occ;
+  if (bound < G) G = bound;
   G = ((G + 7) / 8) * 8;
   if (G < 8) G = 8;
-  hipLaunchKernelGGL((grouped_gemm_kernel<Cfg, Prob>), dim3(G), dim3(Cfg::NT), 0, st, p);
+  hipLaunchKernelGGL(kern, dim3((unsigned)G), dim3(Cfg::NT), 0, st, p);
   return hipGetLastError();
 }
 
-static int tiles_m_bound(int R, int E, int BM, int N, int BN) {
-  int64_t b = ((int64_t)R / BM + E) * ((N + BN - 1) / BN);
-  return b > (1 << 30) ? (1 << 30) : (int)b;
+template <class Prob>
+static hipError_t launch(Tile t, const Prob& p, hipStream_t st) {
+  switch (t) {
+    case Tile::t128x256: return launch_cfg<TileCfg<128, 256, 2, 2>>(p, st);
+    case Tile::t256x128: return launch_cfg<TileCfg<256, 128, 2, 2>>(p, st);
+    case Tile::t256x256: return launch_cfg<TileCfg<256, 256, 2, 2>>(p, st);
+    case Tile::t64x128: return launch_cfg<TileCfg<64, 128, 1, 4>>(p, st);
+    case Tile::t32x128: return launch_cfg<TileCfg<32, 128, 1, 4>>(p, st);
+    default: return launch_cfg<TileCfg<128, 128, 2, 2>>(p, st);
+  }
 }
 
 hipError_t gemm1_fwd_bf16(const GemmShape& s, const int* offsets, const bf16_t* X, const bf16_t* W1,
                           const bf16_t* W3, bf16_t* ab, bf16_t* h, hipStream_t st) {
-  ProbGemm1 p{s.R, 2 * s.f, s.d, s.E, s.f, offsets, X, W1, W3, ab, h};
-  return launch<Cfg128>(p, tiles_m_bound(s.R, s.E, Cfg128::BM, p.N, Cfg128::BN), st);
+  ProbGemm1 p;
+  p.M = s.R; p.N = 2 * s.f; p.K = s.d; p.E = s.E; p.offsets = offsets; p.f = s.f;
+  p.X = X; p.W1 = W1; p.W3 = W3; p.ab = ab; p.h = h;
+  return launch(tile_for("GEMM1", Tile::t128x128), p, st);
 }
 hipError_t gemm2_fwd_bf16(const GemmShape& s, const int* offsets, const bf16_t* H, const bf16_t* W2, bf16_t* Y,
                           hipStream_t st) {
-  ProbGemm2 p{s.R, s.d, s.f, s.E, offsets, H, W2, Y};
-  return launch<Cfg128>(p, tiles_m_bound(s.R, s.E, Cfg128::BM, p.N, Cfg128::BN), st);
+  ProbGemm2 p;
+  p.M = s.R; p.N = s.d; p.K = s.f; p.E = s.E; p.offsets = offsets;
+  p.Hm = H; p.W2 = W2; p.Y = Y;
+  return launch(tile_for("GEMM2", Tile::t128x128), p, st);
 }
 hipError_t dgrad2_bf16(const GemmShape& s, const int* offsets, const bf16_t* dY, const bf16_t* W2,
                        const bf16_t* ab, bf16_t* dab, hipStream_t st) {
-  ProbDgrad2 p{s.R, s.f, s.d, s.E, offsets, dY, W2, ab, dab};
-  return launch<Cfg128>(p, tiles_m_bound(s.R, s.E, Cfg128::BM, p.N, Cfg128::BN), st);
+  ProbDgrad2 p;
+  p.M = s.R; p.N = s.f; p.K = s.d; p.E = s.E; p.offsets = offsets;
+  p.dY = dY; p.W2 = W2; p.ab = ab; p.dab = dab;
+  return launch(tile_for("DGRAD2", Tile::t128x128), p, st);
 }
 hipError_t wgrad2_bf16(const GemmShape& s, const int* offsets, const bf16_t* H, const bf16_t* dY, bf16_t* dW2,
                        hipStream_t st) {
-  ProbWgrad2 p{s.d, s.f, s.R, s.E, offsets, dY, H, dW2};
-  int bound = s.E * ((s.d + 127) / 128) * ((s.f + 127) / 128);
-  return launch<Cfg128>(p, bound, st);
+  ProbWgrad2 p;
+  p.M = s.d; p.N = s.f; p.K = s.R; p.E = s.E; p.offsets = offsets;
+  p.dY = dY; p.Hm = H; p.dW2 = dW2;
+  return launch(tile_for("WGRAD2", Tile::t128x128), p, st);
 }
 hipError_t dgrad1_bf16(const GemmShape& s, const int* offsets, const bf16_t* dab, const bf16_t* W1,
                        const bf16_t* W3, bf16_t* dX, hipStream_t st) {
-  ProbDgrad1 p{s.R, s.d, 2 * s.f, s.E, s.f, offsets, dab, W1, W3, dX};
-  return launch<Cfg128>(p, tiles_m_bound(s.R, s.E, Cfg128::BM, p.N, Cfg128::BN), st);
+  ProbDgrad1 p;
+  p.M = s.R; p.N = s.d; p.K = 2 * s.f; p.E = s.E; p.offsets = offsets; p.f = s.f;
+  p.dab = dab; p.W1 = W1; p.W3 = W3; p.dX = dX;
+  return launch(tile_for("DGRAD1", Tile::t128x128), p, st);
 }
 hipError_t wgrad1_bf16(const GemmShape& s, const int* offsets, const bf16_t* X, const bf16_t* dab, bf16_t* dW1,
                        bf16_t* dW3, hipStream_t st) {
-  ProbWgrad1 p{2 * s.f, s.d, s.R, s.E, s.f, offsets, dab, X, dW1, dW3};
-  int bound = s.E * ((2 * s.f + 127) / 128) * ((s.d + 127) / 128);
-  return launch<Cfg128>(p, bound, st);
+  ProbWgrad1 p;
+  p.M = 2 * s.f; p.N = s.d; p.K = s.R; p.E = s.E; p.offsets = offsets; p.f = s.f;
+  p.dab = dab; p.X = X; p.dW1 = dW1; p.dW3 = dW3;
+  return launch(tile_for("WGRAD1", Tile::t128x128), p, st);
 }
 hipError_t router_fwd_bf16(int T, int d, int E, const bf16_t* X, const bf16_t* Wr, const float* bias, float* L,
                            hipStream_t st) {
-  ProbRouterFwd p{T, E, d, 1, nullptr, X, Wr, bias, L};
-  return launch<Cfg128>(p, tiles_m_bound(T, 1, 128, E, 128), st);
+  ProbRouterFwd p;
+  p.M = T; p.N = E; p.K = d; p.E = 1; p.seg_len = T; p.seg_total = T;
+  p.X = X; p.Wr = Wr; p.bias = bias; p.L = L;
+  return launch(tile_for("ROUTER_FWD", Tile::t32x128), p, st);
 }
 hipError_t router_dx_bf16(int T, int d, int E, const float* dL, const bf16_t* Wr, bf16_t* dX, hipStream_t st) {
-  ProbRouterDx p{T, d, E, 1, nullptr, dL, Wr, dX};
-  return launch<Cfg128>(p, tiles_m_bound(T, 1, 128, d, 128), st);
+  ProbRouterDx p;
+  p.M = T; p.N = d; p.K = E; p.E = 1; p.seg_len = T; p.seg_total = T;
+  p.dL = dL; p.Wr = Wr; p.dX = dX;
+  return launch(tile_for("ROUTER_DX", Tile::t128x128), p, st);
 }
-hipError_t router_dw_bf16(int T, int d, int E, const float* dL, const bf16_t* X, float* dW, hipStream_t st) {
-  ProbRouterDw p{E, d, T, 1, nullptr, dL, X, dW};
-  int bound = ((E + 127) / 128) * ((d + 127) / 128);
-  return launch<Cfg128>(p, bound, st);
+
+// Split count of the router weight gradient: about 512 output tiles in flight (two per
+// compute unit of a 256-CU device), splits of at least 64 rows.  Host-only arithmetic.
+int router_dw_splits(int T, int d, int E) {
+  const int tiles = ((E + 127) / 128) * ((d + 127) / 128);
+  int s = (512 + tiles - 1) / tiles;
+  const int max_s = (T + 63) / 64;
+  if (s > max_s) s = max_s;
+  return s < 1 ? 1 : s;
+}
+size_t router_dw_workspace_bytes(int T, int d, int E) {
+  return (size_t)router_dw_splits(T, d, E) * E * d * sizeof(float);
+}
+hipError_t router_dw_bf16(int T, int d, int E, const float* dL, const bf16_t* X, float* dW, void* ws,
+                          hipStream_t st) {
+  int ns = router_dw_splits(T, d, E);
+  const int seg_len = ((T + ns - 1) / ns + 63) / 64 * 64;
+  ns = T == 0 ? 1 : (T + seg_len - 1) / seg_len;
+  ProbRouterDwSplit p;
+  p.M = E; p.N = d; p.K = T; p.E = ns; p.seg_len = seg_len; p.seg_total = T;
+  p.dL = dL; p.X = X; p.part = ns == 1 ? dW : static_cast<float*>(ws);
+  hipError_t err = launch(tile_for("ROUTER_DW", Tile::t128x128), p, st);
+  if (err != hipSuccess || ns == 1) return err;
+  const int64_t n = (int64_t)E * d;
+  hipLaunchKernelGGL(sum_splits_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, n, ns,
+                     static_cast<const float*>(ws), dW);
+  return hipGetLastError();
 }
 
 }  // namespace moe

@@ -101,7 +101,7 @@ class MoEExpertLayer:
         dx_r = None
         if self.learned:
             moe_route_bwd(s, self.dgates, g, self.topk_idx, self.dlogits)
-            moe_router_bwd(s, x, Wr, self.dlogits, self.dx_r, self.dWr)
+            moe_router_bwd(s, x, Wr, self.dlogits, self.dx_r, self.dWr, self.ws)
             dx_r = self.dx_r
         moe_permute_bwd(s, self.dx_perm, self.slot_row, dx_r, self.dx)
         return self.dx
