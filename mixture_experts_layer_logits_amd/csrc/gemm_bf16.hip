@@ -13,7 +13,7 @@
 //   GROUP_K  the reduction is grouped by expert (weight-gradient GEMMs):
 //            C_e[m, n] = sum_{r in [offsets[e], offsets[e+1])} A[r, m] * B[r, n].
 //
-// Tiles are BM x BN with BK = 64, staged through LDS in two buffers.  An operand whose
+// Register-staged kernel (float-A router GEMMs): BM x BN tiles, BK = 64, two LDS buffers.  An operand whose
 // reduction axis is contiguous in memory ("K-contiguous") is kept [mn][k] in LDS and
 // read with 16-byte ds_read_b128; an operand contiguous along M or N is kept [k][mn]
 // as loaded and read with the gfx950 transpose read ds_read_b64_tr_b16, so no operand
@@ -22,6 +22,7 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <type_traits>
 
 #include "common.h"
 #include "gemm.h"
@@ -283,7 +284,7 @@ __global__ void __launch_bounds__(Cfg::NT) grouped_gemm_kernel(const Prob p) {
 #pragma unroll
           for (int j = 0; j < WTN; j += 2) {
             const int hcol = n0 / 2 + ((wave_n * WTN + j) >> 1) * 32 + (lane & 31);
-            p.epilogue_swiglu(m, hcol, acc[i][j][r], acc[i][j + 1][r]);
+            if (hcol < p.N / 2) p.epilogue_swiglu(m, hcol, acc[i][j][r], acc[i][j + 1][r]);
           }
         } else {
 #pragma unroll
@@ -469,32 +470,322 @@ __global__ void sum_splits_kernel(int64_t n, int nsplit, const float* __restrict
 }  // namespace
 
 // ---------------------------------------------------------------------------------------
+// Pipelined kernel for bf16 operands.  Global loads run two k-steps ahead of the MFMAs in
+// two register stages and are written to one of two LDS buffers while the other one is
+// being read (one barrier per k-step).  Loads go through buffer resources that start at a
+// 1 KB segment's first row and end at its last valid byte, so rows past a segment end
+// (ragged experts, reductions that stop mid-tile) and columns past the matrix edge read
+// as zero without any out-of-range access.
+//
+// LDS tiles are unpadded and XOR-swizzled in 16-byte chunks (see swz): 16 consecutive
+// rows read at one logical chunk (K-contiguous tiles, ds_read_b128) or 4 consecutive rows
+// read at a pair of chunks (MN-contiguous tiles, ds_read_b64_tr_b16) fall on distinct
+// banks of the 64-bank LDS.
+// ---------------------------------------------------------------------------------------
+namespace {
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+template <bool KC, int BMN, int TK, int NW>
+struct PipeOperand {
+  static constexpr int TILE_BYTES = BMN * TK * 2;    // TK x BMN bf16
+  static constexpr int SEGS = TILE_BYTES / 1024;     // one load instruction each
+  static constexpr int ROW_BYTES = KC ? TK * 2 : BMN * 2;
+  static constexpr int ROWS_PER_SEG = 1024 / ROW_BYTES;
+  static constexpr int CPR = ROW_BYTES / 16;         // 16-byte chunks per LDS row
+  static_assert(SEGS % NW == 0, "every wave issues the same number of segments");
+  static_assert(KC || CPR >= 4, "MN-contiguous tiles need at least 64 columns");
+
+  // physical 16-byte chunk of logical chunk c in tile row r.  16 consecutive rows read
+  // at one logical chunk (K-contiguous) or 4 consecutive rows read at a pair of chunks
+  // (MN-contiguous, transpose reads) fall on distinct banks of a 64-bank LDS.
+  static __device__ __forceinline__ int swz(int r, int c) {
+    if constexpr (KC) {
+      if constexpr (CPR == 8) return c ^ ((r >> 1) & 7);
+      else return c ^ ((r >> 2) & 3);
+    } else {
+      return c ^ ((4 * (r & 3)) & (CPR - 1));
+    }
+  }
+
+  // Register staging of one tile: this thread's 16-byte chunks.  Chunk q = tid + NT*i
+  // lands at LDS byte q*16, i.e. (row q / CPR, physical chunk q % CPR); the thread fetches
+  // the logical chunk that the swizzle maps there.  The 64 chunks of one wave form one
+  // 1 KB segment, so the bounds (a buffer resource) are wave-uniform.
+  static constexpr int PER_THREAD = SEGS / NW;
+  typedef int v4i __attribute__((ext_vector_type(4)));
+  v4i reg[PER_THREAD];
+
+  // rows are mn (KC) or k (MN-contiguous); rowptr(r) -> element (r, 0); rows r >= row_end
+  // read as zero; KC: columns start at col0 (always in range); MN: columns [col0, col_end)
+  // are valid.
+  template <class RowPtr>
+  __device__ __forceinline__ void load(RowPtr rowptr, int row0, int row_end, int col0, int col_end, int wave,
+                                       int lane, bool live = true) {
+#pragma unroll
+    for (int i = 0; i < PER_THREAD; i++) {
+      const int s = wave + NW * i;  // wave is wave-uniform (readfirstlane), so the resource stays scalar
+      const int r0 = row0 + s * ROWS_PER_SEG;
+      const bf16_t* base = rowptr(r0) + col0;
+      const int64_t stride = rowptr(r0 + 1) - rowptr(r0);
+      int valid = live ? row_end - r0 : 0;
+      valid = valid < 0 ? 0 : (valid > ROWS_PER_SEG ? ROWS_PER_SEG : valid);
+      uint32_t bytes = 0;
+      if (valid > 0) {
+        const int last_cols = KC ? TK : (col_end - col0 < BMN ? col_end - col0 : BMN);
+        bytes = (uint32_t)((valid - 1) * stride * 2 + last_cols * 2);
+      }
+      const int r = lane / CPR, p = lane % CPR;
+      const int c = swz(s * ROWS_PER_SEG + r, p);
+      const uint32_t voff = (uint32_t)(r * stride * 2 + c * 16);
+      // a dead stage (past the reduction) is a zero-byte resource: no memory is touched
+      reg[i] = __builtin_amdgcn_raw_buffer_load_b128(make_rsrc(base, bytes), voff, 0, 0);
+    }
+  }
+  __device__ __forceinline__ void store(char* lds_tile, int wave, int lane) const {
+#pragma unroll
+    for (int i = 0; i < PER_THREAD; i++)
+      *reinterpret_cast<v4i*>(lds_tile + (wave + NW * i) * 1024 + lane * 16) = reg[i];
+  }
+
+  // MFMA operand fragment for k-step kk (16 deep): 8 consecutive k of row/column mn0 + lane%32
+  static __device__ __forceinline__ bf16x8 frag(const char* lds_tile, int kk, int mn0, int lane) {
+    if constexpr (KC) {
+      const int r = mn0 + (lane & 31);
+      const int c = 2 * kk + (lane >> 5);
+      const uint4 q = *reinterpret_cast<const uint4*>(lds_tile + r * ROW_BYTES + (swz(r, c) << 4));
+      return __builtin_bit_cast(bf16x8, q);
+    } else {
+      const int g = lane >> 4, L = lane & 15;
+      const int k = 16 * kk + 8 * (g >> 1) + (L >> 2);
+      const int b = (mn0 + 16 * (g & 1) + 4 * (L & 3)) * 2;
+      const int off = k * ROW_BYTES + (swz(k, b >> 4) << 4) + (b & 15);
+      const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(lds_tile + off));
+      const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(lds_tile + off + 4 * ROW_BYTES));
+      typedef short i16x8 __attribute__((ext_vector_type(8)));
+      const i16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      return __builtin_bit_cast(bf16x8, v);
+    }
+  }
+};
+
+}  // namespace
+
+template <class Cfg, class Prob, int TK>
+__global__ void __launch_bounds__(Cfg::NT) grouped_gemm_pipe_kernel(const Prob p) {
+  constexpr int BM = Cfg::BM, BN = Cfg::BN, NT = Cfg::NT;
+  constexpr int WTM = Cfg::WTM, WTN = Cfg::WTN;
+  constexpr int NW = NT / 64;
+  using OA = PipeOperand<Prob::A_KC, BM, TK, NW>;
+  using OB = PipeOperand<Prob::B_KC, BN, TK, NW>;
+  constexpr int STAGE_BYTES = OA::TILE_BYTES + OB::TILE_BYTES;
+  __shared__ __attribute__((aligned(1024))) char sm0[STAGE_BYTES];
+  __shared__ __attribute__((aligned(1024))) char sm1[STAGE_BYTES];
+  __shared__ int s_map[kMaxExperts + 1];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wave_m = wave / Cfg::WAVES_N, wave_n = wave % Cfg::WAVES_N;
+  const int E = p.E;
+  auto seg = [&](int e) { return p.seg(e); };
+
+  int total_tiles;
+  const int ntn = (p.N + BN - 1) / BN;
+  if constexpr (Prob::GROUP == Group::M) {
+    if (wave == 0) {
+      int carry = 0;
+      for (int base = 0; base < E; base += kWave) {
+        const int e = base + lane;
+        const int x = e < E ? (seg(e + 1) - seg(e) + BM - 1) / BM : 0;
+        int incl = x;
+#pragma unroll
+        for (int o = 1; o < kWave; o <<= 1) {
+          const int y = __shfl_up(incl, o, kWave);
+          if (lane >= o) incl += y;
+        }
+        if (e < E) s_map[e] = carry + incl - x;
+        carry += __shfl(incl, kWave - 1, kWave);
+      }
+      if (lane == 0) s_map[E] = carry;
+    }
+    __syncthreads();
+    total_tiles = s_map[E] * ntn;
+  } else {
+    for (int e = tid; e < E; e += NT) {
+      const int ce = seg(e + 1) - seg(e);
+      int rank = 0;
+      for (int o = 0; o < E; o++) {
+        const int co = seg(o + 1) - seg(o);
+        rank += (co > ce) || (co == ce && o < e);
+      }
+      s_map[rank] = e;
+    }
+    __syncthreads();
+    total_tiles = E * ((p.M + BM - 1) / BM) * ntn;
+  }
+
+  const int G = gridDim.x;
+  const int wg = (blockIdx.x % 8) * (G / 8) + blockIdx.x / 8;
+
+  for (int t = wg; t < total_tiles; t += G) {
+    int e, m0, m_end, n0, k_beg, k_end;
+    if constexpr (Prob::GROUP == Group::M) {
+      const int mt = t / ntn;
+      n0 = (t % ntn) * BN;
+      int lo = 0, hi = E;
+      while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (s_map[mid] <= mt) lo = mid; else hi = mid;
+      }
+      e = lo;
+      m0 = seg(e) + (mt - s_map[e]) * BM;
+      m_end = seg(e + 1);
+      k_beg = 0;
+      k_end = p.K;
+    } else {
+      const int mtn = (p.M + BM - 1) / BM;
+      const int per_e = mtn * ntn;
+      e = s_map[t / per_e];
+      const int rem = t % per_e;
+      m0 = (rem / ntn) * BM;
+      n0 = (rem % ntn) * BN;
+      m_end = p.M;
+      k_beg = seg(e);
+      k_end = seg(e + 1);
+    }
+
+    f32x16 acc[WTM][WTN];
+#pragma unroll
+    for (int i = 0; i < WTM; i++)
+#pragma unroll
+      for (int j = 0; j < WTN; j++)
+#pragma unroll
+        for (int r = 0; r < 16; r++) acc[i][j][r] = 0.f;
+
+    // two register stages (even / odd k-steps) in flight while two LDS buffers ping-pong
+    OA ra0, ra1;
+    OB rb0, rb1;
+    // loads are issued on every path (dead stages read nothing) so the compiler's
+    // wait counts see the same two stages in flight everywhere
+    auto load_stage = [&](OA& ra, OB& rb, int kt) {
+      const bool live = kt < k_end;
+      if constexpr (Prob::A_KC) ra.load([&](int r) { return p.a_row(e, r); }, m0, m_end, kt, 0, wave, lane, live);
+      else ra.load([&](int r) { return p.a_row(e, r); }, kt, k_end, m0, m_end, wave, lane, live);
+      if constexpr (Prob::B_KC) rb.load([&](int r) { return p.b_row(e, r); }, n0, p.N, kt, 0, wave, lane, live);
+      else rb.load([&](int r) { return p.b_row(e, r); }, kt, k_end, n0, p.N, wave, lane, live);
+    };
+    auto store_stage = [&](const OA& ra, const OB& rb, char* base) {
+      ra.store(base, wave, lane);
+      rb.store(base + OA::TILE_BYTES, wave, lane);
+    };
+    auto compute = [&](const char* st) {
+#pragma unroll
+      for (int kk = 0; kk < TK / 16; kk++) {
+        bf16x8 af[WTM], bfr[WTN];
+#pragma unroll
+        for (int i = 0; i < WTM; i++) af[i] = OA::frag(st, kk, (wave_m * WTM + i) * 32, lane);
+#pragma unroll
+        for (int jj = 0; jj < WTN; jj++) bfr[jj] = OB::frag(st + OA::TILE_BYTES, kk, (wave_n * WTN + jj) * 32, lane);
+#pragma unroll
+        for (int i = 0; i < WTM; i++)
+#pragma unroll
+          for (int jj = 0; jj < WTN; jj++)
+            acc[i][jj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[jj], acc[i][jj], 0, 0, 0);
+      }
+    };
+    // LDS writes of this wave done, then every wave past the barrier
+    auto lds_barrier = [&]() {
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+    };
+
+    const int nk = (k_end - k_beg + TK - 1) / TK;
+    if (nk > 0) {
+      load_stage(ra0, rb0, k_beg);
+      load_stage(ra1, rb1, k_beg + TK);
+      lds_barrier();  // every wave is done reading the previous tile's buffers
+      store_stage(ra0, rb0, sm0);
+      load_stage(ra0, rb0, k_beg + 2 * TK);
+      lds_barrier();
+      // k-step it computes buffer it % 2; stage it+1 sits in registers (set (it+1) % 2) and
+      // is written to the other buffer; that set is then refilled with stage it+3
+      for (int it = 0; it < nk; it += 2) {
+        compute(sm0);
+        if (it + 1 < nk) store_stage(ra1, rb1, sm1);
+        load_stage(ra1, rb1, k_beg + (it + 3) * TK);
+        lds_barrier();
+        if (it + 1 < nk) compute(sm1);
+        if (it + 2 < nk) store_stage(ra0, rb0, sm0);
+        load_stage(ra0, rb0, k_beg + (it + 4) * TK);
+        lds_barrier();
+      }
+    }
+
+#pragma unroll
+    for (int i = 0; i < WTM; i++) {
+#pragma unroll
+      for (int r = 0; r < 16; r++) {
+        const int m = m0 + (wave_m * WTM + i) * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
+        if (m >= m_end) continue;
+        if constexpr (Prob::EPI == Epi::SwiGLU) {
+#pragma unroll
+          for (int j = 0; j < WTN; j += 2) {
+            const int hcol = n0 / 2 + ((wave_n * WTN + j) >> 1) * 32 + (lane & 31);
+            if (hcol < p.N / 2) p.epilogue_swiglu(m, hcol, acc[i][j][r], acc[i][j + 1][r]);
+          }
+        } else {
+#pragma unroll
+          for (int j = 0; j < WTN; j++) {
+            const int n = n0 + (wave_n * WTN + j) * 32 + (lane & 31);
+            if (n < p.N) p.epilogue(e, m, n, acc[i][j][r]);
+          }
+        }
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------------------
 // Launchers: tile shape per GEMM (MOE_TILE_<GEMM>=128x256 etc. overrides the default)
 // ---------------------------------------------------------------------------------------
-enum class Tile { t128x128, t128x256, t256x128, t256x256, t64x128, t32x128 };
+enum class Tile { t128x128, t128x256, t256x128, t64x128, t32x128, t256x128w8, t128x256w8, t256x256w8 };
 
 static bool parse_tile(const char* v, Tile* t) {
   if (!v) return false;
   const struct { const char* s; Tile t; } tab[] = {{"128x128", Tile::t128x128}, {"128x256", Tile::t128x256},
-                                                  {"256x128", Tile::t256x128}, {"256x256", Tile::t256x256},
-                                                  {"64x128", Tile::t64x128},   {"32x128", Tile::t32x128}};
+                                                  {"256x128", Tile::t256x128},
+                                                  {"64x128", Tile::t64x128},   {"32x128", Tile::t32x128},
+                                                  {"256x128w8", Tile::t256x128w8}, {"128x256w8", Tile::t128x256w8},
+                                                  {"256x256w8", Tile::t256x256w8}};
   for (const auto& e : tab)
     if (strcmp(v, e.s) == 0) { *t = e.t; return true; }
   return false;
 }
 
-static Tile tile_for(const char* name, Tile dflt) {
+struct TileChoice {
+  Tile tile;
+  int bk;
+};
+
+// Tile shape and k-tile of one GEMM: MOE_TILE_<NAME> / MOE_TILE and MOE_GEMM_BK override
+// the default chosen by measurement on MI355X.
+static TileChoice tile_for(const char* name, Tile dflt, int dflt_bk) {
   char key[64];
   snprintf(key, sizeof key, "MOE_TILE_%s", name);
   Tile t = dflt;
   if (!parse_tile(getenv(key), &t)) parse_tile(getenv("MOE_TILE"), &t);
-  return t;
+  const char* bk = getenv("MOE_GEMM_BK");
+  int b = bk ? atoi(bk) : dflt_bk;
+  return TileChoice{t, b == 64 ? 64 : 32};
 }
 
-template <class Cfg, class Prob>
-static hipError_t launch_cfg(const Prob& p, hipStream_t st) {
-  const auto kern = grouped_gemm_kernel<Cfg, Prob>;
-  static int occ = 0;  // resident workgroups per CU for this instantiation
+// Persistent grid: resident workgroups per CU x CUs, capped by the tile bound known on the
+// host, rounded to a multiple of the 8 XCDs.
+template <class Cfg, class Prob, class Kern>
+static hipError_t launch_kernel(Kern kern, const Prob& p, hipStream_t st, int& occ) {
   if (occ == 0) {
     int o = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&o, kern, Cfg::NT, 0) != hipSuccess || o < 1) o = 1;
@@ -512,15 +803,37 @@ static hipError_t launch_cfg(const Prob& p, hipStream_t st) {
   return hipGetLastError();
 }
 
+template <class Cfg, class Prob, int TK>
+static hipError_t launch_pipe(const Prob& p, hipStream_t st) {
+  static int occ = 0;
+  return launch_kernel<Cfg>(grouped_gemm_pipe_kernel<Cfg, Prob, TK>, p, st, occ);
+}
+
+// bf16 problems use the pipelined kernel, the float-A router problems the register kernel
+template <class Cfg, class Prob>
+static hipError_t launch_cfg(const Prob& p, hipStream_t st, int bk) {
+  if constexpr (std::is_same<typename Prob::TA, bf16_t>::value) {
+    if constexpr (Cfg::BM >= 64 && Cfg::BN >= 64) {
+      if (bk == 32) return launch_pipe<Cfg, Prob, 32>(p, st);
+    }
+    return launch_pipe<Cfg, Prob, 64>(p, st);
+  } else {
+    static int occ = 0;
+    return launch_kernel<Cfg>(grouped_gemm_kernel<Cfg, Prob>, p, st, occ);
+  }
+}
+
 template <class Prob>
-static hipError_t launch(Tile t, const Prob& p, hipStream_t st) {
-  switch (t) {
-    case Tile::t128x256: return launch_cfg<TileCfg<128, 256, 2, 2>>(p, st);
-    case Tile::t256x128: return launch_cfg<TileCfg<256, 128, 2, 2>>(p, st);
-    case Tile::t256x256: return launch_cfg<TileCfg<256, 256, 2, 2>>(p, st);
-    case Tile::t64x128: return launch_cfg<TileCfg<64, 128, 1, 4>>(p, st);
-    case Tile::t32x128: return launch_cfg<TileCfg<32, 128, 1, 4>>(p, st);
-    default: return launch_cfg<TileCfg<128, 128, 2, 2>>(p, st);
+static hipError_t launch(TileChoice c, const Prob& p, hipStream_t st) {
+  switch (c.tile) {
+    case Tile::t128x256: return launch_cfg<TileCfg<128, 256, 2, 2>>(p, st, c.bk);
+    case Tile::t256x128: return launch_cfg<TileCfg<256, 128, 2, 2>>(p, st, c.bk);
+    case Tile::t64x128: return launch_cfg<TileCfg<64, 128, 1, 4>>(p, st, c.bk);
+    case Tile::t32x128: return launch_cfg<TileCfg<32, 128, 1, 4>>(p, st, c.bk);
+    case Tile::t256x128w8: return launch_cfg<TileCfg<256, 128, 4, 2>>(p, st, c.bk);
+    case Tile::t128x256w8: return launch_cfg<TileCfg<128, 256, 2, 4>>(p, st, c.bk);
+    case Tile::t256x256w8: return launch_cfg<TileCfg<256, 256, 2, 4>>(p, st, c.bk);
+    default: return launch_cfg<TileCfg<128, 128, 2, 2>>(p, st, c.bk);
   }
 }
 
@@ -529,55 +842,55 @@ hipError_t gemm1_fwd_bf16(const GemmShape& s, const int* offsets, const bf16_t* 
   ProbGemm1 p;
   p.M = s.R; p.N = 2 * s.f; p.K = s.d; p.E = s.E; p.offsets = offsets; p.f = s.f;
   p.X = X; p.W1 = W1; p.W3 = W3; p.ab = ab; p.h = h;
-  return launch(tile_for("GEMM1", Tile::t128x128), p, st);
+  return launch(tile_for("GEMM1", Tile::t128x256w8, 64), p, st);
 }
 hipError_t gemm2_fwd_bf16(const GemmShape& s, const int* offsets, const bf16_t* H, const bf16_t* W2, bf16_t* Y,
                           hipStream_t st) {
   ProbGemm2 p;
   p.M = s.R; p.N = s.d; p.K = s.f; p.E = s.E; p.offsets = offsets;
   p.Hm = H; p.W2 = W2; p.Y = Y;
-  return launch(tile_for("GEMM2", Tile::t128x128), p, st);
+  return launch(tile_for("GEMM2", Tile::t128x256w8, 32), p, st);
 }
 hipError_t dgrad2_bf16(const GemmShape& s, const int* offsets, const bf16_t* dY, const bf16_t* W2,
                        const bf16_t* ab, bf16_t* dab, hipStream_t st) {
   ProbDgrad2 p;
   p.M = s.R; p.N = s.f; p.K = s.d; p.E = s.E; p.offsets = offsets;
   p.dY = dY; p.W2 = W2; p.ab = ab; p.dab = dab;
-  return launch(tile_for("DGRAD2", Tile::t128x128), p, st);
+  return launch(tile_for("DGRAD2", Tile::t128x256w8, 32), p, st);
 }
 hipError_t wgrad2_bf16(const GemmShape& s, const int* offsets, const bf16_t* H, const bf16_t* dY, bf16_t* dW2,
                        hipStream_t st) {
   ProbWgrad2 p;
   p.M = s.d; p.N = s.f; p.K = s.R; p.E = s.E; p.offsets = offsets;
   p.dY = dY; p.Hm = H; p.dW2 = dW2;
-  return launch(tile_for("WGRAD2", Tile::t128x128), p, st);
+  return launch(tile_for("WGRAD2", Tile::t256x128w8, 32), p, st);
 }
 hipError_t dgrad1_bf16(const GemmShape& s, const int* offsets, const bf16_t* dab, const bf16_t* W1,
                        const bf16_t* W3, bf16_t* dX, hipStream_t st) {
   ProbDgrad1 p;
   p.M = s.R; p.N = s.d; p.K = 2 * s.f; p.E = s.E; p.offsets = offsets; p.f = s.f;
   p.dab = dab; p.W1 = W1; p.W3 = W3; p.dX = dX;
-  return launch(tile_for("DGRAD1", Tile::t128x128), p, st);
+  return launch(tile_for("DGRAD1", Tile::t128x256w8, 32), p, st);
 }
 hipError_t wgrad1_bf16(const GemmShape& s, const int* offsets, const bf16_t* X, const bf16_t* dab, bf16_t* dW1,
                        bf16_t* dW3, hipStream_t st) {
   ProbWgrad1 p;
   p.M = 2 * s.f; p.N = s.d; p.K = s.R; p.E = s.E; p.offsets = offsets; p.f = s.f;
   p.dab = dab; p.X = X; p.dW1 = dW1; p.dW3 = dW3;
-  return launch(tile_for("WGRAD1", Tile::t128x128), p, st);
+  return launch(tile_for("WGRAD1", Tile::t256x128w8, 32), p, st);
 }
 hipError_t router_fwd_bf16(int T, int d, int E, const bf16_t* X, const bf16_t* Wr, const float* bias, float* L,
                            hipStream_t st) {
   ProbRouterFwd p;
   p.M = T; p.N = E; p.K = d; p.E = 1; p.seg_len = T; p.seg_total = T;
   p.X = X; p.Wr = Wr; p.bias = bias; p.L = L;
-  return launch(tile_for("ROUTER_FWD", Tile::t32x128), p, st);
+  return launch(tile_for("ROUTER_FWD", Tile::t32x128, 64), p, st);
 }
 hipError_t router_dx_bf16(int T, int d, int E, const float* dL, const bf16_t* Wr, bf16_t* dX, hipStream_t st) {
   ProbRouterDx p;
   p.M = T; p.N = d; p.K = E; p.E = 1; p.seg_len = T; p.seg_total = T;
   p.dL = dL; p.Wr = Wr; p.dX = dX;
-  return launch(tile_for("ROUTER_DX", Tile::t128x128), p, st);
+  return launch(tile_for("ROUTER_DX", Tile::t128x128, 64), p, st);
 }
 
 // Split count of the router weight gradient: about 512 output tiles in flight (two per
@@ -600,7 +913,7 @@ hipError_t router_dw_bf16(int T, int d, int E, const float* dL, const bf16_t* X,
   ProbRouterDwSplit p;
   p.M = E; p.N = d; p.K = T; p.E = ns; p.seg_len = seg_len; p.seg_total = T;
   p.dL = dL; p.X = X; p.part = ns == 1 ? dW : static_cast<float*>(ws);
-  hipError_t err = launch(tile_for("ROUTER_DW", Tile::t128x128), p, st);
+  hipError_t err = launch(tile_for("ROUTER_DW", Tile::t128x128, 64), p, st);
   if (err != hipSuccess || ns == 1) return err;
   const int64_t n = (int64_t)E * d;
   hipLaunchKernelGGL(sum_splits_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, n, ns,
