@@ -1,0 +1,142 @@
+"""GPU parity at the workloads' full sizes, in the launch configuration bench.py times.
+
+The oracle cannot run whole layers of these sizes in seconds, so:
+  * routing (top-k ids, counts, offsets, packed rows) is checked in full, bit for bit;
+  * the dispatch copy is checked bit for bit on sampled packed rows;
+  * values are checked on sampled tokens (forward output, input gradient, gate and score
+    gradients) and on sampled experts (weight gradients, which sum over all of an
+    expert's rows), each recomputed by the oracle from that token's or expert's inputs;
+  * the router weight gradient is checked in full against fp64 dlogits^T x taken from
+    the GPU's own dlogits (its per-token inputs are checked separately).
+Tolerance: 2e-2 normwise against fp64, as for the small cases.
+"""
+import numpy as np
+import pytest
+import torch
+
+import workloads
+from gpu_common import TOL, host, normwise_err, run_layer, say
+
+pytestmark = pytest.mark.gpu
+
+FULL = ["e8_k4_t8192", "e128_k4_t8192", "e128_k4_t16384_zipf", "e128_k4_t16384_random", "e32_k4_t16384_d4096_bf16"]
+
+
+def _f64(t):
+    return np.asarray(t.float().numpy() if t.dtype == torch.bfloat16 else t.numpy(), dtype=np.float64)
+
+
+def _token_reference(inp, w, t, idx_t, learned):
+    """Forward and backward of one token through its chosen experts (oracle primitives)."""
+    from oracle import moe_ref as ref
+    x = _f64(inp["x"][t:t + 1])
+    dy = _f64(inp["dy"][t:t + 1])
+    ys, rows = [], []
+    for e in idx_t:
+        a, b, h, y = ref.expert_ffn_fwd(x, [0, 1], inp["W1"][e:e + 1], inp["W3"][e:e + 1], inp["W2"][e:e + 1])
+        ys.append(y[0])
+        rows.append((a, b))
+    if learned:
+        L = ref.router_logits(x, inp["Wr"], inp["router_bias"])[0]
+        sel = L[np.asarray(idx_t)]
+        g = np.exp(sel - sel.max())
+        g = g / g.sum()
+    else:
+        g = _f64(inp["gates"][t])
+    y = sum(g[j] * ys[j] for j in range(len(idx_t)))
+    dg = np.array([float(dy[0] @ ys[j]) for j in range(len(idx_t))])
+    dx = np.zeros(w.d)
+    for j, e in enumerate(idx_t):
+        a, b = rows[j]
+        dxp, *_ = ref.expert_ffn_bwd(g[j] * dy, x, a, b, [0, 1], inp["W1"][e:e + 1], inp["W3"][e:e + 1],
+                                     inp["W2"][e:e + 1])
+        dx += dxp[0]
+    out = {"y": y, "dgates": dg}
+    if learned:
+        dL = ref.route_bwd(dg[None], g[None], np.asarray(idx_t)[None], w.E)[0]
+        out["dlogits"] = dL
+        dx += dL @ _f64(inp["Wr"])
+    out["dx"] = dx
+    return out
+
+
+def _expert_reference(inp, w, e, idx, gates_f64):
+    """Weight gradients of expert e from all of its routed rows (oracle primitives)."""
+    from oracle import moe_ref as ref
+    tt, jj = np.nonzero(idx == e)
+    if len(tt) == 0:
+        z = np.zeros
+        return z((w.f, w.d)), z((w.f, w.d)), z((w.d, w.f))
+    X = _f64(inp["x"][torch.from_numpy(tt)])
+    dY = gates_f64[tt, jj][:, None] * _f64(inp["dy"][torch.from_numpy(tt)])
+    a, b, h, y = ref.expert_ffn_fwd(X, [0, len(tt)], inp["W1"][e:e + 1], inp["W3"][e:e + 1], inp["W2"][e:e + 1])
+    _, dW1, dW3, dW2, _, _ = ref.expert_ffn_bwd(dY, X, a, b, [0, len(tt)], inp["W1"][e:e + 1],
+                                               inp["W3"][e:e + 1], inp["W2"][e:e + 1])
+    return dW1[0], dW3[0], dW2[0]
+
+
+@pytest.mark.parametrize("name", FULL)
+def test_full_size_layer(name):
+    from oracle import moe_ref as ref
+    w = workloads.WORKLOADS[name]
+    inp = workloads.make_inputs(w)
+    learned = w.routing != "given_uniform"
+    say(f"[gpu] full-size layer {w}")
+    L = run_layer(w, inp)
+    tol = TOL[w.gemm]
+    rng = np.random.default_rng(7)
+
+    # routing in full, bit for bit (selection on the GPU's fp32 scores)
+    if learned:
+        gl = host(L.logits)
+        idx, _ = ref.topk_gates(gl, w.k)
+        assert np.array_equal(host(L.topk_idx), idx)
+    else:
+        idx = inp["topk_idx"].numpy()
+    counts, offsets, slot_row, row_src = ref.dispatch(idx, w.E)
+    assert np.array_equal(host(L.counts), counts)
+    assert np.array_equal(host(L.offsets), offsets)
+    assert np.array_equal(host(L.slot_row), slot_row)
+    assert np.array_equal(host(L.row_src), row_src)
+    rows = rng.choice(w.R, 64, replace=False)
+    assert torch.equal(L.x_perm[torch.from_numpy(rows).cuda()].cpu(), inp["x"][torch.from_numpy(row_src[rows]).long()])
+
+    # sampled tokens: forward output and gradients
+    toks = rng.choice(w.T, 24, replace=False)
+    got = {"y": host(L.y[toks]), "dx": host(L.dx[toks]), "dgates": host(L.dgates[toks])}
+    if learned:
+        got["dlogits"] = host(L.dlogits[toks])
+        L64 = ref.router_logits(inp["x"][toks], inp["Wr"], inp["router_bias"])
+        got_logits = host(L.logits[toks])
+        assert normwise_err(got_logits, L64) < 1e-5
+    refs = {k: [] for k in got}
+    for t in toks:
+        r = _token_reference(inp, w, int(t), idx[t], learned)
+        for k in got:
+            refs[k].append(r[k])
+    errs = {k: normwise_err(got[k], np.stack(refs[k])) for k in got}
+
+    # sampled experts: weight gradients (a median-load and the lightest expert)
+    if learned:
+        g_sel = np.take_along_axis(ref.router_logits(inp["x"], inp["Wr"], inp["router_bias"]), idx.astype(np.int64), 1)
+        gw = np.exp(g_sel - g_sel[:, :1])
+        gates64 = gw / gw.sum(axis=1, keepdims=True)
+    else:
+        gates64 = _f64(inp["gates"])
+    order = np.argsort(counts, kind="stable")
+    for e in {int(order[len(order) // 2]), int(order[0])}:
+        dW1, dW3, dW2 = _expert_reference(inp, w, e, idx, gates64)
+        errs[f"dW1[{e}]"] = normwise_err(host(L.dW1[e]), dW1)
+        errs[f"dW3[{e}]"] = normwise_err(host(L.dW3[e]), dW3)
+        errs[f"dW2[{e}]"] = normwise_err(host(L.dW2[e]), dW2)
+    if learned:
+        dWr_ref = host(L.dlogits).astype(np.float64).T @ _f64(inp["x"])
+        errs["dWr"] = normwise_err(host(L.dWr), dWr_ref)
+    print(name, {k: f"{v:.2e}" for k, v in errs.items()})
+    bad = {k: v for k, v in errs.items() if v > tol}
+    assert not bad, (name, bad)
+
+    # bitwise reproducible at full size
+    y0, dx0, dW10 = L.y.clone(), L.dx.clone(), L.dW1.clone()
+    run_layer(w, inp, layer=L)
+    assert torch.equal(y0, L.y) and torch.equal(dx0, L.dx) and torch.equal(dW10, L.dW1)
