@@ -26,6 +26,7 @@
 
 #include "common.h"
 #include "gemm.h"
+#include "tilemap.h"
 
 namespace moe {
 
@@ -156,76 +157,15 @@ __global__ void __launch_bounds__(Cfg::NT) grouped_gemm_kernel(const Prob p) {
   auto seg = [&](int e) { return p.seg(e); };
 
   // ---- tile map
-  int total_tiles;
-  const int ntn = (p.N + BN - 1) / BN;
-  if constexpr (Prob::GROUP == Group::M) {
-    if (wave == 0) {
-      int carry = 0;
-      for (int base = 0; base < E; base += kWave) {
-        const int e = base + lane;
-        const int x = e < E ? (seg(e + 1) - seg(e) + BM - 1) / BM : 0;
-        int incl = x;
-#pragma unroll
-        for (int o = 1; o < kWave; o <<= 1) {
-          const int y = __shfl_up(incl, o, kWave);
-          if (lane >= o) incl += y;
-        }
-        if (e < E) s_map[e] = carry + incl - x;
-        carry += __shfl(incl, kWave - 1, kWave);
-      }
-      if (lane == 0) s_map[E] = carry;
-    }
-    __syncthreads();
-    total_tiles = s_map[E] * ntn;
-  } else {
-    // order experts by descending row count (ties: lower id first) so the longest
-    // reductions start first; rank by counting
-    for (int e = tid; e < E; e += NT) {
-      const int ce = seg(e + 1) - seg(e);
-      int rank = 0;
-      for (int o = 0; o < E; o++) {
-        const int co = seg(o + 1) - seg(o);
-        rank += (co > ce) || (co == ce && o < e);
-      }
-      s_map[rank] = e;
-    }
-    __syncthreads();
-    total_tiles = E * ((p.M + BM - 1) / BM) * ntn;
-  }
-
-  // ---- XCD-aware persistent schedule: consecutive logical workgroups share an XCD
-  // (hardware dispatches workgroup b to XCD b % 8), and consecutive tiles share operands.
+  const int total_tiles = build_tile_map<Prob::GROUP, BM, BN, NT>(s_map, seg, E, p.M, p.N, tid);
   const int G = gridDim.x;
-  const int wg = (blockIdx.x % 8) * (G / 8) + blockIdx.x / 8;
+  const int wg = xcd_logical_wg();
 
   SA sa;
   SB sb;
   for (int t = wg; t < total_tiles; t += G) {
-    int e, m0, m_end, n0, k_beg, k_end;
-    if constexpr (Prob::GROUP == Group::M) {
-      const int mt = t / ntn;
-      n0 = (t % ntn) * BN;
-      int lo = 0, hi = E;  // largest e with s_map[e] <= mt
-      while (hi - lo > 1) {
-        const int mid = (lo + hi) >> 1;
-        if (s_map[mid] <= mt) lo = mid; else hi = mid;
-      }
-      e = lo;
-      m0 = seg(e) + (mt - s_map[e]) * BM;
-      m_end = seg(e + 1);
-      k_beg = 0;
-      k_end = p.K;
-    } else {
-      const int mtn = (p.M + BM - 1) / BM;
-      const int per_e = mtn * ntn;
-      e = s_map[t / per_e];
-      const int rem = t % per_e;
-      m0 = (rem / ntn) * BM;
-      n0 = (rem % ntn) * BN;
-      m_end = p.M;
-      k_beg = seg(e);
-      k_end = seg(e + 1);
-    }
+    const TileRange tr = tile_at<Prob::GROUP, BM, BN>(t, s_map, seg, E, p.M, p.N, p.K);
+    const int e = tr.e, m0 = tr.m0, m_end = tr.m_end, n0 = tr.n0, k_beg = tr.k_beg, k_end = tr.k_end;
 
     f32x16 acc[WTM][WTN];
 #pragma unroll
@@ -591,70 +531,13 @@ __global__ void __launch_bounds__(Cfg::NT) grouped_gemm_pipe_kernel(const Prob p
   const int E = p.E;
   auto seg = [&](int e) { return p.seg(e); };
 
-  int total_tiles;
-  const int ntn = (p.N + BN - 1) / BN;
-  if constexpr (Prob::GROUP == Group::M) {
-    if (wave == 0) {
-      int carry = 0;
-      for (int base = 0; base < E; base += kWave) {
-        const int e = base + lane;
-        const int x = e < E ? (seg(e + 1) - seg(e) + BM - 1) / BM : 0;
-        int incl = x;
-#pragma unroll
-        for (int o = 1; o < kWave; o <<= 1) {
-          const int y = __shfl_up(incl, o, kWave);
-          if (lane >= o) incl += y;
-        }
-        if (e < E) s_map[e] = carry + incl - x;
-        carry += __shfl(incl, kWave - 1, kWave);
-      }
-      if (lane == 0) s_map[E] = carry;
-    }
-    __syncthreads();
-    total_tiles = s_map[E] * ntn;
-  } else {
-    for (int e = tid; e < E; e += NT) {
-      const int ce = seg(e + 1) - seg(e);
-      int rank = 0;
-      for (int o = 0; o < E; o++) {
-        const int co = seg(o + 1) - seg(o);
-        rank += (co > ce) || (co == ce && o < e);
-      }
-      s_map[rank] = e;
-    }
-    __syncthreads();
-    total_tiles = E * ((p.M + BM - 1) / BM) * ntn;
-  }
-
+  const int total_tiles = build_tile_map<Prob::GROUP, BM, BN, NT>(s_map, seg, E, p.M, p.N, tid);
   const int G = gridDim.x;
-  const int wg = (blockIdx.x % 8) * (G / 8) + blockIdx.x / 8;
+  const int wg = xcd_logical_wg();
 
   for (int t = wg; t < total_tiles; t += G) {
-    int e, m0, m_end, n0, k_beg, k_end;
-    if constexpr (Prob::GROUP == Group::M) {
-      const int mt = t / ntn;
-      n0 = (t % ntn) * BN;
-      int lo = 0, hi = E;
-      while (hi - lo > 1) {
-        const int mid = (lo + hi) >> 1;
-        if (s_map[mid] <= mt) lo = mid; else hi = mid;
-      }
-      e = lo;
-      m0 = seg(e) + (mt - s_map[e]) * BM;
-      m_end = seg(e + 1);
-      k_beg = 0;
-      k_end = p.K;
-    } else {
-      const int mtn = (p.M + BM - 1) / BM;
-      const int per_e = mtn * ntn;
-      e = s_map[t / per_e];
-      const int rem = t % per_e;
-      m0 = (rem / ntn) * BM;
-      n0 = (rem % ntn) * BN;
-      m_end = p.M;
-      k_beg = seg(e);
-      k_end = seg(e + 1);
-    }
+    const TileRange tr = tile_at<Prob::GROUP, BM, BN>(t, s_map, seg, E, p.M, p.N, p.K);
+    const int e = tr.e, m0 = tr.m0, m_end = tr.m_end, n0 = tr.n0, k_beg = tr.k_beg, k_end = tr.k_end;
 
     f32x16 acc[WTM][WTN];
 #pragma unroll

@@ -154,3 +154,113 @@ def dequantize_segment_cols(codes, scales, offsets, block: int = BLOCK) -> np.nd
         rep = np.repeat(s, block, axis=0)[: hi - lo]
         out[lo:hi] = e4m3_decode(c[lo:hi]) * np.exp2(rep)
     return out
+
+
+# ----------------------------------------------------------------------------- MXFP8 layer
+# The expert FFN with MXFP8 GEMMs: every GEMM operand is block-quantised along that
+# GEMM's reduction axis (forward: activations and weights along the model / hidden
+# width; data gradient: the upstream gradient along its width and the weights along the
+# other axis; weight gradient: both operands along the expert's rows), dequantised
+# exactly, and multiplied in fp64.  The GEMMs produce bf16 (round to nearest even at each
+# stored activation and gradient), and it is those bf16 values that the next GEMM
+# quantises: the E4M3 code of a value depends on its bf16 rounding, so the oracle takes
+# that decision on the same bf16 values as the device.  Everything else (routing,
+# dispatch, gates, combine, SwiGLU and its gradient) is the plain layer of moe_ref.
+# quant=False and bf16=False recover the unquantised, unrounded layer exactly.
+
+def bf16_round(v) -> np.ndarray:
+    """Round to bfloat16 (nearest, ties to even) through fp32, returned as float64."""
+    f = np.asarray(v, dtype=np.float64).astype(np.float32)
+    u = f.view(np.uint32).astype(np.uint64)
+    nan = np.isnan(f)
+    u = (u + 0x7FFF + ((u >> 16) & 1)) & 0xFFFF0000
+    out = u.astype(np.uint32).view(np.float32).astype(np.float64)
+    return np.where(nan, np.nan, out)
+
+
+def _q_rows(v, quant=True):
+    if not quant:
+        return np.asarray(v, dtype=np.float64)
+    c, s = quantize_rows(v)
+    return dequantize_rows(c, s)
+
+
+def _q_cols(v, quant=True):
+    """Blocks down the columns of one segment (all rows of v)."""
+    if not quant:
+        return np.asarray(v, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    c, s = quantize_segment_cols(v, [0, v.shape[0]])
+    return dequantize_segment_cols(c, s, [0, v.shape[0]])
+
+
+def mx_expert_weights(W1e, W3e, W2e, quant=True) -> dict:
+    """The dequantised weight operands of one expert for the three GEMMs that read it:
+    forward (W1, W3 along d; W2 along f) and data gradient (W2 along d; W1, W3 along f)."""
+    W1e, W3e, W2e = (np.asarray(w, dtype=np.float64) for w in (W1e, W3e, W2e))
+    return {"W1": _q_rows(W1e, quant), "W3": _q_rows(W3e, quant), "W2": _q_rows(W2e, quant),
+            "W2t": _q_cols(W2e, quant),
+            "W13t": np.concatenate([_q_cols(W1e, quant), _q_cols(W3e, quant)], axis=0)}
+
+
+def mx_expert_fwd(X, Wq: dict, quant=True, bf16=True):
+    """One expert's rows X [n, d]: a = q(X) q(W1)^T, b likewise (stored bf16),
+    h = silu(a) b from the unrounded a, b (stored bf16), y = q(h) q(W2)^T (stored bf16)."""
+    from oracle import moe_ref as ref
+    rnd = bf16_round if bf16 else (lambda z: z)
+    Xq = _q_rows(X, quant)
+    a = Xq @ Wq["W1"].T
+    b = Xq @ Wq["W3"].T
+    h = rnd(ref.silu(a) * b)
+    y = rnd(_q_rows(h, quant) @ Wq["W2"].T)
+    return rnd(a), rnd(b), h, y
+
+
+def mx_expert_bwd(dY, X, a, b, h, Wq: dict, quant=True, bf16=True):
+    """Backward of mx_expert_fwd for one expert's rows (a, b, h as stored): returns dX,
+    dW1, dW3, dW2.  dh = q(dY) q_d(W2); dW2 = q_r(dY)^T q_r(h); [da|db] from dh and the
+    stored a, b (stored bf16); dX = q([da|db]) q_f([W1; W3]); [dW1; dW3] =
+    q_r([da|db])^T q_r(X)  (q_r: blocks along the expert's rows)."""
+    from oracle import moe_ref as ref
+    rnd = bf16_round if bf16 else (lambda z: z)
+    f = Wq["W1"].shape[0]
+    dh = _q_rows(dY, quant) @ Wq["W2t"]
+    dW2 = rnd(_q_cols(dY, quant).T @ _q_cols(h, quant))
+    s = ref.sigmoid(a)
+    dab = rnd(np.concatenate([dh * b * s * (1.0 + a * (1.0 - s)), dh * a * s], axis=1))
+    dX = rnd(_q_rows(dab, quant) @ Wq["W13t"])
+    dW13 = rnd(_q_cols(dab, quant).T @ _q_cols(X, quant))
+    return dX, dW13[:f], dW13[f:], dW2
+
+
+def mx_layer(x, W1, W3, W2, k, topk_idx, gates, dy, quant=True, bf16=True):
+    """Whole layer forward + backward with MXFP8 expert GEMMs, for tokens that arrive
+    routed (topk_idx, gates given).  Returns a dict like moe_ref's forward/backward."""
+    from oracle import moe_ref as ref
+    rnd = bf16_round if bf16 else (lambda z: z)
+    W1, W3, W2 = ref.f64(W1), ref.f64(W3), ref.f64(W2)
+    E = W1.shape[0]
+    idx = np.asarray(topk_idx).astype(np.int32)
+    g = ref.f64(gates)
+    counts, offsets, slot_row, row_src = ref.dispatch(idx, E)
+    xp = ref.permute(x, row_src)
+    R, d = xp.shape
+    f = W1.shape[1]
+    Wq = [mx_expert_weights(W1[e], W3[e], W2[e], quant) if counts[e] else None for e in range(E)]
+    a = np.zeros((R, f)); b = np.zeros((R, f)); h = np.zeros((R, f)); yp = np.zeros((R, d))
+    for e in range(E):
+        lo, hi = offsets[e], offsets[e + 1]
+        if hi > lo:
+            a[lo:hi], b[lo:hi], h[lo:hi], yp[lo:hi] = mx_expert_fwd(xp[lo:hi], Wq[e], quant, bf16)
+    y = rnd(ref.combine(yp, g, slot_row))
+    dyp, dgates = ref.combine_bwd(dy, yp, g, slot_row)
+    dyp = rnd(dyp)
+    dxp = np.zeros((R, d)); dW1 = np.zeros_like(W1); dW3 = np.zeros_like(W3); dW2 = np.zeros_like(W2)
+    for e in range(E):
+        lo, hi = offsets[e], offsets[e + 1]
+        if hi > lo:
+            dxp[lo:hi], dW1[e], dW3[e], dW2[e] = mx_expert_bwd(dyp[lo:hi], xp[lo:hi], a[lo:hi], b[lo:hi], h[lo:hi],
+                                                               Wq[e], quant, bf16)
+    dx = rnd(ref.unpermute_sum(dxp, slot_row))
+    return dict(counts=counts, offsets=offsets, slot_row=slot_row, x_perm=xp, a=a, b=b, h=h, y_perm=yp, y=y,
+                dgates=dgates, dx_perm=dxp, dW1=dW1, dW3=dW3, dW2=dW2, dx=dx)

@@ -4,7 +4,8 @@ and compare with the CPU oracle under the tolerances of the method.
 Tolerances (normwise: max|got - ref| / max|ref|, per tensor):
   bf16 path   2e-2   (values and gradients against the fp64 oracle)
   fp32 path   1e-4
-  MXFP8 path  6e-2
+  MXFP8 path  6e-2   (against the fp64 oracle of the MXFP8 method: operands quantised
+                     along each GEMM's reduction axis, dequantised, multiplied in fp64)
 Integers (expert ids, counts, offsets, packed rows, row sources, E4M3/E8M0 bytes) must
 match bit for bit.
 """
@@ -66,6 +67,18 @@ def oracle_for(w, inp: dict, gpu_logits=None):
     fp32 scores (the selection is an integer decision taken in fp32 on both sides)."""
     from oracle import moe_ref as ref
     learned = w.routing != "given_uniform"
+    if w.gemm == "mxfp8":
+        # the MXFP8 method: every expert GEMM operand block-quantised along its reduction
+        # axis, dequantised exactly, multiplied in fp64 (tokens arrive routed)
+        from oracle import mx_ref
+        assert not learned, "the MXFP8 workloads take pre-routed tokens"
+        out = mx_ref.mx_layer(inp["x"], inp["W1"], inp["W3"], inp["W2"], w.k, inp["topk_idx"].numpy(), inp["gates"],
+                              inp["dy"])
+        fw = {k: out[k] for k in ("counts", "offsets", "slot_row", "x_perm", "a", "b", "h", "y_perm", "y")}
+        fw["topk_idx"] = inp["topk_idx"].numpy()
+        fw["row_src"] = ref.dispatch(fw["topk_idx"], w.E)[3]
+        bw = {k: out[k] for k in ("dgates", "dx_perm", "dW1", "dW3", "dW2", "dx")}
+        return fw, bw
     if learned:
         fw = ref.layer_forward(inp["x"], inp["W1"], inp["W3"], inp["W2"], w.k, Wr=inp["Wr"],
                                bias=inp["router_bias"], select_logits=gpu_logits)

@@ -8,7 +8,8 @@ The oracle cannot run whole layers of these sizes in seconds, so:
     expert's rows), each recomputed by the oracle from that token's or expert's inputs;
   * the router weight gradient is checked in full against fp64 dlogits^T x taken from
     the GPU's own dlogits (its per-token inputs are checked separately).
-Tolerance: 2e-2 normwise against fp64, as for the small cases.
+Tolerance: 2e-2 normwise against fp64 (6e-2 against the fp64 MXFP8 oracle for the MXFP8
+workload), as for the small cases.
 """
 import numpy as np
 import pytest
@@ -19,23 +20,57 @@ from gpu_common import TOL, host, normwise_err, run_layer, say
 
 pytestmark = pytest.mark.gpu
 
-FULL = ["e8_k4_t8192", "e128_k4_t8192", "e128_k4_t16384_zipf", "e128_k4_t16384_random", "e32_k4_t16384_d4096_bf16"]
+FULL = ["e8_k4_t8192", "e128_k4_t8192", "e128_k4_t16384_zipf", "e128_k4_t16384_random", "e32_k4_t16384_d4096_bf16",
+        "e32_k4_t16384_d4096_mxfp8"]
 
 
 def _f64(t):
     return np.asarray(t.float().numpy() if t.dtype == torch.bfloat16 else t.numpy(), dtype=np.float64)
 
 
-def _token_reference(inp, w, t, idx_t, learned):
-    """Forward and backward of one token through its chosen experts (oracle primitives)."""
+_MXW = {}  # (workload, expert) -> dequantised MXFP8 weight operands
+
+
+def _mx_weights(inp, e):
+    from oracle import mx_ref
+    key = (id(inp["W1"]), e)
+    if key not in _MXW:
+        say(f"  [oracle] quantising the weights of expert {e}")
+        _MXW[key] = mx_ref.mx_expert_weights(_f64(inp["W1"][e]), _f64(inp["W3"][e]), _f64(inp["W2"][e]))
+    return _MXW[key]
+
+
+def _ffn_fwd(inp, X, e, mxfp8):
     from oracle import moe_ref as ref
+    from oracle import mx_ref
+    if mxfp8:
+        return mx_ref.mx_expert_fwd(X, _mx_weights(inp, e))
+    return ref.expert_ffn_fwd(X, [0, len(X)], inp["W1"][e:e + 1], inp["W3"][e:e + 1], inp["W2"][e:e + 1])
+
+
+def _ffn_bwd(inp, dY, X, a, b, h, e, mxfp8):
+    """(dX, dW1_e, dW3_e, dW2_e) of one expert's rows."""
+    from oracle import moe_ref as ref
+    from oracle import mx_ref
+    if mxfp8:
+        return mx_ref.mx_expert_bwd(mx_ref.bf16_round(dY), X, a, b, h, _mx_weights(inp, e))
+    dx, dW1, dW3, dW2, _, _ = ref.expert_ffn_bwd(dY, X, a, b, [0, len(X)], inp["W1"][e:e + 1], inp["W3"][e:e + 1],
+                                                 inp["W2"][e:e + 1])
+    return dx, dW1[0], dW3[0], dW2[0]
+
+
+def _token_reference(inp, w, t, idx_t, learned):
+    """Forward and backward of one token through its chosen experts (oracle primitives;
+    the MXFP8 workload quantises every expert GEMM operand as the MXFP8 method does)."""
+    from oracle import moe_ref as ref
+    mxfp8 = w.gemm == "mxfp8"
     x = _f64(inp["x"][t:t + 1])
     dy = _f64(inp["dy"][t:t + 1])
     ys, rows = [], []
     for e in idx_t:
-        a, b, h, y = ref.expert_ffn_fwd(x, [0, 1], inp["W1"][e:e + 1], inp["W3"][e:e + 1], inp["W2"][e:e + 1])
+        a, b, h, y = _ffn_fwd(inp, x, e, mxfp8)
         ys.append(y[0])
-        rows.append((a, b))
+        rows.append((a, b, h))
     if learned:
         L = ref.router_logits(x, inp["Wr"], inp["router_bias"])[0]
         sel = L[np.asarray(idx_t)]
@@ -47,9 +82,8 @@ def _token_reference(inp, w, t, idx_t, learned):
     dg = np.array([float(dy[0] @ ys[j]) for j in range(len(idx_t))])
     dx = np.zeros(w.d)
     for j, e in enumerate(idx_t):
-        a, b = rows[j]
-        dxp, *_ = ref.expert_ffn_bwd(g[j] * dy, x, a, b, [0, 1], inp["W1"][e:e + 1], inp["W3"][e:e + 1],
-                                     inp["W2"][e:e + 1])
+        a, b, h = rows[j]
+        dxp, *_ = _ffn_bwd(inp, g[j] * dy, x, a, b, h, e, mxfp8)
         dx += dxp[0]
     out = {"y": y, "dgates": dg}
     if learned:
@@ -69,10 +103,10 @@ def _expert_reference(inp, w, e, idx, gates_f64):
         return z((w.f, w.d)), z((w.f, w.d)), z((w.d, w.f))
     X = _f64(inp["x"][torch.from_numpy(tt)])
     dY = gates_f64[tt, jj][:, None] * _f64(inp["dy"][torch.from_numpy(tt)])
-    a, b, h, y = ref.expert_ffn_fwd(X, [0, len(tt)], inp["W1"][e:e + 1], inp["W3"][e:e + 1], inp["W2"][e:e + 1])
-    _, dW1, dW3, dW2, _, _ = ref.expert_ffn_bwd(dY, X, a, b, [0, len(tt)], inp["W1"][e:e + 1],
-                                               inp["W3"][e:e + 1], inp["W2"][e:e + 1])
-    return dW1[0], dW3[0], dW2[0]
+    mxfp8 = w.gemm == "mxfp8"
+    a, b, h, y = _ffn_fwd(inp, X, e, mxfp8)
+    _, dW1, dW3, dW2 = _ffn_bwd(inp, dY, X, a, b, h, e, mxfp8)
+    return dW1, dW3, dW2
 
 
 @pytest.mark.parametrize("name", FULL)
@@ -102,7 +136,7 @@ def test_full_size_layer(name):
     assert torch.equal(L.x_perm[torch.from_numpy(rows).cuda()].cpu(), inp["x"][torch.from_numpy(row_src[rows]).long()])
 
     # sampled tokens: forward output and gradients
-    toks = rng.choice(w.T, 24, replace=False)
+    toks = rng.choice(w.T, 8 if w.gemm == "mxfp8" else 24, replace=False)
     got = {"y": host(L.y[toks]), "dx": host(L.dx[toks]), "dgates": host(L.dgates[toks])}
     if learned:
         got["dlogits"] = host(L.dlogits[toks])

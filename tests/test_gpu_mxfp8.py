@@ -1,0 +1,167 @@
+"""MXFP8 path on the GPU: quantiser bytes bit-exact against the oracle; each MXFP8
+grouped GEMM against fp64 GEMMs of its dequantised operands; and the MXFP8 layer (all six
+grouped GEMMs on E4M3 operands with E8M0 block scales) within 6e-2 normwise of the fp64
+oracle of the MXFP8 method, with the format's own error against the unquantised layer
+reported beside it."""
+import numpy as np
+import pytest
+import torch
+
+import workloads
+from gpu_common import TOL, host, normwise_err, oracle_for, run_layer, say
+
+pytestmark = pytest.mark.gpu
+
+
+def _bf16_sample(rows, cols, seed):
+    """bf16 values over a wide exponent range: zero rows, bf16 subnormals, huge values,
+    negative zeros, and ordinary Gaussians."""
+    g = torch.Generator().manual_seed(seed)
+    v = torch.randn(rows, cols, generator=g) * torch.exp2(torch.randint(-30, 30, (rows, 1), generator=g).float())
+    if rows >= 5:
+        v[0] = 0.0
+        v[1] = -0.0
+        v[2, :8] = torch.tensor([1e-39, -2e-39, 3e-40, 0.0, 5e-41, -1e-38, 2e-38, 1e-45])  # fp32/bf16 subnormals
+        v[3] = torch.randn(cols, generator=g) * 1e30
+        v[4, ::3] = 0.0
+    return v.to(torch.bfloat16)
+
+
+def test_mx_quantize_rows_bit_exact():
+    import mixture_experts_layer_logits_amd as m
+    from oracle import mx_ref
+    for (rows, cols, seed) in [(1, 32, 1), (77, 96, 2), (256, 2048, 3)]:
+        say(f"[gpu] mx quantize rows {rows}x{cols}")
+        src = _bf16_sample(rows, cols, seed)
+        q = torch.empty(rows, cols, dtype=torch.uint8, device="cuda")
+        s = torch.empty(rows, cols // 32, dtype=torch.uint8, device="cuda")
+        m.moe_mx_quantize(rows, cols, 0, None, 0, src.cuda(), q, s)
+        torch.cuda.synchronize()
+        codes, scales = mx_ref.quantize_rows(src.float().numpy().astype(np.float64))
+        assert np.array_equal(host(q), codes)
+        assert np.array_equal(host(s), scales)
+
+
+def test_mx_quantize_segment_cols_bit_exact():
+    import mixture_experts_layer_logits_amd as m
+    from oracle import mx_ref
+    for (offsets, cols, seed) in [([0, 5, 5, 45, 200, 333], 96, 4), ([0, 0, 128, 129, 400], 64, 5),
+                                  ([0, 300], 32, 6)]:
+        offsets = np.asarray(offsets, dtype=np.int32)
+        rows, nseg = int(offsets[-1]), len(offsets) - 1
+        say(f"[gpu] mx quantize segment cols {offsets.tolist()} x {cols}")
+        src = _bf16_sample(rows, cols, seed)
+        rows_pad = rows + 128 * nseg
+        q = torch.full((cols, rows_pad), 0xAB, dtype=torch.uint8, device="cuda")
+        s = torch.full((cols, rows_pad // 32), 0xAB, dtype=torch.uint8, device="cuda")
+        m.moe_mx_quantize(rows, cols, 1, torch.from_numpy(offsets).cuda(), nseg, src.cuda(), q, s)
+        torch.cuda.synchronize()
+        codes, scales = mx_ref.quantize_segment_cols(src.float().numpy().astype(np.float64), offsets)
+        gq, gs = host(q), host(s)
+        P = 0
+        for e in range(nseg):
+            lo, hi = offsets[e], offsets[e + 1]
+            n = hi - lo
+            npad = -(-n // 128) * 128
+            assert np.array_equal(gq[:, P:P + n], codes[lo:hi].T)
+            assert not gq[:, P + n:P + npad].any()                  # padding rows: zero codes
+            nb = -(-n // 32)
+            assert np.array_equal(gs[:, P // 32:P // 32 + nb], scales[e].T)
+            assert not gs[:, P // 32 + nb:(P + npad) // 32].any()   # all-padding blocks: zero scale byte
+            P += npad
+
+
+MX_CASES = [
+    dict(T=256, d=256, f=256, E=8, k=4, name="mx_small"),
+    dict(T=300, d=384, f=256, E=32, k=4, name="mx_ragged_e32"),
+    dict(T=200, d=256, f=384, E=16, k=2, name="mx_k2"),
+]
+
+
+@pytest.mark.parametrize("over", MX_CASES, ids=[c["name"] for c in MX_CASES])
+def test_mxfp8_layer_parity(over):
+    from oracle import mx_ref
+    w = workloads.scaled(workloads.WORKLOADS["e32_k4_t16384_d4096_mxfp8"], **over)
+    inp = workloads.make_inputs(w)
+    say(f"[gpu] mxfp8 layer {w}")
+    L = run_layer(w, inp)
+    fw, bw = oracle_for(w, inp)        # fp64 oracle of the MXFP8 method
+    assert np.array_equal(host(L.slot_row), fw["slot_row"])
+    keys = {"h": (L.h, fw["h"]), "y": (L.y, fw["y"]), "dgates": (L.dgates, bw["dgates"]),
+            "dx": (L.dx, bw["dx"]), "dW1": (L.dW1, bw["dW1"]), "dW3": (L.dW3, bw["dW3"]), "dW2": (L.dW2, bw["dW2"])}
+    errs = {k: normwise_err(host(g), r) for k, (g, r) in keys.items()}
+    # the format's own error: the same layer without quantisation (reported, bounded loosely)
+    plain = mx_ref.mx_layer(inp["x"], inp["W1"], inp["W3"], inp["W2"], w.k, inp["topk_idx"].numpy(), inp["gates"],
+                            inp["dy"], quant=False, bf16=False)
+    fmt = {k: normwise_err(host(keys[k][0]), plain[k]) for k in ("y", "dx", "dW1", "dW3", "dW2")}
+    print(w.name, "vs MXFP8 oracle", {k: f"{v:.2e}" for k, v in errs.items()},
+          "| vs unquantised", {k: f"{v:.2e}" for k, v in fmt.items()})
+    bad = {k: v for k, v in errs.items() if v > TOL["mxfp8"]}
+    assert not bad, (w.name, bad)
+    assert max(fmt.values()) < 0.25
+    for e in np.nonzero(fw["counts"] == 0)[0]:
+        assert not host(L.dW1[e]).any() and not host(L.dW2[e]).any()
+
+
+def test_mx_gemms_match_dequantized_operands():
+    """Each MXFP8 grouped GEMM equals the fp64 GEMM of its dequantised operands (the
+    oracle's quantiser is bit-exact with the GPU's), up to fp32 accumulation and the bf16
+    rounding of the outputs: a check of the scaled-MFMA operand and scale layouts."""
+    from oracle import moe_ref as ref
+    from oracle import mx_ref as mx
+    w = workloads.scaled(workloads.WORKLOADS["e32_k4_t16384_d4096_mxfp8"], T=300, d=256, f=384, E=8, k=4,
+                         name="mx_emulated")
+    inp = workloads.make_inputs(w)
+    say(f"[gpu] mxfp8 GEMMs vs dequantised operands {w}")
+    L = run_layer(w, inp)
+    off = host(L.offsets).astype(np.int64)
+    E, d, f = w.E, w.d, w.f
+
+    def deq_rows(t):
+        c, s = mx.quantize_rows(np.asarray(t, dtype=np.float64))
+        return mx.dequantize_rows(c, s)
+
+    def deq_cols(t, offsets):
+        c, s = mx.quantize_segment_cols(np.asarray(t, dtype=np.float64), offsets)
+        return mx.dequantize_segment_cols(c, s, offsets)
+
+    X, H, dY, dAB = host(L.x_perm), host(L.h), host(L.dy_perm), host(L.dab)
+    W1 = host(inp["W1"]).reshape(E * f, d)
+    W3 = host(inp["W3"]).reshape(E * f, d)
+    W2 = host(inp["W2"]).reshape(E * d, f)
+    Xq, Hq, dYq, dABq = deq_rows(X), deq_rows(H), deq_rows(dY), deq_rows(dAB)
+    W1q, W3q, W2q = deq_rows(W1).reshape(E, f, d), deq_rows(W3).reshape(E, f, d), deq_rows(W2).reshape(E, d, f)
+    # backward weights: blocks along the other axis, one segment per expert
+    W2t = deq_cols(W2, np.arange(E + 1) * d).reshape(E, d, f)
+    W1t = deq_cols(W1, np.arange(E + 1) * f).reshape(E, f, d)
+    W3t = deq_cols(W3, np.arange(E + 1) * f).reshape(E, f, d)
+    # weight-gradient operands: blocks along the rows of each expert
+    dYc, Hc, dABc, Xc = deq_cols(dY, off), deq_cols(H, off), deq_cols(dAB, off), deq_cols(X, off)
+    R = w.R
+    a = np.zeros((R, f)); b = np.zeros((R, f)); y = np.zeros((R, d)); dh = np.zeros((R, f)); dx = np.zeros((R, d))
+    dW1 = np.zeros((E, f, d)); dW3 = np.zeros((E, f, d)); dW2 = np.zeros((E, d, f))
+    for e in range(E):
+        lo, hi = off[e], off[e + 1]
+        a[lo:hi] = Xq[lo:hi] @ W1q[e].T
+        b[lo:hi] = Xq[lo:hi] @ W3q[e].T
+        y[lo:hi] = Hq[lo:hi] @ W2q[e].T
+        dh[lo:hi] = dYq[lo:hi] @ W2t[e]
+        dx[lo:hi] = dABq[lo:hi, :f] @ W1t[e] + dABq[lo:hi, f:] @ W3t[e]
+        dW2[e] = dYc[lo:hi].T @ Hc[lo:hi]
+        dW1[e] = dABc[lo:hi, :f].T @ Xc[lo:hi]
+        dW3[e] = dABc[lo:hi, f:].T @ Xc[lo:hi]
+    AB = host(L.ab)
+    ga, gb = AB[:, :f].astype(np.float64), AB[:, f:].astype(np.float64)
+    s_ = ref.sigmoid(ga)
+    errs = {
+        "a": normwise_err(AB[:, :f], a), "b": normwise_err(AB[:, f:], b),
+        "y_perm": normwise_err(host(L.y_perm), y),
+        "da": normwise_err(dAB[:, :f], dh * gb * s_ * (1 + ga * (1 - s_))),
+        "db": normwise_err(dAB[:, f:], dh * ga * s_),
+        "dx_perm": normwise_err(host(L.dx_perm), dx),
+        "dW1": normwise_err(host(L.dW1), dW1), "dW3": normwise_err(host(L.dW3), dW3),
+        "dW2": normwise_err(host(L.dW2), dW2),
+    }
+    print({k: f"{v:.2e}" for k, v in errs.items()})
+    bad = {k: v for k, v in errs.items() if v > 1e-2}
+    assert not bad, bad

@@ -93,3 +93,58 @@ def test_segment_cols_equals_rows_of_transposed_segments():
         assert np.array_equal(codes[lo:hi], c2.T) and np.array_equal(scales[e], s2.T)
     deq = mx.dequantize_segment_cols(codes, scales, offsets)
     assert np.abs(deq - v).max() <= np.abs(v).max() * 2.0 ** -4   # half-ulp of a 3-bit mantissa
+
+
+def _mx_case(seed, T=40, d=64, f=96, E=4, k=2):
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((T, d))
+    W1 = rng.standard_normal((E, f, d)) * 0.3
+    W3 = rng.standard_normal((E, f, d)) * 0.3
+    W2 = rng.standard_normal((E, d, f)) * 0.3
+    dy = rng.standard_normal((T, d))
+    idx = np.stack([rng.permutation(E)[:k] for _ in range(T)]).astype(np.int32)
+    g = rng.dirichlet(np.ones(k), size=T)
+    return x, W1, W3, W2, dy, idx, g
+
+
+def test_mx_layer_without_quantisation_is_the_plain_layer():
+    from oracle import moe_ref as ref
+    x, W1, W3, W2, dy, idx, g = _mx_case(1)
+    out = mx.mx_layer(x, W1, W3, W2, 2, idx, g, dy, quant=False, bf16=False)
+    fw = ref.layer_forward(x, W1, W3, W2, 2, topk_idx=idx, gates=g)
+    bw = ref.layer_backward(fw, dy, x, W1, W3, W2, learned=False)
+    for key, want in [("y", fw["y"]), ("dx", bw["dx"]), ("dW1", bw["dW1"]), ("dW3", bw["dW3"]),
+                      ("dW2", bw["dW2"]), ("dgates", bw["dgates"])]:
+        assert np.allclose(out[key], want, rtol=1e-12, atol=1e-12), key
+
+
+def test_mx_layer_on_grid_operands_forward_gemm_exact():
+    """Operands already on the MXFP8 grid quantise to themselves: the first forward GEMM
+    of the MXFP8 layer then equals the unquantised one exactly."""
+    x, W1, W3, W2, dy, idx, g = _mx_case(2)
+    # snap x and W1/W3 onto the grid (quantise once); a second quantisation is the identity
+    xg = mx.dequantize_rows(*mx.quantize_rows(x))
+    W1g = mx.dequantize_rows(*mx.quantize_rows(W1.reshape(-1, 64))).reshape(W1.shape)
+    W3g = mx.dequantize_rows(*mx.quantize_rows(W3.reshape(-1, 64))).reshape(W3.shape)
+    assert np.array_equal(mx.dequantize_rows(*mx.quantize_rows(xg)), xg)
+    Wq = mx.mx_expert_weights(W1g[0], W3g[0], W2[0])
+    a_q, b_q, _, _ = mx.mx_expert_fwd(xg[:10], Wq, quant=True, bf16=False)
+    assert np.array_equal(a_q, xg[:10] @ W1g[0].T) and np.array_equal(b_q, xg[:10] @ W3g[0].T)
+
+
+def test_mx_layer_error_is_the_formats():
+    """Quantisation changes the layer by a few percent (a 3-bit mantissa), not by more."""
+    x, W1, W3, W2, dy, idx, g = _mx_case(3, T=64, d=128, f=128)
+    q = mx.mx_layer(x, W1, W3, W2, 2, idx, g, dy, quant=True)
+    p = mx.mx_layer(x, W1, W3, W2, 2, idx, g, dy, quant=False, bf16=False)
+    for key in ("y", "dx", "dW1", "dW3", "dW2"):
+        rel = np.abs(q[key] - p[key]).max() / np.abs(p[key]).max()
+        assert 1e-3 < rel < 0.25, (key, rel)
+
+
+def test_bf16_round_matches_torch():
+    import torch
+    rng = np.random.default_rng(11)
+    v = np.concatenate([rng.standard_normal(5000) * np.exp2(rng.integers(-40, 40, 5000)), [0.0, -0.0, 1.0, 3.0]])
+    want = torch.tensor(v, dtype=torch.float64).to(torch.float32).to(torch.bfloat16).to(torch.float64).numpy()
+    assert np.array_equal(mx.bf16_round(v), want)
