@@ -27,6 +27,7 @@
 #include "common.h"
 #include "gemm.h"
 #include "tilemap.h"
+#include "epilogue.h"
 
 namespace moe {
 
@@ -252,6 +253,10 @@ struct ProbBase {
     const int64_t v = (int64_t)e * seg_len;
     return v < seg_total ? (int)v : seg_total;
   }
+  // B rows that change tensor at k = k_split() (the pipelined kernel restarts its address
+  // streams there)
+  static constexpr bool K_SPLIT = false;
+  __device__ int k_split() const { return 0; }
 };
 
 // Forward GEMM1 with the SwiGLU epilogue: [a | b] = X_e [W1_e | W3_e]^T, the B tile's
@@ -270,13 +275,15 @@ struct ProbGemm1 : ProbBase {
     const bf16_t* W = (blk & 1) ? W3 : W1;
     return W + ((int64_t)e * f + col) * K;
   }
-  __device__ void epilogue_swiglu(int m, int hcol, float a, float b) const {
+  __device__ void epilogue_swiglu4(int m, int hcol, const float (&a)[4], const float (&b)[4]) const {
     bf16_t* abr = ab + (int64_t)m * 2 * f;
-    abr[hcol] = f2bf(a);
-    abr[f + hcol] = f2bf(b);
-    h[(int64_t)m * f + hcol] = f2bf(a * sigmoidf_(a) * b);
+    store_bf16x4(abr + hcol, a);
+    store_bf16x4(abr + f + hcol, b);
+    float hv[4];
+#pragma unroll
+    for (int c = 0; c < 4; c++) hv[c] = a[c] * sigmoidf_(a[c]) * b[c];
+    store_bf16x4(h + (int64_t)m * f + hcol, hv);
   }
-  __device__ void epilogue(int, int, int, float) const {}
 };
 
 // y_perm = h W2_e^T
@@ -289,7 +296,7 @@ struct ProbGemm2 : ProbBase {
   bf16_t* Y = nullptr;
   __device__ const bf16_t* a_row(int, int m) const { return Hm + (int64_t)m * K; }
   __device__ const bf16_t* b_row(int e, int n) const { return W2 + ((int64_t)e * N + n) * K; }
-  __device__ void epilogue(int, int m, int n, float v) const { Y[(int64_t)m * N + n] = f2bf(v); }
+  __device__ void epilogue4(int, int m, int n, const float (&v)[4]) const { store_bf16x4(Y + (int64_t)m * N + n, v); }
 };
 
 // dh = dy_e W2_e (B = W2_e read [k=d][n=f]) with the SwiGLU-gradient epilogue
@@ -302,13 +309,20 @@ struct ProbDgrad2 : ProbBase {
   bf16_t* dab = nullptr;
   __device__ const bf16_t* a_row(int, int m) const { return dY + (int64_t)m * K; }
   __device__ const bf16_t* b_row(int e, int k) const { return W2 + ((int64_t)e * K + k) * N; }
-  __device__ void epilogue(int, int m, int n, float dh) const {
+  __device__ void epilogue4(int, int m, int n, const float (&dh)[4]) const {
     const bf16_t* abr = ab + (int64_t)m * 2 * N;
-    const float a = bf2f(abr[n]), b = bf2f(abr[N + n]);
-    const float s = sigmoidf_(a);
+    float a[4], b[4], da[4], db[4];
+    load_bf16x4(abr + n, a);
+    load_bf16x4(abr + N + n, b);
+#pragma unroll
+    for (int c = 0; c < 4; c++) {
+      const float s = sigmoidf_(a[c]);
+      da[c] = dh[c] * b[c] * s * (1.f + a[c] * (1.f - s));
+      db[c] = dh[c] * a[c] * s;
+    }
     bf16_t* o = dab + (int64_t)m * 2 * N;
-    o[n] = f2bf(dh * b * s * (1.f + a * (1.f - s)));
-    o[N + n] = f2bf(dh * a * s);
+    store_bf16x4(o + n, da);
+    store_bf16x4(o + N + n, db);
   }
 };
 
@@ -322,7 +336,9 @@ struct ProbWgrad2 : ProbBase {
   bf16_t* dW2 = nullptr;
   __device__ const bf16_t* a_row(int, int r) const { return dY + (int64_t)r * M; }
   __device__ const bf16_t* b_row(int, int r) const { return Hm + (int64_t)r * N; }
-  __device__ void epilogue(int e, int m, int n, float v) const { dW2[((int64_t)e * M + m) * N + n] = f2bf(v); }
+  __device__ void epilogue4(int e, int m, int n, const float (&v)[4]) const {
+    store_bf16x4(dW2 + ((int64_t)e * M + m) * N + n, v);
+  }
 };
 
 // dx_e = [da | db] [W1_e ; W3_e]: K = 2f, B rows k < f from W1, else W3 (read [k][n=d])
@@ -338,7 +354,9 @@ struct ProbDgrad1 : ProbBase {
   __device__ const bf16_t* b_row(int e, int k) const {
     return k < f ? W1 + ((int64_t)e * f + k) * N : W3 + ((int64_t)e * f + (k - f)) * N;
   }
-  __device__ void epilogue(int, int m, int n, float v) const { dX[(int64_t)m * N + n] = f2bf(v); }
+  static constexpr bool K_SPLIT = true;
+  __device__ int k_split() const { return f; }
+  __device__ void epilogue4(int, int m, int n, const float (&v)[4]) const { store_bf16x4(dX + (int64_t)m * N + n, v); }
 };
 
 // [dW1_e ; dW3_e] [2f, d] = [da | db]_e^T X_e: A[m][k=r] = dab[r][m], B[k=r][n] = x_perm[r][n]
@@ -352,9 +370,9 @@ struct ProbWgrad1 : ProbBase {
   bf16_t* dW1 = nullptr; bf16_t* dW3 = nullptr;
   __device__ const bf16_t* a_row(int, int r) const { return dab + (int64_t)r * M; }
   __device__ const bf16_t* b_row(int, int r) const { return X + (int64_t)r * N; }
-  __device__ void epilogue(int e, int m, int n, float v) const {
+  __device__ void epilogue4(int e, int m, int n, const float (&v)[4]) const {
     bf16_t* W = m < f ? dW1 + ((int64_t)e * f + m) * N : dW3 + ((int64_t)e * f + (m - f)) * N;
-    W[n] = f2bf(v);
+    store_bf16x4(W + n, v);
   }
 };
 
@@ -368,7 +386,11 @@ struct ProbRouterFwd : ProbBase {
   float* L = nullptr;
   __device__ const bf16_t* a_row(int, int m) const { return X + (int64_t)m * K; }
   __device__ const bf16_t* b_row(int, int n) const { return Wr + (int64_t)n * K; }
-  __device__ void epilogue(int, int m, int n, float v) const { L[(int64_t)m * N + n] = v + (bias ? bias[n] : 0.f); }
+  __device__ void epilogue4(int, int m, int n, const float (&v)[4]) const {
+#pragma unroll
+    for (int c = 0; c < 4; c++)
+      if (n + c < N) L[(int64_t)m * N + n + c] = v[c] + (bias ? bias[n + c] : 0.f);
+  }
 };
 
 // dx_r = dlogits Wr: A = dlogits [T][E] float (rounded to bf16 on staging), B[k=e][n] = Wr[e][n]
@@ -458,30 +480,68 @@ struct PipeOperand {
   typedef int v4i __attribute__((ext_vector_type(4)));
   v4i reg[PER_THREAD];
 
-  // rows are mn (KC) or k (MN-contiguous); rowptr(r) -> element (r, 0); rows r >= row_end
-  // read as zero; KC: columns start at col0 (always in range); MN: columns [col0, col_end)
-  // are valid.
+  // Scalar load state of the operand for the load cursor (kept in scalar registers and
+  // shared by both register stages): per segment of this wave, the address of its first
+  // row at the current k-step, the row stride and, for K-contiguous tiles, the bytes it
+  // may read.  Rows are mn (K-contiguous tiles) or k (MN-contiguous tiles).  Set up once
+  // per tile (begin); each k-step then moves the addresses by one add (next).
+  struct Stream {
+    const char* ptr[PER_THREAD];
+    uint32_t bytes[PER_THREAD];  // K-contiguous: bytes readable from ptr
+    uint32_t rb;                 // bytes between consecutive rows
+    int k_left;                  // MN-contiguous: rows left from this step to the reduction end
+    uint32_t col_bytes;          // MN-contiguous: valid bytes of a row
+  };
+
+  // K-contiguous: rows [row0, row_end) valid, k-step starting at column kt
   template <class RowPtr>
-  __device__ __forceinline__ void load(RowPtr rowptr, int row0, int row_end, int col0, int col_end, int wave,
-                                       int lane, bool live = true) {
+  static __device__ __forceinline__ void begin_kc(Stream& st, RowPtr rowptr, int row0, int row_end, int kt, int wave,
+                                                  bool live) {
+    st.rb = (uint32_t)((rowptr(row0 + 1) - rowptr(row0)) * 2);
 #pragma unroll
     for (int i = 0; i < PER_THREAD; i++) {
-      const int s = wave + NW * i;  // wave is wave-uniform (readfirstlane), so the resource stays scalar
-      const int r0 = row0 + s * ROWS_PER_SEG;
-      const bf16_t* base = rowptr(r0) + col0;
-      const int64_t stride = rowptr(r0 + 1) - rowptr(r0);
+      const int r0 = row0 + (wave + NW * i) * ROWS_PER_SEG;
+      st.ptr[i] = reinterpret_cast<const char*>(rowptr(r0) + kt);
       int valid = live ? row_end - r0 : 0;
       valid = valid < 0 ? 0 : (valid > ROWS_PER_SEG ? ROWS_PER_SEG : valid);
-      uint32_t bytes = 0;
-      if (valid > 0) {
-        const int last_cols = KC ? TK : (col_end - col0 < BMN ? col_end - col0 : BMN);
-        bytes = (uint32_t)((valid - 1) * stride * 2 + last_cols * 2);
+      st.bytes[i] = valid > 0 ? (uint32_t)(valid - 1) * st.rb + TK * 2 : 0u;
+    }
+  }
+  // MN-contiguous: k rows [k0, k_end) valid, columns [col0, col_end) valid
+  template <class RowPtr>
+  static __device__ __forceinline__ void begin_mn(Stream& st, RowPtr rowptr, int k0, int k_end, int col0, int col_end,
+                                                  int wave, bool live) {
+    st.rb = (uint32_t)((rowptr(k0 + 1) - rowptr(k0)) * 2);
+#pragma unroll
+    for (int i = 0; i < PER_THREAD; i++)
+      st.ptr[i] = reinterpret_cast<const char*>(rowptr(k0 + (wave + NW * i) * ROWS_PER_SEG) + col0);
+    st.k_left = live ? k_end - k0 : 0;
+    st.col_bytes = (uint32_t)((col_end - col0 < BMN ? col_end - col0 : BMN) * 2);
+  }
+  // the next k-step of the same rows
+  static __device__ __forceinline__ void next(Stream& st) {
+#pragma unroll
+    for (int i = 0; i < PER_THREAD; i++) st.ptr[i] += KC ? TK * 2 : (int64_t)TK * st.rb;
+    if constexpr (!KC) st.k_left -= TK;
+  }
+
+  __device__ __forceinline__ void issue(const Stream& st, int wave, int lane) {
+#pragma unroll
+    for (int i = 0; i < PER_THREAD; i++) {
+      const int s = wave + NW * i;
+      uint32_t bytes;
+      if constexpr (KC) {
+        bytes = st.bytes[i];
+      } else {
+        int valid = st.k_left - s * ROWS_PER_SEG;
+        valid = valid < 0 ? 0 : (valid > ROWS_PER_SEG ? ROWS_PER_SEG : valid);
+        bytes = valid > 0 ? (uint32_t)(valid - 1) * st.rb + st.col_bytes : 0u;
       }
       const int r = lane / CPR, p = lane % CPR;
       const int c = swz(s * ROWS_PER_SEG + r, p);
-      const uint32_t voff = (uint32_t)(r * stride * 2 + c * 16);
-      // a dead stage (past the reduction) is a zero-byte resource: no memory is touched
-      reg[i] = __builtin_amdgcn_raw_buffer_load_b128(make_rsrc(base, bytes), voff, 0, 0);
+      const uint32_t voff = (uint32_t)r * st.rb + (uint32_t)(c * 16);
+      // a zero-byte resource (rows past the end, steps past the last tile) reads nothing
+      reg[i] = __builtin_amdgcn_raw_buffer_load_b128(make_rsrc(st.ptr[i], bytes), voff, 0, 0);
     }
   }
   __device__ __forceinline__ void store(char* lds_tile, int wave, int lane) const {
@@ -514,7 +574,8 @@ struct PipeOperand {
 }  // namespace
 
 template <class Cfg, class Prob, int TK>
-__global__ void __launch_bounds__(Cfg::NT) grouped_gemm_pipe_kernel(const Prob p) {
+__global__ void __launch_bounds__(Cfg::NT) __attribute__((amdgpu_waves_per_eu(TK == 32 ? 4 : 2)))
+grouped_gemm_pipe_kernel(const Prob p) {
   constexpr int BM = Cfg::BM, BN = Cfg::BN, NT = Cfg::NT;
   constexpr int WTM = Cfg::WTM, WTN = Cfg::WTN;
   constexpr int NW = NT / 64;
@@ -524,110 +585,173 @@ __global__ void __launch_bounds__(Cfg::NT) grouped_gemm_pipe_kernel(const Prob p
   __shared__ __attribute__((aligned(1024))) char sm0[STAGE_BYTES];
   __shared__ __attribute__((aligned(1024))) char sm1[STAGE_BYTES];
   __shared__ int s_map[kMaxExperts + 1];
+  __shared__ int s_seg[kMaxExperts + 1];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wave_m = wave / Cfg::WAVES_N, wave_n = wave % Cfg::WAVES_N;
   const int E = p.E;
-  auto seg = [&](int e) { return p.seg(e); };
+  // group starts are read once into LDS: the tile walk then never waits on global loads
+  // (a global load there would also drain the operand loads in flight)
+  for (int e = tid; e <= E; e += NT) s_seg[e] = p.seg(e);
+  __syncthreads();
+  auto seg = [&](int e) { return s_seg[e]; };
 
   const int total_tiles = build_tile_map<Prob::GROUP, BM, BN, NT>(s_map, seg, E, p.M, p.N, tid);
   const int G = gridDim.x;
   const int wg = xcd_logical_wg();
 
-  for (int t = wg; t < total_tiles; t += G) {
-    const TileRange tr = tile_at<Prob::GROUP, BM, BN>(t, s_map, seg, E, p.M, p.N, p.K);
-    const int e = tr.e, m0 = tr.m0, m_end = tr.m_end, n0 = tr.n0, k_beg = tr.k_beg, k_end = tr.k_end;
+  if (wg >= total_tiles) return;  // uniform over the workgroup
+  // tile ranges are workgroup-uniform: keep them in scalar registers
+  auto tile = [&](int t) {
+    TileRange r = tile_at<Prob::GROUP, BM, BN>(t, s_map, seg, E, p.M, p.N, p.K);
+    r.e = __builtin_amdgcn_readfirstlane(r.e);
+    r.m0 = __builtin_amdgcn_readfirstlane(r.m0);
+    r.m_end = __builtin_amdgcn_readfirstlane(r.m_end);
+    r.n0 = __builtin_amdgcn_readfirstlane(r.n0);
+    r.k_beg = __builtin_amdgcn_readfirstlane(r.k_beg);
+    r.k_end = __builtin_amdgcn_readfirstlane(r.k_end);
+    return r;
+  };
 
-    f32x16 acc[WTM][WTN];
+  // The workgroup's tiles form one stream of k-steps: every tile takes
+  // max(1, ceil(k range / TK)) steps (a tile with an empty reduction still runs one step
+  // on zero operands and stores its zeros).  The load cursor runs up to three steps ahead
+  // of the MFMAs across tile boundaries, so the next tile's first stages are in flight
+  // while the current tile's epilogue stores.
+  struct Cursor {
+    int t, k;
+    TileRange tr;
+  };
+  Cursor lc;
+  lc.t = wg;
+  lc.tr = tile(wg);
+  lc.k = lc.tr.k_beg;
+  // address streams of the two operands at the load cursor
+  typename OA::Stream sa;
+  typename OB::Stream sb;
+  auto begin_streams = [&]() {
+    const TileRange& r = lc.tr;
+    const bool live = lc.t < total_tiles;
+    if constexpr (Prob::A_KC)
+      OA::begin_kc(sa, [&](int x) { return p.a_row(r.e, x); }, r.m0, r.m_end, lc.k, wave, live && lc.k < r.k_end);
+    else
+      OA::begin_mn(sa, [&](int x) { return p.a_row(r.e, x); }, lc.k, r.k_end, r.m0, r.m_end, wave, live);
+    if constexpr (Prob::B_KC)
+      OB::begin_kc(sb, [&](int x) { return p.b_row(r.e, x); }, r.n0, p.N, lc.k, wave, live && lc.k < r.k_end);
+    else
+      OB::begin_mn(sb, [&](int x) { return p.b_row(r.e, x); }, lc.k, r.k_end, r.n0, p.N, wave, live);
+  };
+  auto advance = [&]() {
+    lc.k += TK;
+    if (lc.k >= lc.tr.k_end) {
+      lc.t += G;
+      if (lc.t < total_tiles) lc.tr = tile(lc.t);
+      lc.k = lc.tr.k_beg;
+      begin_streams();
+    } else if (Prob::K_SPLIT && lc.k == p.k_split()) {
+      begin_streams();
+    } else {
+      OA::next(sa);
+      OB::next(sb);
+    }
+  };
+  begin_streams();
+
+  // two register stages (even / odd steps) in flight while two LDS buffers ping-pong
+  OA ra0, ra1;
+  OB rb0, rb1;
+  // loads are issued for every step (steps past the reduction or past the last tile read
+  // nothing through a zero-byte resource) so the compiler's wait counts see the same two
+  // stages in flight on every path
+  auto load_stage = [&](OA& ra, OB& rb) {
+    ra.issue(sa, wave, lane);
+    rb.issue(sb, wave, lane);
+    advance();
+  };
+  auto store_stage = [&](const OA& ra, const OB& rb, char* base) {
+    ra.store(base, wave, lane);
+    rb.store(base + OA::TILE_BYTES, wave, lane);
+  };
+
+  f32x16 acc[WTM][WTN];
+  auto zero_acc = [&]() {
 #pragma unroll
     for (int i = 0; i < WTM; i++)
 #pragma unroll
       for (int j = 0; j < WTN; j++)
 #pragma unroll
         for (int r = 0; r < 16; r++) acc[i][j][r] = 0.f;
+  };
+  auto compute = [&](const char* st) {
+#pragma unroll
+    for (int kk = 0; kk < TK / 16; kk++) {
+      bf16x8 af[WTM], bfr[WTN];
+#pragma unroll
+      for (int i = 0; i < WTM; i++) af[i] = OA::frag(st, kk, (wave_m * WTM + i) * 32, lane);
+#pragma unroll
+      for (int jj = 0; jj < WTN; jj++) bfr[jj] = OB::frag(st + OA::TILE_BYTES, kk, (wave_n * WTN + jj) * 32, lane);
+#pragma unroll
+      for (int i = 0; i < WTM; i++)
+#pragma unroll
+        for (int jj = 0; jj < WTN; jj++)
+          acc[i][jj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[jj], acc[i][jj], 0, 0, 0);
+    }
+  };
+  // LDS writes of this wave done, then every wave past the barrier
+  auto lds_barrier = [&]() {
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+  };
+  auto epilogue = [&](const TileRange& tr) { tile_epilogue<Prob, WTM, WTN>(p, acc, tr, wave_m, wave_n, lane); };
+  auto steps_of = [&](const TileRange& r) {
+    const int n = (r.k_end - r.k_beg + TK - 1) / TK;
+    return n < 1 ? 1 : n;
+  };
 
-    // two register stages (even / odd k-steps) in flight while two LDS buffers ping-pong
-    OA ra0, ra1;
-    OB rb0, rb1;
-    // loads are issued on every path (dead stages read nothing) so the compiler's
-    // wait counts see the same two stages in flight everywhere
-    auto load_stage = [&](OA& ra, OB& rb, int kt) {
-      const bool live = kt < k_end;
-      if constexpr (Prob::A_KC) ra.load([&](int r) { return p.a_row(e, r); }, m0, m_end, kt, 0, wave, lane, live);
-      else ra.load([&](int r) { return p.a_row(e, r); }, kt, k_end, m0, m_end, wave, lane, live);
-      if constexpr (Prob::B_KC) rb.load([&](int r) { return p.b_row(e, r); }, n0, p.N, kt, 0, wave, lane, live);
-      else rb.load([&](int r) { return p.b_row(e, r); }, kt, k_end, n0, p.N, wave, lane, live);
-    };
-    auto store_stage = [&](const OA& ra, const OB& rb, char* base) {
-      ra.store(base, wave, lane);
-      rb.store(base + OA::TILE_BYTES, wave, lane);
-    };
-    auto compute = [&](const char* st) {
-#pragma unroll
-      for (int kk = 0; kk < TK / 16; kk++) {
-        bf16x8 af[WTM], bfr[WTN];
-#pragma unroll
-        for (int i = 0; i < WTM; i++) af[i] = OA::frag(st, kk, (wave_m * WTM + i) * 32, lane);
-#pragma unroll
-        for (int jj = 0; jj < WTN; jj++) bfr[jj] = OB::frag(st + OA::TILE_BYTES, kk, (wave_n * WTN + jj) * 32, lane);
-#pragma unroll
-        for (int i = 0; i < WTM; i++)
-#pragma unroll
-          for (int jj = 0; jj < WTN; jj++)
-            acc[i][jj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[jj], acc[i][jj], 0, 0, 0);
-      }
-    };
-    // LDS writes of this wave done, then every wave past the barrier
-    auto lds_barrier = [&]() {
-      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-      __builtin_amdgcn_s_barrier();
-      asm volatile("" ::: "memory");
-    };
+  // compute cursor: tile ct (range ctr), step cs of its ncs steps
+  int ct = wg;
+  TileRange ctr = lc.tr;
+  int ncs = steps_of(ctr), cs = 0;
+  zero_acc();
 
-    const int nk = (k_end - k_beg + TK - 1) / TK;
-    if (nk > 0) {
-      load_stage(ra0, rb0, k_beg);
-      load_stage(ra1, rb1, k_beg + TK);
-      lds_barrier();  // every wave is done reading the previous tile's buffers
-      store_stage(ra0, rb0, sm0);
-      load_stage(ra0, rb0, k_beg + 2 * TK);
-      lds_barrier();
-      // k-step it computes buffer it % 2; stage it+1 sits in registers (set (it+1) % 2) and
-      // is written to the other buffer; that set is then refilled with stage it+3
-      for (int it = 0; it < nk; it += 2) {
-        compute(sm0);
-        if (it + 1 < nk) store_stage(ra1, rb1, sm1);
-        load_stage(ra1, rb1, k_beg + (it + 3) * TK);
-        lds_barrier();
-        if (it + 1 < nk) compute(sm1);
-        if (it + 2 < nk) store_stage(ra0, rb0, sm0);
-        load_stage(ra0, rb0, k_beg + (it + 4) * TK);
-        lds_barrier();
+  // step s sits in register set s % 2 and is computed from LDS buffer s % 2
+  load_stage(ra0, rb0);  // step 0
+  load_stage(ra1, rb1);  // step 1
+  store_stage(ra0, rb0, sm0);
+  load_stage(ra0, rb0);  // step 2
+  lds_barrier();
+  // one exit, at the bottom: a workgroup whose last tile ends on an even step runs one
+  // more (discarded) odd step.  Exits after both halves would give the compiler a path
+  // into the loop head with the other load order, and with it conservative waits.
+  bool done = false;
+  auto finish_step = [&]() {
+    if (++cs == ncs) {
+      epilogue(ctr);
+      ct += G;
+      if (ct < total_tiles) {
+        ctr = tile(ct);
+        ncs = steps_of(ctr);
+        cs = 0;
+        zero_acc();
+      } else {
+        done = true;
       }
     }
-
-#pragma unroll
-    for (int i = 0; i < WTM; i++) {
-#pragma unroll
-      for (int r = 0; r < 16; r++) {
-        const int m = m0 + (wave_m * WTM + i) * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
-        if (m >= m_end) continue;
-        if constexpr (Prob::EPI == Epi::SwiGLU) {
-#pragma unroll
-          for (int j = 0; j < WTN; j += 2) {
-            const int hcol = n0 / 2 + ((wave_n * WTN + j) >> 1) * 32 + (lane & 31);
-            if (hcol < p.N / 2) p.epilogue_swiglu(m, hcol, acc[i][j][r], acc[i][j + 1][r]);
-          }
-        } else {
-#pragma unroll
-          for (int j = 0; j < WTN; j++) {
-            const int n = n0 + (wave_n * WTN + j) * 32 + (lane & 31);
-            if (n < p.N) p.epilogue(e, m, n, acc[i][j][r]);
-          }
-        }
-      }
-    }
+  };
+  for (;;) {
+    compute(sm0);
+    store_stage(ra1, rb1, sm1);
+    load_stage(ra1, rb1);
+    lds_barrier();
+    finish_step();
+    compute(sm1);
+    store_stage(ra0, rb0, sm0);
+    load_stage(ra0, rb0);
+    lds_barrier();
+    if (!done) finish_step();
+    if (done) break;
   }
 }
 
@@ -739,7 +863,7 @@ hipError_t dgrad2_bf16(const GemmShape& s, const int* offsets, const bf16_t* dY,
   ProbDgrad2 p;
   p.M = s.R; p.N = s.f; p.K = s.d; p.E = s.E; p.offsets = offsets;
   p.dY = dY; p.W2 = W2; p.ab = ab; p.dab = dab;
-  return launch(tile_for("DGRAD2", Tile::t128x256w8, 32), p, st);
+  return launch(tile_for("DGRAD2", Tile::t128x256w8, 64), p, st);
 }
 hipError_t wgrad2_bf16(const GemmShape& s, const int* offsets, const bf16_t* H, const bf16_t* dY, bf16_t* dW2,
                        hipStream_t st) {
