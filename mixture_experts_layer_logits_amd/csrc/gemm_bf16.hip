@@ -446,6 +446,8 @@ __global__ void sum_splits_kernel(int64_t n, int nsplit, const float* __restrict
 // ---------------------------------------------------------------------------------------
 namespace {
 
+typedef __attribute__((address_space(3))) void lds_void_t;
+
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 }
@@ -544,6 +546,28 @@ struct PipeOperand {
       reg[i] = __builtin_amdgcn_raw_buffer_load_b128(make_rsrc(st.ptr[i], bytes), voff, 0, 0);
     }
   }
+  // The same loads straight into LDS (buffer_load ... lds): lane l of a wave's segment
+  // lands at segment base + 16 l, which is where store() puts it; lanes past the
+  // resource's byte count write zeros.
+  static __device__ __forceinline__ void dma(const Stream& st, char* lds_tile, int wave, int lane) {
+#pragma unroll
+    for (int i = 0; i < PER_THREAD; i++) {
+      const int s = wave + NW * i;
+      uint32_t bytes;
+      if constexpr (KC) {
+        bytes = st.bytes[i];
+      } else {
+        int valid = st.k_left - s * ROWS_PER_SEG;
+        valid = valid < 0 ? 0 : (valid > ROWS_PER_SEG ? ROWS_PER_SEG : valid);
+        bytes = valid > 0 ? (uint32_t)(valid - 1) * st.rb + st.col_bytes : 0u;
+      }
+      const int r = lane / CPR, p = lane % CPR;
+      const int c = swz(s * ROWS_PER_SEG + r, p);
+      const uint32_t voff = (uint32_t)r * st.rb + (uint32_t)(c * 16);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(make_rsrc(st.ptr[i], bytes), (lds_void_t*)(lds_tile + s * 1024), 16,
+                                               voff, 0, 0, 0);
+    }
+  }
   __device__ __forceinline__ void store(char* lds_tile, int wave, int lane) const {
 #pragma unroll
     for (int i = 0; i < PER_THREAD; i++)
@@ -573,8 +597,19 @@ struct PipeOperand {
 
 }  // namespace
 
+// Occupancy target: 8-wave tiles with 2x2 accumulator blocks per wave at a k-depth of 32
+// fit 4 waves per SIMD (two workgroups per compute unit) in 128 registers; tiles with
+// 4x4 blocks per wave keep their accumulators in AGPRs at one wave per SIMD.
+template <class Cfg, int TK>
+constexpr int pipe_waves_per_eu() {
+  return Cfg::WTM * Cfg::WTN >= 16 ? 1 : (TK == 32 && Cfg::WTM * Cfg::WTN <= 4 ? 4 : 2);
+}
+
+// Group starts and the tile map live in dynamic LDS sized by the expert count.
+static inline size_t pipe_dyn_lds_bytes(int E) { return (size_t)2 * (E + 1) * sizeof(int); }
+
 template <class Cfg, class Prob, int TK>
-__global__ void __launch_bounds__(Cfg::NT) __attribute__((amdgpu_waves_per_eu(TK == 32 ? 4 : 2)))
+__global__ void __launch_bounds__(Cfg::NT) __attribute__((amdgpu_waves_per_eu(pipe_waves_per_eu<Cfg, TK>())))
 grouped_gemm_pipe_kernel(const Prob p) {
   constexpr int BM = Cfg::BM, BN = Cfg::BN, NT = Cfg::NT;
   constexpr int WTM = Cfg::WTM, WTN = Cfg::WTN;
@@ -582,15 +617,19 @@ grouped_gemm_pipe_kernel(const Prob p) {
   using OA = PipeOperand<Prob::A_KC, BM, TK, NW>;
   using OB = PipeOperand<Prob::B_KC, BN, TK, NW>;
   constexpr int STAGE_BYTES = OA::TILE_BYTES + OB::TILE_BYTES;
+  // three stage buffers as separate objects: the compiler then tracks the loads into each
+  // one separately and waits only for those a read of it depends on
   __shared__ __attribute__((aligned(1024))) char sm0[STAGE_BYTES];
   __shared__ __attribute__((aligned(1024))) char sm1[STAGE_BYTES];
-  __shared__ int s_map[kMaxExperts + 1];
-  __shared__ int s_seg[kMaxExperts + 1];
+  __shared__ __attribute__((aligned(1024))) char sm2[STAGE_BYTES];
+  extern __shared__ __attribute__((aligned(16))) int s_dyn[];
+  const int E = p.E;
+  int* s_map = s_dyn;
+  int* s_seg = s_dyn + E + 1;
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wave_m = wave / Cfg::WAVES_N, wave_n = wave % Cfg::WAVES_N;
-  const int E = p.E;
   // group starts are read once into LDS: the tile walk then never waits on global loads
   // (a global load there would also drain the operand loads in flight)
   for (int e = tid; e <= E; e += NT) s_seg[e] = p.seg(e);
@@ -616,9 +655,9 @@ grouped_gemm_pipe_kernel(const Prob p) {
 
   // The workgroup's tiles form one stream of k-steps: every tile takes
   // max(1, ceil(k range / TK)) steps (a tile with an empty reduction still runs one step
-  // on zero operands and stores its zeros).  The load cursor runs up to three steps ahead
-  // of the MFMAs across tile boundaries, so the next tile's first stages are in flight
-  // while the current tile's epilogue stores.
+  // on zero operands and stores its zeros).  The load cursor runs two steps ahead of the
+  // MFMAs across tile boundaries, so the next tile's first stages are in flight while the
+  // current tile's epilogue stores.
   struct Cursor {
     int t, k;
     TileRange tr;
@@ -658,20 +697,22 @@ grouped_gemm_pipe_kernel(const Prob p) {
   };
   begin_streams();
 
-  // two register stages (even / odd steps) in flight while two LDS buffers ping-pong
-  OA ra0, ra1;
-  OB rb0, rb1;
-  // loads are issued for every step (steps past the reduction or past the last tile read
-  // nothing through a zero-byte resource) so the compiler's wait counts see the same two
-  // stages in flight on every path
-  auto load_stage = [&](OA& ra, OB& rb) {
-    ra.issue(sa, wave, lane);
-    rb.issue(sb, wave, lane);
+  // operands of the load cursor's step go straight into a stage buffer; steps past the
+  // reduction or past the last tile read nothing and leave zeros
+  auto load_stage = [&](char* base) {
+    OA::dma(sa, base, wave, lane);
+    OB::dma(sb, base + OA::TILE_BYTES, wave, lane);
     advance();
   };
-  auto store_stage = [&](const OA& ra, const OB& rb, char* base) {
-    ra.store(base, wave, lane);
-    rb.store(base + OA::TILE_BYTES, wave, lane);
+  // this wave's loads into buf have landed (a read of buf makes the compiler wait for
+  // exactly those), then every wave meets: buf is complete, and every wave is done with
+  // the buffer computed in the previous step
+  auto ready = [&](const char* buf) {
+    typedef __attribute__((address_space(3))) const volatile int lds_int_t;
+    const int v = *(lds_int_t*)(buf + lane * 4);
+    asm volatile("s_waitcnt lgkmcnt(0)" ::"v"(v) : "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
   };
 
   f32x16 acc[WTM][WTN];
@@ -683,26 +724,37 @@ grouped_gemm_pipe_kernel(const Prob p) {
 #pragma unroll
         for (int r = 0; r < 16; r++) acc[i][j][r] = 0.f;
   };
+  // MFMAs of one k-step.  Fragments are double-buffered: slice kk+1 is read from LDS
+  // before slice kk's MFMAs issue, so its latency runs under them.
   auto compute = [&](const char* st) {
+    constexpr int KS = TK / 16;
+    bf16x8 af[2][WTM], bfr[2][WTN];
+    auto read = [&](int kk, int b) {
 #pragma unroll
-    for (int kk = 0; kk < TK / 16; kk++) {
-      bf16x8 af[WTM], bfr[WTN];
+      for (int i = 0; i < WTM; i++) af[b][i] = OA::frag(st, kk, (wave_m * WTM + i) * 32, lane);
 #pragma unroll
-      for (int i = 0; i < WTM; i++) af[i] = OA::frag(st, kk, (wave_m * WTM + i) * 32, lane);
+      for (int j = 0; j < WTN; j++) bfr[b][j] = OB::frag(st + OA::TILE_BYTES, kk, (wave_n * WTN + j) * 32, lane);
+    };
+    read(0, 0);
 #pragma unroll
-      for (int jj = 0; jj < WTN; jj++) bfr[jj] = OB::frag(st + OA::TILE_BYTES, kk, (wave_n * WTN + jj) * 32, lane);
+    for (int kk = 0; kk < KS; kk++) {
+      if (kk + 1 < KS) read(kk + 1, (kk + 1) & 1);
 #pragma unroll
       for (int i = 0; i < WTM; i++)
 #pragma unroll
-        for (int jj = 0; jj < WTN; jj++)
-          acc[i][jj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[jj], acc[i][jj], 0, 0, 0);
+        for (int j = 0; j < WTN; j++)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[kk & 1][i], bfr[kk & 1][j], acc[i][j], 0, 0, 0);
     }
-  };
-  // LDS writes of this wave done, then every wave past the barrier
-  auto lds_barrier = [&]() {
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
+    // issue order: slice 0's reads, then per slice the next slice's reads ahead of this
+    // slice's MFMAs (LDS reads: mask 0x100, MFMA: mask 0x8)
+    constexpr int NREAD = (Prob::A_KC ? 1 : 2) * WTM + (Prob::B_KC ? 1 : 2) * WTN;
+    __builtin_amdgcn_sched_group_barrier(0x100, NREAD, 0);
+#pragma unroll
+    for (int kk = 0; kk < KS; kk++) {
+      if (kk + 1 < KS) __builtin_amdgcn_sched_group_barrier(0x100, NREAD, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, WTM * WTN, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
   };
   auto epilogue = [&](const TileRange& tr) { tile_epilogue<Prob, WTM, WTN>(p, acc, tr, wave_m, wave_n, lane); };
   auto steps_of = [&](const TileRange& r) {
@@ -715,16 +767,6 @@ grouped_gemm_pipe_kernel(const Prob p) {
   TileRange ctr = lc.tr;
   int ncs = steps_of(ctr), cs = 0;
   zero_acc();
-
-  // step s sits in register set s % 2 and is computed from LDS buffer s % 2
-  load_stage(ra0, rb0);  // step 0
-  load_stage(ra1, rb1);  // step 1
-  store_stage(ra0, rb0, sm0);
-  load_stage(ra0, rb0);  // step 2
-  lds_barrier();
-  // one exit, at the bottom: a workgroup whose last tile ends on an even step runs one
-  // more (discarded) odd step.  Exits after both halves would give the compiler a path
-  // into the loop head with the other load order, and with it conservative waits.
   bool done = false;
   auto finish_step = [&]() {
     if (++cs == ncs) {
@@ -740,16 +782,24 @@ grouped_gemm_pipe_kernel(const Prob p) {
       }
     }
   };
+
+  // step s is loaded into buffer s % 3 two steps ahead; the buffer it overwrites was
+  // computed in the step before (every wave is past that step's barrier).  One exit, at
+  // the bottom: up to two discarded steps run after a workgroup's last tile.
+  load_stage(sm0);  // step 0
+  load_stage(sm1);  // step 1
   for (;;) {
+    ready(sm0);
+    load_stage(sm2);
     compute(sm0);
-    store_stage(ra1, rb1, sm1);
-    load_stage(ra1, rb1);
-    lds_barrier();
     finish_step();
+    ready(sm1);
+    load_stage(sm0);
     compute(sm1);
-    store_stage(ra0, rb0, sm0);
-    load_stage(ra0, rb0);
-    lds_barrier();
+    if (!done) finish_step();
+    ready(sm2);
+    load_stage(sm1);
+    compute(sm2);
     if (!done) finish_step();
     if (done) break;
   }
@@ -758,7 +808,8 @@ grouped_gemm_pipe_kernel(const Prob p) {
 // ---------------------------------------------------------------------------------------
 // Launchers: tile shape per GEMM (MOE_TILE_<GEMM>=128x256 etc. overrides the default)
 // ---------------------------------------------------------------------------------------
-enum class Tile { t128x128, t128x256, t256x128, t64x128, t32x128, t256x128w8, t128x256w8, t256x256w8 };
+enum class Tile { t128x128, t128x256, t256x128, t64x128, t32x128, t256x128w8, t128x256w8, t256x256w8, t256x256w4,
+                  t128x256w2, t128x256m1 };
 
 static bool parse_tile(const char* v, Tile* t) {
   if (!v) return false;
@@ -766,7 +817,8 @@ static bool parse_tile(const char* v, Tile* t) {
                                                   {"256x128", Tile::t256x128},
                                                   {"64x128", Tile::t64x128},   {"32x128", Tile::t32x128},
                                                   {"256x128w8", Tile::t256x128w8}, {"128x256w8", Tile::t128x256w8},
-                                                  {"256x256w8", Tile::t256x256w8}};
+                                                  {"256x256w8", Tile::t256x256w8}, {"256x256w4", Tile::t256x256w4},
+                                                  {"128x256w2", Tile::t128x256w2}, {"128x256m1", Tile::t128x256m1}};
   for (const auto& e : tab)
     if (strcmp(v, e.s) == 0) { *t = e.t; return true; }
   return false;
@@ -792,10 +844,10 @@ static TileChoice tile_for(const char* name, Tile dflt, int dflt_bk) {
 // Persistent grid: resident workgroups per CU x CUs, capped by the tile bound known on the
 // host, rounded to a multiple of the 8 XCDs.
 template <class Cfg, class Prob, class Kern>
-static hipError_t launch_kernel(Kern kern, const Prob& p, hipStream_t st, int& occ) {
+static hipError_t launch_kernel(Kern kern, const Prob& p, hipStream_t st, int& occ, size_t dyn_lds = 0) {
   if (occ == 0) {
     int o = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&o, kern, Cfg::NT, 0) != hipSuccess || o < 1) o = 1;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&o, kern, Cfg::NT, dyn_lds) != hipSuccess || o < 1) o = 1;
     occ = o;
   }
   int64_t bound;
@@ -806,24 +858,29 @@ static hipError_t launch_kernel(Kern kern, const Prob& p, hipStream_t st, int& o
   if (bound < G) G = bound;
   G = ((G + 7) / 8) * 8;
   if (G < 8) G = 8;
-  hipLaunchKernelGGL(kern, dim3((unsigned)G), dim3(Cfg::NT), 0, st, p);
+  hipLaunchKernelGGL(kern, dim3((unsigned)G), dim3(Cfg::NT), dyn_lds, st, p);
   return hipGetLastError();
 }
 
 template <class Cfg, class Prob, int TK>
 static hipError_t launch_pipe(const Prob& p, hipStream_t st) {
-  static int occ = 0;
-  return launch_kernel<Cfg>(grouped_gemm_pipe_kernel<Cfg, Prob, TK>, p, st, occ);
+  // occupancy depends on the dynamic LDS, i.e. on the expert count: cache it per count
+  static int occ_e = -1, occ = 0;
+  if (occ_e != p.E) { occ_e = p.E; occ = 0; }
+  return launch_kernel<Cfg>(grouped_gemm_pipe_kernel<Cfg, Prob, TK>, p, st, occ, pipe_dyn_lds_bytes(p.E));
 }
 
 // bf16 problems use the pipelined kernel, the float-A router problems the register kernel
 template <class Cfg, class Prob>
 static hipError_t launch_cfg(const Prob& p, hipStream_t st, int bk) {
   if constexpr (std::is_same<typename Prob::TA, bf16_t>::value) {
+    // three stage buffers must fit the 160 KB of LDS with room for the tile map
+    constexpr bool fits64 = 3 * (Cfg::BM + Cfg::BN) * 64 * 2 <= 152 * 1024;
     if constexpr (Cfg::BM >= 64 && Cfg::BN >= 64) {
-      if (bk == 32) return launch_pipe<Cfg, Prob, 32>(p, st);
+      if (bk == 32 || !fits64) return launch_pipe<Cfg, Prob, 32>(p, st);
     }
-    return launch_pipe<Cfg, Prob, 64>(p, st);
+    if constexpr (fits64) return launch_pipe<Cfg, Prob, 64>(p, st);
+    return hipErrorInvalidConfiguration;
   } else {
     static int occ = 0;
     return launch_kernel<Cfg>(grouped_gemm_kernel<Cfg, Prob>, p, st, occ);
@@ -840,6 +897,9 @@ static hipError_t launch(TileChoice c, const Prob& p, hipStream_t st) {
     case Tile::t256x128w8: return launch_cfg<TileCfg<256, 128, 4, 2>>(p, st, c.bk);
     case Tile::t128x256w8: return launch_cfg<TileCfg<128, 256, 2, 4>>(p, st, c.bk);
     case Tile::t256x256w8: return launch_cfg<TileCfg<256, 256, 2, 4>>(p, st, c.bk);
+    case Tile::t256x256w4: return launch_cfg<TileCfg<256, 256, 2, 2>>(p, st, c.bk);
+    case Tile::t128x256w2: return launch_cfg<TileCfg<128, 256, 1, 2>>(p, st, c.bk);
+    case Tile::t128x256m1: return launch_cfg<TileCfg<128, 256, 1, 4>>(p, st, c.bk);
     default: return launch_cfg<TileCfg<128, 128, 2, 2>>(p, st, c.bk);
   }
 }
@@ -856,7 +916,7 @@ hipError_t gemm2_fwd_bf16(const GemmShape& s, const int* offsets, const bf16_t* 
   ProbGemm2 p;
   p.M = s.R; p.N = s.d; p.K = s.f; p.E = s.E; p.offsets = offsets;
   p.Hm = H; p.W2 = W2; p.Y = Y;
-  return launch(tile_for("GEMM2", Tile::t128x256w8, 32), p, st);
+  return launch(tile_for("GEMM2", Tile::t128x256w8, 64), p, st);
 }
 hipError_t dgrad2_bf16(const GemmShape& s, const int* offsets, const bf16_t* dY, const bf16_t* W2,
                        const bf16_t* ab, bf16_t* dab, hipStream_t st) {
@@ -870,7 +930,7 @@ hipError_t wgrad2_bf16(const GemmShape& s, const int* offsets, const bf16_t* H, 
   ProbWgrad2 p;
   p.M = s.d; p.N = s.f; p.K = s.R; p.E = s.E; p.offsets = offsets;
   p.dY = dY; p.Hm = H; p.dW2 = dW2;
-  return launch(tile_for("WGRAD2", Tile::t256x128w8, 32), p, st);
+  return launch(tile_for("WGRAD2", Tile::t256x256w8, 32), p, st);
 }
 hipError_t dgrad1_bf16(const GemmShape& s, const int* offsets, const bf16_t* dab, const bf16_t* W1,
                        const bf16_t* W3, bf16_t* dX, hipStream_t st) {
@@ -884,7 +944,7 @@ hipError_t wgrad1_bf16(const GemmShape& s, const int* offsets, const bf16_t* X, 
   ProbWgrad1 p;
   p.M = 2 * s.f; p.N = s.d; p.K = s.R; p.E = s.E; p.offsets = offsets; p.f = s.f;
   p.dab = dab; p.X = X; p.dW1 = dW1; p.dW3 = dW3;
-  return launch(tile_for("WGRAD1", Tile::t256x128w8, 32), p, st);
+  return launch(tile_for("WGRAD1", Tile::t256x256w8, 32), p, st);
 }
 hipError_t router_fwd_bf16(int T, int d, int E, const bf16_t* X, const bf16_t* Wr, const float* bias, float* L,
                            hipStream_t st) {
