@@ -1,6 +1,12 @@
 """Throughput of the MoE expert layer (forward + backward) on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+    python bench.py --profile-kernel NAME [--steps K] [--workload NAME]   # one call, K times
+    python bench.py --copy-mib N [--steps K]                              # plain copy, K times
+
+The last two forms run under rocprofv3 counter passes: one layer call (after one full
+step to set up its inputs) or a plain device copy of N MiB (the reference against which
+FETCH_SIZE / WRITE_SIZE are scaled).
 
 A step is one pass of the whole layer over one batch of synthetic, seeded input that is
 already resident in HBM: router scores, top-k routing, dispatch into per-expert buffers,
@@ -40,14 +46,20 @@ def parse():
     ap.add_argument("--workload", default="e128_k4_t8192")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-tokens", type=int, default=1024)
+    ap.add_argument("--profile-kernel", default=None, help="run only this call of the step, --steps times")
+    ap.add_argument("--copy-mib", type=int, default=0, help="run a plain device copy of this many MiB, --steps times")
     return ap.parse_args()
 
 
-def kernel_sources_digest(files):
+def kernel_sources_digest():
+    """Digest of every kernel source: stored traffic counters count only for the kernels
+    they were taken on."""
     h = hashlib.sha256()
-    for f in files:
-        with open(os.path.join(ROOT, "mixture_experts_layer_logits_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+    csrc = os.path.join(ROOT, "mixture_experts_layer_logits_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        if f.endswith((".hip", ".h", ".cpp")):
+            with open(os.path.join(csrc, f), "rb") as fh:
+                h.update(f.encode() + b"\0" + fh.read())
     return h.hexdigest()[:16]
 
 
@@ -146,6 +158,16 @@ def main():
         sys.exit(2)
     import torch
 
+    if args.copy_mib:
+        n = args.copy_mib << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(args.steps):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes": n, "steps": args.steps}), flush=True)
+        return
+
     import mixture_experts_layer_logits_amd as m
     import workloads
 
@@ -160,6 +182,16 @@ def main():
     L.forward(d_inp["x"], d_inp["W1"], d_inp["W3"], d_inp["W2"], Wr=d_inp["Wr"], bias=d_inp["router_bias"],
               topk_idx=d_inp["topk_idx"], gates=d_inp["gates"])
     calls = step_calls(m, L, d_inp, learned)
+
+    if args.profile_kernel:
+        for _, fn in calls:  # one whole step sets up every call's inputs
+            fn()
+        fn = dict(calls)[args.profile_kernel]
+        for _ in range(args.steps):
+            fn()
+        torch.cuda.synchronize()
+        print(json.dumps({"workload": w.name, "kernel": args.profile_kernel, "steps": args.steps}), flush=True)
+        return
 
     for _ in range(args.warmup):
         for _, fn in calls:
@@ -193,11 +225,15 @@ def main():
         if name in byt:
             e["gbs"] = round(byt[name] / (ms * 1e-3) / 1e9, 1)
         kernels[name] = e
+    # dominant kernel: the GEMM taking the most time; its roof is whichever of MFMA peak and
+    # HBM bandwidth bounds its algorithmic work from below
     dom = max(gem, key=lambda n: per_call_ms[n])
-    achieved = gem[dom] / (per_call_ms[dom] * 1e-3) / 1e12
     peak = PEAK_TFLOPS[w.gemm]
+    t_mfma = gem[dom] / (peak * 1e12)
+    t_hbm = byt[dom] / (PEAK_HBM_GBS * 1e9)
+    sec = per_call_ms[dom] * 1e-3
     traffic = None
-    digest = kernel_sources_digest(["gemm_bf16.hip", "gemm.h", "common.h"])
+    digest = kernel_sources_digest()
     if os.path.exists(TRAFFIC_FILE):
         try:
             rec = json.load(open(TRAFFIC_FILE)).get(f"{w.name}:{dom}")
@@ -205,14 +241,23 @@ def main():
                 traffic = rec["bytes_per_launch"]
         except Exception:
             traffic = None
-    roofline = {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 1), "peak": peak, "unit": "TFLOP/s",
-                "frac": round(achieved / peak, 4), "traffic": traffic,
-                "algorithmic_flops_per_launch": gem[dom]}
+    if t_hbm >= t_mfma:
+        achieved = byt[dom] / sec / 1e9
+        roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                    "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": traffic}
+    else:
+        achieved = gem[dom] / sec / 1e12
+        roofline = {"bound": "mfma", "achieved": round(achieved, 1), "peak": peak, "unit": "TFLOP/s",
+                    "frac": round(achieved / peak, 4), "traffic": traffic}
+    roofline.update({"kernel": dom, "ms_per_launch": round(per_call_ms[dom], 4),
+                     "algorithmic_bytes_per_launch": byt[dom], "algorithmic_flops_per_launch": gem[dom],
+                     "mfma_frac": round(gem[dom] / sec / 1e12 / peak, 4),
+                     "hbm_frac": round(byt[dom] / sec / 1e9 / PEAK_HBM_GBS, 4)})
     gemm_ms = sum(per_call_ms[n] for n in gem)
     out = {
         "metric": METRIC, "value": round(tokens_per_s, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": "bf16" if w.dtype == "bf16" else "f32", "data": "synthetic",
+        "vs_baseline": None, "dtype": w.gemm, "data": "synthetic",
         "config": {"workload": w.name, "T": w.T, "d": w.d, "f": w.f, "E": w.E, "k": w.k, "routing": w.routing,
                    "gemm": w.gemm},
         "roofline": roofline,
