@@ -12,6 +12,7 @@
 #include "common.h"
 #include "mx.h"
 #include "tilemap.h"
+#include "epilogue.h"
 
 namespace moe {
 
@@ -47,13 +48,21 @@ __device__ __forceinline__ float exp2i(int s) { return __uint_as_float((uint32_t
 
 namespace {
 
-// one thread per 32-element block of a row
+// one thread per 32-element block of a row.  il_rows > 0: the rows are E stacked weights
+// of il_rows rows each, written to the 32-row-interleaved pair layout of the forward GEMM
+// (block b of weight e lands at rows e * 2 il_rows + 64 (b / 32) + 32 il_which + b % 32).
 __global__ void mx_rows_kernel(int rows, int cols, const bf16_t* __restrict__ src, uint8_t* __restrict__ q,
-                               uint8_t* __restrict__ scales) {
+                               uint8_t* __restrict__ scales, int il_rows, int il_which) {
   const int nb = cols / kMxBlock;
   const int64_t b = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (b >= (int64_t)rows * nb) return;
   const bf16_t* p = src + b * kMxBlock;
+  int64_t ob = b;
+  if (il_rows > 0) {
+    const int64_t row = b / nb, e = row / il_rows, rr = row % il_rows;
+    const int64_t orow = e * 2 * il_rows + ((rr >> 5) << 6) + ((int64_t)il_which << 5) + (rr & 31);
+    ob = orow * nb + b % nb;
+  }
   float v[32];
 #pragma unroll
   for (int i = 0; i < 4; i++) {
@@ -75,10 +84,10 @@ __global__ void mx_rows_kernel(int rows, int cols, const bf16_t* __restrict__ sr
 #pragma unroll
     for (int j = 0; j < 4; j++) w[i] |= e4m3_rne(v[4 * i + j] * r1 * r2) << (8 * j);
   }
-  uint4* o = reinterpret_cast<uint4*>(q + b * kMxBlock);
+  uint4* o = reinterpret_cast<uint4*>(q + ob * kMxBlock);
   o[0] = make_uint4(w[0], w[1], w[2], w[3]);
   o[1] = make_uint4(w[4], w[5], w[6], w[7]);
-  scales[b] = (uint8_t)(s + 127);
+  scales[ob] = (uint8_t)(s + 127);
 }
 
 // Transposing quantiser: column c of the rows of segment e (blocks of 32 rows, restarting
@@ -100,14 +109,24 @@ struct TransQ {
   uint8_t* s;
   int64_t lds, s_seg;
   int col_off;
-  int nblocks;         // 32-row blocks to cover (padded total / 32)
 };
 
-__global__ void mx_trans_kernel(TransQ a) {
+// One workgroup per tile of 128 source rows (four 32-row blocks of one segment; output
+// segments are padded to 128 rows, so a tile never straddles two) by 64 columns.  Rows
+// are read as 16-byte chunks into LDS, each thread then quantises one 32-row block of one
+// column, and the codes leave through a second LDS tile as full 128-byte lines of the
+// transposed output.
+constexpr int kTransRows = 128, kTransCols = 64, kTransThreads = 256;
+constexpr int kTransOutPitch = kTransRows + 16;  // bytes per staged output row (bank spread)
+
+__global__ void __launch_bounds__(kTransThreads) mx_trans_kernel(TransQ a) {
   __shared__ int s_pstart[kMaxExperts + 1];
+  __shared__ __attribute__((aligned(16))) bf16_t s_in[kTransRows][kTransCols];
+  __shared__ __attribute__((aligned(16))) uint8_t s_out[kTransCols][kTransOutPitch];
+  const int tid = threadIdx.x;
   const bool padded = a.seg != nullptr;
   if (padded) {
-    if (threadIdx.x == 0) {
+    if (tid == 0) {
       int acc = 0;
       for (int e = 0; e < a.nseg; e++) {
         s_pstart[e] = acc;
@@ -118,53 +137,77 @@ __global__ void mx_trans_kernel(TransQ a) {
     }
     __syncthreads();
   }
-  const int c = blockIdx.x * blockDim.x + threadIdx.x;  // column
-  if (c >= a.cols) return;
-  for (int pb = blockIdx.y; pb < a.nblocks; pb += gridDim.y) {
-  const int prow = pb * kMxBlock;                       // first padded row of this block
-  int e, r0, r1;
-  int64_t qb, sb;
-  if (padded) {
-    if (prow >= s_pstart[a.nseg]) break;
-    int lo = 0, hi = a.nseg;  // segment with s_pstart[e] <= prow < s_pstart[e+1]
-    while (hi - lo > 1) {
-      const int mid = (lo + hi) >> 1;
-      if (s_pstart[mid] <= prow) lo = mid; else hi = mid;
+  const int c0 = blockIdx.x * kTransCols;
+  const int tiles_per_seg = (a.len + kTransRows - 1) / kTransRows;  // uniform mode
+  const int ntiles = padded ? s_pstart[a.nseg] / kTransRows : a.nseg * tiles_per_seg;
+  for (int tile = blockIdx.y; tile < ntiles; tile += gridDim.y) {
+    // source rows [r0, r1) of segment e; output rows start at local row `lrow` of the
+    // segment's output, nblk 32-row blocks are stored
+    int r0, r1, nblk;
+    int64_t qrow0, srow0;  // output offsets of (column 0, local row lrow)
+    if (padded) {
+      const int prow = tile * kTransRows;
+      int lo = 0, hi = a.nseg;  // segment with s_pstart[e] <= prow < s_pstart[e+1]
+      while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (s_pstart[mid] <= prow) lo = mid; else hi = mid;
+      }
+      r0 = a.seg[lo] + (prow - s_pstart[lo]);
+      r1 = a.seg[lo + 1];
+      nblk = 4;
+      qrow0 = prow;
+      srow0 = prow / kMxBlock;
+    } else {
+      const int e = tile / tiles_per_seg, local = (tile % tiles_per_seg) * kTransRows;
+      r0 = e * a.len + local;
+      r1 = (e + 1) * a.len;
+      nblk = (a.len - local) / kMxBlock < 4 ? (a.len - local) / kMxBlock : 4;
+      qrow0 = e * a.q_seg + a.col_off + local;
+      srow0 = e * a.s_seg + (a.col_off + local) / kMxBlock;
     }
-    e = lo;
-    r0 = a.seg[e] + (prow - s_pstart[e]);
-    r1 = a.seg[e + 1];
-    qb = (int64_t)c * a.ldq + prow;
-    sb = (int64_t)c * a.lds + prow / kMxBlock;
-  } else {
-    e = prow / a.len;
-    const int local = prow - e * a.len;
-    r0 = e * a.len + local;
-    r1 = (e + 1) * a.len;
-    qb = e * a.q_seg + (int64_t)c * a.ldq + a.col_off + local;
-    sb = e * a.s_seg + (int64_t)c * a.lds + (a.col_off + local) / kMxBlock;
-  }
-  float v[32];
-  float amax = 0.f;
+    // 128 rows x 128 bytes in 16-byte chunks, rows past the segment read as zero
 #pragma unroll
-  for (int i = 0; i < 32; i++) {
-    const int r = r0 + i;
-    v[i] = r < r1 ? bf2f(a.src[(int64_t)r * a.ld_src + c]) : 0.f;
-    amax = fmaxf(amax, fabsf(v[i]));
-  }
-  const int sexp = mx_scale_exp(amax);
-  const float f1 = exp2i(-sexp / 2), f2 = exp2i(-sexp - (-sexp / 2));
-  uint32_t w[8];
+    for (int i = 0; i < kTransRows * kTransCols * 2 / 16 / kTransThreads; i++) {
+      const int q = tid + kTransThreads * i, row = q >> 3, ch = q & 7;
+      uint4 v = make_uint4(0, 0, 0, 0);
+      if (r0 + row < r1 && c0 + ch * 8 < a.cols)  // columns come in whole 8-column chunks (cols % 32 == 0)
+        v = *reinterpret_cast<const uint4*>(a.src + (int64_t)(r0 + row) * a.ld_src + c0 + ch * 8);
+      *reinterpret_cast<uint4*>(&s_in[row][ch * 8]) = v;
+    }
+    __syncthreads();
+    {
+      const int c = tid & (kTransCols - 1), b = tid >> 6;  // column, 32-row block (one per wave)
+      float v[32];
+      float amax = 0.f;
 #pragma unroll
-  for (int i = 0; i < 8; i++) {
-    w[i] = 0;
+      for (int i = 0; i < 32; i++) {
+        v[i] = bf2f(s_in[b * 32 + i][c]);
+        amax = fmaxf(amax, fabsf(v[i]));
+      }
+      const int sexp = mx_scale_exp(amax);
+      const float f1 = exp2i(-sexp / 2), f2 = exp2i(-sexp - (-sexp / 2));
+      uint32_t w[8];
 #pragma unroll
-    for (int j = 0; j < 4; j++) w[i] |= e4m3_rne(v[4 * i + j] * f1 * f2) << (8 * j);
-  }
-  uint4* o = reinterpret_cast<uint4*>(a.q + qb);
-  o[0] = make_uint4(w[0], w[1], w[2], w[3]);
-  o[1] = make_uint4(w[4], w[5], w[6], w[7]);
-  a.s[sb] = (uint8_t)(sexp + 127);
+      for (int i = 0; i < 8; i++) {
+        w[i] = 0;
+#pragma unroll
+        for (int j = 0; j < 4; j++) w[i] |= e4m3_rne(v[4 * i + j] * f1 * f2) << (8 * j);
+      }
+      uint4* o = reinterpret_cast<uint4*>(&s_out[c][b * 32]);
+      o[0] = make_uint4(w[0], w[1], w[2], w[3]);
+      o[1] = make_uint4(w[4], w[5], w[6], w[7]);
+      if (b < nblk && c0 + c < a.cols) a.s[srow0 + (int64_t)(c0 + c) * a.lds + b] = (uint8_t)(sexp + 127);
+    }
+    __syncthreads();
+    // 64 output rows x (32 * nblk) bytes, 8 lanes per 128-byte row
+#pragma unroll
+    for (int i = 0; i < kTransCols * kTransRows / 16 / kTransThreads; i++) {
+      const int q = tid + kTransThreads * i, c = q >> 3, ch = q & 7;
+      if (ch * 16 < nblk * kMxBlock && c0 + c < a.cols)
+        *reinterpret_cast<uint4*>(a.q + qrow0 + (int64_t)(c0 + c) * a.ldq + ch * 16) =
+            *reinterpret_cast<const uint4*>(&s_out[c][ch * 16]);
+    }
+    __syncthreads();  // s_in / s_out are reused by the next tile
   }
 }
 
@@ -173,16 +216,30 @@ __global__ void mx_trans_kernel(TransQ a) {
 hipError_t mx_quantize_rows(int rows, int cols, const bf16_t* src, uint8_t* q, uint8_t* scales, hipStream_t st) {
   const int64_t n = (int64_t)rows * (cols / kMxBlock);
   if (n == 0) return hipSuccess;
-  hipLaunchKernelGGL(mx_rows_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, rows, cols, src, q, scales);
+  hipLaunchKernelGGL(mx_rows_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, rows, cols, src, q, scales,
+                     0, 0);
   return hipGetLastError();
 }
 
-static hipError_t launch_trans(TransQ a, int64_t total_rows_pad, hipStream_t st) {
-  a.nblocks = (int)((total_rows_pad + kMxBlock - 1) / kMxBlock);
-  if (a.cols == 0 || a.nblocks == 0) return hipSuccess;
-  const unsigned gy = (unsigned)(a.nblocks < 32768 ? a.nblocks : 32768);
-  dim3 grid((unsigned)((a.cols + 255) / 256), gy);
-  hipLaunchKernelGGL(mx_trans_kernel, grid, dim3(256), 0, st, a);
+// W1 / W3 [E][f][cols] into one [E][2f][cols] code array whose 32-row blocks alternate
+// W1, W3 (the column order of the forward GEMM's SwiGLU tiles)
+static hipError_t mx_quantize_w13(int E, int f, int cols, const bf16_t* W1, const bf16_t* W3, uint8_t* q,
+                                  uint8_t* scales, hipStream_t st) {
+  const int64_t n = (int64_t)E * f * (cols / kMxBlock);
+  if (n == 0) return hipSuccess;
+  const dim3 grid((unsigned)((n + 255) / 256));
+  hipLaunchKernelGGL(mx_rows_kernel, grid, dim3(256), 0, st, E * f, cols, W1, q, scales, f, 0);
+  hipLaunchKernelGGL(mx_rows_kernel, grid, dim3(256), 0, st, E * f, cols, W3, q, scales, f, 1);
+  return hipGetLastError();
+}
+
+// total_tiles: upper bound of 128-row tiles (padded mode: rows_pad / 128; uniform mode:
+// E * ceil(len / 128)); tiles past the device-side count exit at once.
+static hipError_t launch_trans(TransQ a, int64_t total_tiles, hipStream_t st) {
+  if (a.cols == 0 || total_tiles == 0) return hipSuccess;
+  const unsigned gy = (unsigned)(total_tiles < 16384 ? total_tiles : 16384);
+  dim3 grid((unsigned)((a.cols + kTransCols - 1) / kTransCols), gy);
+  hipLaunchKernelGGL(mx_trans_kernel, grid, dim3(kTransThreads), 0, st, a);
   return hipGetLastError();
 }
 
@@ -190,244 +247,314 @@ static hipError_t launch_trans(TransQ a, int64_t total_rows_pad, hipStream_t st)
 hipError_t mx_quantize_cols_seg(int rows, int cols, const int32_t* seg_offsets, int nseg, const bf16_t* src,
                                 uint8_t* q, uint8_t* scales, hipStream_t st) {
   const int rows_pad = rows + kMxSegPad * nseg;
-  TransQ a{src, cols, cols, seg_offsets, nseg, 0, q, rows_pad, 0, scales, rows_pad / kMxBlock, 0, 0, 0};
-  return launch_trans(a, rows_pad, st);
+  TransQ a{src, cols, cols, seg_offsets, nseg, 0, q, rows_pad, 0, scales, rows_pad / kMxBlock, 0, 0};
+  return launch_trans(a, rows_pad / kTransRows, st);
 }
 
 
 // ---------------------------------------------------------------------------------------
 // MXFP8 grouped GEMM: v_mfma_scale_f32_32x32x64_f8f6f4 with E4M3 operands and one E8M0
 // scale per 32 elements along K.  Every operand arrives K-contiguous from the quantisers
-// above (activations and forward weights row-wise; weight-gradient operands transposed,
-// per expert, 128-padded; backward weights transposed), so the kernel has one operand
-// layout.  Operand register layout of the instruction (per lane l, row/column l % 32,
-// h = l / 32): bytes 0..15 hold k in [16h, 16h + 16), bytes 16..31 hold k in
-// [32 + 16h, 32 + 16h + 16); the lane's scale byte covers the 32-block h of the 64-deep
-// step.  Pipeline as in the bf16 kernel: two register stages of bounded buffer loads,
-// two swizzled LDS buffers, one barrier per k-step; scale words ride along in registers.
+// above (activations and forward weights row-wise, the forward weights of GEMM1 in the
+// W1/W3 32-row interleave; weight-gradient operands transposed, per expert, 128-padded;
+// backward weights transposed), so the kernel has one operand layout and every operand
+// row range is linear.  Operand register layout of the instruction (per lane l,
+// row/column l % 32, h = l / 32): bytes 0..15 hold k in [16h, 16h + 16), bytes 16..31
+// hold k in [32 + 16h, 32 + 16h + 16); the lane's scale byte covers the 32-block h of
+// the 64-deep step.
+//
+// Pipeline as in the bf16 kernel: the workgroup's tiles form one stream of 128-deep
+// k-steps; each step's codes and scale words go straight from global memory into one of
+// three LDS stage buffers two steps ahead of the MFMAs (bounded buffer loads: rows past an
+// operand's end land as zeros); one barrier per step.
 // ---------------------------------------------------------------------------------------
 namespace {
 
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) void mx_lds_void_t;
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t mx_rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 }
 
-// fp8 K-contiguous tile [BMN rows][TKB bytes]
+// fp8 K-contiguous tile [BMN rows][TKB bytes] followed, in its stage buffer, by the
+// step's scale words [BMN] (one dword per row: the E8M0 bytes of its four 32-blocks)
 template <int BMN, int TKB, int NW>
 struct MxOperand {
+  static_assert(TKB == 128, "one scale dword per row and step");
   static constexpr int TILE_BYTES = BMN * TKB;
+  static constexpr int SCALE_BYTES = BMN * 4;
   static constexpr int SEGS = TILE_BYTES / 1024;
   static constexpr int ROWS_PER_SEG = 1024 / TKB;
   static constexpr int CPR = TKB / 16;
   static constexpr int PER_THREAD = SEGS / NW;
+  static constexpr int SCALE_SEGS = BMN / 64;  // 64 rows per scale load
   static_assert(SEGS % NW == 0, "every wave issues the same number of segments");
-  v4i reg[PER_THREAD];
 
-  static __device__ __forceinline__ int swz(int r, int c) {
-    if constexpr (CPR == 8) return c ^ ((r >> 1) & 7);
-    else return c ^ ((r >> 2) & 3);
+  static __device__ __forceinline__ int swz(int r, int c) { return c ^ ((r >> 1) & 7); }
+
+  // Scalar load state at the load cursor: per code segment of this wave its address and
+  // readable bytes; the scale rows' address.  Set up per tile (begin), one add per step.
+  struct Stream {
+    const uint8_t* ptr[PER_THREAD];
+    uint32_t bytes[PER_THREAD];
+    uint32_t rb;                   // bytes per code row
+    const uint8_t* sptr;           // scale word of row row0 at this step
+    uint32_t srb;                  // bytes per scale row
+    int rows;                      // valid rows from row0 (0: nothing is read)
+  };
+  template <class RowPtr, class ScalePtr>
+  static __device__ __forceinline__ void begin(Stream& st, RowPtr rowptr, ScalePtr scaleptr, int row0, int row_end,
+                                               int kt, int wave, bool live) {
+    st.rb = (uint32_t)(rowptr(row0 + 1) - rowptr(row0));
+    st.srb = (uint32_t)(scaleptr(row0 + 1) - scaleptr(row0));
+    st.rows = live ? row_end - row0 : 0;
+#pragma unroll
+    for (int i = 0; i < PER_THREAD; i++) {
+      const int r0 = row0 + (wave + NW * i) * ROWS_PER_SEG;
+      st.ptr[i] = rowptr(r0) + kt;
+      int valid = live ? row_end - r0 : 0;
+      valid = valid < 0 ? 0 : (valid > ROWS_PER_SEG ? ROWS_PER_SEG : valid);
+      st.bytes[i] = valid > 0 ? (uint32_t)(valid - 1) * st.rb + TKB : 0u;
+    }
+    st.sptr = scaleptr(row0) + kt / kMxBlock;
   }
-  // rows [row0, row_end) valid; columns [k0, k0 + TKB) of each row (live == false: nothing)
-  template <class RowPtr>
-  __device__ __forceinline__ void load(RowPtr rowptr, int row0, int row_end, int k0, int wave, int lane, bool live) {
+  static __device__ __forceinline__ void next(Stream& st) {
+#pragma unroll
+    for (int i = 0; i < PER_THREAD; i++) st.ptr[i] += TKB;
+    st.sptr += TKB / kMxBlock;
+  }
+  // codes and (waves sw0 .. sw0 + SCALE_SEGS - 1) scale words of the step into LDS
+  static __device__ __forceinline__ void dma(const Stream& st, char* lds_tile, char* lds_scales, int wave, int lane,
+                                             int sw0) {
 #pragma unroll
     for (int i = 0; i < PER_THREAD; i++) {
       const int s = wave + NW * i;
-      const int r0 = row0 + s * ROWS_PER_SEG;
-      const uint8_t* base = rowptr(r0) + k0;
-      const int64_t stride = rowptr(r0 + 1) - rowptr(r0);
-      int valid = live ? row_end - r0 : 0;
-      valid = valid < 0 ? 0 : (valid > ROWS_PER_SEG ? ROWS_PER_SEG : valid);
-      const uint32_t bytes = valid > 0 ? (uint32_t)((valid - 1) * stride + TKB) : 0u;
       const int r = lane / CPR, p = lane % CPR;
-      const uint32_t voff = (uint32_t)(r * stride + swz(s * ROWS_PER_SEG + r, p) * 16);
-      reg[i] = __builtin_amdgcn_raw_buffer_load_b128(mx_rsrc(base, bytes), voff, 0, 0);
+      const uint32_t voff = (uint32_t)r * st.rb + (uint32_t)(swz(s * ROWS_PER_SEG + r, p) * 16);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(mx_rsrc(st.ptr[i], st.bytes[i]), (mx_lds_void_t*)(lds_tile + s * 1024),
+                                               16, voff, 0, 0, 0);
+    }
+    const int j = wave - sw0;
+    if (j >= 0 && j < SCALE_SEGS) {
+      int valid = st.rows - 64 * j;
+      valid = valid < 0 ? 0 : (valid > 64 ? 64 : valid);
+      const uint32_t bytes = valid > 0 ? (uint32_t)(valid - 1) * st.srb + 4 : 0u;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(mx_rsrc(st.sptr + (int64_t)64 * j * st.srb, bytes),
+                                               (mx_lds_void_t*)(lds_scales + 256 * j), 4,
+                                               (uint32_t)lane * st.srb, 0, 0, 0);
     }
   }
-  __device__ __forceinline__ void store(char* lds, int wave, int lane) const {
-#pragma unroll
-    for (int i = 0; i < PER_THREAD; i++) *reinterpret_cast<v4i*>(lds + (wave + NW * i) * 1024 + lane * 16) = reg[i];
-  }
-  // operand of 64-deep step s for rows mn0 + lane % 32
+  // operand of 64-deep sub-step s for rows mn0 + lane % 32
   static __device__ __forceinline__ i32x8 frag(const char* lds, int s, int mn0, int lane) {
     const int r = mn0 + (lane & 31), h = lane >> 5;
     const v4i lo = *reinterpret_cast<const v4i*>(lds + r * TKB + (swz(r, 4 * s + h) << 4));
     const v4i hi = *reinterpret_cast<const v4i*>(lds + r * TKB + (swz(r, 4 * s + 2 + h) << 4));
     return i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
   }
+  // the lane's scale byte of sub-step s (32-block 2 s + h of the step)
+  static __device__ __forceinline__ int scale(const char* lds_scales, int s, int mn0, int lane) {
+    const uint32_t w = *reinterpret_cast<const uint32_t*>(lds_scales + 4 * (mn0 + (lane & 31)));
+    return (int)((w >> (8 * (2 * s + (lane >> 5)))) & 0xffu);
+  }
 };
 
 }  // namespace
 
+static inline size_t mx_dyn_lds_bytes(int E) { return (size_t)2 * (E + 1) * sizeof(int); }
+
 template <class Cfg, class Prob, int TKB>
-__global__ void __launch_bounds__(Cfg::NT) mx_gemm_kernel(const Prob p) {
+__global__ void __launch_bounds__(Cfg::NT) __attribute__((amdgpu_waves_per_eu(2)))
+mx_gemm_kernel(const Prob p) {
   constexpr int BM = Cfg::BM, BN = Cfg::BN, NT = Cfg::NT;
   constexpr int WTM = Cfg::WTM, WTN = Cfg::WTN;
   constexpr int NW = NT / 64;
   using OA = MxOperand<BM, TKB, NW>;
   using OB = MxOperand<BN, TKB, NW>;
-  constexpr int STAGE_BYTES = OA::TILE_BYTES + OB::TILE_BYTES;
+  constexpr int B_OFF = OA::TILE_BYTES, SA_OFF = B_OFF + OB::TILE_BYTES, SB_OFF = SA_OFF + OA::SCALE_BYTES;
+  constexpr int STAGE_BYTES = SB_OFF + OB::SCALE_BYTES;
+  static_assert(OA::SCALE_SEGS + OB::SCALE_SEGS <= NW, "one scale load per wave");
+  // three stage buffers as separate objects (the compiler then waits only for the loads a
+  // buffer read depends on)
   __shared__ __attribute__((aligned(1024))) char sm0[STAGE_BYTES];
   __shared__ __attribute__((aligned(1024))) char sm1[STAGE_BYTES];
-  __shared__ int s_map[kMaxExperts + 1];
-  __shared__ int s_seg[kMaxExperts + 1];
+  __shared__ __attribute__((aligned(1024))) char sm2[STAGE_BYTES];
+  extern __shared__ __attribute__((aligned(16))) int s_dyn[];
+  const int E = p.E;
+  int* s_map = s_dyn;
+  int* s_seg = s_dyn + E + 1;
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wave_m = wave / Cfg::WAVES_N, wave_n = wave % Cfg::WAVES_N;
-  const int E = p.E;
   // group starts: routed rows (Group::M) or 128-padded reduction starts (Group::K)
-  if (tid == 0) {
-    int acc = 0;
-    for (int e = 0; e <= E; e++) {
-      const int st = p.offsets[e];
-      if constexpr (Prob::GROUP == Group::M) {
-        s_seg[e] = st;
-      } else {
-        s_seg[e] = acc;
-        if (e < E) acc += (p.offsets[e + 1] - st + kMxSegPad - 1) / kMxSegPad * kMxSegPad;
+  if constexpr (Prob::GROUP == Group::M) {
+    for (int e = tid; e <= E; e += NT) s_seg[e] = p.offsets[e];
+  } else {
+    for (int e = tid; e < E; e += NT)
+      s_seg[e + 1] = (p.offsets[e + 1] - p.offsets[e] + kMxSegPad - 1) / kMxSegPad * kMxSegPad;
+    __syncthreads();
+    if (tid < kWave) {  // inclusive scan of the padded lengths by wave 0
+      int carry = 0;
+      for (int base = 1; base <= E; base += kWave) {
+        const int e = base + lane;
+        const int x = e <= E ? s_seg[e] : 0;
+        int incl = x;
+#pragma unroll
+        for (int o = 1; o < kWave; o <<= 1) {
+          const int y = __shfl_up(incl, o, kWave);
+          if (lane >= o) incl += y;
+        }
+        if (e <= E) s_seg[e] = carry + incl;
+        carry += __shfl(incl, kWave - 1, kWave);
       }
+      if (lane == 0) s_seg[0] = 0;
     }
   }
   __syncthreads();
   auto seg = [&](int e) { return s_seg[e]; };
   const int total_tiles = build_tile_map<Prob::GROUP, BM, BN, NT>(s_map, seg, E, p.M, p.N, tid);
   const int G = gridDim.x;
+  const int wg = xcd_logical_wg();
+  if (wg >= total_tiles) return;  // uniform over the workgroup
 
-  for (int t = xcd_logical_wg(); t < total_tiles; t += G) {
-    const TileRange tr = tile_at<Prob::GROUP, BM, BN>(t, s_map, seg, E, p.M, p.N, p.K);
-    const int e = tr.e, m0 = tr.m0, m_end = tr.m_end, n0 = tr.n0, k_beg = tr.k_beg, k_end = tr.k_end;
+  auto tile = [&](int t) {
+    TileRange r = tile_at<Prob::GROUP, BM, BN>(t, s_map, seg, E, p.M, p.N, p.K);
+    r.e = __builtin_amdgcn_readfirstlane(r.e);
+    r.m0 = __builtin_amdgcn_readfirstlane(r.m0);
+    r.m_end = __builtin_amdgcn_readfirstlane(r.m_end);
+    r.n0 = __builtin_amdgcn_readfirstlane(r.n0);
+    r.k_beg = __builtin_amdgcn_readfirstlane(r.k_beg);
+    r.k_end = __builtin_amdgcn_readfirstlane(r.k_end);
+    return r;
+  };
+  // load cursor (tile, k) and the operands' address streams at it
+  struct Cursor {
+    int t, k;
+    TileRange tr;
+  };
+  Cursor lc;
+  lc.t = wg;
+  lc.tr = tile(wg);
+  lc.k = lc.tr.k_beg;
+  typename OA::Stream sa;
+  typename OB::Stream sb;
+  auto begin_streams = [&]() {
+    const TileRange& r = lc.tr;
+    const bool live = lc.t < total_tiles && lc.k < r.k_end;
+    OA::begin(sa, [&](int x) { return p.a_row(r.e, x); }, [&](int x) { return p.a_scale_row(r.e, x); }, r.m0, r.m_end,
+              lc.k, wave, live);
+    OB::begin(sb, [&](int x) { return p.b_row(r.e, x); }, [&](int x) { return p.b_scale_row(r.e, x); }, r.n0, p.N,
+              lc.k, wave, live);
+  };
+  auto advance = [&]() {
+    lc.k += TKB;
+    if (lc.k >= lc.tr.k_end) {
+      lc.t += G;
+      if (lc.t < total_tiles) lc.tr = tile(lc.t);
+      lc.k = lc.tr.k_beg;
+      begin_streams();
+    } else {
+      OA::next(sa);
+      OB::next(sb);
+    }
+  };
+  begin_streams();
+  auto load_stage = [&](char* base) {
+    OA::dma(sa, base, base + SA_OFF, wave, lane, 0);
+    OB::dma(sb, base + B_OFF, base + SB_OFF, wave, lane, OA::SCALE_SEGS);
+    advance();
+  };
+  // this wave's loads into buf have landed, then every wave meets
+  auto ready = [&](const char* buf) {
+    typedef __attribute__((address_space(3))) const volatile int lds_int_t;
+    const int v = *(lds_int_t*)(buf + lane * 4);
+    asm volatile("s_waitcnt lgkmcnt(0)" ::"v"(v) : "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+  };
 
-    f32x16 acc[WTM][WTN];
+  f32x16 acc[WTM][WTN];
+  auto zero_acc = [&]() {
 #pragma unroll
     for (int i = 0; i < WTM; i++)
 #pragma unroll
       for (int j = 0; j < WTN; j++)
 #pragma unroll
         for (int r = 0; r < 16; r++) acc[i][j][r] = 0.f;
-
-    OA ra0, ra1;
-    OB rb0, rb1;
-    int sa0[WTM], sa1[WTM], sb0[WTN], sb1[WTN];  // scale words (4 blocks) per lane and subtile
-    auto load_stage = [&](OA& ra, OB& rb, int (&sa)[WTM], int (&sb)[WTN], int kt) {
-      const bool live = kt < k_end;
-      ra.load([&](int r) { return p.a_row(e, r); }, m0, m_end, kt, wave, lane, live);
-      rb.load([&](int r) { return p.b_row(e, r); }, n0, p.N, kt, wave, lane, live);
-      const int word = (kt / kMxBlock) & ~3;  // 4-byte aligned group of block scales
+  };
+  // MFMAs of one 128-deep step (two 64-deep sub-steps), fragments double-buffered
+  auto compute = [&](const char* st) {
+    constexpr int KS = TKB / 64;
+    i32x8 af[2][WTM], bfr[2][WTN];
+    int xa[2][WTM], xb[2][WTN];
+    auto read = [&](int s, int b) {
 #pragma unroll
       for (int i = 0; i < WTM; i++) {
-        const int rb0_ = m0 + (wave_m * WTM + i) * 32;
-        int valid = live ? m_end - rb0_ : 0;
-        valid = valid < 0 ? 0 : (valid > 32 ? 32 : valid);
-        const uint8_t* b0 = p.a_scale_row(e, rb0_);
-        const int64_t st = p.a_scale_row(e, rb0_ + 1) - b0;
-        sa[i] = __builtin_amdgcn_raw_buffer_load_b32(mx_rsrc(b0, valid > 0 ? (uint32_t)(valid * st) : 0u),
-                                                     (uint32_t)((lane & 31) * st + word), 0, 0);
+        af[b][i] = OA::frag(st, s, (wave_m * WTM + i) * 32, lane);
+        xa[b][i] = OA::scale(st + SA_OFF, s, (wave_m * WTM + i) * 32, lane);
       }
 #pragma unroll
       for (int j = 0; j < WTN; j++) {
-        const int nb0 = n0 + (wave_n * WTN + j) * 32;
-        int valid = live ? p.N - nb0 : 0;
-        valid = valid < 0 ? 0 : (valid > 32 ? 32 : valid);
-        const uint8_t* b0 = p.b_scale_row(e, nb0);
-        const int64_t st = p.b_scale_row(e, nb0 + 1) - b0;
-        sb[j] = __builtin_amdgcn_raw_buffer_load_b32(mx_rsrc(b0, valid > 0 ? (uint32_t)(valid * st) : 0u),
-                                                     (uint32_t)((lane & 31) * st + word), 0, 0);
+        bfr[b][j] = OB::frag(st + B_OFF, s, (wave_n * WTN + j) * 32, lane);
+        xb[b][j] = OB::scale(st + SB_OFF, s, (wave_n * WTN + j) * 32, lane);
       }
     };
-    auto store_stage = [&](const OA& ra, const OB& rb, char* base) {
-      ra.store(base, wave, lane);
-      rb.store(base + OA::TILE_BYTES, wave, lane);
-    };
-    auto compute = [&](const char* st, const int (&sa)[WTM], const int (&sb)[WTN], int kt) {
-      const int byte0 = (kt / kMxBlock) & 3;
+    read(0, 0);
 #pragma unroll
-      for (int s = 0; s < TKB / 64; s++) {
-        i32x8 af[WTM], bfr[WTN];
-        int xa[WTM], xb[WTN];
-        const int sh = 8 * (byte0 + 2 * s + (lane >> 5));
+    for (int s = 0; s < KS; s++) {
+      if (s + 1 < KS) read(s + 1, (s + 1) & 1);
 #pragma unroll
-        for (int i = 0; i < WTM; i++) {
-          af[i] = OA::frag(st, s, (wave_m * WTM + i) * 32, lane);
-          xa[i] = (sa[i] >> sh) & 0xff;
-        }
+      for (int i = 0; i < WTM; i++)
 #pragma unroll
-        for (int j = 0; j < WTN; j++) {
-          bfr[j] = OB::frag(st + OA::TILE_BYTES, s, (wave_n * WTN + j) * 32, lane);
-          xb[j] = (sb[j] >> sh) & 0xff;
-        }
-#pragma unroll
-        for (int i = 0; i < WTM; i++)
-#pragma unroll
-          for (int j = 0; j < WTN; j++)
-            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af[i], bfr[j], acc[i][j], 0, 0, 0, xa[i], 0,
-                                                                         xb[j]);
-      }
-    };
-    auto lds_barrier = [&]() {
-      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-      __builtin_amdgcn_s_barrier();
-      asm volatile("" ::: "memory");
-    };
+        for (int j = 0; j < WTN; j++)
+          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af[s & 1][i], bfr[s & 1][j], acc[i][j], 0, 0, 0,
+                                                                       xa[s & 1][i], 0, xb[s & 1][j]);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  auto steps_of = [&](const TileRange& r) {
+    const int n = (r.k_end - r.k_beg + TKB - 1) / TKB;
+    return n < 1 ? 1 : n;
+  };
 
-    const int nk = (k_end - k_beg + TKB - 1) / TKB;
-    if (nk > 0) {
-      load_stage(ra0, rb0, sa0, sb0, k_beg);
-      load_stage(ra1, rb1, sa1, sb1, k_beg + TKB);
-      lds_barrier();
-      store_stage(ra0, rb0, sm0);
-      int cs0[WTM], cs0b[WTN];  // scales of the stage now in sm0
-#pragma unroll
-      for (int i = 0; i < WTM; i++) cs0[i] = sa0[i];
-#pragma unroll
-      for (int j = 0; j < WTN; j++) cs0b[j] = sb0[j];
-      load_stage(ra0, rb0, sa0, sb0, k_beg + 2 * TKB);
-      lds_barrier();
-      int cs1[WTM], cs1b[WTN];
-      for (int it = 0; it < nk; it += 2) {
-        compute(sm0, cs0, cs0b, k_beg + it * TKB);
-        if (it + 1 < nk) store_stage(ra1, rb1, sm1);
-#pragma unroll
-        for (int i = 0; i < WTM; i++) cs1[i] = sa1[i];
-#pragma unroll
-        for (int j = 0; j < WTN; j++) cs1b[j] = sb1[j];
-        load_stage(ra1, rb1, sa1, sb1, k_beg + (it + 3) * TKB);
-        lds_barrier();
-        if (it + 1 < nk) compute(sm1, cs1, cs1b, k_beg + (it + 1) * TKB);
-        if (it + 2 < nk) store_stage(ra0, rb0, sm0);
-#pragma unroll
-        for (int i = 0; i < WTM; i++) cs0[i] = sa0[i];
-#pragma unroll
-        for (int j = 0; j < WTN; j++) cs0b[j] = sb0[j];
-        load_stage(ra0, rb0, sa0, sb0, k_beg + (it + 4) * TKB);
-        lds_barrier();
+  int ct = wg;
+  TileRange ctr = lc.tr;
+  int ncs = steps_of(ctr), cs = 0;
+  zero_acc();
+  bool done = false;
+  auto finish_step = [&]() {
+    if (++cs == ncs) {
+      tile_epilogue<Prob, WTM, WTN>(p, acc, ctr, wave_m, wave_n, lane);
+      ct += G;
+      if (ct < total_tiles) {
+        ctr = tile(ct);
+        ncs = steps_of(ctr);
+        cs = 0;
+        zero_acc();
+      } else {
+        done = true;
       }
     }
-
-#pragma unroll
-    for (int i = 0; i < WTM; i++) {
-#pragma unroll
-      for (int r = 0; r < 16; r++) {
-        const int m = m0 + (wave_m * WTM + i) * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
-        if (m >= m_end) continue;
-        if constexpr (Prob::EPI == Epi::SwiGLU) {
-#pragma unroll
-          for (int j = 0; j < WTN; j += 2) {
-            const int hcol = n0 / 2 + ((wave_n * WTN + j) >> 1) * 32 + (lane & 31);
-            if (hcol < p.N / 2) p.epilogue_swiglu(m, hcol, acc[i][j][r], acc[i][j + 1][r]);
-          }
-        } else {
-#pragma unroll
-          for (int j = 0; j < WTN; j++) {
-            const int n = n0 + (wave_n * WTN + j) * 32 + (lane & 31);
-            if (n < p.N) p.epilogue(e, m, n, acc[i][j][r]);
-          }
-        }
-      }
-    }
+  };
+  // step s is loaded into buffer s % 3 two steps ahead; one exit, at the bottom
+  load_stage(sm0);
+  load_stage(sm1);
+  for (;;) {
+    ready(sm0);
+    load_stage(sm2);
+    compute(sm0);
+    finish_step();
+    ready(sm1);
+    load_stage(sm0);
+    compute(sm1);
+    if (!done) finish_step();
+    ready(sm2);
+    load_stage(sm1);
+    compute(sm2);
+    if (!done) finish_step();
+    if (done) break;
   }
 }
 
@@ -445,22 +572,21 @@ struct MxGemm1 : MxBase {  // [a | b] = X [W1 | W3]^T, SwiGLU epilogue
   static constexpr Group GROUP = Group::M;
   static constexpr Epi EPI = Epi::SwiGLU;
   int f = 0;
-  const uint8_t *q1 = nullptr, *s1 = nullptr, *q3 = nullptr, *s3 = nullptr;  // [E][f][d]
+  const uint8_t *qb = nullptr, *sb = nullptr;  // [E][2f][d]: 32-row blocks alternate W1, W3
   bf16_t *ab = nullptr, *h = nullptr;
   __device__ const uint8_t* a_row(int, int m) const { return qa + (int64_t)m * K; }
   __device__ const uint8_t* a_scale_row(int, int m) const { return sa + (int64_t)m * (K / kMxBlock); }
-  __device__ int64_t brow(int e, int n) const { return (int64_t)e * f + ((n >> 5) >> 1) * 32 + (n & 31); }
-  __device__ const uint8_t* b_row(int e, int n) const { return ((n >> 5) & 1 ? q3 : q1) + brow(e, n) * K; }
-  __device__ const uint8_t* b_scale_row(int e, int n) const {
-    return ((n >> 5) & 1 ? s3 : s1) + brow(e, n) * (K / kMxBlock);
-  }
-  __device__ void epilogue_swiglu(int m, int hcol, float a, float b) const {
+  __device__ const uint8_t* b_row(int e, int n) const { return qb + ((int64_t)e * N + n) * K; }
+  __device__ const uint8_t* b_scale_row(int e, int n) const { return sb + ((int64_t)e * N + n) * (K / kMxBlock); }
+  __device__ void epilogue_swiglu4(int m, int hcol, const float (&a)[4], const float (&b)[4]) const {
     bf16_t* abr = ab + (int64_t)m * 2 * f;
-    abr[hcol] = f2bf(a);
-    abr[f + hcol] = f2bf(b);
-    h[(int64_t)m * f + hcol] = f2bf(a * sigmoidf_(a) * b);
+    store_bf16x4(abr + hcol, a);
+    store_bf16x4(abr + f + hcol, b);
+    float hv[4];
+#pragma unroll
+    for (int c = 0; c < 4; c++) hv[c] = a[c] * sigmoidf_(a[c]) * b[c];
+    store_bf16x4(h + (int64_t)m * f + hcol, hv);
   }
-  __device__ void epilogue(int, int, int, float) const {}
 };
 
 struct MxPlain : MxBase {  // C[m][n] = sum_k A[m][k] B_e[n][k], bf16 out (Group::M)
@@ -472,20 +598,27 @@ struct MxPlain : MxBase {  // C[m][n] = sum_k A[m][k] B_e[n][k], bf16 out (Group
   __device__ const uint8_t* a_scale_row(int, int m) const { return sa + (int64_t)m * (K / kMxBlock); }
   __device__ const uint8_t* b_row(int e, int n) const { return qb + ((int64_t)e * N + n) * K; }
   __device__ const uint8_t* b_scale_row(int e, int n) const { return sb + ((int64_t)e * N + n) * (K / kMxBlock); }
-  __device__ void epilogue(int, int m, int n, float v) const { C[(int64_t)m * N + n] = f2bf(v); }
+  __device__ void epilogue4(int, int m, int n, const float (&v)[4]) const { store_bf16x4(C + (int64_t)m * N + n, v); }
 };
 
 struct MxDgrad2 : MxPlain {  // dh = dy W2_e, then the SwiGLU gradient from the saved a, b
   static constexpr Epi EPI = Epi::DSwiGLU;
   const bf16_t* ab = nullptr;
   bf16_t* dab = nullptr;
-  __device__ void epilogue(int, int m, int n, float dh) const {
+  __device__ void epilogue4(int, int m, int n, const float (&dh)[4]) const {
     const bf16_t* abr = ab + (int64_t)m * 2 * N;
-    const float a = bf2f(abr[n]), b = bf2f(abr[N + n]);
-    const float s = sigmoidf_(a);
+    float a[4], b[4], da[4], db[4];
+    load_bf16x4(abr + n, a);
+    load_bf16x4(abr + N + n, b);
+#pragma unroll
+    for (int c = 0; c < 4; c++) {
+      const float s = sigmoidf_(a[c]);
+      da[c] = dh[c] * b[c] * s * (1.f + a[c] * (1.f - s));
+      db[c] = dh[c] * a[c] * s;
+    }
     bf16_t* o = dab + (int64_t)m * 2 * N;
-    o[n] = f2bf(dh * b * s * (1.f + a * (1.f - s)));
-    o[N + n] = f2bf(dh * a * s);
+    store_bf16x4(o + n, da);
+    store_bf16x4(o + N + n, db);
   }
 };
 
@@ -500,9 +633,9 @@ struct MxWgrad : MxBase {  // C_e[m][n] = sum over expert e's (padded) rows of A
   __device__ const uint8_t* a_scale_row(int, int m) const { return sa + (int64_t)m * (K / kMxBlock); }
   __device__ const uint8_t* b_row(int, int n) const { return qb + (int64_t)n * K; }
   __device__ const uint8_t* b_scale_row(int, int n) const { return sb + (int64_t)n * (K / kMxBlock); }
-  __device__ void epilogue(int e, int m, int n, float v) const {
+  __device__ void epilogue4(int e, int m, int n, const float (&v)[4]) const {
     bf16_t* W = m < split ? C0 + ((int64_t)e * split + m) * N : C1 + ((int64_t)e * (M - split) + (m - split)) * N;
-    W[n] = f2bf(v);
+    store_bf16x4(W + n, v);
   }
 };
 
@@ -510,10 +643,12 @@ template <class Prob>
 static hipError_t launch_mx(const Prob& p, hipStream_t st) {
   using Cfg = TileCfg<128, 256, 2, 4>;
   const auto kern = mx_gemm_kernel<Cfg, Prob, 128>;
-  static int occ = 0;
+  const size_t dyn = mx_dyn_lds_bytes(p.E);
+  static int occ_e = -1, occ = 0;  // occupancy depends on the dynamic LDS, i.e. on E
+  if (occ_e != p.E) { occ_e = p.E; occ = 0; }
   if (occ == 0) {
     int o = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&o, kern, Cfg::NT, 0) != hipSuccess || o < 1) o = 1;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&o, kern, Cfg::NT, dyn) != hipSuccess || o < 1) o = 1;
     occ = o;
   }
   int64_t bound;
@@ -524,7 +659,7 @@ static hipError_t launch_mx(const Prob& p, hipStream_t st) {
   if (bound < G) G = bound;
   G = ((G + 7) / 8) * 8;
   if (G < 8) G = 8;
-  hipLaunchKernelGGL(kern, dim3((unsigned)G), dim3(Cfg::NT), 0, st, p);
+  hipLaunchKernelGGL(kern, dim3((unsigned)G), dim3(Cfg::NT), dyn, st, p);
   return hipGetLastError();
 }
 
@@ -565,15 +700,13 @@ hipError_t gemm1_fwd_mx(const GemmShape& s, const int* offsets, const bf16_t* X,
   Carve c{static_cast<char*>(ws)};
   const int64_t Ef = (int64_t)s.E * s.f;
   uint8_t *xq = c.take((size_t)s.R * s.d), *xs = c.take((size_t)s.R * s.d / kMxBlock);
-  uint8_t *q1 = c.take((size_t)Ef * s.d), *s1 = c.take((size_t)Ef * s.d / kMxBlock);
-  uint8_t *q3 = c.take((size_t)Ef * s.d), *s3 = c.take((size_t)Ef * s.d / kMxBlock);
+  uint8_t *q13 = c.take((size_t)2 * Ef * s.d), *s13 = c.take((size_t)2 * Ef * s.d / kMxBlock);
   hipError_t err;
   if ((err = mx_quantize_rows(s.R, s.d, X, xq, xs, st)) != hipSuccess) return err;
-  if ((err = mx_quantize_rows((int)Ef, s.d, W1, q1, s1, st)) != hipSuccess) return err;
-  if ((err = mx_quantize_rows((int)Ef, s.d, W3, q3, s3, st)) != hipSuccess) return err;
+  if ((err = mx_quantize_w13(s.E, s.f, s.d, W1, W3, q13, s13, st)) != hipSuccess) return err;
   MxGemm1 p;
   p.M = s.R; p.N = 2 * s.f; p.K = s.d; p.E = s.E; p.offsets = offsets; p.qa = xq; p.sa = xs; p.f = s.f;
-  p.q1 = q1; p.s1 = s1; p.q3 = q3; p.s3 = s3; p.ab = ab; p.h = h;
+  p.qb = q13; p.sb = s13; p.ab = ab; p.h = h;
   return launch_mx(p, st);
 }
 
@@ -597,8 +730,8 @@ hipError_t gemm2_fwd_mx(const GemmShape& s, const int* offsets, const bf16_t* H,
 static hipError_t quantize_weight_t(int E, int rows_e, int cols, const bf16_t* W, uint8_t* q, uint8_t* sc,
                                     int k_len, int col_off, hipStream_t st) {
   TransQ a{W, cols, cols, nullptr, E, rows_e, q, k_len, (int64_t)cols * k_len, sc, k_len / kMxBlock,
-           (int64_t)cols * (k_len / kMxBlock), col_off, 0};
-  return launch_trans(a, (int64_t)E * rows_e, st);
+           (int64_t)cols * (k_len / kMxBlock), col_off};
+  return launch_trans(a, (int64_t)E * ((rows_e + kTransRows - 1) / kTransRows), st);
 }
 
 hipError_t dgrad2_mx(const GemmShape& s, const int* offsets, const bf16_t* dY, const bf16_t* W2, const bf16_t* ab,
