@@ -333,9 +333,8 @@ moe_status moe_router_bwd(const moe_shape* s, const void* x, const void* Wr, con
   }
   if (!ws) return MOE_ENULL;
   if (ws_bytes < router_dw_workspace_bytes(s->T, s->d, s->E)) return MOE_EWORKSPACE;
-  if (s->T > 0 && router_dx_bf16(s->T, s->d, s->E, dlogits, (const bf16_t*)Wr, (bf16_t*)dx_r, S(st)) != hipSuccess)
-    return MOE_ELAUNCH;
-  return launched(router_dw_bf16(s->T, s->d, s->E, dlogits, (const bf16_t*)x, dWr, ws, S(st)));
+  return launched(router_bwd_bf16(s->T, s->d, s->E, dlogits, (const bf16_t*)Wr, (const bf16_t*)x, (bf16_t*)dx_r, dWr,
+                                  ws, S(st)));
 }
 
 moe_status moe_permute_bwd(const moe_shape* s, const void* dx_perm, const int32_t* slot_row, const void* dx_r,

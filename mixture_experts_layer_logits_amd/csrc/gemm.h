@@ -42,10 +42,9 @@ hipError_t wgrad1_bf16(const GemmShape& s, const int* offsets, const bf16_t* X, 
 // router GEMMs (single group)
 hipError_t router_fwd_bf16(int T, int d, int E, const bf16_t* X, const bf16_t* Wr, const float* bias, float* L,
                            hipStream_t st);
-hipError_t router_dx_bf16(int T, int d, int E, const float* dL, const bf16_t* Wr, bf16_t* dX, hipStream_t st);
-hipError_t router_dw_bf16(int T, int d, int E, const float* dL, const bf16_t* X, float* dW, void* ws,
-                          hipStream_t st);
-// workspace of the split-T router weight gradient (any device)
+// dx_r = dlogits Wr, dWr = dlogits^T x (workspace: router_dw_workspace_bytes)
+hipError_t router_bwd_bf16(int T, int d, int E, const float* dL, const bf16_t* Wr, const bf16_t* X, bf16_t* dX,
+                           float* dW, void* ws, hipStream_t st);
 size_t router_dw_workspace_bytes(int T, int d, int E);
 
 // fp32 path (plain FMA kernels; every GEMM of the layer in float)

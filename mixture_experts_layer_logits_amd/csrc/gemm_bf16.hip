@@ -13,12 +13,11 @@
 //   GROUP_K  the reduction is grouped by expert (weight-gradient GEMMs):
 //            C_e[m, n] = sum_{r in [offsets[e], offsets[e+1])} A[r, m] * B[r, n].
 //
-// Register-staged kernel (float-A router GEMMs): BM x BN tiles, BK = 64, two LDS buffers.  An operand whose
-// reduction axis is contiguous in memory ("K-contiguous") is kept [mn][k] in LDS and
-// read with 16-byte ds_read_b128; an operand contiguous along M or N is kept [k][mn]
-// as loaded and read with the gfx950 transpose read ds_read_b64_tr_b16, so no operand
-// is ever transposed in HBM.  MFMA: v_mfma_f32_32x32x16_bf16 (lane l holds row l%32,
-// k = 8*(l/32)..+7 of A; column l%32 of B; accumulator row 8*(i/4)+4*(l/32)+i%4).
+// An operand whose reduction axis is contiguous in memory ("K-contiguous") is kept
+// [mn][k] in LDS and read with 16-byte ds_read_b128; an operand contiguous along M or N
+// is kept [k][mn] as loaded and read with the gfx950 transpose read ds_read_b64_tr_b16,
+// so no operand is ever transposed in HBM.  MFMA: v_mfma_f32_32x32x16_bf16 (lane l holds
+// row l%32, k = 8*(l/32)..+7 of A; column l%32 of B; accumulator row 8*(i/4)+4*(l/32)+i%4).
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
@@ -31,213 +30,7 @@
 
 namespace moe {
 
-namespace {
-
-constexpr int BK = 64;
-constexpr int KC_STRIDE = BK + 8;  // LDS row stride (elements) of a K-contiguous tile
-
-__device__ __forceinline__ uint4 zero4() { return make_uint4(0, 0, 0, 0); }
-
-__device__ __forceinline__ uint4 pack8(const float (&v)[8]) {
-  uint32_t w[4];
-#pragma unroll
-  for (int i = 0; i < 4; i++) w[i] = (uint32_t)f2bf(v[2 * i]) | ((uint32_t)f2bf(v[2 * i + 1]) << 16);
-  return make_uint4(w[0], w[1], w[2], w[3]);
-}
-
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
-
-// Two transpose reads give one lane 8 consecutive k of one m/n column of a [k][mn] tile.
-__device__ __forceinline__ bf16x8 read_mn_frag(const bf16_t* tile, int stride, int k0, int mn0, int lane) {
-  const int g = lane >> 4, L = lane & 15;
-  const int k = k0 + 8 * (g >> 1) + (L >> 2);
-  const int mn = mn0 + 16 * (g & 1) + 4 * (L & 3);
-  const bf16_t* p0 = tile + k * stride + mn;
-  const bf16_t* p1 = p0 + 4 * stride;
-  i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p0));
-  i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p1));
-  typedef short i16x8 __attribute__((ext_vector_type(8)));
-  i16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-  return __builtin_bit_cast(bf16x8, v);
-}
-
-__device__ __forceinline__ bf16x8 read_k_frag(const bf16_t* tile, int k0, int mn0, int lane) {
-  const bf16_t* p = tile + (mn0 + (lane & 31)) * KC_STRIDE + k0 + 8 * (lane >> 5);
-  uint4 q = *reinterpret_cast<const uint4*>(p);
-  return __builtin_bit_cast(bf16x8, q);
-}
-
-// ---------------------------------------------------------------------------------------
-// Operand staging.  A "chunk" is 8 consecutive elements along the contiguous axis.
-// ---------------------------------------------------------------------------------------
-template <typename T, bool KC, int BMN, int NT>
-struct Stager {
-  // K-contiguous: tile rows = mn (BMN), 8 chunks per row.  MN-contiguous: tile rows = k
-  // (BK), BMN/8 chunks per row.
-  static constexpr int CHUNKS = BMN * BK / 8;
-  static constexpr int PER_THREAD = CHUNKS / NT;
-  static constexpr int LDS_ELEMS = KC ? BMN * KC_STRIDE : BK * (BMN + 16);
-  static_assert(CHUNKS % NT == 0, "tile chunks must divide evenly over the workgroup");
-  uint4 reg[PER_THREAD];
-
-  // rowptr(mn) returns the address of element (mn, k=0) for K-contiguous operands, or
-  // (k, mn=0) for MN-contiguous ones; validity is checked by the caller-provided bounds.
-  template <class RowPtr>
-  __device__ __forceinline__ void load(RowPtr rowptr, int mn0, int mn_end, int k0, int k_end, int tid) {
-#pragma unroll
-    for (int i = 0; i < PER_THREAD; i++) {
-      const int c = tid + i * NT;
-      if constexpr (KC) {
-        const int r = c >> 3, kc = (c & 7) * 8;
-        const int mn = mn0 + r, k = k0 + kc;
-        if constexpr (sizeof(T) == 2) {
-          reg[i] = (mn < mn_end && k + 8 <= k_end) ? *reinterpret_cast<const uint4*>(rowptr(mn) + k) : zero4();
-        } else {
-          float v[8];
-          const T* p = rowptr(mn < mn_end ? mn : mn0);
-#pragma unroll
-          for (int j = 0; j < 8; j++) v[j] = (mn < mn_end && k + j < k_end) ? (float)p[k + j] : 0.f;
-          reg[i] = pack8(v);
-        }
-      } else {
-        constexpr int CPR = BMN / 8;
-        const int r = c / CPR, mc = (c % CPR) * 8;
-        const int k = k0 + r, mn = mn0 + mc;
-        if constexpr (sizeof(T) == 2) {
-          reg[i] = (k < k_end && mn + 8 <= mn_end) ? *reinterpret_cast<const uint4*>(rowptr(k) + mn) : zero4();
-        } else {
-          float v[8];
-          const T* p = rowptr(k < k_end ? k : k0);
-#pragma unroll
-          for (int j = 0; j < 8; j++) v[j] = (k < k_end && mn + j < mn_end) ? (float)p[mn + j] : 0.f;
-          reg[i] = pack8(v);
-        }
-      }
-    }
-  }
-  __device__ __forceinline__ void store(bf16_t* lds, int tid) const {
-#pragma unroll
-    for (int i = 0; i < PER_THREAD; i++) {
-      const int c = tid + i * NT;
-      int off;
-      if constexpr (KC) {
-        off = (c >> 3) * KC_STRIDE + (c & 7) * 8;
-      } else {
-        constexpr int CPR = BMN / 8;
-        off = (c / CPR) * (BMN + 16) + (c % CPR) * 8;
-      }
-      *reinterpret_cast<uint4*>(lds + off) = reg[i];
-    }
-  }
-  static __device__ __forceinline__ bf16x8 frag(const bf16_t* lds, int kk, int mn0, int lane) {
-    if constexpr (KC) return read_k_frag(lds, kk, mn0, lane);
-    else return read_mn_frag(lds, BMN + 16, kk, mn0, lane);
-  }
-};
-
-}  // namespace
-
-// ---------------------------------------------------------------------------------------
-// The kernel
-// ---------------------------------------------------------------------------------------
-template <class Cfg, class Prob>
-__global__ void __launch_bounds__(Cfg::NT) grouped_gemm_kernel(const Prob p) {
-  constexpr int BM = Cfg::BM, BN = Cfg::BN, NT = Cfg::NT;
-  constexpr int WTM = Cfg::WTM, WTN = Cfg::WTN;
-  using SA = Stager<typename Prob::TA, Prob::A_KC, BM, NT>;
-  using SB = Stager<bf16_t, Prob::B_KC, BN, NT>;
-  __shared__ __attribute__((aligned(16))) bf16_t lds_a[2][SA::LDS_ELEMS];
-  __shared__ __attribute__((aligned(16))) bf16_t lds_b[2][SB::LDS_ELEMS];
-  // GROUP_M: first m-tile of each expert; GROUP_K: experts by descending row count
-  __shared__ int s_map[kMaxExperts + 1];
-
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wave_m = wave / Cfg::WAVES_N, wave_n = wave % Cfg::WAVES_N;
-  const int E = p.E;
-  // segment e spans [seg(e), seg(e+1)) rows of the grouped dimension
-  auto seg = [&](int e) { return p.seg(e); };
-
-  // ---- tile map
-  const int total_tiles = build_tile_map<Prob::GROUP, BM, BN, NT>(s_map, seg, E, p.M, p.N, tid);
-  const int G = gridDim.x;
-  const int wg = xcd_logical_wg();
-
-  SA sa;
-  SB sb;
-  for (int t = wg; t < total_tiles; t += G) {
-    const TileRange tr = tile_at<Prob::GROUP, BM, BN>(t, s_map, seg, E, p.M, p.N, p.K);
-    const int e = tr.e, m0 = tr.m0, m_end = tr.m_end, n0 = tr.n0, k_beg = tr.k_beg, k_end = tr.k_end;
-
-    f32x16 acc[WTM][WTN];
-#pragma unroll
-    for (int i = 0; i < WTM; i++)
-#pragma unroll
-      for (int j = 0; j < WTN; j++)
-#pragma unroll
-        for (int r = 0; r < 16; r++) acc[i][j][r] = 0.f;
-
-    auto load_stage = [&](int kt) {
-      if constexpr (Prob::A_KC) sa.load([&](int m) { return p.a_row(e, m); }, m0, m_end, kt, k_end, tid);
-      else sa.load([&](int k) { return p.a_row(e, k); }, m0, m_end, kt, k_end, tid);
-      if constexpr (Prob::B_KC) sb.load([&](int n) { return p.b_row(e, n); }, n0, p.N, kt, k_end, tid);
-      else sb.load([&](int k) { return p.b_row(e, k); }, n0, p.N, kt, k_end, tid);
-    };
-
-    if (k_beg < k_end) {
-      load_stage(k_beg);
-      sa.store(lds_a[0], tid);
-      sb.store(lds_b[0], tid);
-      __syncthreads();
-      int cur = 0;
-      for (int kt = k_beg; kt < k_end; kt += BK) {
-        const bool more = kt + BK < k_end;
-        if (more) load_stage(kt + BK);
-#pragma unroll
-        for (int kk = 0; kk < BK; kk += 16) {
-          bf16x8 af[WTM], bfr[WTN];
-#pragma unroll
-          for (int i = 0; i < WTM; i++) af[i] = SA::frag(lds_a[cur], kk, (wave_m * WTM + i) * 32, lane);
-#pragma unroll
-          for (int j = 0; j < WTN; j++) bfr[j] = SB::frag(lds_b[cur], kk, (wave_n * WTN + j) * 32, lane);
-#pragma unroll
-          for (int i = 0; i < WTM; i++)
-#pragma unroll
-            for (int j = 0; j < WTN; j++)
-              acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
-        }
-        if (more) {
-          sa.store(lds_a[cur ^ 1], tid);
-          sb.store(lds_b[cur ^ 1], tid);
-        }
-        __syncthreads();
-        cur ^= 1;
-      }
-    }
-
-    // ---- epilogue straight from the accumulators
-#pragma unroll
-    for (int i = 0; i < WTM; i++) {
-#pragma unroll
-      for (int r = 0; r < 16; r++) {
-        const int m = m0 + (wave_m * WTM + i) * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
-        if (m >= m_end) continue;
-        if constexpr (Prob::EPI == Epi::SwiGLU) {
-#pragma unroll
-          for (int j = 0; j < WTN; j += 2) {
-            const int hcol = n0 / 2 + ((wave_n * WTN + j) >> 1) * 32 + (lane & 31);
-            if (hcol < p.N / 2) p.epilogue_swiglu(m, hcol, acc[i][j][r], acc[i][j + 1][r]);
-          }
-        } else {
-#pragma unroll
-          for (int j = 0; j < WTN; j++) {
-            const int n = n0 + (wave_n * WTN + j) * 32 + (lane & 31);
-            if (n < p.N) p.epilogue(e, m, n, acc[i][j][r]);
-          }
-        }
-      }
-    }
-  }
-}
 
 // ---------------------------------------------------------------------------------------
 // Problem descriptions (operand addressing + epilogue) for each GEMM of the layer.
@@ -393,34 +186,49 @@ struct ProbRouterFwd : ProbBase {
   }
 };
 
-// dx_r = dlogits Wr: A = dlogits [T][E] float (rounded to bf16 on staging), B[k=e][n] = Wr[e][n]
+// dx_r = dlogits Wr: A = the bf16 copy of dlogits [T][lda] (experts zero-padded to lda),
+// B[k=e][n] = Wr[e][n]
 struct ProbRouterDx : ProbBase {
-  using TA = float;
+  using TA = bf16_t;
   static constexpr Group GROUP = Group::M;
   static constexpr bool A_KC = true, B_KC = false;
   static constexpr Epi EPI = Epi::Store;
-  const float* dL = nullptr; const bf16_t* Wr = nullptr;
+  int lda = 0;
+  const bf16_t* dL = nullptr; const bf16_t* Wr = nullptr;
   bf16_t* dX = nullptr;
-  __device__ const float* a_row(int, int m) const { return dL + (int64_t)m * K; }
+  __device__ const bf16_t* a_row(int, int m) const { return dL + (int64_t)m * lda; }
   __device__ const bf16_t* b_row(int, int k) const { return Wr + (int64_t)k * N; }
-  __device__ void epilogue(int, int m, int n, float v) const { dX[(int64_t)m * N + n] = f2bf(v); }
+  __device__ void epilogue4(int, int m, int n, const float (&v)[4]) const { store_bf16x4(dX + (int64_t)m * N + n, v); }
 };
 
 // Partial router weight gradients: split s of the T rows writes
 // part[s][e][i] = sum_{t in split s} dlogits[t, e] x[t, i]; a second kernel sums splits.
 struct ProbRouterDwSplit : ProbBase {
-  using TA = float;
+  using TA = bf16_t;
   static constexpr Group GROUP = Group::K;
   static constexpr bool A_KC = false, B_KC = false;
   static constexpr Epi EPI = Epi::Store;
-  const float* dL = nullptr; const bf16_t* X = nullptr;
+  int lda = 0;
+  const bf16_t* dL = nullptr; const bf16_t* X = nullptr;
   float* part = nullptr;
-  __device__ const float* a_row(int, int r) const { return dL + (int64_t)r * M; }
+  __device__ const bf16_t* a_row(int, int r) const { return dL + (int64_t)r * lda; }
   __device__ const bf16_t* b_row(int, int r) const { return X + (int64_t)r * N; }
-  __device__ void epilogue(int e, int m, int n, float v) const { part[((int64_t)e * M + m) * N + n] = v; }
+  __device__ void epilogue4(int e, int m, int n, const float (&v)[4]) const {
+    *reinterpret_cast<float4*>(part + ((int64_t)e * M + m) * N + n) = make_float4(v[0], v[1], v[2], v[3]);
+  }
 };
 
 namespace {
+// dlogits [T][E] float -> bf16 [T][lda], experts E..lda-1 zero (round to nearest even, as
+// the GEMM operand staging always did)
+__global__ void dlogits_bf16_kernel(int T, int E, int lda, const float* __restrict__ src, bf16_t* __restrict__ dst) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= (int64_t)T * lda) return;
+  const int64_t t = i / lda;
+  const int e = (int)(i - t * lda);
+  dst[i] = e < E ? f2bf(src[t * E + e]) : (bf16_t)0;
+}
+
 // dW[i] = sum over splits s (in order) of part[s][i]
 __global__ void sum_splits_kernel(int64_t n, int nsplit, const float* __restrict__ part, float* __restrict__ out) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -870,21 +678,17 @@ static hipError_t launch_pipe(const Prob& p, hipStream_t st) {
   return launch_kernel<Cfg>(grouped_gemm_pipe_kernel<Cfg, Prob, TK>, p, st, occ, pipe_dyn_lds_bytes(p.E));
 }
 
-// bf16 problems use the pipelined kernel, the float-A router problems the register kernel
+// every problem runs on the pipelined kernel
 template <class Cfg, class Prob>
 static hipError_t launch_cfg(const Prob& p, hipStream_t st, int bk) {
-  if constexpr (std::is_same<typename Prob::TA, bf16_t>::value) {
-    // three stage buffers must fit the 160 KB of LDS with room for the tile map
-    constexpr bool fits64 = 3 * (Cfg::BM + Cfg::BN) * 64 * 2 <= 152 * 1024;
-    if constexpr (Cfg::BM >= 64 && Cfg::BN >= 64) {
-      if (bk == 32 || !fits64) return launch_pipe<Cfg, Prob, 32>(p, st);
-    }
-    if constexpr (fits64) return launch_pipe<Cfg, Prob, 64>(p, st);
-    return hipErrorInvalidConfiguration;
-  } else {
-    static int occ = 0;
-    return launch_kernel<Cfg>(grouped_gemm_kernel<Cfg, Prob>, p, st, occ);
+  static_assert(std::is_same<typename Prob::TA, bf16_t>::value, "bf16 operands");
+  // three stage buffers must fit the 160 KB of LDS with room for the tile map
+  constexpr bool fits64 = 3 * (Cfg::BM + Cfg::BN) * 64 * 2 <= 152 * 1024;
+  if constexpr (Cfg::BM >= 64 && Cfg::BN >= 64) {
+    if (bk == 32 || !fits64) return launch_pipe<Cfg, Prob, 32>(p, st);
   }
+  if constexpr (fits64) return launch_pipe<Cfg, Prob, 64>(p, st);
+  return hipErrorInvalidConfiguration;
 }
 
 template <class Prob>
@@ -953,13 +757,6 @@ hipError_t router_fwd_bf16(int T, int d, int E, const bf16_t* X, const bf16_t* W
   p.X = X; p.Wr = Wr; p.bias = bias; p.L = L;
   return launch(tile_for("ROUTER_FWD", Tile::t32x128, 64), p, st);
 }
-hipError_t router_dx_bf16(int T, int d, int E, const float* dL, const bf16_t* Wr, bf16_t* dX, hipStream_t st) {
-  ProbRouterDx p;
-  p.M = T; p.N = d; p.K = E; p.E = 1; p.seg_len = T; p.seg_total = T;
-  p.dL = dL; p.Wr = Wr; p.dX = dX;
-  return launch(tile_for("ROUTER_DX", Tile::t128x128, 64), p, st);
-}
-
 // Split count of the router weight gradient: about 512 output tiles in flight (two per
 // compute unit of a 256-CU device), splits of at least 64 rows.  Host-only arithmetic.
 int router_dw_splits(int T, int d, int E) {
@@ -969,22 +766,37 @@ int router_dw_splits(int T, int d, int E) {
   if (s > max_s) s = max_s;
   return s < 1 ? 1 : s;
 }
+int router_lda(int E) { return (E + 63) / 64 * 64; }
+static size_t al256(size_t b) { return (b + 255) / 256 * 256; }
 size_t router_dw_workspace_bytes(int T, int d, int E) {
-  return (size_t)router_dw_splits(T, d, E) * E * d * sizeof(float);
+  return al256((size_t)T * router_lda(E) * sizeof(bf16_t)) + (size_t)router_dw_splits(T, d, E) * E * d * sizeof(float);
 }
-hipError_t router_dw_bf16(int T, int d, int E, const float* dL, const bf16_t* X, float* dW, void* ws,
-                          hipStream_t st) {
+// dx_r = dlogits Wr and dWr = dlogits^T x through the bf16 copy of dlogits at the start of
+// ws (split partials of dWr after it)
+hipError_t router_bwd_bf16(int T, int d, int E, const float* dL, const bf16_t* Wr, const bf16_t* X, bf16_t* dX,
+                           float* dW, void* ws, hipStream_t st) {
+  const int lda = router_lda(E);
+  bf16_t* dLb = static_cast<bf16_t*>(ws);
+  float* part = reinterpret_cast<float*>(static_cast<char*>(ws) + al256((size_t)T * lda * sizeof(bf16_t)));
+  hipError_t err;
+  if (T > 0) {
+    const int64_t n = (int64_t)T * lda;
+    hipLaunchKernelGGL(dlogits_bf16_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, T, E, lda, dL, dLb);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+    ProbRouterDx p;
+    p.M = T; p.N = d; p.K = E; p.E = 1; p.seg_len = T; p.seg_total = T;
+    p.lda = lda; p.dL = dLb; p.Wr = Wr; p.dX = dX;
+    if ((err = launch(tile_for("ROUTER_DX", Tile::t128x256w8, 64), p, st)) != hipSuccess) return err;
+  }
   int ns = router_dw_splits(T, d, E);
   const int seg_len = ((T + ns - 1) / ns + 63) / 64 * 64;
   ns = T == 0 ? 1 : (T + seg_len - 1) / seg_len;
-  ProbRouterDwSplit p;
-  p.M = E; p.N = d; p.K = T; p.E = ns; p.seg_len = seg_len; p.seg_total = T;
-  p.dL = dL; p.X = X; p.part = ns == 1 ? dW : static_cast<float*>(ws);
-  hipError_t err = launch(tile_for("ROUTER_DW", Tile::t128x128, 64), p, st);
-  if (err != hipSuccess || ns == 1) return err;
+  ProbRouterDwSplit q;
+  q.M = E; q.N = d; q.K = T; q.E = ns; q.seg_len = seg_len; q.seg_total = T;
+  q.lda = lda; q.dL = dLb; q.X = X; q.part = ns == 1 ? dW : part;
+  if ((err = launch(tile_for("ROUTER_DW", Tile::t128x128, 64), q, st)) != hipSuccess || ns == 1) return err;
   const int64_t n = (int64_t)E * d;
-  hipLaunchKernelGGL(sum_splits_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, n, ns,
-                     static_cast<const float*>(ws), dW);
+  hipLaunchKernelGGL(sum_splits_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, n, ns, part, dW);
   return hipGetLastError();
 }
 
