@@ -416,20 +416,22 @@ constexpr int pipe_waves_per_eu() {
 // Group starts and the tile map live in dynamic LDS sized by the expert count.
 static inline size_t pipe_dyn_lds_bytes(int E) { return (size_t)2 * (E + 1) * sizeof(int); }
 
-template <class Cfg, class Prob, int TK>
+template <class Cfg, class Prob, int TK, int NS>
 __global__ void __launch_bounds__(Cfg::NT) __attribute__((amdgpu_waves_per_eu(pipe_waves_per_eu<Cfg, TK>())))
 grouped_gemm_pipe_kernel(const Prob p) {
+  static_assert(NS == 3 || NS == 4, "three or four stage buffers");
   constexpr int BM = Cfg::BM, BN = Cfg::BN, NT = Cfg::NT;
   constexpr int WTM = Cfg::WTM, WTN = Cfg::WTN;
   constexpr int NW = NT / 64;
   using OA = PipeOperand<Prob::A_KC, BM, TK, NW>;
   using OB = PipeOperand<Prob::B_KC, BN, TK, NW>;
   constexpr int STAGE_BYTES = OA::TILE_BYTES + OB::TILE_BYTES;
-  // three stage buffers as separate objects: the compiler then tracks the loads into each
+  // NS stage buffers as separate objects: the compiler then tracks the loads into each
   // one separately and waits only for those a read of it depends on
   __shared__ __attribute__((aligned(1024))) char sm0[STAGE_BYTES];
   __shared__ __attribute__((aligned(1024))) char sm1[STAGE_BYTES];
   __shared__ __attribute__((aligned(1024))) char sm2[STAGE_BYTES];
+  __shared__ __attribute__((aligned(1024))) char sm3[NS == 4 ? STAGE_BYTES : 16];
   extern __shared__ __attribute__((aligned(16))) int s_dyn[];
   const int E = p.E;
   int* s_map = s_dyn;
@@ -591,24 +593,29 @@ grouped_gemm_pipe_kernel(const Prob p) {
     }
   };
 
-  // step s is loaded into buffer s % 3 two steps ahead; the buffer it overwrites was
+  // step s is loaded into buffer s % NS, NS - 1 steps ahead; the buffer it overwrites was
   // computed in the step before (every wave is past that step's barrier).  One exit, at
-  // the bottom: up to two discarded steps run after a workgroup's last tile.
+  // the bottom: up to NS - 1 discarded steps run after a workgroup's last tile.
+  auto phase = [&](char* cur, char* next_load, bool first) {
+    ready(cur);
+    load_stage(next_load);
+    compute(cur);
+    if (first || !done) finish_step();
+  };
   load_stage(sm0);  // step 0
   load_stage(sm1);  // step 1
+  if constexpr (NS == 4) load_stage(sm2);
   for (;;) {
-    ready(sm0);
-    load_stage(sm2);
-    compute(sm0);
-    finish_step();
-    ready(sm1);
-    load_stage(sm0);
-    compute(sm1);
-    if (!done) finish_step();
-    ready(sm2);
-    load_stage(sm1);
-    compute(sm2);
-    if (!done) finish_step();
+    if constexpr (NS == 3) {
+      phase(sm0, sm2, true);
+      phase(sm1, sm0, false);
+      phase(sm2, sm1, false);
+    } else {
+      phase(sm0, sm3, true);
+      phase(sm1, sm0, false);
+      phase(sm2, sm1, false);
+      phase(sm3, sm2, false);
+    }
     if (done) break;
   }
 }
@@ -635,18 +642,21 @@ static bool parse_tile(const char* v, Tile* t) {
 struct TileChoice {
   Tile tile;
   int bk;
+  int stages;  // LDS stage buffers at a k-depth of 32 (3 or 4, where 4 fit)
 };
 
-// Tile shape and k-tile of one GEMM: MOE_TILE_<NAME> / MOE_TILE and MOE_GEMM_BK override
-// the default chosen by measurement on MI355X.
-static TileChoice tile_for(const char* name, Tile dflt, int dflt_bk) {
+// Tile shape, k-depth and stage count of one GEMM: MOE_TILE_<NAME> / MOE_TILE,
+// MOE_GEMM_BK and MOE_GEMM_STAGES override the defaults chosen by measurement on MI355X.
+static TileChoice tile_for(const char* name, Tile dflt, int dflt_bk, int dflt_stages = 3) {
   char key[64];
   snprintf(key, sizeof key, "MOE_TILE_%s", name);
   Tile t = dflt;
   if (!parse_tile(getenv(key), &t)) parse_tile(getenv("MOE_TILE"), &t);
   const char* bk = getenv("MOE_GEMM_BK");
-  int b = bk ? atoi(bk) : dflt_bk;
-  return TileChoice{t, b == 64 ? 64 : 32};
+  const int b = bk ? atoi(bk) : dflt_bk;
+  const char* ns = getenv("MOE_GEMM_STAGES");
+  const int n = ns ? atoi(ns) : dflt_stages;
+  return TileChoice{t, b == 64 ? 64 : 32, n == 4 ? 4 : 3};
 }
 
 // Persistent grid: resident workgroups per CU x CUs, capped by the tile bound known on the
@@ -670,41 +680,47 @@ static hipError_t launch_kernel(Kern kern, const Prob& p, hipStream_t st, int& o
   return hipGetLastError();
 }
 
-template <class Cfg, class Prob, int TK>
+template <class Cfg, class Prob, int TK, int NS>
 static hipError_t launch_pipe(const Prob& p, hipStream_t st) {
   // occupancy depends on the dynamic LDS, i.e. on the expert count: cache it per count
   static int occ_e = -1, occ = 0;
   if (occ_e != p.E) { occ_e = p.E; occ = 0; }
-  return launch_kernel<Cfg>(grouped_gemm_pipe_kernel<Cfg, Prob, TK>, p, st, occ, pipe_dyn_lds_bytes(p.E));
+  return launch_kernel<Cfg>(grouped_gemm_pipe_kernel<Cfg, Prob, TK, NS>, p, st, occ, pipe_dyn_lds_bytes(p.E));
 }
 
 // every problem runs on the pipelined kernel
 template <class Cfg, class Prob>
-static hipError_t launch_cfg(const Prob& p, hipStream_t st, int bk) {
+static hipError_t launch_cfg(const Prob& p, hipStream_t st, int bk, int stages) {
   static_assert(std::is_same<typename Prob::TA, bf16_t>::value, "bf16 operands");
-  // three stage buffers must fit the 160 KB of LDS with room for the tile map
+  // the stage buffers must fit the 160 KB of LDS with room for the tile map
   constexpr bool fits64 = 3 * (Cfg::BM + Cfg::BN) * 64 * 2 <= 152 * 1024;
+  constexpr bool fits32x4 = 4 * (Cfg::BM + Cfg::BN) * 32 * 2 <= 152 * 1024;
   if constexpr (Cfg::BM >= 64 && Cfg::BN >= 64) {
-    if (bk == 32 || !fits64) return launch_pipe<Cfg, Prob, 32>(p, st);
+    if (bk == 32 || !fits64) {
+      if constexpr (fits32x4) {
+        if (stages == 4) return launch_pipe<Cfg, Prob, 32, 4>(p, st);
+      }
+      return launch_pipe<Cfg, Prob, 32, 3>(p, st);
+    }
   }
-  if constexpr (fits64) return launch_pipe<Cfg, Prob, 64>(p, st);
+  if constexpr (fits64) return launch_pipe<Cfg, Prob, 64, 3>(p, st);
   return hipErrorInvalidConfiguration;
 }
 
 template <class Prob>
 static hipError_t launch(TileChoice c, const Prob& p, hipStream_t st) {
   switch (c.tile) {
-    case Tile::t128x256: return launch_cfg<TileCfg<128, 256, 2, 2>>(p, st, c.bk);
-    case Tile::t256x128: return launch_cfg<TileCfg<256, 128, 2, 2>>(p, st, c.bk);
-    case Tile::t64x128: return launch_cfg<TileCfg<64, 128, 1, 4>>(p, st, c.bk);
-    case Tile::t32x128: return launch_cfg<TileCfg<32, 128, 1, 4>>(p, st, c.bk);
-    case Tile::t256x128w8: return launch_cfg<TileCfg<256, 128, 4, 2>>(p, st, c.bk);
-    case Tile::t128x256w8: return launch_cfg<TileCfg<128, 256, 2, 4>>(p, st, c.bk);
-    case Tile::t256x256w8: return launch_cfg<TileCfg<256, 256, 2, 4>>(p, st, c.bk);
-    case Tile::t256x256w4: return launch_cfg<TileCfg<256, 256, 2, 2>>(p, st, c.bk);
-    case Tile::t128x256w2: return launch_cfg<TileCfg<128, 256, 1, 2>>(p, st, c.bk);
-    case Tile::t128x256m1: return launch_cfg<TileCfg<128, 256, 1, 4>>(p, st, c.bk);
-    default: return launch_cfg<TileCfg<128, 128, 2, 2>>(p, st, c.bk);
+    case Tile::t128x256: return launch_cfg<TileCfg<128, 256, 2, 2>>(p, st, c.bk, c.stages);
+    case Tile::t256x128: return launch_cfg<TileCfg<256, 128, 2, 2>>(p, st, c.bk, c.stages);
+    case Tile::t64x128: return launch_cfg<TileCfg<64, 128, 1, 4>>(p, st, c.bk, c.stages);
+    case Tile::t32x128: return launch_cfg<TileCfg<32, 128, 1, 4>>(p, st, c.bk, c.stages);
+    case Tile::t256x128w8: return launch_cfg<TileCfg<256, 128, 4, 2>>(p, st, c.bk, c.stages);
+    case Tile::t128x256w8: return launch_cfg<TileCfg<128, 256, 2, 4>>(p, st, c.bk, c.stages);
+    case Tile::t256x256w8: return launch_cfg<TileCfg<256, 256, 2, 4>>(p, st, c.bk, c.stages);
+    case Tile::t256x256w4: return launch_cfg<TileCfg<256, 256, 2, 2>>(p, st, c.bk, c.stages);
+    case Tile::t128x256w2: return launch_cfg<TileCfg<128, 256, 1, 2>>(p, st, c.bk, c.stages);
+    case Tile::t128x256m1: return launch_cfg<TileCfg<128, 256, 1, 4>>(p, st, c.bk, c.stages);
+    default: return launch_cfg<TileCfg<128, 128, 2, 2>>(p, st, c.bk, c.stages);
   }
 }
 
@@ -734,7 +750,7 @@ hipError_t wgrad2_bf16(const GemmShape& s, const int* offsets, const bf16_t* H, 
   ProbWgrad2 p;
   p.M = s.d; p.N = s.f; p.K = s.R; p.E = s.E; p.offsets = offsets;
   p.dY = dY; p.Hm = H; p.dW2 = dW2;
-  return launch(tile_for("WGRAD2", Tile::t256x256w8, 32), p, st);
+  return launch(tile_for("WGRAD2", Tile::t256x256w8, 32, 4), p, st);
 }
 hipError_t dgrad1_bf16(const GemmShape& s, const int* offsets, const bf16_t* dab, const bf16_t* W1,
                        const bf16_t* W3, bf16_t* dX, hipStream_t st) {
@@ -748,7 +764,7 @@ hipError_t wgrad1_bf16(const GemmShape& s, const int* offsets, const bf16_t* X, 
   ProbWgrad1 p;
   p.M = 2 * s.f; p.N = s.d; p.K = s.R; p.E = s.E; p.offsets = offsets; p.f = s.f;
   p.dab = dab; p.X = X; p.dW1 = dW1; p.dW3 = dW3;
-  return launch(tile_for("WGRAD1", Tile::t256x256w8, 32), p, st);
+  return launch(tile_for("WGRAD1", Tile::t256x256w8, 32, 4), p, st);
 }
 hipError_t router_fwd_bf16(int T, int d, int E, const bf16_t* X, const bf16_t* Wr, const float* bias, float* L,
                            hipStream_t st) {

@@ -38,6 +38,24 @@ __global__ void __launch_bounds__(kThreads) permute_kernel(int ntok, int d, int 
   if (row_src && lane < k) row_src[slot_row[(int64_t)t * k + lane]] = t;
 }
 
+// Gathers (combine, un-permute) read k rows per token: a wave takes its token's slot rows
+// and gates into lanes once (broadcast with shuffles), then issues the loads of two
+// 16-byte chunks of all k rows before any arithmetic, so up to 2k loads per lane are in
+// flight.  k > kGatherK falls back to one row at a time.
+constexpr int kGatherK = 8;
+
+template <typename T>
+__device__ __forceinline__ void widen8(const uint4& q, float (&v)[8]);
+template <>
+__device__ __forceinline__ void widen8<bf16_t>(const uint4& q, float (&v)[8]) {
+  const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+  for (int i = 0; i < 4; i++) {
+    v[2 * i] = __uint_as_float(w[i] << 16);
+    v[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+  }
+}
+
 // y[t] = sum_j gates[t, j] * y_perm[slot_row[t, j]]
 template <typename T>
 __global__ void __launch_bounds__(kThreads) combine_kernel(int ntok, int d, int k, const T* __restrict__ y_perm,
@@ -47,6 +65,40 @@ __global__ void __launch_bounds__(kThreads) combine_kernel(int ntok, int d, int 
   const int lane = threadIdx.x & 63;
   if (t >= ntok) return;
   const int nchunk = d / 8;
+  if constexpr (sizeof(T) == 2) {
+    if (k <= kGatherK) {
+      const int my_r = lane < k ? slot_row[(int64_t)t * k + lane] : 0;
+      const float my_g = lane < k ? gates[(int64_t)t * k + lane] : 0.f;
+      for (int c0 = lane; c0 < nchunk; c0 += 2 * kWave) {
+        uint4 q[2][kGatherK];
+#pragma unroll
+        for (int u = 0; u < 2; u++)
+#pragma unroll
+          for (int j = 0; j < kGatherK; j++) {
+            const int c = c0 + u * kWave;
+            const int r = __shfl(my_r, j, kWave);
+            if (j < k && c < nchunk) q[u][j] = *reinterpret_cast<const uint4*>(y_perm + (int64_t)r * d + c * 8);
+          }
+#pragma unroll
+        for (int u = 0; u < 2; u++) {
+          const int c = c0 + u * kWave;
+          if (c >= nchunk) break;
+          float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int j = 0; j < kGatherK; j++) {
+            if (j >= k) break;
+            const float g = __shfl(my_g, j, kWave);
+            float v[8];
+            widen8<T>(q[u][j], v);
+#pragma unroll
+            for (int i = 0; i < 8; i++) acc[i] = fmaf(g, v[i], acc[i]);
+          }
+          store8<T>(y + (int64_t)t * d + c * 8, acc);
+        }
+      }
+      return;
+    }
+  }
   for (int c = lane; c < nchunk; c += kWave) {
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
     for (int j = 0; j < k; j++) {
@@ -101,6 +153,42 @@ __global__ void __launch_bounds__(kThreads) unpermute_sum_kernel(int ntok, int d
   const int lane = threadIdx.x & 63;
   if (t >= ntok) return;
   const int nchunk = d / 8;
+  if constexpr (sizeof(T) == 2) {
+    if (k <= kGatherK) {
+      const int my_r = lane < k ? slot_row[(int64_t)t * k + lane] : 0;
+      for (int c0 = lane; c0 < nchunk; c0 += 2 * kWave) {
+        uint4 q[2][kGatherK + 1];
+#pragma unroll
+        for (int u = 0; u < 2; u++) {
+          const int c = c0 + u * kWave;
+          q[u][kGatherK] = make_uint4(0, 0, 0, 0);
+          if (dx_r && c < nchunk) q[u][kGatherK] = *reinterpret_cast<const uint4*>(dx_r + (int64_t)t * d + c * 8);
+#pragma unroll
+          for (int j = 0; j < kGatherK; j++) {
+            const int r = __shfl(my_r, j, kWave);
+            if (j < k && c < nchunk) q[u][j] = *reinterpret_cast<const uint4*>(dx_perm + (int64_t)r * d + c * 8);
+          }
+        }
+#pragma unroll
+        for (int u = 0; u < 2; u++) {
+          const int c = c0 + u * kWave;
+          if (c >= nchunk) break;
+          float acc[8];
+          widen8<T>(q[u][kGatherK], acc);
+#pragma unroll
+          for (int j = 0; j < kGatherK; j++) {
+            if (j >= k) break;
+            float v[8];
+            widen8<T>(q[u][j], v);
+#pragma unroll
+            for (int i = 0; i < 8; i++) acc[i] += v[i];
+          }
+          store8<T>(dx + (int64_t)t * d + c * 8, acc);
+        }
+      }
+      return;
+    }
+  }
   for (int c = lane; c < nchunk; c += kWave) {
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
     if (dx_r) load8<T>(dx_r + (int64_t)t * d + c * 8, acc);
