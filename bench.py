@@ -23,6 +23,7 @@ comparison (bigchange.ai, "Olmo-core 3 –æ—Ç–∫—Ä—ã–≤–∞–µ—Ç —Å—Ç–µ–∫ –æ–±—É—á–µ–Ω–
 from __future__ import annotations
 
 import argparse
+import dataclasses
 import hashlib
 import json
 import os
@@ -48,6 +49,8 @@ def parse():
     ap.add_argument("--cpu-sample-tokens", type=int, default=1024)
     ap.add_argument("--profile-kernel", default=None, help="run only this call of the step, --steps times")
     ap.add_argument("--copy-mib", type=int, default=0, help="run a plain device copy of this many MiB, --steps times")
+    ap.add_argument("--recompute", action="store_true",
+                    help="activation recompute: keep only x_perm and run GEMM1 again in the backward")
     return ap.parse_args()
 
 
@@ -63,8 +66,9 @@ def kernel_sources_digest():
     return h.hexdigest()[:16]
 
 
-def step_calls(m, L, d_inp, learned):
-    """The layer as (name, callable) pairs, in execution order."""
+def step_calls(m, L, d_inp, learned, recompute=False):
+    """The layer as (name, callable) pairs, in execution order (with recompute, GEMM1 runs
+    again at the start of the backward to regenerate a, b and h from x_perm)."""
     s = L.shape
     x, W1, W3, W2 = d_inp["x"], d_inp["W1"], d_inp["W3"], d_inp["W2"]
     Wr, bias, dy = d_inp["Wr"], d_inp["router_bias"], d_inp["dy"]
@@ -77,12 +81,23 @@ def step_calls(m, L, d_inp, learned):
     else:
         calls += [("route_given", lambda: m.moe_route_given(s, d_inp["topk_idx"], L.counts, L.offsets, L.slot_row,
                                                             L.dev_err, L.ws))]
+    sh = d_inp.get("shared")
+    if sh is not None:  # the shared expert: one-group GEMMs over the T token rows
+        ss, so = L.shape_s, L.offsets_s
+        W1s, W3s, W2s = sh
+        calls += [("shared_gemm1", lambda: m.moe_ffn_gemm1_fwd(ss, x, W1s, W3s, so, L.ab_s, L.h_s, L.ws_s)),
+                  ("shared_gemm2", lambda: m.moe_ffn_gemm2_fwd(ss, L.h_s, W2s, so, L.y_s, L.ws_s))]
+    y_add = L.y_s if sh is not None else None
     calls += [
         ("permute", lambda: m.moe_permute(s, x, L.slot_row, L.row_src, L.x_perm)),
         ("gemm1_fwd", lambda: m.moe_ffn_gemm1_fwd(s, L.x_perm, W1, W3, L.offsets, L.ab, L.h, L.ws)),
         ("gemm2_fwd", lambda: m.moe_ffn_gemm2_fwd(s, L.h, W2, L.offsets, L.y_perm, L.ws)),
-        ("combine", lambda: m.moe_combine(s, L.y_perm, g, L.slot_row, L.y)),
+        ("combine", lambda: m.moe_combine(s, L.y_perm, g, L.slot_row, y_add, L.y)),
         ("combine_bwd", lambda: m.moe_combine_bwd(s, dy, L.y_perm, g, L.slot_row, L.dy_perm, L.dgates)),
+    ]
+    if recompute:
+        calls += [("gemm1_recompute", lambda: m.moe_ffn_gemm1_fwd(s, L.x_perm, W1, W3, L.offsets, L.ab, L.h, L.ws))]
+    calls += [
         ("dgrad2", lambda: m.moe_ffn_dgrad2(s, L.dy_perm, W2, L.ab, L.offsets, L.dab, L.ws)),
         ("wgrad2", lambda: m.moe_ffn_wgrad2(s, L.h, L.dy_perm, L.offsets, L.dW2, L.ws)),
         ("dgrad1", lambda: m.moe_ffn_dgrad1(s, L.dab, W1, W3, L.offsets, L.dx_perm, L.ws)),
@@ -91,8 +106,14 @@ def step_calls(m, L, d_inp, learned):
     if learned:
         calls += [("route_bwd", lambda: m.moe_route_bwd(s, L.dgates, g, L.topk_idx, L.dlogits)),
                   ("router_bwd", lambda: m.moe_router_bwd(s, x, Wr, L.dlogits, L.dx_r, L.dWr, L.ws))]
+    if sh is not None:
+        calls += [("shared_dgrad2", lambda: m.moe_ffn_dgrad2(ss, dy, W2s, L.ab_s, so, L.dab_s, L.ws_s)),
+                  ("shared_wgrad2", lambda: m.moe_ffn_wgrad2(ss, L.h_s, dy, so, L.dW2s, L.ws_s)),
+                  ("shared_dgrad1", lambda: m.moe_ffn_dgrad1(ss, L.dab_s, W1s, W3s, so, L.dx_s, L.ws_s)),
+                  ("shared_wgrad1", lambda: m.moe_ffn_wgrad1(ss, x, L.dab_s, so, L.dW1s, L.dW3s, L.ws_s))]
+    dx_add = L.dx_s if sh is not None else None
     calls += [("permute_bwd", lambda: m.moe_permute_bwd(s, L.dx_perm, L.slot_row, L.dx_r if learned else None,
-                                                        L.dx))]
+                                                        dx_add, L.dx))]
     return calls
 
 
@@ -177,11 +198,13 @@ def main():
     act = m.MOE_F32 if w.dtype == "f32" else m.MOE_BF16
     gemm = {"f32": m.MOE_F32, "bf16": m.MOE_BF16, "mxfp8": m.MOE_MXFP8}[w.gemm]
     torch.cuda.set_device(0)
-    L = m.MoEExpertLayer(w.T, w.d, w.f, w.E, w.k, act=act, gemm=gemm)
-    d_inp = {k: (v.cuda() if isinstance(v, torch.Tensor) else v) for k, v in inp.items()}
+    L = m.MoEExpertLayer(w.T, w.d, w.f, w.E, w.k, act=act, gemm=gemm, shared_f=w.shared_f)
+    dev = lambda v: v.cuda() if isinstance(v, torch.Tensor) else (tuple(u.cuda() for u in v)  # noqa: E731
+                                                                 if isinstance(v, tuple) else v)
+    d_inp = {k: dev(v) for k, v in inp.items()}
     L.forward(d_inp["x"], d_inp["W1"], d_inp["W3"], d_inp["W2"], Wr=d_inp["Wr"], bias=d_inp["router_bias"],
-              topk_idx=d_inp["topk_idx"], gates=d_inp["gates"])
-    calls = step_calls(m, L, d_inp, learned)
+              topk_idx=d_inp["topk_idx"], gates=d_inp["gates"], shared=d_inp["shared"])
+    calls = step_calls(m, L, d_inp, learned, args.recompute)
 
     if args.profile_kernel:
         for _, fn in calls:  # one whole step sets up every call's inputs
@@ -217,6 +240,14 @@ def main():
 
     eb = 4 if w.dtype == "f32" else 2
     gem, byt = algorithmic_work(w, eb)
+    if w.shared_f:  # the shared expert's GEMMs: the routed ones with R = T, f = fs, one expert
+        ws_ = dataclasses.replace(w, k=1, E=1, f=w.shared_f)
+        gs, bs = algorithmic_work(ws_, eb)
+        for n in ("gemm1_fwd", "gemm2_fwd", "dgrad2", "wgrad2", "dgrad1", "wgrad1"):
+            key = "shared_" + n.replace("_fwd", "")
+            gem[key], byt[key] = gs[n], bs[n]
+    if args.recompute:
+        gem["gemm1_recompute"], byt["gemm1_recompute"] = gem["gemm1_fwd"], byt["gemm1_fwd"]
     kernels = {}
     for name, ms in per_call_ms.items():
         e = {"ms": round(ms, 4)}
@@ -259,12 +290,15 @@ def main():
         "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": w.gemm, "data": "synthetic",
         "config": {"workload": w.name, "T": w.T, "d": w.d, "f": w.f, "E": w.E, "k": w.k, "routing": w.routing,
-                   "gemm": w.gemm},
+                   "gemm": w.gemm, "recompute": bool(args.recompute), "shared_f": w.shared_f},
         "roofline": roofline,
         "grouped_gemm_mfma_frac_all6": round(sum(gem.values()) / (gemm_ms * 1e-3) / 1e12 / peak, 4),
         "kernels": kernels,
         "expert_load": {"max": int(L.counts.max().item()), "mean": w.T * w.k / w.E,
                         "empty": int((L.counts == 0).sum().item())},
+        # expert-FFN activations held from the forward to the backward (x_perm, y_perm, and
+        # ab, h unless recomputed)
+        "activation_bytes_held": 2 * w.R * w.d * eb + (0 if args.recompute else w.R * 3 * w.f * eb),
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, inp, min(args.cpu_sample_tokens, w.T))

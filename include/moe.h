@@ -135,10 +135,14 @@ moe_status moe_ffn_gemm1_fwd(const moe_shape* s, const void* x_perm, const void*
 moe_status moe_ffn_gemm2_fwd(const moe_shape* s, const void* h, const void* W2, const int32_t* offsets,
                              void* y_perm, void* ws, size_t ws_bytes, void* stream);
 
-/* Weighted combine: y[t] = sum_j gates[t, j] * y_perm[slot_row[t, j]] (float accumulation
- * in j order).  y_perm [R, d] act, gates [T, k] float, y [T, d] act (written). */
+/* Weighted combine: y[t] = y_add[t] + sum_j gates[t, j] * y_perm[slot_row[t, j]] (float
+ * accumulation, y_add first, then j in order).  y_perm [R, d] act, gates [T, k] float,
+ * y_add [T, d] act or NULL (the always-on shared expert's output, when the layer has one:
+ * bigchange.ai, "Olmo-core 3 открывает стек обучения MoE…", section "Что инженер может
+ * попробовать на практике", top-four routing plus one shared expert), y [T, d] act
+ * (written). */
 moe_status moe_combine(const moe_shape* s, const void* y_perm, const float* gates, const int32_t* slot_row,
-                       void* y, void* stream);
+                       const void* y_add, void* y, void* stream);
 
 /* ---------------------------------------------------------------- backward */
 
@@ -181,10 +185,11 @@ moe_status moe_route_bwd(const moe_shape* s, const float* dgates, const float* g
 moe_status moe_router_bwd(const moe_shape* s, const void* x, const void* Wr, const float* dlogits,
                           void* dx_r, float* dWr, void* ws, size_t ws_bytes, void* stream);
 
-/* Un-permute and sum: dx[t] = dx_r[t] + sum_j dx_perm[slot_row[t, j]] (float accumulation,
- * dx_r may be NULL).  dx_perm [R, d], dx_r [T, d], dx [T, d] act. */
+/* Un-permute and sum: dx[t] = dx_r[t] + dx_add[t] + sum_j dx_perm[slot_row[t, j]] (float
+ * accumulation in that order; dx_r, the router's input gradient, and dx_add, the shared
+ * expert's, may each be NULL).  dx_perm [R, d], dx_r / dx_add [T, d], dx [T, d] act. */
 moe_status moe_permute_bwd(const moe_shape* s, const void* dx_perm, const int32_t* slot_row,
-                           const void* dx_r, void* dx, void* stream);
+                           const void* dx_r, const void* dx_add, void* dx, void* stream);
 
 /* ---------------------------------------------------------------- MXFP8 */
 

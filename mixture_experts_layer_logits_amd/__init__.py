@@ -55,7 +55,7 @@ _SIGS = {
     "moe_grouped_ffn_fwd": [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _SZ, _VP],
     "moe_ffn_gemm1_fwd": [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _SZ, _VP],
     "moe_ffn_gemm2_fwd": [_VP, _VP, _VP, _VP, _VP, _SZ, _VP],
-    "moe_combine": [_VP, _VP, _VP, _VP, _VP],
+    "moe_combine": [_VP, _VP, _VP, _VP, _VP, _VP],
     "moe_combine_bwd": [_VP, _VP, _VP, _VP, _VP, _VP, _VP],
     "moe_grouped_ffn_bwd": [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _SZ, _VP],
     "moe_ffn_dgrad2": [_VP, _VP, _VP, _VP, _VP, _VP, _SZ, _VP],
@@ -64,7 +64,7 @@ _SIGS = {
     "moe_ffn_wgrad1": [_VP, _VP, _VP, _VP, _VP, _VP, _SZ, _VP],
     "moe_route_bwd": [_VP, _VP, _VP, _VP, _VP],
     "moe_router_bwd": [_VP, _VP, _VP, _VP, _VP, _VP, _SZ, _VP],
-    "moe_permute_bwd": [_VP, _VP, _VP, _VP, _VP],
+    "moe_permute_bwd": [_VP, _VP, _VP, _VP, _VP, _VP],
 }
 EXPORTED = sorted(list(_SIGS) + ["moe_mx_quantize", "moe_workspace_size", "moe_status_str"])
 
@@ -161,8 +161,8 @@ def moe_ffn_gemm2_fwd(shape, h, W2, offsets, y_perm, ws, stream=None):
     _call("moe_ffn_gemm2_fwd", shape, h, W2, offsets, y_perm, ws, _ws(ws), stream=stream)
 
 
-def moe_combine(shape, y_perm, gates, slot_row, y, stream=None):
-    _call("moe_combine", shape, y_perm, gates, slot_row, y, stream=stream)
+def moe_combine(shape, y_perm, gates, slot_row, y_add, y, stream=None):
+    _call("moe_combine", shape, y_perm, gates, slot_row, y_add, y, stream=stream)
 
 
 # ------------------------------------------------------------------ backward
@@ -200,8 +200,8 @@ def moe_router_bwd(shape, x, Wr, dlogits, dx_r, dWr, ws, stream=None):
     _call("moe_router_bwd", shape, x, Wr, dlogits, dx_r, dWr, ws, _ws(ws), stream=stream)
 
 
-def moe_permute_bwd(shape, dx_perm, slot_row, dx_r, dx, stream=None):
-    _call("moe_permute_bwd", shape, dx_perm, slot_row, dx_r, dx, stream=stream)
+def moe_permute_bwd(shape, dx_perm, slot_row, dx_r, dx_add, dx, stream=None):
+    _call("moe_permute_bwd", shape, dx_perm, slot_row, dx_r, dx_add, dx, stream=stream)
 
 
 # ------------------------------------------------------------------ MXFP8

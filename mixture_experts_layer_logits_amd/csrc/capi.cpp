@@ -200,12 +200,13 @@ moe_status moe_grouped_ffn_fwd(const moe_shape* s, const void* x_perm, const voi
   return moe_ffn_gemm2_fwd(s, h, W2, offsets, y_perm, ws, ws_bytes, st);
 }
 
-moe_status moe_combine(const moe_shape* s, const void* y_perm, const float* gates, const int32_t* slot_row, void* y,
-                       void* st) {
+moe_status moe_combine(const moe_shape* s, const void* y_perm, const float* gates, const int32_t* slot_row,
+                       const void* y_add, void* y, void* st) {
   MOE_TRY(check_shape(s));
   MOE_TRY(check_rows(s, {y_perm, y}));
   if (!rows_ok(s, gates) || !rows_ok(s, slot_row)) return MOE_ENULL;
-  return launched(combine_rows(elem_bytes(s), s->T, s->d, s->k, y_perm, gates, slot_row, y, S(st)));
+  if (y_add && !aligned16(y_add)) return MOE_EALIGN;
+  return launched(combine_rows(elem_bytes(s), s->T, s->d, s->k, y_perm, gates, slot_row, y_add, y, S(st)));
 }
 
 moe_status moe_combine_bwd(const moe_shape* s, const void* dy, const void* y_perm, const float* gates,
@@ -338,12 +339,13 @@ moe_status moe_router_bwd(const moe_shape* s, const void* x, const void* Wr, con
 }
 
 moe_status moe_permute_bwd(const moe_shape* s, const void* dx_perm, const int32_t* slot_row, const void* dx_r,
-                           void* dx, void* st) {
+                           const void* dx_add, void* dx, void* st) {
   MOE_TRY(check_shape(s));
   MOE_TRY(check_rows(s, {dx_perm, dx}));
   if (!rows_ok(s, slot_row)) return MOE_ENULL;
-  if (dx_r && !aligned16(dx_r)) return MOE_EALIGN;
-  return launched(unpermute_sum_rows(elem_bytes(s), s->T, s->d, s->k, dx_perm, slot_row, dx_r, dx, S(st)));
+  if ((dx_r && !aligned16(dx_r)) || (dx_add && !aligned16(dx_add))) return MOE_EALIGN;
+  return launched(
+      unpermute_sum_rows(elem_bytes(s), s->T, s->d, s->k, dx_perm, slot_row, dx_r, dx_add, dx, S(st)));
 }
 
 moe_status moe_mx_quantize(int32_t rows, int32_t cols, int32_t axis, const int32_t* seg_offsets, int32_t nseg,

@@ -23,11 +23,11 @@ hipError_t route_backward(int T, int E, int k, const float* dgates, const float*
 hipError_t permute_rows(int elem_bytes, int T, int d, int k, const void* x, const int32_t* slot_row,
                         int32_t* row_src, void* x_perm, hipStream_t st);
 hipError_t combine_rows(int elem_bytes, int T, int d, int k, const void* y_perm, const float* gates,
-                        const int32_t* slot_row, void* y, hipStream_t st);
+                        const int32_t* slot_row, const void* y_add, void* y, hipStream_t st);
 hipError_t combine_rows_bwd(int elem_bytes, int T, int d, int k, const void* dy, const void* y_perm,
                             const float* gates, const int32_t* slot_row, void* dy_perm, float* dgates,
                             hipStream_t st);
 hipError_t unpermute_sum_rows(int elem_bytes, int T, int d, int k, const void* dx_perm, const int32_t* slot_row,
-                              const void* dx_r, void* dx, hipStream_t st);
+                              const void* dx_r, const void* dx_add, void* dx, hipStream_t st);
 
 }  // namespace moe

@@ -56,11 +56,12 @@ __device__ __forceinline__ void widen8<bf16_t>(const uint4& q, float (&v)[8]) {
   }
 }
 
-// y[t] = sum_j gates[t, j] * y_perm[slot_row[t, j]]
+// y[t] = y_add[t] + sum_j gates[t, j] * y_perm[slot_row[t, j]]   (y_add may be null)
 template <typename T>
 __global__ void __launch_bounds__(kThreads) combine_kernel(int ntok, int d, int k, const T* __restrict__ y_perm,
                                                            const float* __restrict__ gates,
-                                                           const int32_t* __restrict__ slot_row, T* __restrict__ y) {
+                                                           const int32_t* __restrict__ slot_row,
+                                                           const T* __restrict__ y_add, T* __restrict__ y) {
   const int t = blockIdx.x * kTokPerBlock + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   if (t >= ntok) return;
@@ -70,20 +71,24 @@ __global__ void __launch_bounds__(kThreads) combine_kernel(int ntok, int d, int 
       const int my_r = lane < k ? slot_row[(int64_t)t * k + lane] : 0;
       const float my_g = lane < k ? gates[(int64_t)t * k + lane] : 0.f;
       for (int c0 = lane; c0 < nchunk; c0 += 2 * kWave) {
-        uint4 q[2][kGatherK];
+        uint4 q[2][kGatherK + 1];
 #pragma unroll
-        for (int u = 0; u < 2; u++)
+        for (int u = 0; u < 2; u++) {
+          const int c = c0 + u * kWave;
+          q[u][kGatherK] = make_uint4(0, 0, 0, 0);
+          if (y_add && c < nchunk) q[u][kGatherK] = *reinterpret_cast<const uint4*>(y_add + (int64_t)t * d + c * 8);
 #pragma unroll
           for (int j = 0; j < kGatherK; j++) {
-            const int c = c0 + u * kWave;
             const int r = __shfl(my_r, j, kWave);
             if (j < k && c < nchunk) q[u][j] = *reinterpret_cast<const uint4*>(y_perm + (int64_t)r * d + c * 8);
           }
+        }
 #pragma unroll
         for (int u = 0; u < 2; u++) {
           const int c = c0 + u * kWave;
           if (c >= nchunk) break;
-          float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+          float acc[8];
+          widen8<T>(q[u][kGatherK], acc);
 #pragma unroll
           for (int j = 0; j < kGatherK; j++) {
             if (j >= k) break;
@@ -101,6 +106,7 @@ __global__ void __launch_bounds__(kThreads) combine_kernel(int ntok, int d, int 
   }
   for (int c = lane; c < nchunk; c += kWave) {
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    if (y_add) load8<T>(y_add + (int64_t)t * d + c * 8, acc);
     for (int j = 0; j < k; j++) {
       const int r = slot_row[(int64_t)t * k + j];
       const float g = gates[(int64_t)t * k + j];
@@ -144,11 +150,12 @@ __global__ void __launch_bounds__(kThreads) combine_bwd_kernel(int ntok, int d, 
   }
 }
 
-// dx[t] = dx_r[t] + sum_j dx_perm[slot_row[t, j]]
+// dx[t] = dx_r[t] + dx_add[t] + sum_j dx_perm[slot_row[t, j]]   (dx_r, dx_add may be null)
 template <typename T>
 __global__ void __launch_bounds__(kThreads) unpermute_sum_kernel(int ntok, int d, int k, const T* __restrict__ dx_perm,
                                                                  const int32_t* __restrict__ slot_row,
-                                                                 const T* __restrict__ dx_r, T* __restrict__ dx) {
+                                                                 const T* __restrict__ dx_r,
+                                                                 const T* __restrict__ dx_add, T* __restrict__ dx) {
   const int t = blockIdx.x * kTokPerBlock + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   if (t >= ntok) return;
@@ -157,12 +164,15 @@ __global__ void __launch_bounds__(kThreads) unpermute_sum_kernel(int ntok, int d
     if (k <= kGatherK) {
       const int my_r = lane < k ? slot_row[(int64_t)t * k + lane] : 0;
       for (int c0 = lane; c0 < nchunk; c0 += 2 * kWave) {
-        uint4 q[2][kGatherK + 1];
+        uint4 q[2][kGatherK + 2];
 #pragma unroll
         for (int u = 0; u < 2; u++) {
           const int c = c0 + u * kWave;
           q[u][kGatherK] = make_uint4(0, 0, 0, 0);
+          q[u][kGatherK + 1] = make_uint4(0, 0, 0, 0);
           if (dx_r && c < nchunk) q[u][kGatherK] = *reinterpret_cast<const uint4*>(dx_r + (int64_t)t * d + c * 8);
+          if (dx_add && c < nchunk)
+            q[u][kGatherK + 1] = *reinterpret_cast<const uint4*>(dx_add + (int64_t)t * d + c * 8);
 #pragma unroll
           for (int j = 0; j < kGatherK; j++) {
             const int r = __shfl(my_r, j, kWave);
@@ -173,8 +183,11 @@ __global__ void __launch_bounds__(kThreads) unpermute_sum_kernel(int ntok, int d
         for (int u = 0; u < 2; u++) {
           const int c = c0 + u * kWave;
           if (c >= nchunk) break;
-          float acc[8];
+          float acc[8], w[8];
           widen8<T>(q[u][kGatherK], acc);
+          widen8<T>(q[u][kGatherK + 1], w);
+#pragma unroll
+          for (int i = 0; i < 8; i++) acc[i] += w[i];
 #pragma unroll
           for (int j = 0; j < kGatherK; j++) {
             if (j >= k) break;
@@ -192,6 +205,12 @@ __global__ void __launch_bounds__(kThreads) unpermute_sum_kernel(int ntok, int d
   for (int c = lane; c < nchunk; c += kWave) {
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
     if (dx_r) load8<T>(dx_r + (int64_t)t * d + c * 8, acc);
+    if (dx_add) {
+      float w[8];
+      load8<T>(dx_add + (int64_t)t * d + c * 8, w);
+#pragma unroll
+      for (int i = 0; i < 8; i++) acc[i] += w[i];
+    }
     for (int j = 0; j < k; j++) {
       const int r = slot_row[(int64_t)t * k + j];
       float v[8];
@@ -220,14 +239,14 @@ hipError_t permute_rows(int eb, int T, int d, int k, const void* x, const int32_
 }
 
 hipError_t combine_rows(int eb, int T, int d, int k, const void* y_perm, const float* gates, const int32_t* slot_row,
-                        void* y, hipStream_t st) {
+                        const void* y_add, void* y, hipStream_t st) {
   if (T == 0) return hipSuccess;
   if (eb == 2)
     hipLaunchKernelGGL(combine_kernel<bf16_t>, tok_grid(T), dim3(kThreads), 0, st, T, d, k, (const bf16_t*)y_perm,
-                       gates, slot_row, (bf16_t*)y);
+                       gates, slot_row, (const bf16_t*)y_add, (bf16_t*)y);
   else
     hipLaunchKernelGGL(combine_kernel<float>, tok_grid(T), dim3(kThreads), 0, st, T, d, k, (const float*)y_perm, gates,
-                       slot_row, (float*)y);
+                       slot_row, (const float*)y_add, (float*)y);
   return hipGetLastError();
 }
 
@@ -244,14 +263,14 @@ hipError_t combine_rows_bwd(int eb, int T, int d, int k, const void* dy, const v
 }
 
 hipError_t unpermute_sum_rows(int eb, int T, int d, int k, const void* dx_perm, const int32_t* slot_row,
-                              const void* dx_r, void* dx, hipStream_t st) {
+                              const void* dx_r, const void* dx_add, void* dx, hipStream_t st) {
   if (T == 0) return hipSuccess;
   if (eb == 2)
     hipLaunchKernelGGL(unpermute_sum_kernel<bf16_t>, tok_grid(T), dim3(kThreads), 0, st, T, d, k,
-                       (const bf16_t*)dx_perm, slot_row, (const bf16_t*)dx_r, (bf16_t*)dx);
+                       (const bf16_t*)dx_perm, slot_row, (const bf16_t*)dx_r, (const bf16_t*)dx_add, (bf16_t*)dx);
   else
     hipLaunchKernelGGL(unpermute_sum_kernel<float>, tok_grid(T), dim3(kThreads), 0, st, T, d, k,
-                       (const float*)dx_perm, slot_row, (const float*)dx_r, (float*)dx);
+                       (const float*)dx_perm, slot_row, (const float*)dx_r, (const float*)dx_add, (float*)dx);
   return hipGetLastError();
 }
 

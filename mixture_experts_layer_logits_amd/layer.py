@@ -15,6 +15,21 @@ Nothing is copied back to the host between calls; routing counts and offsets sta
 the GPU (unite.ai, "Ai2 κυκλοφορεί το Olmo-Core 3…", section "Παραλληλισμός, Ακρίβεια
 και Τεχνικές Μνήμης").  ``MoEExpertFunction`` wraps the same calls as a
 torch.autograd.Function.
+
+Shared expert (``shared_f > 0``): one always-on SwiGLU expert of width ``shared_f`` sees
+every token (bigchange.ai, "Olmo-core 3 открывает стек обучения MoE…", section "Что
+инженер может попробовать на практике": the production rows use top-four routing and
+one shared expert).  It runs as a one-group call of the same grouped GEMMs over the T
+token rows (E = 1, k = 1, offsets [0, T]); its output enters through moe_combine's
+``y_add`` and its input gradient through moe_permute_bwd's ``dx_add``.
+
+Activation recompute (``recompute=True``): the forward keeps only ``x_perm`` of the
+expert FFN; ``ab = [a | b]`` and ``h`` live in buffers allocated for the forward's GEMM1 /
+GEMM2 and released right after, and the backward runs GEMM1 again (same kernel, same
+inputs, so bit-identical ``ab`` and ``h``) before the gradient GEMMs.  This trades one
+extra GEMM1 per step for R * 3f activation elements held between the passes, the
+memory / throughput trade the pages report for recomputing activations (unite.ai,
+section "Παραλληλισμός, Ακρίβεια και Τεχνικές Μνήμης").
 """
 from __future__ import annotations
 
@@ -26,8 +41,10 @@ from . import (MOE_BF16, MOE_F32, make_shape, moe_combine, moe_combine_bwd, moe_
 
 
 class MoEExpertLayer:
-    def __init__(self, T, d, f, E, k, act=MOE_BF16, gemm=None, device="cuda"):
+    def __init__(self, T, d, f, E, k, act=MOE_BF16, gemm=None, device="cuda", recompute=False, shared_f=0):
         self.shape = make_shape(T, d, f, E, k, act, gemm)
+        self.recompute = recompute
+        self.shared_f = shared_f
         self.T, self.d, self.f, self.E, self.k = T, d, f, E, k
         self.R = T * k
         dt = torch.float32 if act == MOE_F32 else torch.bfloat16
@@ -46,8 +63,9 @@ class MoEExpertLayer:
         self.row_src = e(R, dtype=i32)
         self.dev_err = torch.zeros(1, dtype=i32, device=dev)
         self.x_perm = e(R, d)
-        self.ab = e(R, 2 * f)
-        self.h = e(R, f)
+        self._e = e
+        self.ab = None if recompute else e(R, 2 * f)
+        self.h = None if recompute else e(R, f)
         self.y_perm = e(R, d)
         self.y = e(T, d)
         # backward buffers
@@ -65,6 +83,15 @@ class MoEExpertLayer:
         self.ws = torch.empty(moe_workspace_size(self.shape), dtype=torch.uint8, device=dev)
         self.learned = True
         self._params = None
+        self._shared = None
+        if shared_f:
+            fs = shared_f
+            self.shape_s = make_shape(T, d, fs, 1, 1, act, gemm)
+            self.offsets_s = torch.tensor([0, T], dtype=i32, device=dev)
+            self.ab_s, self.h_s, self.y_s = e(T, 2 * fs), e(T, fs), e(T, d)
+            self.dab_s, self.dx_s = e(T, 2 * fs), e(T, d)
+            self.dW1s, self.dW3s, self.dW2s = e(1, fs, d), e(1, fs, d), e(1, d, fs)
+            self.ws_s = torch.empty(moe_workspace_size(self.shape_s), dtype=torch.uint8, device=dev)
 
     # -------------------------------------------------------------- forward
     def route(self, x=None, Wr=None, bias=None, topk_idx=None):
@@ -78,15 +105,28 @@ class MoEExpertLayer:
             self.topk_idx = topk_idx
             moe_route_given(s, topk_idx, self.counts, self.offsets, self.slot_row, self.dev_err, self.ws)
 
-    def forward(self, x, W1, W3, W2, Wr=None, bias=None, topk_idx=None, gates=None):
+    def forward(self, x, W1, W3, W2, Wr=None, bias=None, topk_idx=None, gates=None, shared=None):
+        """shared: (W1s [1, fs, d], W3s [1, fs, d], W2s [1, d, fs]) of the shared expert."""
         s = self.shape
         self.route(x, Wr, bias, topk_idx)
         g = self.gates if topk_idx is None else gates
         self._params = (x, W1, W3, W2, Wr, g)
+        self._shared = shared
+        y_add = None
+        if shared is not None:
+            W1s, W3s, W2s = shared
+            ss = self.shape_s
+            moe_ffn_gemm1_fwd(ss, x, W1s, W3s, self.offsets_s, self.ab_s, self.h_s, self.ws_s)
+            moe_ffn_gemm2_fwd(ss, self.h_s, W2s, self.offsets_s, self.y_s, self.ws_s)
+            y_add = self.y_s
         moe_permute(s, x, self.slot_row, self.row_src, self.x_perm)
+        if self.recompute:
+            self.ab, self.h = self._e(self.R, 2 * self.f), self._e(self.R, self.f)
         moe_ffn_gemm1_fwd(s, self.x_perm, W1, W3, self.offsets, self.ab, self.h, self.ws)
         moe_ffn_gemm2_fwd(s, self.h, W2, self.offsets, self.y_perm, self.ws)
-        moe_combine(s, self.y_perm, g, self.slot_row, self.y)
+        if self.recompute:  # the SwiGLU activations are not kept for the backward
+            self.ab = self.h = None
+        moe_combine(s, self.y_perm, g, self.slot_row, y_add, self.y)
         return self.y
 
     # -------------------------------------------------------------- backward
@@ -94,6 +134,9 @@ class MoEExpertLayer:
         s = self.shape
         x, W1, W3, W2, Wr, g = self._params
         moe_combine_bwd(s, dy, self.y_perm, g, self.slot_row, self.dy_perm, self.dgates)
+        if self.recompute:  # regenerate a, b and h from the kept x_perm
+            self.ab, self.h = self._e(self.R, 2 * self.f), self._e(self.R, self.f)
+            moe_ffn_gemm1_fwd(s, self.x_perm, W1, W3, self.offsets, self.ab, self.h, self.ws)
         moe_ffn_dgrad2(s, self.dy_perm, W2, self.ab, self.offsets, self.dab, self.ws)
         moe_ffn_wgrad2(s, self.h, self.dy_perm, self.offsets, self.dW2, self.ws)
         moe_ffn_dgrad1(s, self.dab, W1, W3, self.offsets, self.dx_perm, self.ws)
@@ -103,8 +146,28 @@ class MoEExpertLayer:
             moe_route_bwd(s, self.dgates, g, self.topk_idx, self.dlogits)
             moe_router_bwd(s, x, Wr, self.dlogits, self.dx_r, self.dWr, self.ws)
             dx_r = self.dx_r
-        moe_permute_bwd(s, self.dx_perm, self.slot_row, dx_r, self.dx)
+        dx_add = None
+        if self._shared is not None:
+            W1s, W3s, W2s = self._shared
+            ss, off = self.shape_s, self.offsets_s
+            moe_ffn_dgrad2(ss, dy, W2s, self.ab_s, off, self.dab_s, self.ws_s)
+            moe_ffn_wgrad2(ss, self.h_s, dy, off, self.dW2s, self.ws_s)
+            moe_ffn_dgrad1(ss, self.dab_s, W1s, W3s, off, self.dx_s, self.ws_s)
+            moe_ffn_wgrad1(ss, x, self.dab_s, off, self.dW1s, self.dW3s, self.ws_s)
+            dx_add = self.dx_s
+        moe_permute_bwd(s, self.dx_perm, self.slot_row, dx_r, dx_add, self.dx)
+        if self.recompute:
+            self.ab = self.h = None
         return self.dx
+
+    def activation_bytes(self):
+        """Bytes of expert-FFN activations held from the forward to the backward
+        (x_perm, y_perm, and ab and h unless they are recomputed)."""
+        eb = self.x_perm.element_size()
+        n = 2 * self.R * self.d
+        if not self.recompute:
+            n += self.R * 3 * self.f
+        return n * eb
 
 
 class MoEExpertFunction(torch.autograd.Function):

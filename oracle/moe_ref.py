@@ -267,14 +267,24 @@ def unpermute_sum(dx_perm, slot_row, dx_r=None) -> np.ndarray:
 
 
 # ----------------------------------------------------------------------------- composite
+def shared_expert_fwd(x, W1s, W3s, W2s):
+    """The always-on shared expert: the SwiGLU FFN applied to every token, i.e. the
+    grouped FFN with one group spanning all T rows (bigchange.ai, "Olmo-core 3
+    открывает стек обучения MoE…", section "Что инженер может попробовать на практике":
+    top-four routing plus one shared expert).  W1s, W3s [1, fs, d], W2s [1, d, fs]."""
+    X = f64(x)
+    return expert_ffn_fwd(X, [0, X.shape[0]], W1s, W3s, W2s)
+
+
 def layer_forward(x, W1, W3, W2, k: int, Wr=None, bias=None, select_logits=None,
-                  topk_idx=None, gates=None) -> dict:
+                  topk_idx=None, gates=None, shared=None) -> dict:
     """Whole layer forward.
 
     Learned routing: pass Wr (and optionally bias).  The selection runs on
     ``select_logits`` when given (the scores whose fp32 comparison decides the
     integer routing), else on the fp64 scores.
     Given routing: pass topk_idx and gates; no router runs.
+    shared: (W1s, W3s, W2s) of a shared expert, whose output is added to every token's.
     """
     E = f64(W1).shape[0]
     out = {}
@@ -298,11 +308,16 @@ def layer_forward(x, W1, W3, W2, k: int, Wr=None, bias=None, select_logits=None,
     a, b, h, y_perm = expert_ffn_fwd(out["x_perm"], offsets, W1, W3, W2)
     out.update(a=a, b=b, h=h, y_perm=y_perm)
     out["y"] = combine(y_perm, out["gates"], slot_row)
+    if shared is not None:
+        a_s, b_s, h_s, y_s = shared_expert_fwd(x, *shared)
+        out["shared"] = dict(a=a_s, b=b_s, h=h_s, y=y_s)
+        out["y"] = y_s + out["y"]
     return out
 
 
-def layer_backward(fw: dict, dy, x, W1, W3, W2, Wr=None, learned: bool = True) -> dict:
-    """Whole layer backward from the forward record ``fw``."""
+def layer_backward(fw: dict, dy, x, W1, W3, W2, Wr=None, learned: bool = True, shared=None) -> dict:
+    """Whole layer backward from the forward record ``fw`` (shared: the shared expert's
+    weights when the forward had one)."""
     E = f64(W1).shape[0]
     g = {}
     dy_perm, dgates = combine_bwd(dy, fw["y_perm"], fw["gates"], fw["slot_row"])
@@ -315,5 +330,11 @@ def layer_backward(fw: dict, dy, x, W1, W3, W2, Wr=None, learned: bool = True) -
         dL = route_bwd(dgates, fw["gates"], fw["topk_idx"], E)
         dx_r, dWr = router_bwd(x, Wr, dL)
         g.update(dlogits=dL, dWr=dWr, dx_r=dx_r)
+    if shared is not None:
+        T = f64(x).shape[0]
+        sh = fw["shared"]
+        dx_s, dW1s, dW3s, dW2s, _, _ = expert_ffn_bwd(dy, x, sh["a"], sh["b"], [0, T], *shared)
+        g.update(dx_s=dx_s, dW1s=dW1s, dW3s=dW3s, dW2s=dW2s)
+        dx_r = dx_s if dx_r is None else dx_r + dx_s
     g["dx"] = unpermute_sum(dx_perm, fw["slot_row"], dx_r)
     return g

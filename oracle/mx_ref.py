@@ -233,9 +233,12 @@ def mx_expert_bwd(dY, X, a, b, h, Wq: dict, quant=True, bf16=True):
     return dX, dW13[:f], dW13[f:], dW2
 
 
-def mx_layer(x, W1, W3, W2, k, topk_idx, gates, dy, quant=True, bf16=True):
+def mx_layer(x, W1, W3, W2, k, topk_idx, gates, dy, quant=True, bf16=True, shared=None):
     """Whole layer forward + backward with MXFP8 expert GEMMs, for tokens that arrive
-    routed (topk_idx, gates given).  Returns a dict like moe_ref's forward/backward."""
+    routed (topk_idx, gates given).  Returns a dict like moe_ref's forward/backward.
+    shared: (W1s, W3s, W2s) of a shared expert run with the same MXFP8 GEMMs on every
+    token; its output (bf16, as stored) joins the combine and its input gradient the
+    un-permute sum."""
     from oracle import moe_ref as ref
     rnd = bf16_round if bf16 else (lambda z: z)
     W1, W3, W2 = ref.f64(W1), ref.f64(W3), ref.f64(W2)
@@ -252,7 +255,13 @@ def mx_layer(x, W1, W3, W2, k, topk_idx, gates, dy, quant=True, bf16=True):
         lo, hi = offsets[e], offsets[e + 1]
         if hi > lo:
             a[lo:hi], b[lo:hi], h[lo:hi], yp[lo:hi] = mx_expert_fwd(xp[lo:hi], Wq[e], quant, bf16)
-    y = rnd(ref.combine(yp, g, slot_row))
+    ys = None
+    if shared is not None:
+        Wq_s = mx_expert_weights(ref.f64(shared[0])[0], ref.f64(shared[1])[0], ref.f64(shared[2])[0], quant)
+        xs = ref.f64(x)
+        a_s, b_s, h_s, ys = mx_expert_fwd(xs, Wq_s, quant, bf16)
+    y = ref.combine(yp, g, slot_row)
+    y = rnd(y if ys is None else ys + y)
     dyp, dgates = ref.combine_bwd(dy, yp, g, slot_row)
     dyp = rnd(dyp)
     dxp = np.zeros((R, d)); dW1 = np.zeros_like(W1); dW3 = np.zeros_like(W3); dW2 = np.zeros_like(W2)
@@ -261,6 +270,14 @@ def mx_layer(x, W1, W3, W2, k, topk_idx, gates, dy, quant=True, bf16=True):
         if hi > lo:
             dxp[lo:hi], dW1[e], dW3[e], dW2[e] = mx_expert_bwd(dyp[lo:hi], xp[lo:hi], a[lo:hi], b[lo:hi], h[lo:hi],
                                                                Wq[e], quant, bf16)
-    dx = rnd(ref.unpermute_sum(dxp, slot_row))
-    return dict(counts=counts, offsets=offsets, slot_row=slot_row, x_perm=xp, a=a, b=b, h=h, y_perm=yp, y=y,
-                dgates=dgates, dx_perm=dxp, dW1=dW1, dW3=dW3, dW2=dW2, dx=dx)
+    out = {}
+    dx_add = None
+    if shared is not None:
+        dx_s, dW1s, dW3s, dW2s = mx_expert_bwd(bf16_round(ref.f64(dy)) if bf16 else ref.f64(dy), xs, a_s, b_s, h_s,
+                                               Wq_s, quant, bf16)
+        dx_add = rnd(dx_s)
+        out.update(dW1s=dW1s[None], dW3s=dW3s[None], dW2s=dW2s[None], dx_s=dx_add, y_s=ys)
+    dx = rnd(ref.unpermute_sum(dxp, slot_row, dx_add))
+    out.update(dict(counts=counts, offsets=offsets, slot_row=slot_row, x_perm=xp, a=a, b=b, h=h, y_perm=yp, y=y,
+                    dgates=dgates, dx_perm=dxp, dW1=dW1, dW3=dW3, dW2=dW2, dx=dx))
+    return out

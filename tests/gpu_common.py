@@ -36,7 +36,13 @@ def host(t) -> np.ndarray:
 
 
 def to_dev(inp: dict) -> dict:
-    return {k: (v.cuda() if isinstance(v, torch.Tensor) else v) for k, v in inp.items()}
+    def dev(v):
+        if isinstance(v, torch.Tensor):
+            return v.cuda()
+        if isinstance(v, tuple):
+            return tuple(dev(u) for u in v)
+        return v
+    return {k: dev(v) for k, v in inp.items()}
 
 
 def say(msg: str):
@@ -51,12 +57,13 @@ def run_layer(w, inp: dict, layer=None):
     act = m.MOE_F32 if w.dtype == "f32" else m.MOE_BF16
     gemm = {"f32": m.MOE_F32, "bf16": m.MOE_BF16, "mxfp8": m.MOE_MXFP8}[w.gemm]
     if layer is None:
-        layer = m.MoEExpertLayer(w.T, w.d, w.f, w.E, w.k, act=act, gemm=gemm)
+        layer = m.MoEExpertLayer(w.T, w.d, w.f, w.E, w.k, act=act, gemm=gemm, shared_f=w.shared_f)
     d = to_dev(inp)
+    sh = d.get("shared")
     if w.routing == "given_uniform":
-        layer.forward(d["x"], d["W1"], d["W3"], d["W2"], topk_idx=d["topk_idx"], gates=d["gates"])
+        layer.forward(d["x"], d["W1"], d["W3"], d["W2"], topk_idx=d["topk_idx"], gates=d["gates"], shared=sh)
     else:
-        layer.forward(d["x"], d["W1"], d["W3"], d["W2"], Wr=d["Wr"], bias=d["router_bias"])
+        layer.forward(d["x"], d["W1"], d["W3"], d["W2"], Wr=d["Wr"], bias=d["router_bias"], shared=sh)
     layer.backward(d["dy"])
     torch.cuda.synchronize()
     return layer
@@ -73,18 +80,20 @@ def oracle_for(w, inp: dict, gpu_logits=None):
         from oracle import mx_ref
         assert not learned, "the MXFP8 workloads take pre-routed tokens"
         out = mx_ref.mx_layer(inp["x"], inp["W1"], inp["W3"], inp["W2"], w.k, inp["topk_idx"].numpy(), inp["gates"],
-                              inp["dy"])
+                              inp["dy"], shared=inp.get("shared"))
         fw = {k: out[k] for k in ("counts", "offsets", "slot_row", "x_perm", "a", "b", "h", "y_perm", "y")}
         fw["topk_idx"] = inp["topk_idx"].numpy()
         fw["row_src"] = ref.dispatch(fw["topk_idx"], w.E)[3]
-        bw = {k: out[k] for k in ("dgates", "dx_perm", "dW1", "dW3", "dW2", "dx")}
+        bw = {k: out[k] for k in ("dgates", "dx_perm", "dW1", "dW3", "dW2", "dx") + (
+            ("dW1s", "dW3s", "dW2s") if inp.get("shared") is not None else ())}
         return fw, bw
+    sh = inp.get("shared")
     if learned:
         fw = ref.layer_forward(inp["x"], inp["W1"], inp["W3"], inp["W2"], w.k, Wr=inp["Wr"],
-                               bias=inp["router_bias"], select_logits=gpu_logits)
+                               bias=inp["router_bias"], select_logits=gpu_logits, shared=sh)
     else:
         fw = ref.layer_forward(inp["x"], inp["W1"], inp["W3"], inp["W2"], w.k,
-                               topk_idx=inp["topk_idx"].numpy(), gates=inp["gates"])
+                               topk_idx=inp["topk_idx"].numpy(), gates=inp["gates"], shared=sh)
     bw = ref.layer_backward(fw, inp["dy"], inp["x"], inp["W1"], inp["W3"], inp["W2"], Wr=inp["Wr"],
-                            learned=learned)
+                            learned=learned, shared=sh)
     return fw, bw

@@ -20,8 +20,8 @@ from gpu_common import TOL, host, normwise_err, run_layer, say
 
 pytestmark = pytest.mark.gpu
 
-FULL = ["e8_k4_t8192", "e128_k4_t8192", "e128_k4_t16384_zipf", "e128_k4_t16384_random", "e32_k4_t16384_d4096_bf16",
-        "e32_k4_t16384_d4096_mxfp8"]
+FULL = ["e8_k4_t8192", "e128_k4_t8192", "e128_k4_t8192_shared", "e128_k4_t16384_zipf", "e128_k4_t16384_random",
+        "e32_k4_t16384_d4096_bf16", "e32_k4_t16384_d4096_mxfp8"]
 
 
 def _f64(t):
@@ -81,6 +81,11 @@ def _token_reference(inp, w, t, idx_t, learned):
     y = sum(g[j] * ys[j] for j in range(len(idx_t)))
     dg = np.array([float(dy[0] @ ys[j]) for j in range(len(idx_t))])
     dx = np.zeros(w.d)
+    if inp.get("shared") is not None:  # the shared expert sees every token
+        sh = [_f64(u) for u in inp["shared"]]
+        a_s, b_s, h_s, y_s = ref.shared_expert_fwd(x, *sh)
+        y = y + y_s[0]
+        dx += ref.expert_ffn_bwd(dy, x, a_s, b_s, [0, 1], *sh)[0][0]
     for j, e in enumerate(idx_t):
         a, b, h = rows[j]
         dxp, *_ = _ffn_bwd(inp, g[j] * dy, x, a, b, h, e, mxfp8)
@@ -166,6 +171,14 @@ def test_full_size_layer(name):
     if learned:
         dWr_ref = host(L.dlogits).astype(np.float64).T @ _f64(inp["x"])
         errs["dWr"] = normwise_err(host(L.dWr), dWr_ref)
+    if inp.get("shared") is not None:  # shared expert weight gradients over all T tokens
+        sh = [_f64(u) for u in inp["shared"]]
+        X = _f64(inp["x"])
+        a_s, b_s, _, _ = ref.shared_expert_fwd(X, *sh)
+        _, dW1s, dW3s, dW2s, _, _ = ref.expert_ffn_bwd(_f64(inp["dy"]), X, a_s, b_s, [0, w.T], *sh)
+        errs["dW1s"] = normwise_err(host(L.dW1s), dW1s)
+        errs["dW3s"] = normwise_err(host(L.dW3s), dW3s)
+        errs["dW2s"] = normwise_err(host(L.dW2s), dW2s)
     print(name, {k: f"{v:.2e}" for k, v in errs.items()})
     bad = {k: v for k, v in errs.items() if v > tol}
     assert not bad, (name, bad)

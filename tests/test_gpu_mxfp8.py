@@ -75,6 +75,7 @@ MX_CASES = [
     dict(T=256, d=256, f=256, E=8, k=4, name="mx_small"),
     dict(T=300, d=384, f=256, E=32, k=4, name="mx_ragged_e32"),
     dict(T=200, d=256, f=384, E=16, k=2, name="mx_k2"),
+    dict(T=260, d=256, f=256, E=8, k=4, shared_f=256, name="mx_shared_expert"),
 ]
 
 
@@ -89,10 +90,12 @@ def test_mxfp8_layer_parity(over):
     assert np.array_equal(host(L.slot_row), fw["slot_row"])
     keys = {"h": (L.h, fw["h"]), "y": (L.y, fw["y"]), "dgates": (L.dgates, bw["dgates"]),
             "dx": (L.dx, bw["dx"]), "dW1": (L.dW1, bw["dW1"]), "dW3": (L.dW3, bw["dW3"]), "dW2": (L.dW2, bw["dW2"])}
+    if w.shared_f:
+        keys.update(dW1s=(L.dW1s, bw["dW1s"]), dW3s=(L.dW3s, bw["dW3s"]), dW2s=(L.dW2s, bw["dW2s"]))
     errs = {k: normwise_err(host(g), r) for k, (g, r) in keys.items()}
     # the format's own error: the same layer without quantisation (reported, bounded loosely)
     plain = mx_ref.mx_layer(inp["x"], inp["W1"], inp["W3"], inp["W2"], w.k, inp["topk_idx"].numpy(), inp["gates"],
-                            inp["dy"], quant=False, bf16=False)
+                            inp["dy"], quant=False, bf16=False, shared=inp.get("shared"))
     fmt = {k: normwise_err(host(keys[k][0]), plain[k]) for k in ("y", "dx", "dW1", "dW3", "dW2")}
     print(w.name, "vs MXFP8 oracle", {k: f"{v:.2e}" for k, v in errs.items()},
           "| vs unquantised", {k: f"{v:.2e}" for k, v in fmt.items()})

@@ -24,6 +24,7 @@ CASES = [
     ("e128_k4_t16384_random", dict(T=333, d=192, f=128)),
     ("e8_k4_t8192", dict(T=77, d=64, f=64, E=1, k=1, name="single_expert")),
     ("e8_k4_t8192", dict(T=130, d=128, f=64, E=4, k=4, name="k_equals_E")),
+    ("e128_k4_t8192_shared", dict(T=300, d=256, f=192, shared_f=128, name="shared_expert")),
 ]
 
 
@@ -58,6 +59,10 @@ def _check_layer(w, inp, layer):
     errs["dW3"] = normwise_err(host(layer.dW3), bw["dW3"])
     errs["dW2"] = normwise_err(host(layer.dW2), bw["dW2"])
     errs["dx"] = normwise_err(host(layer.dx), bw["dx"])
+    if w.shared_f:
+        errs["dW1s"] = normwise_err(host(layer.dW1s), bw["dW1s"])
+        errs["dW3s"] = normwise_err(host(layer.dW3s), bw["dW3s"])
+        errs["dW2s"] = normwise_err(host(layer.dW2s), bw["dW2s"])
     if learned:
         errs["dlogits"] = normwise_err(host(layer.dlogits), bw["dlogits"])
         errs["dWr"] = normwise_err(host(layer.dWr), bw["dWr"])
@@ -88,6 +93,26 @@ def test_layer_deterministic():
     b = run_layer(w, inp, layer=a)
     for t0, t1 in zip(outs, (b.y, b.dx, b.dW1, b.dW2, b.dW3, b.dWr, b.slot_row)):
         assert torch.equal(t0, t1)
+
+
+@pytest.mark.parametrize("wname", ["e128_k4_t8192", "e32_k4_t16384_d4096_mxfp8"])
+def test_activation_recompute_bitwise(wname):
+    """Recomputing GEMM1 in the backward (keeping only x_perm) gives the same outputs and
+    gradients bit for bit as keeping a, b and h: GEMM1 is deterministic, so the
+    regenerated activations are identical."""
+    import mixture_experts_layer_logits_amd as m
+    over = dict(T=300, d=256, f=192) if wname == "e128_k4_t8192" else dict(T=300, d=256, f=256, E=8)
+    w = workloads.scaled(W[wname], **over)
+    inp = workloads.make_inputs(w)
+    say(f"[gpu] activation recompute {w}")
+    kept = run_layer(w, inp)
+    gemm = {"bf16": m.MOE_BF16, "mxfp8": m.MOE_MXFP8}[w.gemm]
+    rec = run_layer(w, inp, layer=m.MoEExpertLayer(w.T, w.d, w.f, w.E, w.k, gemm=gemm, recompute=True))
+    names = ["y", "dgates", "dx_perm", "dW1", "dW3", "dW2", "dx"] + (["dWr"] if kept.learned else [])
+    for n in names:
+        assert torch.equal(getattr(kept, n), getattr(rec, n)), n
+    assert rec.ab is None and rec.h is None
+    assert rec.activation_bytes() == kept.activation_bytes() - w.R * 3 * w.f * 2
 
 
 def test_empty_batch():

@@ -221,3 +221,48 @@ def test_backward_finite_differences(learned):
             fd = (lp - lm) / (2 * h)
             an = float((g * D).sum())
             assert abs(fd - an) <= 1e-7 * max(1.0, abs(an)), (pi, fd, an)
+
+
+# ------------------------------------------------------------------ shared expert
+def test_shared_expert_forward_per_token_bruteforce():
+    """y = shared SwiGLU FFN of every token + the routed layer; the shared part checked
+    token by token with matrix-vector products and torch's silu."""
+    x, Wr, W1, W3, W2, _ = _rand_case(21, 17, 12, 20, 5, 2)
+    rng = np.random.default_rng(22)
+    fs = 16
+    Ws = (rng.standard_normal((1, fs, 12)) * 0.3, rng.standard_normal((1, fs, 12)) * 0.3,
+          rng.standard_normal((1, 12, fs)) * 0.3)
+    fw = ref.layer_forward(x, W1, W3, W2, 2, Wr=Wr, shared=Ws)
+    plain = ref.layer_forward(x, W1, W3, W2, 2, Wr=Wr)
+    for t in range(17):
+        xt = torch.tensor(x[t])
+        ht = torch.nn.functional.silu(torch.tensor(Ws[0][0]) @ xt) * (torch.tensor(Ws[1][0]) @ xt)
+        ys = (torch.tensor(Ws[2][0]) @ ht).numpy()
+        assert np.allclose(fw["y"][t], plain["y"][t] + ys, rtol=1e-12, atol=1e-12)
+
+
+def test_shared_expert_backward_finite_differences():
+    T, d, f, E, k, fs = 16, 8, 10, 4, 2, 12
+    x, Wr, W1, W3, W2, dy = _rand_case(23, T, d, f, E, k, scale_w=0.5)
+    rng = np.random.default_rng(24)
+    idx = np.stack([rng.permutation(E)[:k] for _ in range(T)]).astype(np.int32)
+    gates = rng.dirichlet(np.ones(k), size=T)
+    Ws = [rng.standard_normal((1, fs, d)) * 0.5, rng.standard_normal((1, fs, d)) * 0.5,
+          rng.standard_normal((1, d, fs)) * 0.5]
+    params = [x, W1, W3, W2, *Ws]
+
+    def loss(p):
+        fw = ref.layer_forward(p[0], p[1], p[2], p[3], k, topk_idx=idx, gates=gates, shared=p[4:])
+        return float((fw["y"] * dy).sum())
+
+    fw = ref.layer_forward(x, W1, W3, W2, k, topk_idx=idx, gates=gates, shared=Ws)
+    bw = ref.layer_backward(fw, dy, x, W1, W3, W2, learned=False, shared=Ws)
+    grads = {0: bw["dx"], 1: bw["dW1"], 2: bw["dW3"], 3: bw["dW2"], 4: bw["dW1s"], 5: bw["dW3s"], 6: bw["dW2s"]}
+    h = 1e-5
+    for pi, g in grads.items():
+        D = rng.standard_normal(params[pi].shape)
+        plus = list(params); plus[pi] = params[pi] + h * D
+        minus = list(params); minus[pi] = params[pi] - h * D
+        fd = (loss(plus) - loss(minus)) / (2 * h)
+        an = float((g * D).sum())
+        assert abs(fd - an) <= 1e-7 * max(1.0, abs(an)), (pi, fd, an)

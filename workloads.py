@@ -54,6 +54,7 @@ class Workload:
     gemm: str             # "f32", "bf16" or "mxfp8": grouped expert GEMM arithmetic
     routing: str          # "learned", "learned_zipf" or "given_uniform"
     note: str = ""
+    shared_f: int = 0     # width of an always-on shared expert (0: none)
 
     @property
     def R(self) -> int:
@@ -72,6 +73,9 @@ WORKLOADS = {
                  "batch 2 x seq 4096; about 4096 rows per expert"),
         Workload("e128_k4_t8192", 1003, 8192, 2048, 1024, 128, 4, "bf16", "bf16", "learned",
                  "expert pool grown 8 -> 128 at fixed active compute; uneven learned-style load"),
+        Workload("e128_k4_t8192_shared", 1003, 8192, 2048, 1024, 128, 4, "bf16", "bf16", "learned",
+                 "the E=128 k=4 layer plus one always-on shared expert of width f (production rows' layout)",
+                 shared_f=1024),
         Workload("e128_k4_t16384_zipf", 1004, 16384, 2048, 1024, 128, 4, "bf16", "bf16", "learned_zipf",
                  "router logits get a Zipf(1.1) per-expert bias: hottest expert ~10x mean, some empty"),
         Workload("e128_k4_t16384_random", 1005, 16384, 2048, 1024, 128, 4, "bf16", "bf16", "given_uniform",
@@ -86,11 +90,12 @@ WORKLOADS = {
 
 def scaled(w: Workload, T: Optional[int] = None, d: Optional[int] = None, f: Optional[int] = None,
            E: Optional[int] = None, k: Optional[int] = None, seed: Optional[int] = None,
-           name: Optional[str] = None) -> Workload:
+           name: Optional[str] = None, shared_f: Optional[int] = None) -> Workload:
     """A smaller copy of a workload (same routing mode and dtype) for oracle-sized tests."""
     return dataclasses.replace(
         w, T=T or w.T, d=d or w.d, f=f or w.f, E=E or w.E, k=k or w.k,
-        seed=w.seed if seed is None else seed, name=name or (w.name + "_scaled"))
+        seed=w.seed if seed is None else seed, name=name or (w.name + "_scaled"),
+        shared_f=w.shared_f if shared_f is None else shared_f)
 
 
 def _round(t: torch.Tensor, dtype) -> torch.Tensor:
@@ -117,9 +122,10 @@ def zipf_beta(w: Workload) -> float:
 def make_inputs(w: Workload, zipf_beta_override: Optional[float] = None) -> dict:
     """Draw the workload's tensors on the CPU.
 
-    Draw order is fixed: x, Wr, W1, W3, W2, dy, then routing-mode extras.
-    x ~ N(0,1); weights ~ N(0, 0.02^2) (0.02 is the standard deviation);
-    dy ~ N(0,1).  Values are drawn in fp32 and rounded to the workload dtype.
+    Draw order is fixed: x, Wr, W1, W3, W2, dy, then routing-mode extras, then the
+    shared expert's W1s, W3s, W2s ([1, fs, d], [1, fs, d], [1, d, fs]) when the
+    workload has one.  x ~ N(0,1); weights ~ N(0, 0.02^2) (0.02 is the standard
+    deviation); dy ~ N(0,1).  Values are drawn in fp32 and rounded to the workload dtype.
     """
     gen = torch.Generator("cpu").manual_seed(w.seed)
     dt = w.torch_dtype()
@@ -145,4 +151,10 @@ def make_inputs(w: Workload, zipf_beta_override: Optional[float] = None) -> dict
         u = torch.rand(w.T, w.k, generator=gen, dtype=torch.float64)
         ex = -torch.log1p(-u)
         out["gates"] = (ex / ex.sum(dim=1, keepdim=True)).to(torch.float32).contiguous()
+    out["shared"] = None
+    if w.shared_f:
+        fs = w.shared_f
+        out["shared"] = (_round(torch.randn(1, fs, w.d, generator=gen) * 0.02, dt),
+                         _round(torch.randn(1, fs, w.d, generator=gen) * 0.02, dt),
+                         _round(torch.randn(1, w.d, fs, generator=gen) * 0.02, dt))
     return out
