@@ -108,6 +108,10 @@ size_t moe_workspace_size(const moe_shape* s) {
     const size_t r = router_dw_workspace_bytes(s->T, s->d, s->E);
     if (r > b) b = r;
   }
+  if (s->gemm == MOE_BF16) {
+    const size_t w = wgrad_split_workspace_bytes(gshape(s));
+    if (w > b) b = w;
+  }
   if (s->gemm == MOE_MXFP8) {
     const size_t m = mx_workspace_bytes(s->T * s->k, s->d, s->f, s->E);
     if (m > b) b = m;
@@ -251,7 +255,8 @@ moe_status moe_ffn_wgrad2(const moe_shape* s, const void* h, const void* dy_perm
     case MOE_F32:
       return launched(wgrad2_f32(g, offsets, (const float*)h, (const float*)dy_perm, (float*)dW2, S(st)));
     case MOE_BF16:
-      return launched(wgrad2_bf16(g, offsets, (const bf16_t*)h, (const bf16_t*)dy_perm, (bf16_t*)dW2, S(st)));
+      if (g.E == 1 && ws_bytes < wgrad_split_workspace_bytes(g)) return MOE_EWORKSPACE;
+      return launched(wgrad2_bf16(g, offsets, (const bf16_t*)h, (const bf16_t*)dy_perm, (bf16_t*)dW2, ws, S(st)));
     default:
       if (!ws) return MOE_ENULL;
       if (ws_bytes < mx_workspace_bytes(g.R, g.d, g.f, g.E)) return MOE_EWORKSPACE;
@@ -293,8 +298,9 @@ moe_status moe_ffn_wgrad1(const moe_shape* s, const void* x_perm, const void* da
       return launched(wgrad1_f32(g, offsets, (const float*)x_perm, (const float*)dab, (float*)dW1, (float*)dW3,
                                  S(st)));
     case MOE_BF16:
+      if (g.E == 1 && ws_bytes < wgrad_split_workspace_bytes(g)) return MOE_EWORKSPACE;
       return launched(wgrad1_bf16(g, offsets, (const bf16_t*)x_perm, (const bf16_t*)dab, (bf16_t*)dW1,
-                                  (bf16_t*)dW3, S(st)));
+                                  (bf16_t*)dW3, ws, S(st)));
     default:
       if (!ws) return MOE_ENULL;
       if (ws_bytes < mx_workspace_bytes(g.R, g.d, g.f, g.E)) return MOE_EWORKSPACE;

@@ -33,12 +33,15 @@ hipError_t gemm2_fwd_bf16(const GemmShape& s, const int* offsets, const bf16_t* 
                           hipStream_t st);
 hipError_t dgrad2_bf16(const GemmShape& s, const int* offsets, const bf16_t* dY, const bf16_t* W2,
                        const bf16_t* ab, bf16_t* dab, hipStream_t st);
+// weight gradients; with a single group (E == 1) and ws of wgrad_split_workspace_bytes
+// the reduction over the rows is split (ws may be null: no split)
 hipError_t wgrad2_bf16(const GemmShape& s, const int* offsets, const bf16_t* H, const bf16_t* dY, bf16_t* dW2,
-                       hipStream_t st);
+                       void* ws, hipStream_t st);
 hipError_t dgrad1_bf16(const GemmShape& s, const int* offsets, const bf16_t* dab, const bf16_t* W1,
                        const bf16_t* W3, bf16_t* dX, hipStream_t st);
 hipError_t wgrad1_bf16(const GemmShape& s, const int* offsets, const bf16_t* X, const bf16_t* dab, bf16_t* dW1,
-                       bf16_t* dW3, hipStream_t st);
+                       bf16_t* dW3, void* ws, hipStream_t st);
+size_t wgrad_split_workspace_bytes(const GemmShape& s);
 // router GEMMs (single group)
 hipError_t router_fwd_bf16(int T, int d, int E, const bf16_t* X, const bf16_t* Wr, const float* bias, float* L,
                            hipStream_t st);

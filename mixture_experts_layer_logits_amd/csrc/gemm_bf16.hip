@@ -218,7 +218,40 @@ struct ProbRouterDwSplit : ProbBase {
   }
 };
 
+// Weight gradient of a single group (E == 1) split over the rows: split s writes
+// part[s][m][n] = sum_{r in split s} A[r][m] B[r][n] (A [R][M], B [R][N] bf16)
+struct ProbWgradSplit : ProbBase {
+  using TA = bf16_t;
+  static constexpr Group GROUP = Group::K;
+  static constexpr bool A_KC = false, B_KC = false;
+  static constexpr Epi EPI = Epi::Store;
+  const bf16_t* A = nullptr; const bf16_t* B = nullptr;
+  float* part = nullptr;
+  __device__ const bf16_t* a_row(int, int r) const { return A + (int64_t)r * M; }
+  __device__ const bf16_t* b_row(int, int r) const { return B + (int64_t)r * N; }
+  __device__ void epilogue4(int e, int m, int n, const float (&v)[4]) const {
+    *reinterpret_cast<float4*>(part + ((int64_t)e * M + m) * N + n) = make_float4(v[0], v[1], v[2], v[3]);
+  }
+};
+
 namespace {
+// out = sum over splits s (in order) of part[s], rounded to bf16; rows m < split_row go
+// to O0 + m * N, the others to O1 + (m - split_row) * N.  Four elements per thread.
+__global__ void sum_splits_bf16_kernel(int64_t mn, int N, int nsplit, const float* __restrict__ part, int split_row,
+                                       bf16_t* __restrict__ O0, bf16_t* __restrict__ O1) {
+  const int64_t i = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) * 4;
+  if (i >= mn) return;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int s = 0; s < nsplit; s++) {
+    const float4 v = *reinterpret_cast<const float4*>(part + (int64_t)s * mn + i);
+    acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
+  }
+  const int64_t m = i / N, n = i % N;
+  bf16_t* o = m < split_row ? O0 + m * N + n : O1 + (m - split_row) * N + n;
+  const float a[4] = {acc.x, acc.y, acc.z, acc.w};
+  store_bf16x4(o, a);
+}
+
 // dlogits [T][E] float -> bf16 [T][lda], experts E..lda-1 zero (round to nearest even, as
 // the GEMM operand staging always did)
 __global__ void dlogits_bf16_kernel(int T, int E, int lda, const float* __restrict__ src, bf16_t* __restrict__ dst) {
@@ -745,8 +778,44 @@ hipError_t dgrad2_bf16(const GemmShape& s, const int* offsets, const bf16_t* dY,
   p.dY = dY; p.W2 = W2; p.ab = ab; p.dab = dab;
   return launch(tile_for("DGRAD2", Tile::t128x256w8, 64), p, st);
 }
+// Single-group weight gradients: with one expert the output has few tiles (64 for
+// 2048 x 2048 at 256 x 256), so the reduction over the R rows is split to give about two
+// tiles per CU of a 256-CU device (splits of at least 512 rows); partial sums go to ws and
+// are added in split order.  Host-only arithmetic.
+static int wgrad_single_splits(int R, int M, int N) {
+  const int tiles = ((M + 255) / 256) * ((N + 255) / 256);
+  int s = (512 + tiles - 1) / tiles;
+  const int max_s = R / 512;
+  if (s > max_s) s = max_s;
+  return s < 1 ? 1 : s;
+}
+size_t wgrad_split_workspace_bytes(const GemmShape& s) {
+  if (s.E != 1) return 0;
+  const int s1 = wgrad_single_splits(s.R, 2 * s.f, s.d), s2 = wgrad_single_splits(s.R, s.d, s.f);
+  const size_t a = s1 > 1 ? (size_t)s1 * 2 * s.f * s.d * sizeof(float) : 0;
+  const size_t b = s2 > 1 ? (size_t)s2 * s.d * s.f * sizeof(float) : 0;
+  return a > b ? a : b;
+}
+static hipError_t wgrad_split(int R, int M, int N, int nsplit, const bf16_t* A, const bf16_t* B, float* part,
+                              int split_row, bf16_t* O0, bf16_t* O1, hipStream_t st) {
+  const int seg_len = (R + nsplit - 1) / nsplit;
+  ProbWgradSplit p;
+  p.M = M; p.N = N; p.K = R; p.E = (R + seg_len - 1) / seg_len; p.seg_len = seg_len; p.seg_total = R;
+  p.A = A; p.B = B; p.part = part;
+  hipError_t err = launch(tile_for("WGRAD_SPLIT", Tile::t256x256w8, 32, 4), p, st);
+  if (err != hipSuccess) return err;
+  const int64_t mn = (int64_t)M * N;
+  hipLaunchKernelGGL(sum_splits_bf16_kernel, dim3((unsigned)((mn / 4 + 255) / 256)), dim3(256), 0, st, mn, N, p.E,
+                     part, split_row, O0, O1);
+  return hipGetLastError();
+}
+
 hipError_t wgrad2_bf16(const GemmShape& s, const int* offsets, const bf16_t* H, const bf16_t* dY, bf16_t* dW2,
-                       hipStream_t st) {
+                       void* ws, hipStream_t st) {
+  if (s.E == 1 && ws) {
+    const int ns = wgrad_single_splits(s.R, s.d, s.f);
+    if (ns > 1) return wgrad_split(s.R, s.d, s.f, ns, dY, H, static_cast<float*>(ws), s.d, dW2, dW2, st);
+  }
   ProbWgrad2 p;
   p.M = s.d; p.N = s.f; p.K = s.R; p.E = s.E; p.offsets = offsets;
   p.dY = dY; p.Hm = H; p.dW2 = dW2;
@@ -760,7 +829,11 @@ hipError_t dgrad1_bf16(const GemmShape& s, const int* offsets, const bf16_t* dab
   return launch(tile_for("DGRAD1", Tile::t128x256w8, 32), p, st);
 }
 hipError_t wgrad1_bf16(const GemmShape& s, const int* offsets, const bf16_t* X, const bf16_t* dab, bf16_t* dW1,
-                       bf16_t* dW3, hipStream_t st) {
+                       bf16_t* dW3, void* ws, hipStream_t st) {
+  if (s.E == 1 && ws) {
+    const int ns = wgrad_single_splits(s.R, 2 * s.f, s.d);
+    if (ns > 1) return wgrad_split(s.R, 2 * s.f, s.d, ns, dab, X, static_cast<float*>(ws), s.f, dW1, dW3, st);
+  }
   ProbWgrad1 p;
   p.M = 2 * s.f; p.N = s.d; p.K = s.R; p.E = s.E; p.offsets = offsets; p.f = s.f;
   p.dab = dab; p.X = X; p.dW1 = dW1; p.dW3 = dW3;
