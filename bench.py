@@ -51,6 +51,9 @@ def parse():
     ap.add_argument("--copy-mib", type=int, default=0, help="run a plain device copy of this many MiB, --steps times")
     ap.add_argument("--recompute", action="store_true",
                     help="activation recompute: keep only x_perm and run GEMM1 again in the backward")
+    ap.add_argument("--bf16-dispatch", action="store_true",
+                    help="MXFP8 workloads: dispatch bf16 rows and let each GEMM quantise them (default: the "
+                         "MXFP8 dispatch writes E4M3 rows)")
     return ap.parse_args()
 
 
@@ -88,21 +91,42 @@ def step_calls(m, L, d_inp, learned, recompute=False):
         calls += [("shared_gemm1", lambda: m.moe_ffn_gemm1_fwd(ss, x, W1s, W3s, so, L.ab_s, L.h_s, L.ws_s)),
                   ("shared_gemm2", lambda: m.moe_ffn_gemm2_fwd(ss, L.h_s, W2s, so, L.y_s, L.ws_s))]
     y_add = L.y_s if sh is not None else None
-    calls += [
-        ("permute", lambda: m.moe_permute(s, x, L.slot_row, L.row_src, L.x_perm)),
-        ("gemm1_fwd", lambda: m.moe_ffn_gemm1_fwd(s, L.x_perm, W1, W3, L.offsets, L.ab, L.h, L.ws)),
-        ("gemm2_fwd", lambda: m.moe_ffn_gemm2_fwd(s, L.h, W2, L.offsets, L.y_perm, L.ws)),
-        ("combine", lambda: m.moe_combine(s, L.y_perm, g, L.slot_row, y_add, L.y)),
-        ("combine_bwd", lambda: m.moe_combine_bwd(s, dy, L.y_perm, g, L.slot_row, L.dy_perm, L.dgates)),
-    ]
-    if recompute:
-        calls += [("gemm1_recompute", lambda: m.moe_ffn_gemm1_fwd(s, L.x_perm, W1, W3, L.offsets, L.ab, L.h, L.ws))]
-    calls += [
-        ("dgrad2", lambda: m.moe_ffn_dgrad2(s, L.dy_perm, W2, L.ab, L.offsets, L.dab, L.ws)),
-        ("wgrad2", lambda: m.moe_ffn_wgrad2(s, L.h, L.dy_perm, L.offsets, L.dW2, L.ws)),
-        ("dgrad1", lambda: m.moe_ffn_dgrad1(s, L.dab, W1, W3, L.offsets, L.dx_perm, L.ws)),
-        ("wgrad1", lambda: m.moe_ffn_wgrad1(s, L.x_perm, L.dab, L.offsets, L.dW1, L.dW3, L.ws)),
-    ]
+    if L.mx_dispatch:  # routed rows of x and dy exist only as E4M3 codes (row and column layouts)
+        gemm1 = lambda: m.moe_ffn_gemm1_fwd_mx(s, L.xq_rows, L.xs_rows, W1, W3, L.offsets, L.ab, L.h, L.ws)  # noqa: E731
+        calls += [
+            ("permute", lambda: m.moe_permute_mx(s, x, L.slot_row, L.offsets, L.row_src, L.xq_rows, L.xs_rows,
+                                                 L.xq_cols, L.xs_cols)),
+            ("gemm1_fwd", gemm1),
+            ("gemm2_fwd", lambda: m.moe_ffn_gemm2_fwd(s, L.h, W2, L.offsets, L.y_perm, L.ws)),
+            ("combine", lambda: m.moe_combine(s, L.y_perm, g, L.slot_row, y_add, L.y)),
+            ("combine_bwd", lambda: m.moe_combine_bwd_mx(s, dy, L.y_perm, g, L.slot_row, L.row_src, L.offsets,
+                                                         L.dgates, L.dyq_rows, L.dys_rows, L.dyq_cols, L.dys_cols)),
+        ]
+        if recompute:
+            calls += [("gemm1_recompute", gemm1)]
+        calls += [
+            ("dgrad2", lambda: m.moe_ffn_dgrad2_mx(s, L.dyq_rows, L.dys_rows, W2, L.ab, L.offsets, L.dab, L.ws)),
+            ("wgrad2", lambda: m.moe_ffn_wgrad2_mx(s, L.h, L.dyq_cols, L.dys_cols, L.offsets, L.dW2, L.ws)),
+            ("dgrad1", lambda: m.moe_ffn_dgrad1(s, L.dab, W1, W3, L.offsets, L.dx_perm, L.ws)),
+            ("wgrad1", lambda: m.moe_ffn_wgrad1_mx(s, L.xq_cols, L.xs_cols, L.dab, L.offsets, L.dW1, L.dW3, L.ws)),
+        ]
+    else:
+        calls += [
+            ("permute", lambda: m.moe_permute(s, x, L.slot_row, L.row_src, L.x_perm)),
+            ("gemm1_fwd", lambda: m.moe_ffn_gemm1_fwd(s, L.x_perm, W1, W3, L.offsets, L.ab, L.h, L.ws)),
+            ("gemm2_fwd", lambda: m.moe_ffn_gemm2_fwd(s, L.h, W2, L.offsets, L.y_perm, L.ws)),
+            ("combine", lambda: m.moe_combine(s, L.y_perm, g, L.slot_row, y_add, L.y)),
+            ("combine_bwd", lambda: m.moe_combine_bwd(s, dy, L.y_perm, g, L.slot_row, L.dy_perm, L.dgates)),
+        ]
+        if recompute:
+            calls += [("gemm1_recompute",
+                       lambda: m.moe_ffn_gemm1_fwd(s, L.x_perm, W1, W3, L.offsets, L.ab, L.h, L.ws))]
+        calls += [
+            ("dgrad2", lambda: m.moe_ffn_dgrad2(s, L.dy_perm, W2, L.ab, L.offsets, L.dab, L.ws)),
+            ("wgrad2", lambda: m.moe_ffn_wgrad2(s, L.h, L.dy_perm, L.offsets, L.dW2, L.ws)),
+            ("dgrad1", lambda: m.moe_ffn_dgrad1(s, L.dab, W1, W3, L.offsets, L.dx_perm, L.ws)),
+            ("wgrad1", lambda: m.moe_ffn_wgrad1(s, L.x_perm, L.dab, L.offsets, L.dW1, L.dW3, L.ws)),
+        ]
     if learned:
         calls += [("route_bwd", lambda: m.moe_route_bwd(s, L.dgates, g, L.topk_idx, L.dlogits)),
                   ("router_bwd", lambda: m.moe_router_bwd(s, x, Wr, L.dlogits, L.dx_r, L.dWr, L.ws))]
@@ -117,8 +141,10 @@ def step_calls(m, L, d_inp, learned, recompute=False):
     return calls
 
 
-def algorithmic_work(w, eb):
-    """Per-launch algorithmic flops (GEMMs) and HBM bytes (everything) of each call."""
+def algorithmic_work(w, eb, mx_dispatch=False):
+    """Per-launch algorithmic flops (GEMMs) and HBM bytes (everything) of each call.  With
+    the MXFP8 dispatch the routed rows of x and dy are written once in each of two E4M3
+    layouts (1 + 1/32 bytes per element with the scales) and read in that form."""
     T, d, f, E, k = w.T, w.d, w.f, w.E, w.k
     R = T * k
     gem = {"gemm1_fwd": 2.0 * R * d * 2 * f, "gemm2_fwd": 2.0 * R * f * d, "dgrad2": 2.0 * R * d * f,
@@ -141,6 +167,16 @@ def algorithmic_work(w, eb):
         "router_bwd": 2 * T * E * 4 + E * d * eb + 2 * T * d * eb + E * d * 4,
         "permute_bwd": R * d * eb + 2 * T * d * eb + R * 4,
     }
+    if mx_dispatch:
+        q = R * d * 33 // 32  # one E4M3 layout of the routed rows with its scales
+        byt.update({
+            "permute": T * d * eb + 2 * q + R * 8,
+            "combine_bwd": T * d * eb + R * d * eb + 2 * q + R * 12 + T * k * 4,
+            "gemm1_fwd": q + 2 * wbytes + R * 3 * f * eb,
+            "dgrad2": q + wbytes + R * 2 * f * eb * 2,
+            "wgrad2": q + R * f * eb + wbytes,
+            "wgrad1": R * 2 * f * eb + q + 2 * wbytes,
+        })
     return gem, byt
 
 
@@ -198,7 +234,8 @@ def main():
     act = m.MOE_F32 if w.dtype == "f32" else m.MOE_BF16
     gemm = {"f32": m.MOE_F32, "bf16": m.MOE_BF16, "mxfp8": m.MOE_MXFP8}[w.gemm]
     torch.cuda.set_device(0)
-    L = m.MoEExpertLayer(w.T, w.d, w.f, w.E, w.k, act=act, gemm=gemm, shared_f=w.shared_f)
+    mx_dispatch = gemm == m.MOE_MXFP8 and not args.bf16_dispatch
+    L = m.MoEExpertLayer(w.T, w.d, w.f, w.E, w.k, act=act, gemm=gemm, shared_f=w.shared_f, mx_dispatch=mx_dispatch)
     dev = lambda v: v.cuda() if isinstance(v, torch.Tensor) else (tuple(u.cuda() for u in v)  # noqa: E731
                                                                  if isinstance(v, tuple) else v)
     d_inp = {k: dev(v) for k, v in inp.items()}
@@ -239,7 +276,7 @@ def main():
     tokens_per_s = w.T * args.steps / elapsed
 
     eb = 4 if w.dtype == "f32" else 2
-    gem, byt = algorithmic_work(w, eb)
+    gem, byt = algorithmic_work(w, eb, L.mx_dispatch)
     if w.shared_f:  # the shared expert's GEMMs: the routed ones with R = T, f = fs, one expert
         ws_ = dataclasses.replace(w, k=1, E=1, f=w.shared_f)
         gs, bs = algorithmic_work(ws_, eb)
@@ -290,15 +327,16 @@ def main():
         "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": w.gemm, "data": "synthetic",
         "config": {"workload": w.name, "T": w.T, "d": w.d, "f": w.f, "E": w.E, "k": w.k, "routing": w.routing,
-                   "gemm": w.gemm, "recompute": bool(args.recompute), "shared_f": w.shared_f},
+                   "gemm": w.gemm, "recompute": bool(args.recompute), "shared_f": w.shared_f,
+                   "mx_dispatch": L.mx_dispatch},
         "roofline": roofline,
         "grouped_gemm_mfma_frac_all6": round(sum(gem.values()) / (gemm_ms * 1e-3) / 1e12 / peak, 4),
         "kernels": kernels,
         "expert_load": {"max": int(L.counts.max().item()), "mean": w.T * w.k / w.E,
                         "empty": int((L.counts == 0).sum().item())},
-        # expert-FFN activations held from the forward to the backward (x_perm, y_perm, and
-        # ab, h unless recomputed)
-        "activation_bytes_held": 2 * w.R * w.d * eb + (0 if args.recompute else w.R * 3 * w.f * eb),
+        # expert-FFN activations held from the forward to the backward (the routed rows of x,
+        # y_perm, and ab, h unless recomputed)
+        "activation_bytes_held": L.activation_bytes() - (w.R * 3 * w.f * eb if args.recompute else 0),
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, inp, min(args.cpu_sample_tokens, w.T))

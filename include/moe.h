@@ -211,6 +211,68 @@ moe_status moe_permute_bwd(const moe_shape* s, const void* dx_perm, const int32_
 moe_status moe_mx_quantize(int32_t rows, int32_t cols, int32_t axis, const int32_t* seg_offsets,
                            int32_t nseg, const void* src, uint8_t* q, uint8_t* scales, void* stream);
 
+/* ---------------------------------------------------------------------------------------
+ * MXFP8 dispatch (shapes with gemm = MOE_MXFP8).  The routed rows leave the dispatch
+ * already block-quantised, so no bf16 copy of x_perm or dy_perm is written and the expert
+ * GEMMs quantise no activation that the dispatch has produced: MXFP8 serves the data moved
+ * to the experts as well as the expert FFN compute (unite.ai, "Ai2 κυκλοφορεί το
+ * Olmo-Core 3…", section "Παραλληλισμός, Ακρίβεια και Τεχνικές Μνήμης"; ettayeb.fr,
+ * "Olmo-core 3 ouvre l'entraînement des MoE…", section "Trois parallélismes, trois
+ * optimisations de routage").
+ *
+ * Each dispatch writes an [R, d] row set v in two layouts, with exactly the bytes
+ * moe_mx_quantize would write for v:
+ *   row layout     q_rows [R, d] u8, s_rows [R, d/32] u8     (axis 0)
+ *   column layout  q_cols [d, L] u8, s_cols [d, L/32] u8     (axis 1 with seg_offsets =
+ *                  offsets: blocks down each column restarting at every expert, expert e
+ *                  at columns [P_e, P_e + roundup(n_e, 128)), padding zero)
+ * with L = moe_mx_cols_ld(s) = R + 128 E.  Columns of the column layout past the last
+ * expert's padded end are not written.  Every buffer is caller-owned device memory,
+ * 16-byte aligned; the row and column layouts are what the *_mx GEMM calls below read.
+ * --------------------------------------------------------------------------------------- */
+
+/* L = T*k + 128*E, the row count of a column layout (pure host function; 0 for a bad shape). */
+size_t moe_mx_cols_ld(const moe_shape* s);
+
+/* Forward dispatch: v[r] = x[row_src[r]], with row_src[slot_row[t, j]] = t written first
+ * (as moe_permute).  x [T, d] bf16, slot_row [T, k], offsets [E + 1] (from moe_route /
+ * moe_route_given), row_src [R] int32 written.  Returns MOE_EUNSUPPORTED unless gemm =
+ * MOE_MXFP8. */
+moe_status moe_permute_mx(const moe_shape* s, const void* x, const int32_t* slot_row, const int32_t* offsets,
+                          int32_t* row_src, uint8_t* q_rows, uint8_t* s_rows, uint8_t* q_cols,
+                          uint8_t* s_cols, void* stream);
+
+/* Combine backward with the routed gradient quantised in the dispatch:
+ * dgates[t, j] = <dy[t], y_perm[slot_row[t, j]]> (float, bit-identical with
+ * moe_combine_bwd), and v[slot_row[t, j]] = bf16(gates[t, j] * dy[t]) (the values
+ * moe_combine_bwd would store in dy_perm) written only in the two MXFP8 layouts.
+ * row_src is the one moe_permute_mx wrote. */
+moe_status moe_combine_bwd_mx(const moe_shape* s, const void* dy, const void* y_perm, const float* gates,
+                              const int32_t* slot_row, const int32_t* row_src, const int32_t* offsets,
+                              float* dgates, uint8_t* q_rows, uint8_t* s_rows, uint8_t* q_cols,
+                              uint8_t* s_cols, void* stream);
+
+/* The expert GEMMs of moe_ffn_gemm1_fwd, moe_ffn_dgrad2, moe_ffn_wgrad2 and moe_ffn_wgrad1
+ * with the dispatched operand given in its MXFP8 layout instead of bf16 (bit-identical
+ * results, since the bytes are those the GEMM would have produced itself):
+ *   gemm1_fwd_mx: x rows (q_rows, s_rows of moe_permute_mx)
+ *   dgrad2_mx:    dy rows (q_rows, s_rows of moe_combine_bwd_mx)
+ *   wgrad2_mx:    dy columns (q_cols, s_cols of moe_combine_bwd_mx)
+ *   wgrad1_mx:    x columns (q_cols, s_cols of moe_permute_mx)
+ * Other arguments, workspace and errors as the bf16-operand calls. */
+moe_status moe_ffn_gemm1_fwd_mx(const moe_shape* s, const uint8_t* xq_rows, const uint8_t* xs_rows,
+                                const void* W1, const void* W3, const int32_t* offsets, void* ab, void* h,
+                                void* ws, size_t ws_bytes, void* stream);
+moe_status moe_ffn_dgrad2_mx(const moe_shape* s, const uint8_t* dyq_rows, const uint8_t* dys_rows,
+                             const void* W2, const void* ab, const int32_t* offsets, void* dab, void* ws,
+                             size_t ws_bytes, void* stream);
+moe_status moe_ffn_wgrad2_mx(const moe_shape* s, const void* h, const uint8_t* dyq_cols,
+                             const uint8_t* dys_cols, const int32_t* offsets, void* dW2, void* ws,
+                             size_t ws_bytes, void* stream);
+moe_status moe_ffn_wgrad1_mx(const moe_shape* s, const uint8_t* xq_cols, const uint8_t* xs_cols,
+                             const void* dab, const int32_t* offsets, void* dW1, void* dW3, void* ws,
+                             size_t ws_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

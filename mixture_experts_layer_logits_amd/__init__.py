@@ -65,8 +65,15 @@ _SIGS = {
     "moe_route_bwd": [_VP, _VP, _VP, _VP, _VP],
     "moe_router_bwd": [_VP, _VP, _VP, _VP, _VP, _VP, _SZ, _VP],
     "moe_permute_bwd": [_VP, _VP, _VP, _VP, _VP, _VP],
+    # MXFP8 dispatch and the GEMMs that read its quantised rows
+    "moe_permute_mx": [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP],
+    "moe_combine_bwd_mx": [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP],
+    "moe_ffn_gemm1_fwd_mx": [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _SZ, _VP],
+    "moe_ffn_dgrad2_mx": [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _SZ, _VP],
+    "moe_ffn_wgrad2_mx": [_VP, _VP, _VP, _VP, _VP, _VP, _SZ, _VP],
+    "moe_ffn_wgrad1_mx": [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _SZ, _VP],
 }
-EXPORTED = sorted(list(_SIGS) + ["moe_mx_quantize", "moe_workspace_size", "moe_status_str"])
+EXPORTED = sorted(list(_SIGS) + ["moe_mx_quantize", "moe_workspace_size", "moe_mx_cols_ld", "moe_status_str"])
 
 _lib = None
 
@@ -88,6 +95,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.moe_mx_quantize.restype = ctypes.c_int
     lib.moe_workspace_size.argtypes = [_SHP]
     lib.moe_workspace_size.restype = ctypes.c_size_t
+    lib.moe_mx_cols_ld.argtypes = [_SHP]
+    lib.moe_mx_cols_ld.restype = ctypes.c_size_t
     lib.moe_status_str.argtypes = [ctypes.c_int]
     lib.moe_status_str.restype = ctypes.c_char_p
     _lib = lib
@@ -122,6 +131,10 @@ def _call(name, shape, *args, stream=None):
 
 def moe_workspace_size(shape: moe_shape) -> int:
     return int(load_library().moe_workspace_size(ctypes.byref(shape)))
+
+
+def moe_mx_cols_ld(shape: moe_shape) -> int:
+    return int(load_library().moe_mx_cols_ld(ctypes.byref(shape)))
 
 
 def moe_status_str(status: int) -> str:
@@ -210,6 +223,32 @@ def moe_mx_quantize(rows, cols, axis, seg_offsets, nseg, src, q, scales, stream=
     st = lib.moe_mx_quantize(rows, cols, axis, _p(seg_offsets), nseg, _p(src), _p(q), _p(scales), _stream(stream))
     if st != 0:
         raise MoeError("moe_mx_quantize", st, lib.moe_status_str(st).decode())
+
+
+def moe_permute_mx(shape, x, slot_row, offsets, row_src, q_rows, s_rows, q_cols, s_cols, stream=None):
+    _call("moe_permute_mx", shape, x, slot_row, offsets, row_src, q_rows, s_rows, q_cols, s_cols, stream=stream)
+
+
+def moe_combine_bwd_mx(shape, dy, y_perm, gates, slot_row, row_src, offsets, dgates, q_rows, s_rows, q_cols, s_cols,
+                       stream=None):
+    _call("moe_combine_bwd_mx", shape, dy, y_perm, gates, slot_row, row_src, offsets, dgates, q_rows, s_rows, q_cols,
+          s_cols, stream=stream)
+
+
+def moe_ffn_gemm1_fwd_mx(shape, xq_rows, xs_rows, W1, W3, offsets, ab, h, ws, stream=None):
+    _call("moe_ffn_gemm1_fwd_mx", shape, xq_rows, xs_rows, W1, W3, offsets, ab, h, ws, _ws(ws), stream=stream)
+
+
+def moe_ffn_dgrad2_mx(shape, dyq_rows, dys_rows, W2, ab, offsets, dab, ws, stream=None):
+    _call("moe_ffn_dgrad2_mx", shape, dyq_rows, dys_rows, W2, ab, offsets, dab, ws, _ws(ws), stream=stream)
+
+
+def moe_ffn_wgrad2_mx(shape, h, dyq_cols, dys_cols, offsets, dW2, ws, stream=None):
+    _call("moe_ffn_wgrad2_mx", shape, h, dyq_cols, dys_cols, offsets, dW2, ws, _ws(ws), stream=stream)
+
+
+def moe_ffn_wgrad1_mx(shape, xq_cols, xs_cols, dab, offsets, dW1, dW3, ws, stream=None):
+    _call("moe_ffn_wgrad1_mx", shape, xq_cols, xs_cols, dab, offsets, dW1, dW3, ws, _ws(ws), stream=stream)
 
 
 from .layer import MoEExpertLayer  # noqa: E402  (re-export)

@@ -364,4 +364,91 @@ moe_status moe_mx_quantize(int32_t rows, int32_t cols, int32_t axis, const int32
   return launched(mx_quantize_cols_seg(rows, cols, seg_offsets, nseg, (const bf16_t*)src, q, scales, S(st)));
 }
 
+// ---------------------------------------------------------------------------------------
+// MXFP8 dispatch and the expert GEMMs that take its quantised rows
+// ---------------------------------------------------------------------------------------
+size_t moe_mx_cols_ld(const moe_shape* s) {
+  if (check_shape(s) != MOE_OK) return 0;
+  return (size_t)s->T * s->k + (size_t)kMxSegPad * s->E;
+}
+
+moe_status moe_permute_mx(const moe_shape* s, const void* x, const int32_t* slot_row, const int32_t* offsets,
+                          int32_t* row_src, uint8_t* q_rows, uint8_t* s_rows, uint8_t* q_cols, uint8_t* s_cols,
+                          void* st) {
+  MOE_TRY(check_shape(s));
+  if (s->gemm != MOE_MXFP8) return MOE_EUNSUPPORTED;
+  MOE_TRY(check_rows(s, {x, q_rows, s_rows, q_cols, s_cols}));
+  if (!rows_ok(s, slot_row) || !rows_ok(s, row_src) || !offsets) return MOE_ENULL;
+  if (s->T == 0) return MOE_OK;
+  MOE_TRY(launched(row_src_rows(s->T, s->k, slot_row, row_src, S(st))));
+  return launched(mx_dispatch(s->T * s->k, s->d, s->E, s->k, (const bf16_t*)x, row_src, offsets, nullptr, nullptr,
+                              q_rows, s_rows, q_cols, s_cols, S(st)));
+}
+
+moe_status moe_combine_bwd_mx(const moe_shape* s, const void* dy, const void* y_perm, const float* gates,
+                              const int32_t* slot_row, const int32_t* row_src, const int32_t* offsets, float* dgates,
+                              uint8_t* q_rows, uint8_t* s_rows, uint8_t* q_cols, uint8_t* s_cols, void* st) {
+  MOE_TRY(check_shape(s));
+  if (s->gemm != MOE_MXFP8) return MOE_EUNSUPPORTED;
+  MOE_TRY(check_rows(s, {dy, y_perm, q_rows, s_rows, q_cols, s_cols}));
+  if (!rows_ok(s, gates) || !rows_ok(s, slot_row) || !rows_ok(s, row_src) || !rows_ok(s, dgates) || !offsets)
+    return MOE_ENULL;
+  if (s->T == 0) return MOE_OK;
+  MOE_TRY(launched(dgates_rows(s->T, s->d, s->k, (const bf16_t*)dy, (const bf16_t*)y_perm, slot_row, dgates, S(st))));
+  return launched(mx_dispatch(s->T * s->k, s->d, s->E, s->k, (const bf16_t*)dy, row_src, offsets, gates, slot_row,
+                              q_rows, s_rows, q_cols, s_cols, S(st)));
+}
+
+moe_status moe_ffn_gemm1_fwd_mx(const moe_shape* s, const uint8_t* xq_rows, const uint8_t* xs_rows, const void* W1,
+                                const void* W3, const int32_t* offsets, void* ab, void* h, void* ws, size_t ws_bytes,
+                                void* st) {
+  MOE_TRY(check_shape(s));
+  if (s->gemm != MOE_MXFP8) return MOE_EUNSUPPORTED;
+  MOE_TRY(check_ptrs({W1, W3}));
+  MOE_TRY(check_rows(s, {xq_rows, xs_rows, ab, h}));
+  if (!offsets || !ws) return MOE_ENULL;
+  const GemmShape g = gshape(s);
+  if (ws_bytes < mx_workspace_bytes(g.R, g.d, g.f, g.E)) return MOE_EWORKSPACE;
+  return launched(gemm1_fwd_mx(g, offsets, nullptr, (const bf16_t*)W1, (const bf16_t*)W3, (bf16_t*)ab, (bf16_t*)h, ws,
+                               S(st), MxIn{xq_rows, xs_rows}));
+}
+
+moe_status moe_ffn_dgrad2_mx(const moe_shape* s, const uint8_t* dyq_rows, const uint8_t* dys_rows, const void* W2,
+                             const void* ab, const int32_t* offsets, void* dab, void* ws, size_t ws_bytes, void* st) {
+  MOE_TRY(check_shape(s));
+  if (s->gemm != MOE_MXFP8) return MOE_EUNSUPPORTED;
+  MOE_TRY(check_ptrs({W2}));
+  MOE_TRY(check_rows(s, {dyq_rows, dys_rows, ab, dab}));
+  if (!offsets || !ws) return MOE_ENULL;
+  const GemmShape g = gshape(s);
+  if (ws_bytes < mx_workspace_bytes(g.R, g.d, g.f, g.E)) return MOE_EWORKSPACE;
+  return launched(dgrad2_mx(g, offsets, nullptr, (const bf16_t*)W2, (const bf16_t*)ab, (bf16_t*)dab, ws, S(st),
+                            MxIn{dyq_rows, dys_rows}));
+}
+
+moe_status moe_ffn_wgrad2_mx(const moe_shape* s, const void* h, const uint8_t* dyq_cols, const uint8_t* dys_cols,
+                             const int32_t* offsets, void* dW2, void* ws, size_t ws_bytes, void* st) {
+  MOE_TRY(check_shape(s));
+  if (s->gemm != MOE_MXFP8) return MOE_EUNSUPPORTED;
+  MOE_TRY(check_ptrs({dW2, dyq_cols, dys_cols}));
+  MOE_TRY(check_rows(s, {h}));
+  if (!offsets || !ws) return MOE_ENULL;
+  const GemmShape g = gshape(s);
+  if (ws_bytes < mx_workspace_bytes(g.R, g.d, g.f, g.E)) return MOE_EWORKSPACE;
+  return launched(wgrad2_mx(g, offsets, (const bf16_t*)h, nullptr, (bf16_t*)dW2, ws, S(st), MxIn{dyq_cols, dys_cols}));
+}
+
+moe_status moe_ffn_wgrad1_mx(const moe_shape* s, const uint8_t* xq_cols, const uint8_t* xs_cols, const void* dab,
+                             const int32_t* offsets, void* dW1, void* dW3, void* ws, size_t ws_bytes, void* st) {
+  MOE_TRY(check_shape(s));
+  if (s->gemm != MOE_MXFP8) return MOE_EUNSUPPORTED;
+  MOE_TRY(check_ptrs({dW1, dW3, xq_cols, xs_cols}));
+  MOE_TRY(check_rows(s, {dab}));
+  if (!offsets || !ws) return MOE_ENULL;
+  const GemmShape g = gshape(s);
+  if (ws_bytes < mx_workspace_bytes(g.R, g.d, g.f, g.E)) return MOE_EWORKSPACE;
+  return launched(wgrad1_mx(g, offsets, nullptr, (const bf16_t*)dab, (bf16_t*)dW1, (bf16_t*)dW3, ws, S(st),
+                            MxIn{xq_cols, xs_cols}));
+}
+
 }  // extern "C"

@@ -740,19 +740,23 @@ static hipError_t launch_cfg(const Prob& p, hipStream_t st, int bk, int stages) 
   return hipErrorInvalidConfiguration;
 }
 
+// The default build compiles the tile shapes the defaults use; -DMOE_ALL_TILES adds the
+// rest for tuning sweeps (a tile that is not compiled falls back to 128x128).
 template <class Prob>
 static hipError_t launch(TileChoice c, const Prob& p, hipStream_t st) {
   switch (c.tile) {
+    case Tile::t32x128: return launch_cfg<TileCfg<32, 128, 1, 4>>(p, st, c.bk, c.stages);
+    case Tile::t128x256w8: return launch_cfg<TileCfg<128, 256, 2, 4>>(p, st, c.bk, c.stages);
+    case Tile::t256x256w8: return launch_cfg<TileCfg<256, 256, 2, 4>>(p, st, c.bk, c.stages);
+#ifdef MOE_ALL_TILES
     case Tile::t128x256: return launch_cfg<TileCfg<128, 256, 2, 2>>(p, st, c.bk, c.stages);
     case Tile::t256x128: return launch_cfg<TileCfg<256, 128, 2, 2>>(p, st, c.bk, c.stages);
     case Tile::t64x128: return launch_cfg<TileCfg<64, 128, 1, 4>>(p, st, c.bk, c.stages);
-    case Tile::t32x128: return launch_cfg<TileCfg<32, 128, 1, 4>>(p, st, c.bk, c.stages);
     case Tile::t256x128w8: return launch_cfg<TileCfg<256, 128, 4, 2>>(p, st, c.bk, c.stages);
-    case Tile::t128x256w8: return launch_cfg<TileCfg<128, 256, 2, 4>>(p, st, c.bk, c.stages);
-    case Tile::t256x256w8: return launch_cfg<TileCfg<256, 256, 2, 4>>(p, st, c.bk, c.stages);
     case Tile::t256x256w4: return launch_cfg<TileCfg<256, 256, 2, 2>>(p, st, c.bk, c.stages);
     case Tile::t128x256w2: return launch_cfg<TileCfg<128, 256, 1, 2>>(p, st, c.bk, c.stages);
     case Tile::t128x256m1: return launch_cfg<TileCfg<128, 256, 1, 4>>(p, st, c.bk, c.stages);
+#endif
     default: return launch_cfg<TileCfg<128, 128, 2, 2>>(p, st, c.bk, c.stages);
   }
 }

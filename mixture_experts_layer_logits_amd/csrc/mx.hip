@@ -7,8 +7,9 @@
 //
 // Scale: the smallest 2^s with amax * 2^-s <= 448 (E4M3's largest finite value),
 // s clamped to [-127, 127]; blocks whose amax is zero or an fp32 subnormal get -127.
-// Elements: round-to-nearest-even onto the E4M3 grid, done with integer arithmetic on
-// the fp32 bit pattern (exact: the scaled value v * 2^-s is exact in fp32).
+// Elements: v * 2^-s (exact in fp32) rounded to nearest-even onto the E4M3 grid by
+// gfx950's packed fp8 conversion, two elements per instruction; a GPU test checks it
+// against the oracle's encoder on every bf16 value of magnitude <= 448.
 #include "common.h"
 #include "mx.h"
 #include "tilemap.h"
@@ -24,27 +25,18 @@ __device__ __forceinline__ int mx_scale_exp(float amax) {
   return s < -127 ? -127 : (s > 127 ? 127 : s);
 }
 
-// |v| <= 448 finite -> E4M3 code, round to nearest even
-__device__ __forceinline__ uint32_t e4m3_rne(float v) {
-  const uint32_t u = __float_as_uint(v);
-  const uint32_t sign = (u >> 24) & 0x80u;
-  const float a = fabsf(v);
-  uint32_t code;
-  if (a < 0.015625f) {                       // below 2^-6: subnormal steps of 2^-9
-    code = (uint32_t)__builtin_rintf(a * 512.0f);
-  } else {
-    const uint32_t au = __float_as_uint(a);
-    int e = (int)((au >> 23) & 0xff) - 127;  // -6 .. 8
-    const uint32_t m23 = au & 0x7fffffu;
-    uint32_t m = (m23 + 0x7ffffu + ((m23 >> 20) & 1u)) >> 20;  // RNE to 3 bits: 0..8
-    if (m == 8) { m = 0; e += 1; }
-    code = ((uint32_t)(e + 7) << 3) | m;
-    if (code > 0x7eu) code = 0x7eu;          // guard: never reached for |v| <= 448
-  }
-  return sign | code;
+// Four values of magnitude <= 448 -> four E4M3 codes (bytes 0..3), round to nearest even.
+__device__ __forceinline__ uint32_t e4m3x4(float a, float b, float c, float d) {
+  const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(c, d, lo, true);
 }
 
 __device__ __forceinline__ float exp2i(int s) { return __uint_as_float((uint32_t)(s + 127) << 23); }  // 2^s, s in [-126,127]
+
+// 2^-s as one fp32 factor.  Finite bf16 input has amax < 2^128, so s <= 120 and the factor
+// is a normal number; v * 2^-s is exact unless it falls below 2^-126, where its code is
+// zero either way.
+__device__ __forceinline__ float mx_inv_scale(int s) { return exp2i(-s); }
 
 namespace {
 
@@ -75,15 +67,10 @@ __global__ void mx_rows_kernel(int rows, int cols, const bf16_t* __restrict__ sr
 #pragma unroll
   for (int i = 0; i < 32; i++) amax = fmaxf(amax, fabsf(v[i]));
   const int s = mx_scale_exp(amax);
-  // 2^-s as a product of two normal powers so s = -127 (2^127) and s = 127 stay exact
-  const float r1 = exp2i(-s / 2), r2 = exp2i(-s - (-s / 2));
+  const float r = mx_inv_scale(s);
   uint32_t w[8];
 #pragma unroll
-  for (int i = 0; i < 8; i++) {
-    w[i] = 0;
-#pragma unroll
-    for (int j = 0; j < 4; j++) w[i] |= e4m3_rne(v[4 * i + j] * r1 * r2) << (8 * j);
-  }
+  for (int i = 0; i < 8; i++) w[i] = e4m3x4(v[4 * i] * r, v[4 * i + 1] * r, v[4 * i + 2] * r, v[4 * i + 3] * r);
   uint4* o = reinterpret_cast<uint4*>(q + ob * kMxBlock);
   o[0] = make_uint4(w[0], w[1], w[2], w[3]);
   o[1] = make_uint4(w[4], w[5], w[6], w[7]);
@@ -185,14 +172,10 @@ __global__ void __launch_bounds__(kTransThreads) mx_trans_kernel(TransQ a) {
         amax = fmaxf(amax, fabsf(v[i]));
       }
       const int sexp = mx_scale_exp(amax);
-      const float f1 = exp2i(-sexp / 2), f2 = exp2i(-sexp - (-sexp / 2));
+      const float r = mx_inv_scale(sexp);
       uint32_t w[8];
 #pragma unroll
-      for (int i = 0; i < 8; i++) {
-        w[i] = 0;
-#pragma unroll
-        for (int j = 0; j < 4; j++) w[i] |= e4m3_rne(v[4 * i + j] * f1 * f2) << (8 * j);
-      }
+      for (int i = 0; i < 8; i++) w[i] = e4m3x4(v[4 * i] * r, v[4 * i + 1] * r, v[4 * i + 2] * r, v[4 * i + 3] * r);
       uint4* o = reinterpret_cast<uint4*>(&s_out[c][b * 32]);
       o[0] = make_uint4(w[0], w[1], w[2], w[3]);
       o[1] = make_uint4(w[4], w[5], w[6], w[7]);
@@ -211,7 +194,257 @@ __global__ void __launch_bounds__(kTransThreads) mx_trans_kernel(TransQ a) {
   }
 }
 
+// ---------------------------------------------------------------------------------------
+// MXFP8 dispatch: the routed rows v_r, r in [0, R), are gathered from their tokens and
+// leave only as block-quantised codes, in both layouts the expert GEMMs read, so no bf16
+// copy of them is ever written (MXFP8 for the data moved to the experts: unite.ai, section
+// "Παραλληλισμός, Ακρίβεια και Τεχνικές Μνήμης"):
+//   row layout     q_rows [R][cols], s_rows [R][cols / 32]        (as mx_quantize_rows)
+//   column layout  q_cols [cols][ld], s_cols [cols][ld / 32]       (as mx_quantize_cols_seg:
+//                  blocks down each column restarting at every expert, experts padded to
+//                  128 rows at P_e = sum_{e'<e} roundup(n_e', 128))
+// v_r = src[row_src[r]], or with gates v_r = bf16(gates[t, j] * src[t]) for r = slot_row[t, j]
+// (the product rounded once to bf16, as the routed output gradient is stored in bf16).
+//
+// A workgroup owns one 128-row tile of the padded row space (rows of one expert: its token
+// ids and gates are looked up once) and a run of 64-column tiles.  Per column tile each
+// thread loads four 16-byte chunks (consecutive lanes on consecutive chunks of a row; the
+// next tile's chunks are in flight while the current one is worked on), quantises its row
+// blocks in registers (a 32-column block spans the four lanes of a quad), and stages the
+// bf16 values in LDS; each lane then quantises one column's 32-row block from LDS, and the
+// codes leave through an LDS tile as full 128-byte lines of the column layout.  The row
+// layout gets 64-byte halves of its lines from consecutive column tiles of one workgroup.
+// ---------------------------------------------------------------------------------------
+struct DispatchQ {
+  const bf16_t* src;  // [T][cols]
+  int cols;
+  const int32_t* row_src;  // [R]
+  const int32_t* seg;      // expert offsets [nseg + 1]
+  int nseg;
+  const float* gates;       // [T][k], nullptr: ungated
+  const int32_t* slot_row;  // [T][k] (gated only)
+  int k;
+  uint8_t* q_rows;
+  uint8_t* s_rows;
+  uint8_t* q_cols;
+  uint8_t* s_cols;
+  int64_t ld;     // row count of the column layout (R + 128 nseg)
+  int col_tiles;  // column tiles per workgroup
+};
+
+constexpr int kDispRows = 128, kDispCols = 64, kDispThreads = 256;
+constexpr int kDispRowChunks = kDispCols * 2 / 16;             // 16-byte chunks per staged row: 8
+constexpr int kDispInPitch = kDispCols * 2 + 16;               // bytes per staged bf16 row (bank spread)
+constexpr int kDispOutPitch = kDispRows + 16;                  // bytes per staged column of codes
+constexpr int kDispChunks = kDispRows * kDispRowChunks / kDispThreads;  // chunks per thread: 4
+constexpr int kDispRowStep = kDispThreads / kDispRowChunks;    // rows between a thread's chunks: 32
+static_assert(kDispCols * kDispOutPitch <= kDispRows * kDispInPitch, "code tile reuses the input tile");
+static_assert((kMaxExperts + 1) * 4 <= kDispRows * kDispInPitch, "segment scan reuses the input tile");
+static_assert(kDispCols == kWave && kDispRows == 32 * (kDispThreads / kWave), "one column per lane, one block per wave");
+
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+template <int CTRL>
+__device__ __forceinline__ float quad_max(float v) {
+  return fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, false)));
+}
+
+__device__ __forceinline__ void widen_bf16x8(const uint4& q, float (&v)[8]) {
+  const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+  for (int i = 0; i < 4; i++) {
+    v[2 * i] = __uint_as_float(w[i] << 16);
+    v[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+  }
+}
+
+__global__ void __launch_bounds__(kDispThreads) mx_dispatch_kernel(DispatchQ a) {
+  __shared__ __attribute__((aligned(16))) uint8_t s_buf[kDispRows * kDispInPitch];
+  __shared__ int s_tok[kDispRows];
+  __shared__ float s_gate[kDispRows];
+  __shared__ int s_wsum[kDispThreads / kWave];
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
+
+  // --- padded tile starts of the experts (exclusive scan of roundup(n_e, 128) / 128),
+  //     four experts per thread, in s_buf; then the expert owning this row tile
+  int* s_tstart = reinterpret_cast<int*>(s_buf);
+  {
+    int cnt[4], local = 0;
+#pragma unroll
+    for (int u = 0; u < 4; u++) {
+      const int e = tid * 4 + u;
+      cnt[u] = e < a.nseg ? (a.seg[e + 1] - a.seg[e] + kDispRows - 1) / kDispRows : 0;
+      local += cnt[u];
+    }
+    int incl = local;
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+      const int v = __shfl_up(incl, o, kWave);
+      if (lane >= o) incl += v;
+    }
+    if (lane == kWave - 1) s_wsum[wave] = incl;
+    __syncthreads();
+    int excl = incl - local;
+    for (int w = 0; w < wave; w++) excl += s_wsum[w];
+#pragma unroll
+    for (int u = 0; u < 4; u++) {
+      const int e = tid * 4 + u;
+      if (e < a.nseg) s_tstart[e] = excl;
+      excl += cnt[u];
+    }
+    if (tid == 0) s_tstart[a.nseg] = s_wsum[0] + s_wsum[1] + s_wsum[2] + s_wsum[3];
+    __syncthreads();
+  }
+  const int rt = blockIdx.x;
+  if (rt >= s_tstart[a.nseg]) return;  // whole workgroup: past the last padded tile
+  int e = 0;
+  {
+    int hi = a.nseg;  // last expert with s_tstart[e] <= rt (it owns >= 1 tile)
+    while (hi - e > 1) {
+      const int mid = (e + hi) >> 1;
+      if (s_tstart[mid] <= rt) e = mid; else hi = mid;
+    }
+  }
+  const int r0 = a.seg[e] + (rt - s_tstart[e]) * kDispRows;
+  const int nvalid = min(kDispRows, a.seg[e + 1] - r0);
+  const int64_t prow = (int64_t)rt * kDispRows;  // first row of this tile in the column layout
+  if (tid < kDispRows) {
+    int t = -1;
+    float g = 1.f;
+    if (tid < nvalid) {
+      const int r = r0 + tid;
+      t = a.row_src[r];
+      if (a.gates) {
+        for (int j = 0; j < a.k; j++)
+          if (a.slot_row[(int64_t)t * a.k + j] == r) g = a.gates[(int64_t)t * a.k + j];
+      }
+    }
+    s_tok[tid] = t;
+    s_gate[tid] = g;
+  }
+  __syncthreads();  // s_tstart is dead from here on; s_buf becomes the tile buffer
+
+  const int chunk = tid % kDispRowChunks, row_base = tid / kDispRowChunks;  // rows row_base + 32 i
+  const int ct_begin = blockIdx.y * a.col_tiles;
+  const int ct_end = min(ct_begin + a.col_tiles, a.cols / kDispCols);
+  const int nbc = a.cols / kMxBlock;
+  // a thread's source rows (padding rows read row 0 and are zeroed after the load, so no
+  // load sits in a branch)
+  const bf16_t* srcp[kDispChunks];
+  uint32_t keep[kDispChunks];  // all ones for a routed row, zero for padding
+#pragma unroll
+  for (int i = 0; i < kDispChunks; i++) {
+    const int t = s_tok[row_base + kDispRowStep * i];
+    keep[i] = t >= 0 ? 0xffffffffu : 0u;
+    srcp[i] = a.src + (int64_t)(t < 0 ? 0 : t) * a.cols + chunk * 8;
+  }
+  // the row layout of this tile's rows as one buffer: stores of padding rows fall past its
+  // end and are dropped by the hardware, so no store sits in a branch either
+  const __amdgpu_buffer_rsrc_t rq =
+      __builtin_amdgcn_make_buffer_rsrc(a.q_rows + (int64_t)r0 * a.cols, (short)0, nvalid * a.cols, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rs =
+      __builtin_amdgcn_make_buffer_rsrc(a.s_rows + (int64_t)r0 * nbc, (short)0, nvalid * nbc, 0x00020000);
+
+  auto load = [&](uint4 (&v)[kDispChunks], int ct) {
+#pragma unroll
+    for (int i = 0; i < kDispChunks; i++) v[i] = *reinterpret_cast<const uint4*>(srcp[i] + ct * kDispCols);
+  };
+  uint4 cur[kDispChunks], nxt[kDispChunks];
+  if (ct_begin < ct_end) load(cur, ct_begin);
+  for (int ct = ct_begin; ct < ct_end; ct++) {
+    const int c0 = ct * kDispCols;
+    load(nxt, min(ct + 1, ct_end - 1));  // the next tile's rows are in flight during this one
+    // --- row blocks, straight from registers
+#pragma unroll
+    for (int i = 0; i < kDispChunks; i++) {
+      const int row = row_base + kDispRowStep * i;
+      cur[i] = make_uint4(cur[i].x & keep[i], cur[i].y & keep[i], cur[i].z & keep[i], cur[i].w & keep[i]);
+      float v[8];
+      widen_bf16x8(cur[i], v);
+      if (a.gates) {  // v = bf16(g * src): the stored routed gradient
+        const float g = s_gate[row];
+        uint32_t w[4];
+#pragma unroll
+        for (int u = 0; u < 4; u++) w[u] = (uint32_t)f2bf(g * v[2 * u]) | ((uint32_t)f2bf(g * v[2 * u + 1]) << 16);
+        cur[i] = make_uint4(w[0], w[1], w[2], w[3]);
+        widen_bf16x8(cur[i], v);
+      }
+      float amax = 0.f;
+#pragma unroll
+      for (int u = 0; u < 8; u++) amax = fmaxf(amax, fabsf(v[u]));
+      amax = quad_max<0xB1>(amax);  // the four lanes of a 32-column block
+      amax = quad_max<0x4E>(amax);
+      const int sexp = mx_scale_exp(amax);
+      const float r = mx_inv_scale(sexp);
+      const uint32_t w0 = e4m3x4(v[0] * r, v[1] * r, v[2] * r, v[3] * r);
+      const uint32_t w1 = e4m3x4(v[4] * r, v[5] * r, v[6] * r, v[7] * r);
+      // the scale bytes of the row's two blocks, gathered into the lane of chunk 0 (the
+      // other lanes' stores are aimed past the buffer and dropped)
+      const uint32_t sb = (uint32_t)(sexp + 127);
+      const uint32_t sw = sb | (__shfl_down(sb, 4, kDispRowChunks) << 8);
+      const uint2 codes = make_uint2(w0, w1);
+      __builtin_amdgcn_raw_buffer_store_b64(*reinterpret_cast<const u32x2*>(&codes), rq,
+                                            row * a.cols + c0 + chunk * 8, 0, 0);
+      __builtin_amdgcn_raw_buffer_store_b16((uint16_t)sw, rs, chunk == 0 ? row * nbc + c0 / kMxBlock : 0x7ffffff0,
+                                            0, 0);
+      *reinterpret_cast<uint4*>(s_buf + row * kDispInPitch + chunk * 16) = cur[i];
+    }
+    __syncthreads();
+    // --- column blocks: wave w takes rows [32 w, 32 w + 32) of column `lane`; two passes
+    //     over the staged values (block maximum, then the codes)
+    uint32_t q[8];
+    {
+      const uint8_t* col = s_buf + wave * 32 * kDispInPitch + lane * 2;
+      float m = 0.f;
+#pragma unroll
+      for (int i = 0; i < 32; i++)
+        m = fmaxf(m, fabsf(bf2f(*reinterpret_cast<const bf16_t*>(col + i * kDispInPitch))));
+      const int sexp = mx_scale_exp(m);
+      const float r = mx_inv_scale(sexp);
+      auto at = [&](int i) { return bf2f(*reinterpret_cast<const bf16_t*>(col + i * kDispInPitch)) * r; };
+#pragma unroll
+      for (int i = 0; i < 8; i++) q[i] = e4m3x4(at(4 * i), at(4 * i + 1), at(4 * i + 2), at(4 * i + 3));
+      a.s_cols[(int64_t)(c0 + lane) * (a.ld / kMxBlock) + prow / kMxBlock + wave] = (uint8_t)(sexp + 127);
+    }
+    __syncthreads();  // every wave is done reading the bf16 tile
+    {
+      uint4* o = reinterpret_cast<uint4*>(s_buf + lane * kDispOutPitch + wave * 32);
+      o[0] = make_uint4(q[0], q[1], q[2], q[3]);
+      o[1] = make_uint4(q[4], q[5], q[6], q[7]);
+    }
+    __syncthreads();
+    // 64 columns x 128 bytes, 8 lanes per line
+#pragma unroll
+    for (int u = 0; u < kDispCols * kDispRows / 16 / kDispThreads; u++) {
+      const int i = tid + kDispThreads * u, c = i >> 3, ch = i & 7;
+      *reinterpret_cast<uint4*>(a.q_cols + (int64_t)(c0 + c) * a.ld + prow + ch * 16) =
+          *reinterpret_cast<const uint4*>(s_buf + c * kDispOutPitch + ch * 16);
+    }
+    __syncthreads();  // the tile buffer is rewritten by the next column tile
+#pragma unroll
+    for (int i = 0; i < kDispChunks; i++) cur[i] = nxt[i];
+  }
+}
+
 }  // namespace
+
+hipError_t mx_dispatch(int R, int cols, int E, int k, const bf16_t* src, const int32_t* row_src,
+                       const int32_t* offsets, const float* gates, const int32_t* slot_row, uint8_t* q_rows,
+                       uint8_t* s_rows, uint8_t* q_cols, uint8_t* s_cols, hipStream_t st) {
+  if (R == 0) return hipSuccess;
+  if (cols % kDispCols != 0 || E < 1 || E > kMaxExperts) return hipErrorInvalidValue;
+  // upper bound of the padded row tiles: sum_e ceil(n_e / 128) <= ceil(R / 128) + E
+  const int row_tiles = (R + kDispRows - 1) / kDispRows + E;
+  const int col_tiles = cols / kDispCols;
+  // about 2048 workgroups, each on a run of column tiles of one row tile
+  int per = (int)(((int64_t)row_tiles * col_tiles + 2047) / 2048);
+  per = per < 1 ? 1 : (per > col_tiles ? col_tiles : per);
+  DispatchQ a{src, cols, row_src, offsets, E, gates, slot_row, k, q_rows, s_rows, q_cols, s_cols,
+              (int64_t)R + (int64_t)kMxSegPad * E, per};
+  const dim3 grid((unsigned)row_tiles, (unsigned)((col_tiles + per - 1) / per));
+  hipLaunchKernelGGL(mx_dispatch_kernel, grid, dim3(kDispThreads), 0, st, a);
+  return hipGetLastError();
+}
 
 hipError_t mx_quantize_rows(int rows, int cols, const bf16_t* src, uint8_t* q, uint8_t* scales, hipStream_t st) {
   const int64_t n = (int64_t)rows * (cols / kMxBlock);
@@ -696,13 +929,18 @@ struct Carve {
 }  // namespace
 
 hipError_t gemm1_fwd_mx(const GemmShape& s, const int* offsets, const bf16_t* X, const bf16_t* W1, const bf16_t* W3,
-                        bf16_t* ab, bf16_t* h, void* ws, hipStream_t st) {
+                        bf16_t* ab, bf16_t* h, void* ws, hipStream_t st, MxIn x_rows) {
   Carve c{static_cast<char*>(ws)};
   const int64_t Ef = (int64_t)s.E * s.f;
   uint8_t *xq = c.take((size_t)s.R * s.d), *xs = c.take((size_t)s.R * s.d / kMxBlock);
   uint8_t *q13 = c.take((size_t)2 * Ef * s.d), *s13 = c.take((size_t)2 * Ef * s.d / kMxBlock);
   hipError_t err;
-  if ((err = mx_quantize_rows(s.R, s.d, X, xq, xs, st)) != hipSuccess) return err;
+  if (x_rows.q) {
+    xq = const_cast<uint8_t*>(x_rows.q);
+    xs = const_cast<uint8_t*>(x_rows.s);
+  } else if ((err = mx_quantize_rows(s.R, s.d, X, xq, xs, st)) != hipSuccess) {
+    return err;
+  }
   if ((err = mx_quantize_w13(s.E, s.f, s.d, W1, W3, q13, s13, st)) != hipSuccess) return err;
   MxGemm1 p;
   p.M = s.R; p.N = 2 * s.f; p.K = s.d; p.E = s.E; p.offsets = offsets; p.qa = xq; p.sa = xs; p.f = s.f;
@@ -735,13 +973,18 @@ static hipError_t quantize_weight_t(int E, int rows_e, int cols, const bf16_t* W
 }
 
 hipError_t dgrad2_mx(const GemmShape& s, const int* offsets, const bf16_t* dY, const bf16_t* W2, const bf16_t* ab,
-                     bf16_t* dab, void* ws, hipStream_t st) {
+                     bf16_t* dab, void* ws, hipStream_t st, MxIn dy_rows) {
   Carve c{static_cast<char*>(ws)};
   const int64_t Ef = (int64_t)s.E * s.f;
   uint8_t *yq = c.take((size_t)s.R * s.d), *ys = c.take((size_t)s.R * s.d / kMxBlock);
   uint8_t *wq = c.take((size_t)Ef * s.d), *wsc = c.take((size_t)Ef * s.d / kMxBlock);
   hipError_t err;
-  if ((err = mx_quantize_rows(s.R, s.d, dY, yq, ys, st)) != hipSuccess) return err;
+  if (dy_rows.q) {
+    yq = const_cast<uint8_t*>(dy_rows.q);
+    ys = const_cast<uint8_t*>(dy_rows.s);
+  } else if ((err = mx_quantize_rows(s.R, s.d, dY, yq, ys, st)) != hipSuccess) {
+    return err;
+  }
   if ((err = quantize_weight_t(s.E, s.d, s.f, W2, wq, wsc, s.d, 0, st)) != hipSuccess) return err;  // W2_e^T [f][d]
   MxDgrad2 p;
   p.M = s.R; p.N = s.f; p.K = s.d; p.E = s.E; p.offsets = offsets; p.qa = yq; p.sa = ys;
@@ -767,13 +1010,18 @@ hipError_t dgrad1_mx(const GemmShape& s, const int* offsets, const bf16_t* dab, 
 }
 
 hipError_t wgrad2_mx(const GemmShape& s, const int* offsets, const bf16_t* H, const bf16_t* dY, bf16_t* dW2,
-                     void* ws, hipStream_t st) {
+                     void* ws, hipStream_t st, MxIn dy_cols) {
   Carve c{static_cast<char*>(ws)};
   const int64_t Rp = (int64_t)s.R + (int64_t)kMxSegPad * s.E;
   uint8_t *aq = c.take((size_t)(s.d * Rp)), *as = c.take((size_t)(s.d * Rp / kMxBlock));
   uint8_t *bq = c.take((size_t)(s.f * Rp)), *bs = c.take((size_t)(s.f * Rp / kMxBlock));
   hipError_t err;
-  if ((err = mx_quantize_cols_seg(s.R, s.d, offsets, s.E, dY, aq, as, st)) != hipSuccess) return err;
+  if (dy_cols.q) {
+    aq = const_cast<uint8_t*>(dy_cols.q);
+    as = const_cast<uint8_t*>(dy_cols.s);
+  } else if ((err = mx_quantize_cols_seg(s.R, s.d, offsets, s.E, dY, aq, as, st)) != hipSuccess) {
+    return err;
+  }
   if ((err = mx_quantize_cols_seg(s.R, s.f, offsets, s.E, H, bq, bs, st)) != hipSuccess) return err;
   MxWgrad p;
   p.M = s.d; p.N = s.f; p.K = (int)Rp; p.E = s.E; p.offsets = offsets; p.qa = aq; p.sa = as;
@@ -782,14 +1030,19 @@ hipError_t wgrad2_mx(const GemmShape& s, const int* offsets, const bf16_t* H, co
 }
 
 hipError_t wgrad1_mx(const GemmShape& s, const int* offsets, const bf16_t* X, const bf16_t* dab, bf16_t* dW1,
-                     bf16_t* dW3, void* ws, hipStream_t st) {
+                     bf16_t* dW3, void* ws, hipStream_t st, MxIn x_cols) {
   Carve c{static_cast<char*>(ws)};
   const int64_t Rp = (int64_t)s.R + (int64_t)kMxSegPad * s.E;
   uint8_t *aq = c.take((size_t)(2 * s.f * Rp)), *as = c.take((size_t)(2 * s.f * Rp / kMxBlock));
   uint8_t *bq = c.take((size_t)(s.d * Rp)), *bs = c.take((size_t)(s.d * Rp / kMxBlock));
   hipError_t err;
   if ((err = mx_quantize_cols_seg(s.R, 2 * s.f, offsets, s.E, dab, aq, as, st)) != hipSuccess) return err;
-  if ((err = mx_quantize_cols_seg(s.R, s.d, offsets, s.E, X, bq, bs, st)) != hipSuccess) return err;
+  if (x_cols.q) {
+    bq = const_cast<uint8_t*>(x_cols.q);
+    bs = const_cast<uint8_t*>(x_cols.s);
+  } else if ((err = mx_quantize_cols_seg(s.R, s.d, offsets, s.E, X, bq, bs, st)) != hipSuccess) {
+    return err;
+  }
   MxWgrad p;
   p.M = 2 * s.f; p.N = s.d; p.K = (int)Rp; p.E = s.E; p.offsets = offsets; p.qa = aq; p.sa = as;
   p.qb = bq; p.sb = bs; p.C0 = dW1; p.C1 = dW3; p.split = s.f;

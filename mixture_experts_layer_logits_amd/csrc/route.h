@@ -3,6 +3,7 @@
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
+#include "common.h"
 
 namespace moe {
 
@@ -27,6 +28,11 @@ hipError_t combine_rows(int elem_bytes, int T, int d, int k, const void* y_perm,
 hipError_t combine_rows_bwd(int elem_bytes, int T, int d, int k, const void* dy, const void* y_perm,
                             const float* gates, const int32_t* slot_row, void* dy_perm, float* dgates,
                             hipStream_t st);
+// dgates[t, j] = <dy[t], y_perm[slot_row[t, j]]> (bf16 rows), bit-identical with combine_rows_bwd's
+hipError_t dgates_rows(int T, int d, int k, const bf16_t* dy, const bf16_t* y_perm, const int32_t* slot_row,
+                       float* dgates, hipStream_t st);
+// row_src[slot_row[t, j]] = t
+hipError_t row_src_rows(int T, int k, const int32_t* slot_row, int32_t* row_src, hipStream_t st);
 hipError_t unpermute_sum_rows(int elem_bytes, int T, int d, int k, const void* dx_perm, const int32_t* slot_row,
                               const void* dx_r, const void* dx_add, void* dx, hipStream_t st);
 

@@ -150,6 +150,79 @@ __global__ void __launch_bounds__(kThreads) combine_bwd_kernel(int ntok, int d, 
   }
 }
 
+// dgates[t, j] = <dy[t], y_perm[slot_row[t, j]]> alone (the routed gradient rows are
+// written elsewhere).  Same per-lane order as combine_bwd_kernel (chunks ascending, the 8
+// elements of a chunk in order, then a butterfly over the wave), so the two agree bit for
+// bit; the k rows' loads of two chunks are issued before any arithmetic.
+__global__ void __launch_bounds__(kThreads) dgates_kernel(int ntok, int d, int k, const bf16_t* __restrict__ dy,
+                                                          const bf16_t* __restrict__ y_perm,
+                                                          const int32_t* __restrict__ slot_row,
+                                                          float* __restrict__ dgates) {
+  const int t = blockIdx.x * kTokPerBlock + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (t >= ntok) return;
+  const int nchunk = d / 8;
+  if (k > kGatherK) {  // one row at a time
+    for (int j = 0; j < k; j++) {
+      const int r = slot_row[(int64_t)t * k + j];
+      float dot = 0.f;
+      for (int c = lane; c < nchunk; c += kWave) {
+        float u[8], v[8];
+        load8<bf16_t>(dy + (int64_t)t * d + c * 8, u);
+        load8<bf16_t>(y_perm + (int64_t)r * d + c * 8, v);
+#pragma unroll
+        for (int i = 0; i < 8; i++) dot = fmaf(u[i], v[i], dot);
+      }
+      dot = wave_sum(dot);
+      if (lane == 0) dgates[(int64_t)t * k + j] = dot;
+    }
+    return;
+  }
+  const int my_r = lane < k ? slot_row[(int64_t)t * k + lane] : 0;
+  float dot[kGatherK];
+#pragma unroll
+  for (int j = 0; j < kGatherK; j++) dot[j] = 0.f;
+  for (int c0 = lane; c0 < nchunk; c0 += 2 * kWave) {
+    uint4 q[2][kGatherK + 1];
+#pragma unroll
+    for (int u = 0; u < 2; u++) {
+      const int c = c0 + u * kWave;
+      if (c < nchunk) q[u][kGatherK] = *reinterpret_cast<const uint4*>(dy + (int64_t)t * d + c * 8);
+#pragma unroll
+      for (int j = 0; j < kGatherK; j++) {
+        const int r = __shfl(my_r, j, kWave);
+        if (j < k && c < nchunk) q[u][j] = *reinterpret_cast<const uint4*>(y_perm + (int64_t)r * d + c * 8);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < 2; u++) {
+      if (c0 + u * kWave >= nchunk) break;
+      float du[8];
+      widen8<bf16_t>(q[u][kGatherK], du);
+#pragma unroll
+      for (int j = 0; j < kGatherK; j++) {
+        if (j >= k) break;
+        float v[8];
+        widen8<bf16_t>(q[u][j], v);
+#pragma unroll
+        for (int i = 0; i < 8; i++) dot[j] = fmaf(du[i], v[i], dot[j]);
+      }
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < kGatherK; j++) {
+    if (j >= k) break;
+    const float s = wave_sum(dot[j]);
+    if (lane == 0) dgates[(int64_t)t * k + j] = s;
+  }
+}
+
+// row_src[slot_row[t, j]] = t
+__global__ void row_src_kernel(int nslot, int k, const int32_t* __restrict__ slot_row, int32_t* __restrict__ row_src) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < nslot) row_src[slot_row[i]] = i / k;
+}
+
 // dx[t] = dx_r[t] + dx_add[t] + sum_j dx_perm[slot_row[t, j]]   (dx_r, dx_add may be null)
 template <typename T>
 __global__ void __launch_bounds__(kThreads) unpermute_sum_kernel(int ntok, int d, int k, const T* __restrict__ dx_perm,
@@ -259,6 +332,20 @@ hipError_t combine_rows_bwd(int eb, int T, int d, int k, const void* dy, const v
   else
     hipLaunchKernelGGL(combine_bwd_kernel<float>, tok_grid(T), dim3(kThreads), 0, st, T, d, k, (const float*)dy,
                        (const float*)y_perm, gates, slot_row, (float*)dy_perm, dgates);
+  return hipGetLastError();
+}
+
+hipError_t dgates_rows(int T, int d, int k, const bf16_t* dy, const bf16_t* y_perm, const int32_t* slot_row,
+                       float* dgates, hipStream_t st) {
+  if (T == 0) return hipSuccess;
+  hipLaunchKernelGGL(dgates_kernel, tok_grid(T), dim3(kThreads), 0, st, T, d, k, dy, y_perm, slot_row, dgates);
+  return hipGetLastError();
+}
+
+hipError_t row_src_rows(int T, int k, const int32_t* slot_row, int32_t* row_src, hipStream_t st) {
+  const int64_t n = (int64_t)T * k;
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL(row_src_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, (int)n, k, slot_row, row_src);
   return hipGetLastError();
 }
 

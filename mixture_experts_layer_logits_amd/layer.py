@@ -23,6 +23,14 @@ one shared expert).  It runs as a one-group call of the same grouped GEMMs over 
 token rows (E = 1, k = 1, offsets [0, T]); its output enters through moe_combine's
 ``y_add`` and its input gradient through moe_permute_bwd's ``dx_add``.
 
+MXFP8 dispatch (``mx_dispatch``, on by default for MXFP8 expert GEMMs): moe_permute_mx
+and moe_combine_bwd_mx write the routed rows of x and of the output gradient only as
+E4M3 codes with their block scales, in the row layout (forward / data-gradient GEMMs)
+and the per-expert column layout (weight-gradient GEMMs), so no bf16 x_perm or dy_perm
+exists and the GEMMs quantise neither (MXFP8 for the data moved to the experts: unite.ai,
+section "Παραλληλισμός, Ακρίβεια και Τεχνικές Μνήμης").  The results are bit-identical
+with the bf16 dispatch.
+
 Activation recompute (``recompute=True``): the forward keeps only ``x_perm`` of the
 expert FFN; ``ab = [a | b]`` and ``h`` live in buffers allocated for the forward's GEMM1 /
 GEMM2 and released right after, and the backward runs GEMM1 again (same kernel, same
@@ -35,15 +43,22 @@ from __future__ import annotations
 
 import torch
 
-from . import (MOE_BF16, MOE_F32, make_shape, moe_combine, moe_combine_bwd, moe_ffn_dgrad1, moe_ffn_dgrad2,
-               moe_ffn_gemm1_fwd, moe_ffn_gemm2_fwd, moe_ffn_wgrad1, moe_ffn_wgrad2, moe_permute, moe_permute_bwd,
-               moe_route, moe_route_bwd, moe_route_given, moe_router_bwd, moe_router_fwd, moe_workspace_size)
+from . import (MOE_BF16, MOE_F32, MOE_MXFP8, make_shape, moe_combine, moe_combine_bwd, moe_combine_bwd_mx,
+               moe_ffn_dgrad1, moe_ffn_dgrad2, moe_ffn_dgrad2_mx, moe_ffn_gemm1_fwd, moe_ffn_gemm1_fwd_mx,
+               moe_ffn_gemm2_fwd, moe_ffn_wgrad1, moe_ffn_wgrad1_mx, moe_ffn_wgrad2, moe_ffn_wgrad2_mx, moe_mx_cols_ld,
+               moe_permute, moe_permute_bwd, moe_permute_mx, moe_route, moe_route_bwd, moe_route_given, moe_router_bwd,
+               moe_router_fwd, moe_workspace_size)
 
 
 class MoEExpertLayer:
-    def __init__(self, T, d, f, E, k, act=MOE_BF16, gemm=None, device="cuda", recompute=False, shared_f=0):
+    def __init__(self, T, d, f, E, k, act=MOE_BF16, gemm=None, device="cuda", recompute=False, shared_f=0,
+                 mx_dispatch=None):
         self.shape = make_shape(T, d, f, E, k, act, gemm)
         self.recompute = recompute
+        is_mx = self.shape.gemm == MOE_MXFP8
+        self.mx_dispatch = is_mx if mx_dispatch is None else bool(mx_dispatch)
+        if self.mx_dispatch and not is_mx:
+            raise ValueError("the MXFP8 dispatch needs MXFP8 expert GEMMs")
         self.shared_f = shared_f
         self.T, self.d, self.f, self.E, self.k = T, d, f, E, k
         self.R = T * k
@@ -62,14 +77,23 @@ class MoEExpertLayer:
         self.slot_row = e(T, k, dtype=i32)
         self.row_src = e(R, dtype=i32)
         self.dev_err = torch.zeros(1, dtype=i32, device=dev)
-        self.x_perm = e(R, d)
         self._e = e
+        u8 = torch.uint8
+        if self.mx_dispatch:  # routed rows exist only as E4M3 codes, in the row and column layouts
+            L = moe_mx_cols_ld(self.shape)
+            self.x_perm = self.dy_perm = None
+            self.xq_rows, self.xs_rows = e(R, d, dtype=u8), e(R, d // 32, dtype=u8)
+            self.xq_cols, self.xs_cols = e(d, L, dtype=u8), e(d, L // 32, dtype=u8)
+            self.dyq_rows, self.dys_rows = e(R, d, dtype=u8), e(R, d // 32, dtype=u8)
+            self.dyq_cols, self.dys_cols = e(d, L, dtype=u8), e(d, L // 32, dtype=u8)
+        else:
+            self.x_perm = e(R, d)
+            self.dy_perm = e(R, d)
         self.ab = None if recompute else e(R, 2 * f)
         self.h = None if recompute else e(R, f)
         self.y_perm = e(R, d)
         self.y = e(T, d)
         # backward buffers
-        self.dy_perm = e(R, d)
         self.dgates = e(T, k, dtype=f32)
         self.dab = e(R, 2 * f)
         self.dx_perm = e(R, d)
@@ -119,10 +143,14 @@ class MoEExpertLayer:
             moe_ffn_gemm1_fwd(ss, x, W1s, W3s, self.offsets_s, self.ab_s, self.h_s, self.ws_s)
             moe_ffn_gemm2_fwd(ss, self.h_s, W2s, self.offsets_s, self.y_s, self.ws_s)
             y_add = self.y_s
-        moe_permute(s, x, self.slot_row, self.row_src, self.x_perm)
+        if self.mx_dispatch:
+            moe_permute_mx(s, x, self.slot_row, self.offsets, self.row_src, self.xq_rows, self.xs_rows, self.xq_cols,
+                           self.xs_cols)
+        else:
+            moe_permute(s, x, self.slot_row, self.row_src, self.x_perm)
         if self.recompute:
             self.ab, self.h = self._e(self.R, 2 * self.f), self._e(self.R, self.f)
-        moe_ffn_gemm1_fwd(s, self.x_perm, W1, W3, self.offsets, self.ab, self.h, self.ws)
+        self._gemm1(W1, W3)
         moe_ffn_gemm2_fwd(s, self.h, W2, self.offsets, self.y_perm, self.ws)
         if self.recompute:  # the SwiGLU activations are not kept for the backward
             self.ab = self.h = None
@@ -133,14 +161,24 @@ class MoEExpertLayer:
     def backward(self, dy):
         s = self.shape
         x, W1, W3, W2, Wr, g = self._params
-        moe_combine_bwd(s, dy, self.y_perm, g, self.slot_row, self.dy_perm, self.dgates)
-        if self.recompute:  # regenerate a, b and h from the kept x_perm
+        if self.mx_dispatch:
+            moe_combine_bwd_mx(s, dy, self.y_perm, g, self.slot_row, self.row_src, self.offsets, self.dgates,
+                               self.dyq_rows, self.dys_rows, self.dyq_cols, self.dys_cols)
+        else:
+            moe_combine_bwd(s, dy, self.y_perm, g, self.slot_row, self.dy_perm, self.dgates)
+        if self.recompute:  # regenerate a, b and h from the kept routed rows
             self.ab, self.h = self._e(self.R, 2 * self.f), self._e(self.R, self.f)
-            moe_ffn_gemm1_fwd(s, self.x_perm, W1, W3, self.offsets, self.ab, self.h, self.ws)
-        moe_ffn_dgrad2(s, self.dy_perm, W2, self.ab, self.offsets, self.dab, self.ws)
-        moe_ffn_wgrad2(s, self.h, self.dy_perm, self.offsets, self.dW2, self.ws)
-        moe_ffn_dgrad1(s, self.dab, W1, W3, self.offsets, self.dx_perm, self.ws)
-        moe_ffn_wgrad1(s, self.x_perm, self.dab, self.offsets, self.dW1, self.dW3, self.ws)
+            self._gemm1(W1, W3)
+        if self.mx_dispatch:
+            moe_ffn_dgrad2_mx(s, self.dyq_rows, self.dys_rows, W2, self.ab, self.offsets, self.dab, self.ws)
+            moe_ffn_wgrad2_mx(s, self.h, self.dyq_cols, self.dys_cols, self.offsets, self.dW2, self.ws)
+            moe_ffn_dgrad1(s, self.dab, W1, W3, self.offsets, self.dx_perm, self.ws)
+            moe_ffn_wgrad1_mx(s, self.xq_cols, self.xs_cols, self.dab, self.offsets, self.dW1, self.dW3, self.ws)
+        else:
+            moe_ffn_dgrad2(s, self.dy_perm, W2, self.ab, self.offsets, self.dab, self.ws)
+            moe_ffn_wgrad2(s, self.h, self.dy_perm, self.offsets, self.dW2, self.ws)
+            moe_ffn_dgrad1(s, self.dab, W1, W3, self.offsets, self.dx_perm, self.ws)
+            moe_ffn_wgrad1(s, self.x_perm, self.dab, self.offsets, self.dW1, self.dW3, self.ws)
         dx_r = None
         if self.learned:
             moe_route_bwd(s, self.dgates, g, self.topk_idx, self.dlogits)
@@ -160,14 +198,26 @@ class MoEExpertLayer:
             self.ab = self.h = None
         return self.dx
 
+    def _gemm1(self, W1, W3):
+        s = self.shape
+        if self.mx_dispatch:
+            moe_ffn_gemm1_fwd_mx(s, self.xq_rows, self.xs_rows, W1, W3, self.offsets, self.ab, self.h, self.ws)
+        else:
+            moe_ffn_gemm1_fwd(s, self.x_perm, W1, W3, self.offsets, self.ab, self.h, self.ws)
+
     def activation_bytes(self):
-        """Bytes of expert-FFN activations held from the forward to the backward
-        (x_perm, y_perm, and ab and h unless they are recomputed)."""
-        eb = self.x_perm.element_size()
-        n = 2 * self.R * self.d
+        """Bytes of expert-FFN activations held from the forward to the backward: the
+        routed rows (x_perm, or with the MXFP8 dispatch their two E4M3 layouts with
+        scales), y_perm, and ab and h unless they are recomputed."""
+        eb = self.y_perm.element_size()
+        n = self.R * self.d * eb
+        if self.mx_dispatch:
+            n += sum(t.numel() for t in (self.xq_rows, self.xs_rows, self.xq_cols, self.xs_cols))
+        else:
+            n += self.R * self.d * eb
         if not self.recompute:
-            n += self.R * 3 * self.f
-        return n * eb
+            n += self.R * 3 * self.f * eb
+        return n
 
 
 class MoEExpertFunction(torch.autograd.Function):

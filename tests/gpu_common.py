@@ -51,13 +51,15 @@ def say(msg: str):
     sys.stdout.flush()
 
 
-def run_layer(w, inp: dict, layer=None):
-    """Forward + backward of the whole layer on the GPU; returns the layer object."""
+def run_layer(w, inp: dict, layer=None, mx_dispatch=None):
+    """Forward + backward of the whole layer on the GPU; returns the layer object
+    (mx_dispatch: None = the layer's default, on for MXFP8 GEMMs)."""
     import mixture_experts_layer_logits_amd as m
     act = m.MOE_F32 if w.dtype == "f32" else m.MOE_BF16
     gemm = {"f32": m.MOE_F32, "bf16": m.MOE_BF16, "mxfp8": m.MOE_MXFP8}[w.gemm]
     if layer is None:
-        layer = m.MoEExpertLayer(w.T, w.d, w.f, w.E, w.k, act=act, gemm=gemm, shared_f=w.shared_f)
+        layer = m.MoEExpertLayer(w.T, w.d, w.f, w.E, w.k, act=act, gemm=gemm, shared_f=w.shared_f,
+                                 mx_dispatch=mx_dispatch)
     d = to_dev(inp)
     sh = d.get("shared")
     if w.routing == "given_uniform":

@@ -138,7 +138,18 @@ def test_full_size_layer(name):
     assert np.array_equal(host(L.slot_row), slot_row)
     assert np.array_equal(host(L.row_src), row_src)
     rows = rng.choice(w.R, 64, replace=False)
-    assert torch.equal(L.x_perm[torch.from_numpy(rows).cuda()].cpu(), inp["x"][torch.from_numpy(row_src[rows]).long()])
+    if L.mx_dispatch:  # the routed rows exist only as E4M3 codes: sampled rows, two experts' column segments
+        from test_gpu_mxfp8 import check_mx_layouts, routed_dy_rows
+        order = np.argsort(counts, kind="stable")
+        keep = sorted({int(order[len(order) // 2]), int(order[0])})
+        say("  [oracle] quantising sampled dispatched rows and two experts' column segments")
+        check_mx_layouts(L.xq_rows, L.xs_rows, L.xq_cols, L.xs_cols,
+                         lambda i: _f64(inp["x"][torch.from_numpy(row_src[i]).long()]), offsets, rows, keep)
+        check_mx_layouts(L.dyq_rows, L.dys_rows, L.dyq_cols, L.dys_cols,
+                         lambda i: routed_dy_rows(inp, slot_row, row_src, i), offsets, rows, keep)
+    else:
+        assert torch.equal(L.x_perm[torch.from_numpy(rows).cuda()].cpu(),
+                           inp["x"][torch.from_numpy(row_src[rows]).long()])
 
     # sampled tokens: forward output and gradients
     toks = rng.choice(w.T, 8 if w.gemm == "mxfp8" else 24, replace=False)

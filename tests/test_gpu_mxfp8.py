@@ -42,6 +42,39 @@ def test_mx_quantize_rows_bit_exact():
         assert np.array_equal(host(s), scales)
 
 
+def test_mx_quantize_every_bf16_value():
+    """Every bf16 value of magnitude <= 448 (zeros, subnormals and both signs included) in
+    blocks whose maximum is 448, so the block scale is 2^0 and each code is the element's
+    own E4M3 encoding: both quantisers (blocks along rows, and down segment columns) against
+    the oracle's encoder, byte for byte."""
+    import mixture_experts_layer_logits_amd as m
+    from oracle import mx_ref
+    pat = torch.arange(0, 1 << 16, dtype=torch.int32).to(torch.int16).view(torch.bfloat16).float()
+    vals = pat[pat.abs() <= 448]                                   # NaN compares false: dropped
+    nrow = -(-len(vals) // 31)
+    blocks = torch.zeros(nrow * 31)
+    blocks[:len(vals)] = vals
+    src = torch.cat([torch.full((nrow, 1), 448.0), blocks.view(nrow, 31)], dim=1).to(torch.bfloat16)  # [nrow, 32]
+    say(f"[gpu] mx quantize every bf16 value: {len(vals)} values")
+    q = torch.empty(nrow, 32, dtype=torch.uint8, device="cuda")
+    sc = torch.empty(nrow, 1, dtype=torch.uint8, device="cuda")
+    m.moe_mx_quantize(nrow, 32, 0, None, 0, src.cuda(), q, sc)
+    # the same blocks as columns of one 32-row segment (columns padded to a multiple of 32)
+    ncol = -(-nrow // 32) * 32
+    srcT = torch.zeros(32, ncol, dtype=torch.bfloat16)
+    srcT[:, :nrow] = src.T
+    qT = torch.empty(ncol, 32 + 128, dtype=torch.uint8, device="cuda")
+    sT = torch.empty(ncol, (32 + 128) // 32, dtype=torch.uint8, device="cuda")
+    m.moe_mx_quantize(32, ncol, 1, torch.tensor([0, 32], dtype=torch.int32).cuda(), 1, srcT.contiguous().cuda(), qT,
+                      sT)
+    torch.cuda.synchronize()
+    ref = mx_ref.e4m3_encode(src.float().numpy().astype(np.float64))
+    assert (host(sc) == 127).all()                                  # scale 2^0 everywhere
+    assert np.array_equal(host(q), ref)
+    assert np.array_equal(host(qT)[:nrow, :32], ref)
+    assert (host(sT)[:nrow, 0] == 127).all()
+
+
 def test_mx_quantize_segment_cols_bit_exact():
     import mixture_experts_layer_logits_amd as m
     from oracle import mx_ref
@@ -106,6 +139,87 @@ def test_mxfp8_layer_parity(over):
         assert not host(L.dW1[e]).any() and not host(L.dW2[e]).any()
 
 
+def check_mx_layouts(q_rows, s_rows, q_cols, s_cols, vrows, offsets, rows=None, experts=None):
+    """The two MXFP8 layouts of a routed row set against the oracle's quantisers, byte for
+    byte.  vrows(idx) gives the fp64 rows idx of the set; the row layout is checked on
+    `rows` (all rows if None), the column layout on the padded segments of `experts` (all
+    if None), padding included (zero codes, zero scale bytes)."""
+    from oracle import mx_ref
+    offsets = np.asarray(offsets, dtype=np.int64)
+    R = int(offsets[-1])
+    sel = np.arange(R) if rows is None else np.asarray(rows, dtype=np.int64)
+    codes, scales = mx_ref.quantize_rows(vrows(sel))
+    idx = torch.from_numpy(sel).cuda()
+    assert np.array_equal(host(q_rows[idx]), codes)
+    assert np.array_equal(host(s_rows[idx]), scales)
+    npad = -(-np.diff(offsets) // 128) * 128
+    starts = np.concatenate([[0], np.cumsum(npad)])
+    for e in (range(len(offsets) - 1) if experts is None else experts):
+        lo, hi, P, n = int(offsets[e]), int(offsets[e + 1]), int(starts[e]), int(offsets[e + 1] - offsets[e])
+        if n == 0:
+            continue
+        gq, gs = host(q_cols[:, P:P + npad[e]]), host(s_cols[:, P // 32:(P + npad[e]) // 32])
+        ccodes, cscales = mx_ref.quantize_segment_cols(vrows(np.arange(lo, hi)), [0, n])
+        nb = -(-n // 32)
+        assert np.array_equal(gq[:, :n], ccodes.T), e
+        assert np.array_equal(gs[:, :nb], cscales[0].T), e
+        assert not gq[:, n:].any() and not gs[:, nb:].any(), e
+
+
+def routed_dy_rows(inp, slot_row, row_src, idx):
+    """Packed rows idx of bf16(gates[t, j] * dy[t]), the product taken in fp32 and rounded
+    once to bf16 (the precision the routed gradient is stored in), in fp64."""
+    gate_of_row = np.empty(slot_row.size, dtype=np.float32)
+    gate_of_row[slot_row.reshape(-1)] = inp["gates"].numpy().reshape(-1)
+    t = torch.from_numpy(row_src[idx].astype(np.int64))
+    v = torch.from_numpy(gate_of_row[idx])[:, None] * inp["dy"].float()[t]
+    return v.to(torch.bfloat16).float().numpy().astype(np.float64)
+
+
+MX_DISPATCH_CASES = [
+    dict(T=300, d=384, f=256, E=32, k=4, name="mxd_ragged_e32"),
+    dict(T=200, d=256, f=128, E=16, k=2, name="mxd_k2"),
+    dict(T=150, d=256, f=128, E=64, k=2, name="mxd_sparse_e64"),   # many tiny and empty experts
+    dict(T=700, d=128, f=128, E=2, k=2, name="mxd_long_segments"),  # several 128-row tiles per expert
+]
+
+
+@pytest.mark.parametrize("over", MX_DISPATCH_CASES, ids=[c["name"] for c in MX_DISPATCH_CASES])
+def test_mx_dispatch_bytes_bit_exact(over):
+    """moe_permute_mx and moe_combine_bwd_mx write, for the routed rows of x and of the
+    gated output gradient, exactly the E4M3 codes and E8M0 scales the oracle's quantisers
+    give for those rows, in both layouts."""
+    from oracle import moe_ref as ref
+    w = workloads.scaled(workloads.WORKLOADS["e32_k4_t16384_d4096_mxfp8"], **over)
+    inp = workloads.make_inputs(w)
+    say(f"[gpu] mxfp8 dispatch bytes {w}")
+    L = run_layer(w, inp, mx_dispatch=True)
+    counts, offsets, slot_row, row_src = ref.dispatch(inp["topk_idx"].numpy(), w.E)
+    assert np.array_equal(host(L.offsets), offsets)
+    assert np.array_equal(host(L.row_src), row_src)
+    x = inp["x"].float().numpy().astype(np.float64)
+    check_mx_layouts(L.xq_rows, L.xs_rows, L.xq_cols, L.xs_cols, lambda i: x[row_src[i]], offsets)
+    check_mx_layouts(L.dyq_rows, L.dys_rows, L.dyq_cols, L.dys_cols,
+                     lambda i: routed_dy_rows(inp, slot_row, row_src, i), offsets)
+
+
+@pytest.mark.parametrize("over", MX_CASES[:2] + MX_CASES[3:], ids=[c["name"] for c in MX_CASES[:2] + MX_CASES[3:]])
+def test_mx_dispatch_equals_bf16_dispatch_bitwise(over):
+    """The layer with the MXFP8 dispatch gives bit for bit the outputs of the layer that
+    dispatches bf16 rows and quantises them inside each GEMM (the same bytes reach the
+    same GEMM kernels; dgates keeps its summation order)."""
+    w = workloads.scaled(workloads.WORKLOADS["e32_k4_t16384_d4096_mxfp8"], **over)
+    inp = workloads.make_inputs(w)
+    say(f"[gpu] mxfp8 dispatch vs bf16 dispatch {w}")
+    A = run_layer(w, inp, mx_dispatch=True)
+    B = run_layer(w, inp, mx_dispatch=False)
+    names = ["ab", "h", "y_perm", "y", "dgates", "dab", "dx_perm", "dW1", "dW3", "dW2", "dx"]
+    if w.shared_f:
+        names += ["dW1s", "dW3s", "dW2s"]
+    diff = [n for n in names if not torch.equal(getattr(A, n), getattr(B, n))]
+    assert not diff, diff
+
+
 def test_mx_gemms_match_dequantized_operands():
     """Each MXFP8 grouped GEMM equals the fp64 GEMM of its dequantised operands (the
     oracle's quantiser is bit-exact with the GPU's), up to fp32 accumulation and the bf16
@@ -116,7 +230,7 @@ def test_mx_gemms_match_dequantized_operands():
                          name="mx_emulated")
     inp = workloads.make_inputs(w)
     say(f"[gpu] mxfp8 GEMMs vs dequantised operands {w}")
-    L = run_layer(w, inp)
+    L = run_layer(w, inp, mx_dispatch=False)  # keeps bf16 x_perm and dy_perm to quantise here
     off = host(L.offsets).astype(np.int64)
     E, d, f = w.E, w.d, w.f
 
