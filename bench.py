@@ -46,7 +46,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="e128_k4_t8192")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-sample-tokens", type=int, default=1024)
+    ap.add_argument("--cpu-sample-tokens", type=int, default=0,
+                    help="tokens in the oracle's timed sample (0: sized for about 12 s of CPU work)")
     ap.add_argument("--profile-kernel", default=None, help="run only this call of the step, --steps times")
     ap.add_argument("--copy-mib", type=int, default=0, help="run a plain device copy of this many MiB, --steps times")
     ap.add_argument("--recompute", action="store_true",
@@ -180,9 +181,10 @@ def algorithmic_work(w, eb, mx_dispatch=False):
     return gem, byt
 
 
-def cpu_baseline(w, inp, ntok):
+def cpu_baseline(w, inp, ntok=0, target_s=12.0):
     """The oracle as it stands, timed on the host cores on the first `ntok` tokens of the
-    same batch (all experts' weights), forward + backward."""
+    same batch (all experts' weights), forward + backward.  ntok = 0 sizes the sample for
+    about target_s seconds from two short calibration runs (256 and 1024 tokens)."""
     import numpy as np
     from oracle import moe_ref as ref
     try:
@@ -190,18 +192,25 @@ def cpu_baseline(w, inp, ntok):
         threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:  # pragma: no cover
         threads = os.cpu_count() or 1
-    sub = {}
-    for key in ("x", "dy"):
-        sub[key] = inp[key][:ntok]
     learned = w.routing != "given_uniform"
-    t0 = time.perf_counter()
-    if learned:
-        fw = ref.layer_forward(sub["x"], inp["W1"], inp["W3"], inp["W2"], w.k, Wr=inp["Wr"], bias=inp["router_bias"])
-    else:
-        fw = ref.layer_forward(sub["x"], inp["W1"], inp["W3"], inp["W2"], w.k, topk_idx=inp["topk_idx"][:ntok].numpy(),
-                               gates=inp["gates"][:ntok])
-    ref.layer_backward(fw, sub["dy"], sub["x"], inp["W1"], inp["W3"], inp["W2"], Wr=inp["Wr"], learned=learned)
-    dt = time.perf_counter() - t0
+
+    def run(n):
+        x, dy = inp["x"][:n], inp["dy"][:n]
+        t0 = time.perf_counter()
+        if learned:
+            fw = ref.layer_forward(x, inp["W1"], inp["W3"], inp["W2"], w.k, Wr=inp["Wr"], bias=inp["router_bias"])
+        else:
+            fw = ref.layer_forward(x, inp["W1"], inp["W3"], inp["W2"], w.k, topk_idx=inp["topk_idx"][:n].numpy(),
+                                   gates=inp["gates"][:n])
+        ref.layer_backward(fw, dy, x, inp["W1"], inp["W3"], inp["W2"], Wr=inp["Wr"], learned=learned)
+        return time.perf_counter() - t0
+
+    if not ntok:  # per-token and fixed cost from two short runs, then a run of about target_s
+        n0, n1 = min(256, w.T), min(1024, w.T)
+        t0, t1 = run(n0), run(n1)
+        per_tok = max((t1 - t0) / max(n1 - n0, 1), 1e-6)
+        ntok = int(min(w.T, max(n1, (target_s - max(t1 - per_tok * n1, 0.0)) / per_tok)))
+    dt = run(ntok)
     return {"value": ntok / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
             "sample": f"first {ntok} of {w.T} tokens, all {w.E} experts' weights, fwd+bwd in fp64 NumPy "
                       f"({dt:.1f} s)"}
