@@ -25,6 +25,8 @@ CASES = [
     ("e8_k4_t8192", dict(T=77, d=64, f=64, E=1, k=1, name="single_expert")),
     ("e8_k4_t8192", dict(T=130, d=128, f=64, E=4, k=4, name="k_equals_E")),
     ("e128_k4_t8192_shared", dict(T=300, d=256, f=192, shared_f=128, name="shared_expert")),
+    # >= 1024 rows per expert: the 256 x 256 two-stage tiles of the M-grouped GEMMs, ragged in N
+    ("e8_k4_t8192", dict(T=1300, d=256, f=192, E=2, k=2, name="long_segments")),
 ]
 
 
