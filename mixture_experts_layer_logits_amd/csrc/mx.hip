@@ -10,6 +10,9 @@
 // Elements: v * 2^-s (exact in fp32) rounded to nearest-even onto the E4M3 grid by
 // gfx950's packed fp8 conversion, two elements per instruction; a GPU test checks it
 // against the oracle's encoder on every bf16 value of magnitude <= 448.
+#include <cstdlib>
+#include <cstring>
+
 #include "common.h"
 #include "mx.h"
 #include "tilemap.h"
@@ -597,9 +600,10 @@ struct MxOperand {
 
 static inline size_t mx_dyn_lds_bytes(int E) { return (size_t)2 * (E + 1) * sizeof(int); }
 
-template <class Cfg, class Prob, int TKB>
+template <class Cfg, class Prob, int TKB, int NS>
 __global__ void __launch_bounds__(Cfg::NT) __attribute__((amdgpu_waves_per_eu(2)))
 mx_gemm_kernel(const Prob p) {
+  static_assert(NS == 2 || NS == 3, "two or three stage buffers");
   constexpr int BM = Cfg::BM, BN = Cfg::BN, NT = Cfg::NT;
   constexpr int WTM = Cfg::WTM, WTN = Cfg::WTN;
   constexpr int NW = NT / 64;
@@ -608,11 +612,11 @@ mx_gemm_kernel(const Prob p) {
   constexpr int B_OFF = OA::TILE_BYTES, SA_OFF = B_OFF + OB::TILE_BYTES, SB_OFF = SA_OFF + OA::SCALE_BYTES;
   constexpr int STAGE_BYTES = SB_OFF + OB::SCALE_BYTES;
   static_assert(OA::SCALE_SEGS + OB::SCALE_SEGS <= NW, "one scale load per wave");
-  // three stage buffers as separate objects (the compiler then waits only for the loads a
+  // NS stage buffers as separate objects (the compiler then waits only for the loads a
   // buffer read depends on)
   __shared__ __attribute__((aligned(1024))) char sm0[STAGE_BYTES];
   __shared__ __attribute__((aligned(1024))) char sm1[STAGE_BYTES];
-  __shared__ __attribute__((aligned(1024))) char sm2[STAGE_BYTES];
+  __shared__ __attribute__((aligned(1024))) char sm2[NS == 3 ? STAGE_BYTES : 16];
   extern __shared__ __attribute__((aligned(16))) int s_dyn[];
   const int E = p.E;
   int* s_map = s_dyn;
@@ -771,8 +775,23 @@ mx_gemm_kernel(const Prob p) {
       }
     }
   };
-  // step s is loaded into buffer s % 3 two steps ahead; one exit, at the bottom
+  // step s is loaded into buffer s % NS, NS - 1 steps ahead (into the buffer the step
+  // before read, once every wave is past this step's barrier); one exit, at the bottom
   load_stage(sm0);
+  if constexpr (NS == 2) {
+    for (;;) {
+      ready(sm0);
+      load_stage(sm1);
+      compute(sm0);
+      finish_step();
+      ready(sm1);
+      load_stage(sm0);
+      compute(sm1);
+      if (!done) finish_step();
+      if (done) break;
+    }
+    return;
+  }
   load_stage(sm1);
   for (;;) {
     ready(sm0);
@@ -872,10 +891,9 @@ struct MxWgrad : MxBase {  // C_e[m][n] = sum over expert e's (padded) rows of A
   }
 };
 
-template <class Prob>
-static hipError_t launch_mx(const Prob& p, hipStream_t st) {
-  using Cfg = TileCfg<128, 256, 2, 4>;
-  const auto kern = mx_gemm_kernel<Cfg, Prob, 128>;
+template <class Cfg, int NS, class Prob>
+static hipError_t launch_mx_cfg(const Prob& p, hipStream_t st) {
+  const auto kern = mx_gemm_kernel<Cfg, Prob, 128, NS>;
   const size_t dyn = mx_dyn_lds_bytes(p.E);
   static int occ_e = -1, occ = 0;  // occupancy depends on the dynamic LDS, i.e. on E
   if (occ_e != p.E) { occ_e = p.E; occ = 0; }
@@ -894,6 +912,20 @@ static hipError_t launch_mx(const Prob& p, hipStream_t st) {
   if (G < 8) G = 8;
   hipLaunchKernelGGL(kern, dim3((unsigned)G), dim3(Cfg::NT), dyn, st, p);
   return hipGetLastError();
+}
+
+// Tiles: over long expert segments (1024 rows per expert or more on average: the M range of
+// the forward and data-gradient GEMMs, the padded reduction of the weight-gradient ones)
+// every MXFP8 GEMM takes 256 x 256 tiles in two stage buffers, otherwise 128 x 256 in
+// three.  On MI355X at 2048 rows per expert the large tiles are 7-16% faster on each of the
+// six.  MOE_MX_TILE=128x256 / 256x256 overrides the choice.
+template <class Prob>
+static hipError_t launch_mx(const Prob& p, hipStream_t st) {
+  const int64_t rows = Prob::GROUP == Group::M ? p.M : p.K;
+  bool big = rows >= (int64_t)1024 * p.E;
+  if (const char* v = getenv("MOE_MX_TILE")) big = strcmp(v, "256x256") == 0;
+  if (big) return launch_mx_cfg<TileCfg<256, 256, 2, 4>, 2>(p, st);
+  return launch_mx_cfg<TileCfg<128, 256, 2, 4>, 3>(p, st);
 }
 
 // ---------------------------------------------------------------------------------------

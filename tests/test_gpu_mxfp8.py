@@ -109,6 +109,8 @@ MX_CASES = [
     dict(T=300, d=384, f=256, E=32, k=4, name="mx_ragged_e32"),
     dict(T=200, d=256, f=384, E=16, k=2, name="mx_k2"),
     dict(T=260, d=256, f=256, E=8, k=4, shared_f=256, name="mx_shared_expert"),
+    # >= 1024 rows per expert: 256 x 256 tiles in two stages for the M-grouped GEMMs
+    dict(T=1100, d=256, f=384, E=2, k=2, name="mx_long_segments"),
 ]
 
 
