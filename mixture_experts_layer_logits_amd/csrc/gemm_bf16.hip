@@ -302,6 +302,7 @@ struct PipeOperand {
   static constexpr int CPR = ROW_BYTES / 16;         // 16-byte chunks per LDS row
   static_assert(SEGS % NW == 0, "every wave issues the same number of segments");
   static_assert(KC || CPR >= 4, "MN-contiguous tiles need at least 64 columns");
+  static constexpr int PER_THREAD = SEGS / NW;       // 1 KB segments per wave
 
   // physical 16-byte chunk of logical chunk c in tile row r.  16 consecutive rows read
   // at one logical chunk (K-contiguous) or 4 consecutive rows read at a pair of chunks
@@ -315,16 +316,8 @@ struct PipeOperand {
     }
   }
 
-  // Register staging of one tile: this thread's 16-byte chunks.  Chunk q = tid + NT*i
-  // lands at LDS byte q*16, i.e. (row q / CPR, physical chunk q % CPR); the thread fetches
-  // the logical chunk that the swizzle maps there.  The 64 chunks of one wave form one
-  // 1 KB segment, so the bounds (a buffer resource) are wave-uniform.
-  static constexpr int PER_THREAD = SEGS / NW;
-  typedef int v4i __attribute__((ext_vector_type(4)));
-  v4i reg[PER_THREAD];
-
-  // Scalar load state of the operand for the load cursor (kept in scalar registers and
-  // shared by both register stages): per segment of this wave, the address of its first
+  // Scalar load state of the operand for the load cursor (kept in scalar registers): per
+  // segment of this wave, the address of its first
   // row at the current k-step, the row stride and, for K-contiguous tiles, the bytes it
   // may read.  Rows are mn (K-contiguous tiles) or k (MN-contiguous tiles).  Set up once
   // per tile (begin); each k-step then moves the addresses by one add (next).
@@ -368,28 +361,10 @@ struct PipeOperand {
     if constexpr (!KC) st.k_left -= TK;
   }
 
-  __device__ __forceinline__ void issue(const Stream& st, int wave, int lane) {
-#pragma unroll
-    for (int i = 0; i < PER_THREAD; i++) {
-      const int s = wave + NW * i;
-      uint32_t bytes;
-      if constexpr (KC) {
-        bytes = st.bytes[i];
-      } else {
-        int valid = st.k_left - s * ROWS_PER_SEG;
-        valid = valid < 0 ? 0 : (valid > ROWS_PER_SEG ? ROWS_PER_SEG : valid);
-        bytes = valid > 0 ? (uint32_t)(valid - 1) * st.rb + st.col_bytes : 0u;
-      }
-      const int r = lane / CPR, p = lane % CPR;
-      const int c = swz(s * ROWS_PER_SEG + r, p);
-      const uint32_t voff = (uint32_t)r * st.rb + (uint32_t)(c * 16);
-      // a zero-byte resource (rows past the end, steps past the last tile) reads nothing
-      reg[i] = __builtin_amdgcn_raw_buffer_load_b128(make_rsrc(st.ptr[i], bytes), voff, 0, 0);
-    }
-  }
-  // The same loads straight into LDS (buffer_load ... lds): lane l of a wave's segment
-  // lands at segment base + 16 l, which is where store() puts it; lanes past the
-  // resource's byte count write zeros.
+  // A tile's loads go straight into LDS (buffer_load ... lds): the 64 16-byte chunks of
+  // one wave form one 1 KB segment, lane l landing at segment base + 16 l, and each lane
+  // fetches the logical chunk that the swizzle maps there.  The bounds (a buffer resource
+  // per segment) are wave-uniform; lanes past the resource's byte count write zeros.
   static __device__ __forceinline__ void dma(const Stream& st, char* lds_tile, int wave, int lane) {
 #pragma unroll
     for (int i = 0; i < PER_THREAD; i++) {
@@ -409,12 +384,6 @@ struct PipeOperand {
                                                voff, 0, 0, 0);
     }
   }
-  __device__ __forceinline__ void store(char* lds_tile, int wave, int lane) const {
-#pragma unroll
-    for (int i = 0; i < PER_THREAD; i++)
-      *reinterpret_cast<v4i*>(lds_tile + (wave + NW * i) * 1024 + lane * 16) = reg[i];
-  }
-
   // MFMA operand fragment for k-step kk (16 deep): 8 consecutive k of row/column mn0 + lane%32
   static __device__ __forceinline__ bf16x8 frag(const char* lds_tile, int kk, int mn0, int lane) {
     if constexpr (KC) {
