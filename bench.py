@@ -187,7 +187,8 @@ def algorithmic_work(w, eb, mx_dispatch=False):
 def cpu_baseline(w, inp, ntok=0, target_s=12.0):
     """The oracle as it stands, timed on the host cores on the first `ntok` tokens of the
     same batch (all experts' weights), forward + backward.  ntok = 0 sizes the sample for
-    about target_s seconds from two short calibration runs (256 and 1024 tokens)."""
+    about target_s seconds from two short calibration runs (256 and 1024 tokens); when the
+    whole batch takes less, it is run again until about target_s seconds have passed."""
     import numpy as np
     from oracle import moe_ref as ref
     try:
@@ -213,10 +214,13 @@ def cpu_baseline(w, inp, ntok=0, target_s=12.0):
         t0, t1 = run(n0), run(n1)
         per_tok = max((t1 - t0) / max(n1 - n0, 1), 1e-6)
         ntok = int(min(w.T, max(n1, (target_s - max(t1 - per_tok * n1, 0.0)) / per_tok)))
-    dt = run(ntok)
-    return {"value": ntok / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"first {ntok} of {w.T} tokens, all {w.E} experts' weights, fwd+bwd in fp64 NumPy "
-                      f"({dt:.1f} s)"}
+    dt, reps = run(ntok), 1
+    while ntok == w.T and dt < target_s and reps < 8:  # the whole batch is short: repeat it
+        dt += run(ntok)
+        reps += 1
+    what = f"first {ntok} of {w.T} tokens" if ntok < w.T else f"all {w.T} tokens" + (f", {reps} runs" if reps > 1 else "")
+    return {"value": reps * ntok / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{what}, all {w.E} experts' weights, fwd+bwd in fp64 NumPy ({dt:.1f} s)"}
 
 
 def main():
