@@ -129,6 +129,9 @@ moe_status moe_grouped_ffn_fwd(const moe_shape* s, const void* x_perm, const voi
                                const void* W2, const int32_t* offsets, void* ab, void* h, void* y_perm,
                                void* ws, size_t ws_bytes, void* stream);
 
+/* The two forward GEMMs as separate calls (moe_grouped_ffn_fwd runs both): GEMM1 with the
+ * SwiGLU epilogue writes ab and h, GEMM2 writes y_perm.  Arguments as above; ws is used by
+ * MOE_MXFP8 shapes (operand quantisation) and may be NULL otherwise. */
 moe_status moe_ffn_gemm1_fwd(const moe_shape* s, const void* x_perm, const void* W1, const void* W3,
                              const int32_t* offsets, void* ab, void* h, void* ws, size_t ws_bytes,
                              void* stream);
@@ -164,6 +167,12 @@ moe_status moe_grouped_ffn_bwd(const moe_shape* s, const void* dy_perm, const vo
                                const int32_t* offsets, void* dab, void* dx_perm, void* dW1, void* dW3,
                                void* dW2, void* ws, size_t ws_bytes, void* stream);
 
+/* The four backward GEMMs as separate calls, in the order moe_grouped_ffn_bwd runs them:
+ * dgrad2 (with the SwiGLU gradient, writes dab), wgrad2 (dW2), dgrad1 (dx_perm), wgrad1
+ * (dW1, dW3).  ws: MOE_MXFP8 shapes quantise their operands into it; with one expert
+ * (E = 1, as for a shared expert) the bf16 weight gradients split their reduction over the
+ * rows and keep fp32 partial sums in it, added in a fixed order (MOE_EWORKSPACE if ws_bytes
+ * is below moe_workspace_size). */
 moe_status moe_ffn_dgrad2(const moe_shape* s, const void* dy_perm, const void* W2, const void* ab,
                           const int32_t* offsets, void* dab, void* ws, size_t ws_bytes, void* stream);
 moe_status moe_ffn_wgrad2(const moe_shape* s, const void* h, const void* dy_perm, const int32_t* offsets,

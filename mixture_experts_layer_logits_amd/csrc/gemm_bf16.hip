@@ -273,12 +273,12 @@ __global__ void sum_splits_kernel(int64_t n, int nsplit, const float* __restrict
 }  // namespace
 
 // ---------------------------------------------------------------------------------------
-// Pipelined kernel for bf16 operands.  Global loads run two k-steps ahead of the MFMAs in
-// two register stages and are written to one of two LDS buffers while the other one is
-// being read (one barrier per k-step).  Loads go through buffer resources that start at a
-// 1 KB segment's first row and end at its last valid byte, so rows past a segment end
-// (ragged experts, reductions that stop mid-tile) and columns past the matrix edge read
-// as zero without any out-of-range access.
+// Pipelined kernel for bf16 operands.  Each k-step's operand tiles go from global memory
+// straight into one of NS (2 to 4) LDS stage buffers, NS - 1 steps ahead of the MFMAs
+// (one barrier per k-step).  Loads go through buffer resources that start at a 1 KB
+// segment's first row and end at its last valid byte, so rows past a segment end (ragged
+// experts, reductions that stop mid-tile) and columns past the matrix edge read as zero
+// without any out-of-range access.
 //
 // LDS tiles are unpadded and XOR-swizzled in 16-byte chunks (see swz): 16 consecutive
 // rows read at one logical chunk (K-contiguous tiles, ds_read_b128) or 4 consecutive rows
@@ -467,9 +467,9 @@ grouped_gemm_pipe_kernel(const Prob p) {
 
   // The workgroup's tiles form one stream of k-steps: every tile takes
   // max(1, ceil(k range / TK)) steps (a tile with an empty reduction still runs one step
-  // on zero operands and stores its zeros).  The load cursor runs two steps ahead of the
-  // MFMAs across tile boundaries, so the next tile's first stages are in flight while the
-  // current tile's epilogue stores.
+  // on zero operands and stores its zeros).  The load cursor runs NS - 1 steps ahead of
+  // the MFMAs across tile boundaries, so the next tile's first stages are in flight while
+  // the current tile's epilogue stores.
   struct Cursor {
     int t, k;
     TileRange tr;

@@ -501,8 +501,8 @@ hipError_t mx_quantize_cols_seg(int rows, int cols, const int32_t* seg_offsets, 
 //
 // Pipeline as in the bf16 kernel: the workgroup's tiles form one stream of 128-deep
 // k-steps; each step's codes and scale words go straight from global memory into one of
-// three LDS stage buffers two steps ahead of the MFMAs (bounded buffer loads: rows past an
-// operand's end land as zeros); one barrier per step.
+// NS (2 or 3) LDS stage buffers, NS - 1 steps ahead of the MFMAs (bounded buffer loads:
+// rows past an operand's end land as zeros); one barrier per step.
 // ---------------------------------------------------------------------------------------
 namespace {
 
