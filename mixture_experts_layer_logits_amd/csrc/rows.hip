@@ -130,6 +130,56 @@ __global__ void __launch_bounds__(kThreads) combine_bwd_kernel(int ntok, int d, 
   const int lane = threadIdx.x & 63;
   if (t >= ntok) return;
   const int nchunk = d / 8;
+  if constexpr (sizeof(T) == 2) {
+    if (k <= kGatherK) {  // dy read once per chunk, the k rows' loads of two chunks issued together
+      const int my_r = lane < k ? slot_row[(int64_t)t * k + lane] : 0;
+      const float my_g = lane < k ? gates[(int64_t)t * k + lane] : 0.f;
+      float dot[kGatherK];
+#pragma unroll
+      for (int j = 0; j < kGatherK; j++) dot[j] = 0.f;
+      for (int c0 = lane; c0 < nchunk; c0 += 2 * kWave) {
+        uint4 q[2][kGatherK + 1];
+#pragma unroll
+        for (int u = 0; u < 2; u++) {
+          const int c = c0 + u * kWave;
+          if (c < nchunk) q[u][kGatherK] = *reinterpret_cast<const uint4*>(dy + (int64_t)t * d + c * 8);
+#pragma unroll
+          for (int j = 0; j < kGatherK; j++) {
+            const int r = __shfl(my_r, j, kWave);
+            if (j < k && c < nchunk) q[u][j] = *reinterpret_cast<const uint4*>(y_perm + (int64_t)r * d + c * 8);
+          }
+        }
+#pragma unroll
+        for (int u = 0; u < 2; u++) {
+          const int c = c0 + u * kWave;
+          if (c >= nchunk) break;
+          float du[8];
+          widen8<T>(q[u][kGatherK], du);
+#pragma unroll
+          for (int j = 0; j < kGatherK; j++) {
+            if (j >= k) break;
+            const int r = __shfl(my_r, j, kWave);
+            const float g = __shfl(my_g, j, kWave);
+            float v[8], o[8];
+            widen8<T>(q[u][j], v);
+#pragma unroll
+            for (int i = 0; i < 8; i++) {
+              dot[j] = fmaf(du[i], v[i], dot[j]);
+              o[i] = g * du[i];
+            }
+            store8<T>(dy_perm + (int64_t)r * d + c * 8, o);
+          }
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < kGatherK; j++) {
+        if (j >= k) break;
+        const float sj = wave_sum(dot[j]);
+        if (lane == 0) dgates[(int64_t)t * k + j] = sj;
+      }
+      return;
+    }
+  }
   for (int j = 0; j < k; j++) {
     const int r = slot_row[(int64_t)t * k + j];
     const float g = gates[(int64_t)t * k + j];
@@ -153,7 +203,7 @@ __global__ void __launch_bounds__(kThreads) combine_bwd_kernel(int ntok, int d, 
 // dgates[t, j] = <dy[t], y_perm[slot_row[t, j]]> alone (the routed gradient rows are
 // written elsewhere).  Same per-lane order as combine_bwd_kernel (chunks ascending, the 8
 // elements of a chunk in order, then a butterfly over the wave), so the two agree bit for
-// bit; the k rows' loads of two chunks are issued before any arithmetic.
+// bit; the k rows' loads of two chunks are issued before any arithmetic, as there.
 __global__ void __launch_bounds__(kThreads) dgates_kernel(int ntok, int d, int k, const bf16_t* __restrict__ dy,
                                                           const bf16_t* __restrict__ y_perm,
                                                           const int32_t* __restrict__ slot_row,
