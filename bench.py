@@ -53,6 +53,8 @@ def parse():
     ap.add_argument("--copy-mib", type=int, default=0, help="run a plain device copy of this many MiB, --steps times")
     ap.add_argument("--recompute", action="store_true",
                     help="activation recompute: keep only x_perm and run GEMM1 again in the backward")
+    ap.add_argument("--seed-offset", type=int, default=0,
+                    help="draw the workload's inputs at its seed + this offset (the time spread over seeds)")
     ap.add_argument("--no-graph", action="store_true",
                     help="time the step as eager launches (default: replays of the step captured as a HIP graph)")
     ap.add_argument("--bf16-dispatch", action="store_true",
@@ -245,6 +247,8 @@ def main():
     import workloads
 
     w = workloads.WORKLOADS[args.workload]
+    if args.seed_offset:
+        w = dataclasses.replace(w, seed=w.seed + args.seed_offset)
     inp = workloads.make_inputs(w)
     learned = w.routing != "given_uniform"
     act = m.MOE_F32 if w.dtype == "f32" else m.MOE_BF16
@@ -311,7 +315,39 @@ def main():
             graph.replay()
         torch.cuda.synchronize()
         elapsed = time.perf_counter() - t0
+        # the spread of single steps: each of K more replays between two events
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+        for a, b in evs:
+            a.record()
+            graph.replay()
+            b.record()
+        torch.cuda.synchronize()
+        step_ms = sorted(a.elapsed_time(b) for a, b in evs)
+    else:
+        step_ms = sorted(sum(ev[name][i][0].elapsed_time(ev[name][i][1]) for name, _ in calls)
+                         for i in range(args.steps))
     ms_per_step = elapsed * 1e3 / args.steps
+    pct = lambda q: round(step_ms[min(len(step_ms) - 1, int(q * len(step_ms)))], 4)  # noqa: E731
+
+    # the HBM-bound row movement cold: L2 and the 256 MiB MALL flushed by reading 512 MiB
+    # before every launch (the routed buffers of these workloads fit in the MALL; a read
+    # evicts them without leaving dirty lines to drain during the timed launch)
+    flush = torch.ones(128 << 20, dtype=torch.int32, device="cuda")
+    cold_ms = {}
+    for name, fn in calls:
+        if name not in ("permute", "combine", "combine_bwd", "permute_bwd"):
+            continue
+        ts = []
+        for _ in range(5):
+            flush.sum()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            fn()
+            b.record()
+            torch.cuda.synchronize()
+            ts.append(a.elapsed_time(b))
+        cold_ms[name] = sorted(ts)[len(ts) // 2]
+    del flush
     tokens_per_s = w.T * args.steps / elapsed
 
     eb = 4 if w.dtype == "f32" else 2
@@ -368,10 +404,13 @@ def main():
         "vs_baseline": None, "dtype": w.gemm, "data": "synthetic",
         "config": {"workload": w.name, "T": w.T, "d": w.d, "f": w.f, "E": w.E, "k": w.k, "routing": w.routing,
                    "gemm": w.gemm, "recompute": bool(args.recompute), "shared_f": w.shared_f,
-                   "mx_dispatch": L.mx_dispatch, "hip_graph": not args.no_graph},
+                   "mx_dispatch": L.mx_dispatch, "hip_graph": not args.no_graph, "seed": w.seed},
+        "step_ms_p10_p50_p90": [pct(0.1), pct(0.5), pct(0.9)],
         "roofline": roofline,
         "grouped_gemm_mfma_frac_all6": round(sum(gem.values()) / (gemm_ms * 1e-3) / 1e12 / peak, 4),
         "kernels": kernels,
+        # median of 5 launches, each after a 512 MiB read that flushes L2 and the MALL
+        "kernels_cold": {n: {"ms": round(v, 4), "gbs": round(byt[n] / (v * 1e-3) / 1e9, 1)} for n, v in cold_ms.items()},
         "expert_load": {"max": int(L.counts.max().item()), "mean": w.T * w.k / w.E,
                         "empty": int((L.counts == 0).sum().item())},
         # expert-FFN activations held from the forward to the backward (the routed rows of x,
