@@ -409,22 +409,30 @@ struct PipeOperand {
 
 // Occupancy target: 8-wave tiles with 2x2 accumulator blocks per wave at a k-depth of 32
 // fit 4 waves per SIMD (two workgroups per compute unit) in 128 registers; tiles with
-// 4x4 blocks per wave keep their accumulators in AGPRs at one wave per SIMD.
-template <class Cfg, int TK>
+// 4x4 blocks per wave keep their accumulators in AGPRs at one wave per SIMD.  With NL
+// loader waves added, the workgroup's waves share the SIMDs at (compute + NL) / 4 each.
+template <class Cfg, int TK, int NL>
 constexpr int pipe_waves_per_eu() {
+  if constexpr (NL > 0) return (Cfg::NT / 64 + NL) / 4;
   return Cfg::WTM * Cfg::WTN >= 16 ? 1 : (TK == 32 && Cfg::WTM * Cfg::WTN <= 4 ? 4 : 2);
 }
 
 // Group starts and the tile map live in dynamic LDS sized by the expert count.
 static inline size_t pipe_dyn_lds_bytes(int E) { return (size_t)2 * (E + 1) * sizeof(int); }
 
-template <class Cfg, class Prob, int TK, int NS>
-__global__ void __launch_bounds__(Cfg::NT) __attribute__((amdgpu_waves_per_eu(pipe_waves_per_eu<Cfg, TK>())))
-grouped_gemm_pipe_kernel(const Prob p) {
+// NL = 0: every wave loads operands and computes.  NL > 0: the Cfg::NT threads compute
+// and NL more waves ("loaders") issue every operand load.  The compute waves then issue no
+// load of their own, so nothing makes them wait on the memory counter that their
+// epilogue stores also count in: a tile's stores drain while the next tile's MFMAs run.
+template <class Cfg, class Prob, int TK, int NS, int NL = 0>
+__global__ void __launch_bounds__(Cfg::NT + 64 * NL)
+    __attribute__((amdgpu_waves_per_eu(pipe_waves_per_eu<Cfg, TK, NL>()))) grouped_gemm_pipe_kernel(const Prob p) {
   static_assert(NS >= 2 && NS <= 4, "two to four stage buffers");
   constexpr int BM = Cfg::BM, BN = Cfg::BN, NT = Cfg::NT;
   constexpr int WTM = Cfg::WTM, WTN = Cfg::WTN;
-  constexpr int NW = NT / 64;
+  constexpr int NWC = NT / 64;                // waves holding accumulators
+  constexpr int NTT = NT + 64 * NL;           // threads of the workgroup
+  constexpr int NW = NL > 0 ? NL : NWC;       // waves issuing operand loads
   using OA = PipeOperand<Prob::A_KC, BM, TK, NW>;
   using OB = PipeOperand<Prob::B_KC, BN, TK, NW>;
   constexpr int STAGE_BYTES = OA::TILE_BYTES + OB::TILE_BYTES;
@@ -442,13 +450,14 @@ grouped_gemm_pipe_kernel(const Prob p) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wave_m = wave / Cfg::WAVES_N, wave_n = wave % Cfg::WAVES_N;
+  const int lwave = NL > 0 ? wave - NWC : wave;  // index among the loading waves
   // group starts are read once into LDS: the tile walk then never waits on global loads
   // (a global load there would also drain the operand loads in flight)
-  for (int e = tid; e <= E; e += NT) s_seg[e] = p.seg(e);
+  for (int e = tid; e <= E; e += NTT) s_seg[e] = p.seg(e);
   __syncthreads();
   auto seg = [&](int e) { return s_seg[e]; };
 
-  const int total_tiles = build_tile_map<Prob::GROUP, BM, BN, NT>(s_map, seg, E, p.M, p.N, tid);
+  const int total_tiles = build_tile_map<Prob::GROUP, BM, BN, NTT>(s_map, seg, E, p.M, p.N, tid);
   const int G = gridDim.x;
   const int wg = xcd_logical_wg();
 
@@ -478,22 +487,24 @@ grouped_gemm_pipe_kernel(const Prob p) {
   lc.t = wg;
   lc.tr = tile(wg);
   lc.k = lc.tr.k_beg;
-  // address streams of the two operands at the load cursor
+  // address streams of the two operands at the load cursor.  The lambdas that set them up
+  // and move them are forced inline: a call left out of line keeps the streams in scratch
+  // memory (seen with four loader waves, 64-deep steps and a split B operand).
   typename OA::Stream sa;
   typename OB::Stream sb;
-  auto begin_streams = [&]() {
+  auto begin_streams = [&]() __attribute__((always_inline)) {
     const TileRange& r = lc.tr;
     const bool live = lc.t < total_tiles;
     if constexpr (Prob::A_KC)
-      OA::begin_kc(sa, [&](int x) { return p.a_row(r.e, x); }, r.m0, r.m_end, lc.k, wave, live && lc.k < r.k_end);
+      OA::begin_kc(sa, [&](int x) { return p.a_row(r.e, x); }, r.m0, r.m_end, lc.k, lwave, live && lc.k < r.k_end);
     else
-      OA::begin_mn(sa, [&](int x) { return p.a_row(r.e, x); }, lc.k, r.k_end, r.m0, r.m_end, wave, live);
+      OA::begin_mn(sa, [&](int x) { return p.a_row(r.e, x); }, lc.k, r.k_end, r.m0, r.m_end, lwave, live);
     if constexpr (Prob::B_KC)
-      OB::begin_kc(sb, [&](int x) { return p.b_row(r.e, x); }, r.n0, p.N, lc.k, wave, live && lc.k < r.k_end);
+      OB::begin_kc(sb, [&](int x) { return p.b_row(r.e, x); }, r.n0, p.N, lc.k, lwave, live && lc.k < r.k_end);
     else
-      OB::begin_mn(sb, [&](int x) { return p.b_row(r.e, x); }, lc.k, r.k_end, r.n0, p.N, wave, live);
+      OB::begin_mn(sb, [&](int x) { return p.b_row(r.e, x); }, lc.k, r.k_end, r.n0, p.N, lwave, live);
   };
-  auto advance = [&]() {
+  auto advance = [&]() __attribute__((always_inline)) {
     lc.k += TK;
     if (lc.k >= lc.tr.k_end) {
       lc.t += G;
@@ -507,13 +518,12 @@ grouped_gemm_pipe_kernel(const Prob p) {
       OB::next(sb);
     }
   };
-  begin_streams();
 
   // operands of the load cursor's step go straight into a stage buffer; steps past the
   // reduction or past the last tile read nothing and leave zeros
-  auto load_stage = [&](char* base) {
-    OA::dma(sa, base, wave, lane);
-    OB::dma(sb, base + OA::TILE_BYTES, wave, lane);
+  auto load_stage = [&](char* base) __attribute__((always_inline)) {
+    OA::dma(sa, base, lwave, lane);
+    OB::dma(sb, base + OA::TILE_BYTES, lwave, lane);
     advance();
   };
   // this wave's loads into buf have landed (a read of buf makes the compiler wait for
@@ -523,6 +533,13 @@ grouped_gemm_pipe_kernel(const Prob p) {
     typedef __attribute__((address_space(3))) const volatile int lds_int_t;
     const int v = *(lds_int_t*)(buf + lane * 4);
     asm volatile("s_waitcnt lgkmcnt(0)" ::"v"(v) : "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+  };
+  // a compute wave beside loader waves only meets them: its reads of the previous buffer
+  // were consumed by that step's MFMAs
+  auto meet = [&]() {
+    asm volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
   };
@@ -574,21 +591,22 @@ grouped_gemm_pipe_kernel(const Prob p) {
     return n < 1 ? 1 : n;
   };
 
-  // compute cursor: tile ct (range ctr), step cs of its ncs steps
+  // compute cursor: tile ct (range ctr), step cs of its ncs steps.  Every wave runs it
+  // (loader waves too) so that all of them take the same steps and barriers.
   int ct = wg;
   TileRange ctr = lc.tr;
   int ncs = steps_of(ctr), cs = 0;
-  zero_acc();
   bool done = false;
-  auto finish_step = [&]() {
+  // with_acc: the wave holds accumulators, stores the finished tile and clears them
+  auto finish_step = [&](bool with_acc) {
     if (++cs == ncs) {
-      epilogue(ctr);
+      if (with_acc) epilogue(ctr);
       ct += G;
       if (ct < total_tiles) {
         ctr = tile(ct);
         ncs = steps_of(ctr);
         cs = 0;
-        zero_acc();
+        if (with_acc) zero_acc();
       } else {
         done = true;
       }
@@ -598,30 +616,55 @@ grouped_gemm_pipe_kernel(const Prob p) {
   // step s is loaded into buffer s % NS, NS - 1 steps ahead; the buffer it overwrites was
   // computed in the step before (every wave is past that step's barrier).  One exit, at
   // the bottom: up to NS - 1 discarded steps run after a workgroup's last tile.
-  auto phase = [&](char* cur, char* next_load, bool first) {
-    ready(cur);
-    load_stage(next_load);
-    compute(cur);
-    if (first || !done) finish_step();
-  };
-  load_stage(sm0);  // step 0
-  if constexpr (NS >= 3) load_stage(sm1);  // step 1
-  if constexpr (NS == 4) load_stage(sm2);
-  for (;;) {
-    if constexpr (NS == 2) {
-      phase(sm0, sm1, true);
-      phase(sm1, sm0, false);
-    } else if constexpr (NS == 3) {
-      phase(sm0, sm2, true);
-      phase(sm1, sm0, false);
-      phase(sm2, sm1, false);
-    } else {
-      phase(sm0, sm3, true);
-      phase(sm1, sm0, false);
-      phase(sm2, sm1, false);
-      phase(sm3, sm2, false);
+  auto pipeline = [&](auto&& phase) {
+    for (;;) {
+      if constexpr (NS == 2) {
+        phase(sm0, sm1, true);
+        phase(sm1, sm0, false);
+      } else if constexpr (NS == 3) {
+        phase(sm0, sm2, true);
+        phase(sm1, sm0, false);
+        phase(sm2, sm1, false);
+      } else {
+        phase(sm0, sm3, true);
+        phase(sm1, sm0, false);
+        phase(sm2, sm1, false);
+        phase(sm3, sm2, false);
+      }
+      if (done) break;
     }
-    if (done) break;
+  };
+  auto prologue_loads = [&]() {
+    begin_streams();
+    load_stage(sm0);  // step 0
+    if constexpr (NS >= 3) load_stage(sm1);  // step 1
+    if constexpr (NS == 4) load_stage(sm2);
+  };
+  if constexpr (NL == 0) {
+    zero_acc();
+    prologue_loads();
+    pipeline([&](char* cur, char* next_load, bool first) {
+      ready(cur);
+      load_stage(next_load);
+      compute(cur);
+      if (first || !done) finish_step(true);
+    });
+  } else if (wave >= NWC) {
+    // loader: the two roles run separate loops, so no operand load is on a compute
+    // wave's path and the compiler puts no memory-counter wait there
+    prologue_loads();
+    pipeline([&](char* cur, char* next_load, bool first) {
+      ready(cur);
+      load_stage(next_load);
+      if (first || !done) finish_step(false);
+    });
+  } else {
+    zero_acc();
+    pipeline([&](char* cur, char*, bool first) {
+      meet();
+      compute(cur);
+      if (first || !done) finish_step(true);
+    });
   }
 }
 
@@ -647,12 +690,14 @@ static bool parse_tile(const char* v, Tile* t) {
 struct TileChoice {
   Tile tile;
   int bk;
-  int stages;  // LDS stage buffers: 3, or 4 at a k-depth of 32, or 2 at a k-depth of 64 (where they fit)
+  int stages;   // LDS stage buffers: 3, or 4 at a k-depth of 32, or 2 at a k-depth of 64 (where they fit)
+  int loaders;  // extra waves that issue every operand load (0, or 4 for 8-wave 128 x 256 tiles)
 };
 
-// Tile shape, k-depth and stage count of one GEMM: MOE_TILE_<NAME> / MOE_TILE,
-// MOE_GEMM_BK and MOE_GEMM_STAGES override the defaults chosen by measurement on MI355X.
-static TileChoice tile_for(const char* name, Tile dflt, int dflt_bk, int dflt_stages = 3) {
+// Tile shape, k-depth, stage count and loader waves of one GEMM: MOE_TILE_<NAME> /
+// MOE_TILE, MOE_GEMM_BK, MOE_GEMM_STAGES and MOE_GEMM_LOADERS override the defaults chosen
+// by measurement on MI355X.
+static TileChoice tile_for(const char* name, Tile dflt, int dflt_bk, int dflt_stages = 3, int dflt_loaders = 0) {
   char key[64];
   snprintf(key, sizeof key, "MOE_TILE_%s", name);
   Tile t = dflt;
@@ -661,16 +706,18 @@ static TileChoice tile_for(const char* name, Tile dflt, int dflt_bk, int dflt_st
   const int b = bk ? atoi(bk) : dflt_bk;
   const char* ns = getenv("MOE_GEMM_STAGES");
   const int n = ns ? atoi(ns) : dflt_stages;
-  return TileChoice{t, b == 64 ? 64 : 32, n == 4 ? 4 : (n == 2 ? 2 : 3)};
+  const char* nl = getenv("MOE_GEMM_LOADERS");
+  const int l = nl ? atoi(nl) : dflt_loaders;
+  return TileChoice{t, b == 64 ? 64 : 32, n == 4 ? 4 : (n == 2 ? 2 : 3), l == 4 ? 4 : 0};
 }
 
 // Persistent grid: resident workgroups per CU x CUs, capped by the tile bound known on the
 // host, rounded to a multiple of the 8 XCDs.
 template <class Cfg, class Prob, class Kern>
-static hipError_t launch_kernel(Kern kern, const Prob& p, hipStream_t st, int& occ, size_t dyn_lds = 0) {
+static hipError_t launch_kernel(Kern kern, const Prob& p, hipStream_t st, int& occ, size_t dyn_lds, int threads) {
   if (occ == 0) {
     int o = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&o, kern, Cfg::NT, dyn_lds) != hipSuccess || o < 1) o = 1;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&o, kern, threads, dyn_lds) != hipSuccess || o < 1) o = 1;
     occ = o;
   }
   int64_t bound;
@@ -681,26 +728,35 @@ static hipError_t launch_kernel(Kern kern, const Prob& p, hipStream_t st, int& o
   if (bound < G) G = bound;
   G = ((G + 7) / 8) * 8;
   if (G < 8) G = 8;
-  hipLaunchKernelGGL(kern, dim3((unsigned)G), dim3(Cfg::NT), dyn_lds, st, p);
+  hipLaunchKernelGGL(kern, dim3((unsigned)G), dim3(threads), dyn_lds, st, p);
   return hipGetLastError();
 }
 
-template <class Cfg, class Prob, int TK, int NS>
+template <class Cfg, class Prob, int TK, int NS, int NL = 0>
 static hipError_t launch_pipe(const Prob& p, hipStream_t st) {
   // occupancy depends on the dynamic LDS, i.e. on the expert count: cache it per count
   static int occ_e = -1, occ = 0;
   if (occ_e != p.E) { occ_e = p.E; occ = 0; }
-  return launch_kernel<Cfg>(grouped_gemm_pipe_kernel<Cfg, Prob, TK, NS>, p, st, occ, pipe_dyn_lds_bytes(p.E));
+  return launch_kernel<Cfg>(grouped_gemm_pipe_kernel<Cfg, Prob, TK, NS, NL>, p, st, occ, pipe_dyn_lds_bytes(p.E),
+                            Cfg::NT + 64 * NL);
 }
 
 // every problem runs on the pipelined kernel
 template <class Cfg, class Prob>
-static hipError_t launch_cfg(const Prob& p, hipStream_t st, int bk, int stages) {
+static hipError_t launch_cfg(const Prob& p, hipStream_t st, int bk, int stages, int loaders) {
   static_assert(std::is_same<typename Prob::TA, bf16_t>::value, "bf16 operands");
   // the stage buffers must fit the 160 KB of LDS with room for the tile map
   constexpr bool fits64 = 3 * (Cfg::BM + Cfg::BN) * 64 * 2 <= 152 * 1024;
   constexpr bool fits32x4 = 4 * (Cfg::BM + Cfg::BN) * 32 * 2 <= 152 * 1024;
   constexpr bool fits64x2 = 2 * (Cfg::BM + Cfg::BN) * 64 * 2 <= 152 * 1024;
+  // loader waves (GEMMs grouped along M): 8 compute waves with 2 x 2 accumulator blocks
+  // each, three stages
+  if constexpr (Prob::GROUP == Group::M && Cfg::BM == 128 && Cfg::BN == 256 && Cfg::NT == 512) {
+    if (loaders == 4 && stages == 3) {
+      if (bk == 64) return launch_pipe<Cfg, Prob, 64, 3, 4>(p, st);
+      return launch_pipe<Cfg, Prob, 32, 3, 4>(p, st);
+    }
+  }
   if constexpr (Cfg::BM >= 64 && Cfg::BN >= 64 && fits64x2) {
     if (bk == 64 && stages == 2) return launch_pipe<Cfg, Prob, 64, 2>(p, st);
   }
@@ -721,29 +777,32 @@ static hipError_t launch_cfg(const Prob& p, hipStream_t st, int bk, int stages) 
 template <class Prob>
 static hipError_t launch(TileChoice c, const Prob& p, hipStream_t st) {
   switch (c.tile) {
-    case Tile::t32x128: return launch_cfg<TileCfg<32, 128, 1, 4>>(p, st, c.bk, c.stages);
-    case Tile::t128x256w8: return launch_cfg<TileCfg<128, 256, 2, 4>>(p, st, c.bk, c.stages);
-    case Tile::t256x256w8: return launch_cfg<TileCfg<256, 256, 2, 4>>(p, st, c.bk, c.stages);
+    case Tile::t32x128: return launch_cfg<TileCfg<32, 128, 1, 4>>(p, st, c.bk, c.stages, c.loaders);
+    case Tile::t128x256w8: return launch_cfg<TileCfg<128, 256, 2, 4>>(p, st, c.bk, c.stages, c.loaders);
+    case Tile::t256x256w8: return launch_cfg<TileCfg<256, 256, 2, 4>>(p, st, c.bk, c.stages, c.loaders);
 #ifdef MOE_ALL_TILES
-    case Tile::t128x256: return launch_cfg<TileCfg<128, 256, 2, 2>>(p, st, c.bk, c.stages);
-    case Tile::t256x128: return launch_cfg<TileCfg<256, 128, 2, 2>>(p, st, c.bk, c.stages);
-    case Tile::t64x128: return launch_cfg<TileCfg<64, 128, 1, 4>>(p, st, c.bk, c.stages);
-    case Tile::t256x128w8: return launch_cfg<TileCfg<256, 128, 4, 2>>(p, st, c.bk, c.stages);
-    case Tile::t256x256w4: return launch_cfg<TileCfg<256, 256, 2, 2>>(p, st, c.bk, c.stages);
-    case Tile::t128x256w2: return launch_cfg<TileCfg<128, 256, 1, 2>>(p, st, c.bk, c.stages);
-    case Tile::t128x256m1: return launch_cfg<TileCfg<128, 256, 1, 4>>(p, st, c.bk, c.stages);
+    case Tile::t128x256: return launch_cfg<TileCfg<128, 256, 2, 2>>(p, st, c.bk, c.stages, c.loaders);
+    case Tile::t256x128: return launch_cfg<TileCfg<256, 128, 2, 2>>(p, st, c.bk, c.stages, c.loaders);
+    case Tile::t64x128: return launch_cfg<TileCfg<64, 128, 1, 4>>(p, st, c.bk, c.stages, c.loaders);
+    case Tile::t256x128w8: return launch_cfg<TileCfg<256, 128, 4, 2>>(p, st, c.bk, c.stages, c.loaders);
+    case Tile::t256x256w4: return launch_cfg<TileCfg<256, 256, 2, 2>>(p, st, c.bk, c.stages, c.loaders);
+    case Tile::t128x256w2: return launch_cfg<TileCfg<128, 256, 1, 2>>(p, st, c.bk, c.stages, c.loaders);
+    case Tile::t128x256m1: return launch_cfg<TileCfg<128, 256, 1, 4>>(p, st, c.bk, c.stages, c.loaders);
 #endif
-    default: return launch_cfg<TileCfg<128, 128, 2, 2>>(p, st, c.bk, c.stages);
+    default: return launch_cfg<TileCfg<128, 128, 2, 2>>(p, st, c.bk, c.stages, c.loaders);
   }
 }
 
 // Tiles of the GEMMs grouped along M (forward and data gradients).  Long expert segments
 // (1024 rows per expert or more on average) take 256 x 256 tiles, 64 deep, in two stage
 // buffers: on MI355X at 2048 rows per expert that is 4-16% faster than 128 x 256 with
-// three stages, which stays best for short segments (256 rows per expert).
+// three stages, which stays best for short segments (256 rows per expert).  There, at a
+// k-depth of 64, four loader waves beside the eight compute waves take 5-7% off each GEMM
+// (the compute waves' epilogue stores no longer wait behind operand loads); at a depth of
+// 32 they gained nothing measurable.
 static TileChoice m_grouped_tile(const char* name, const GemmShape& s, int short_bk) {
   if ((int64_t)s.R >= (int64_t)1024 * s.E) return tile_for(name, Tile::t256x256w8, 64, 2);
-  return tile_for(name, Tile::t128x256w8, short_bk);
+  return tile_for(name, Tile::t128x256w8, short_bk, 3, short_bk == 64 ? 4 : 0);
 }
 
 hipError_t gemm1_fwd_bf16(const GemmShape& s, const int* offsets, const bf16_t* X, const bf16_t* W1,
