@@ -114,8 +114,9 @@ def step_calls(m, L, d_inp, learned, recompute=False):
             ("dgrad2", lambda: m.moe_ffn_dgrad2_mx(s, L.dyq_rows, L.dys_rows, W2, L.ab, L.offsets, L.dab, L.ws)),
             ("wgrad2", lambda: m.moe_ffn_wgrad2_mx(s, L.h, L.dyq_cols, L.dys_cols, L.offsets, L.dW2, L.ws)),
             ("dgrad1", lambda: m.moe_ffn_dgrad1(s, L.dab, W1, W3, L.offsets, L.dx_perm, L.ws)),
-            ("wgrad1", lambda: m.moe_ffn_wgrad1_mx(s, L.xq_cols, L.xs_cols, L.dab, L.offsets, L.dW1, L.dW3, L.ws)),
         ]
+        wgrad1 = ("wgrad1", lambda: m.moe_ffn_wgrad1_mx(s, L.xq_cols, L.xs_cols, L.dab, L.offsets, L.dW1, L.dW3,
+                                                          L.ws))
     else:
         calls += [
             ("permute", lambda: m.moe_permute(s, x, L.slot_row, L.row_src, L.x_perm)),
@@ -131,8 +132,8 @@ def step_calls(m, L, d_inp, learned, recompute=False):
             ("dgrad2", lambda: m.moe_ffn_dgrad2(s, L.dy_perm, W2, L.ab, L.offsets, L.dab, L.ws)),
             ("wgrad2", lambda: m.moe_ffn_wgrad2(s, L.h, L.dy_perm, L.offsets, L.dW2, L.ws)),
             ("dgrad1", lambda: m.moe_ffn_dgrad1(s, L.dab, W1, W3, L.offsets, L.dx_perm, L.ws)),
-            ("wgrad1", lambda: m.moe_ffn_wgrad1(s, L.x_perm, L.dab, L.offsets, L.dW1, L.dW3, L.ws)),
         ]
+        wgrad1 = ("wgrad1", lambda: m.moe_ffn_wgrad1(s, L.x_perm, L.dab, L.offsets, L.dW1, L.dW3, L.ws))
     if learned:
         calls += [("route_bwd", lambda: m.moe_route_bwd(s, L.dgates, g, L.topk_idx, L.dlogits)),
                   ("router_bwd", lambda: m.moe_router_bwd(s, x, Wr, L.dlogits, L.dx_r, L.dWr, L.ws))]
@@ -144,6 +145,9 @@ def step_calls(m, L, d_inp, learned, recompute=False):
     dx_add = L.dx_s if sh is not None else None
     calls += [("permute_bwd", lambda: m.moe_permute_bwd(s, L.dx_perm, L.slot_row, L.dx_r if learned else None,
                                                         dx_add, L.dx))]
+    # wgrad1 last, as in the layer's backward: its gradient writes would otherwise push
+    # dx_perm out of the memory-side cache before the un-permute reads it
+    calls += [wgrad1]
     return calls
 
 

@@ -7,7 +7,8 @@
 // MoE…", section "Trois parallélismes, trois optimisations de routage").
 //
 // Three launches, all with host-known grids:
-//   1. per chunk of 32 tokens: wave-level top-k of each token's E scores, its gates, and
+//   1. per chunk of 32 tokens (16 waves, two tokens each): wave-level top-k of each
+//      token's E scores, its gates, and
 //      a stable in-chunk rank of every routed slot (ballot matching) plus the chunk's
 //      per-expert histogram;
 //   2. one workgroup: per-expert running sums over chunks (chunk bases), counts, and the
@@ -21,8 +22,11 @@
 namespace moe {
 namespace {
 
-constexpr int kThreads = 256;
+// 16 waves per chunk, two tokens each: the per-token top-k is a chain of dependent
+// cross-lane reductions, so many waves per compute unit keep it fed
+constexpr int kThreads = 1024;
 constexpr int kTokPerWave = kRouteChunk / (kThreads / kWave);
+static_assert(kTokPerWave * (kThreads / kWave) == kRouteChunk, "whole tokens per wave");
 
 // (value desc, index asc) total order on (score, expert)
 __device__ __forceinline__ bool beats(float v1, int i1, float v2, int i2) {
@@ -124,29 +128,40 @@ __global__ void __launch_bounds__(kThreads) route_chunk_kernel(int T, int E, int
 }
 
 // One workgroup: chunk bases (exclusive running sums over chunks, in place over the
-// histograms), counts and offsets.
+// histograms), counts and offsets.  Each expert's chunks are split into P contiguous runs
+// walked by P neighbouring lanes (P a power of two, P * E <= 1024): every lane sums its
+// run, the lanes scan the P sums, and each rewrites its run with the running bases.
 __global__ void __launch_bounds__(1024) route_scan_kernel(int E, int nchunks, int32_t* __restrict__ hist,
                                                            int32_t* __restrict__ counts, int32_t* __restrict__ offsets) {
   __shared__ int s_wave[16];
+  __shared__ int s_cnt[kMaxExperts];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  int run = 0;
-  if (tid < E) {
-    int c = 0;
-    for (; c + 8 <= nchunks; c += 8) {
-      int h[8];
-#pragma unroll
-      for (int u = 0; u < 8; u++) h[u] = hist[(int64_t)(c + u) * E + tid];
-#pragma unroll
-      for (int u = 0; u < 8; u++) { hist[(int64_t)(c + u) * E + tid] = run; run += h[u]; }
+  int P = 1;
+  while (P < kWave && 2 * P * E <= 1024) P *= 2;
+  const int ex = tid / P, part = tid % P;
+  if (ex < E) {  // uniform over each group of P lanes
+    const int c0 = (int)((int64_t)part * nchunks / P), c1 = (int)((int64_t)(part + 1) * nchunks / P);
+    int sum = 0;
+#pragma unroll 8
+    for (int c = c0; c < c1; c++) sum += hist[(int64_t)c * E + ex];
+    int incl = sum;
+    for (int o = 1; o < P; o <<= 1) {
+      const int y = __shfl_up(incl, o, P);
+      if (part >= o) incl += y;
     }
-    for (; c < nchunks; c++) {
-      const int h = hist[(int64_t)c * E + tid];
-      hist[(int64_t)c * E + tid] = run;
+    int run = incl - sum;
+#pragma unroll 8
+    for (int c = c0; c < c1; c++) {
+      const int h = hist[(int64_t)c * E + ex];
+      hist[(int64_t)c * E + ex] = run;
       run += h;
     }
-    counts[tid] = run;
+    if (part == P - 1) s_cnt[ex] = incl;
   }
-  // exclusive scan of run over experts
+  __syncthreads();
+  const int run = tid < E ? s_cnt[tid] : 0;
+  if (tid < E) counts[tid] = run;
+  // exclusive scan of the counts over experts
   int incl = run;
 #pragma unroll
   for (int o = 1; o < kWave; o <<= 1) {

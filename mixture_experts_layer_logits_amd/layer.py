@@ -7,9 +7,9 @@ backward passes as the library's calls, in order, on the current stream:
   forward   moe_router_fwd -> moe_route        (learned routing)
             or moe_route_given                 (tokens arrive routed)
             -> moe_permute -> moe_grouped_ffn_fwd -> moe_combine
-  backward  moe_combine_bwd -> moe_grouped_ffn_bwd
+  backward  moe_combine_bwd -> the expert GEMMs' dgrad2, wgrad2, dgrad1
             -> moe_route_bwd -> moe_router_bwd (learned routing)
-            -> moe_permute_bwd
+            -> moe_permute_bwd -> wgrad1 (last, after the un-permute has read dx_perm)
 
 Nothing is copied back to the host between calls; routing counts and offsets stay on
 the GPU (unite.ai, "Ai2 κυκλοφορεί το Olmo-Core 3…", section "Παραλληλισμός, Ακρίβεια
@@ -173,12 +173,10 @@ class MoEExpertLayer:
             moe_ffn_dgrad2_mx(s, self.dyq_rows, self.dys_rows, W2, self.ab, self.offsets, self.dab, self.ws)
             moe_ffn_wgrad2_mx(s, self.h, self.dyq_cols, self.dys_cols, self.offsets, self.dW2, self.ws)
             moe_ffn_dgrad1(s, self.dab, W1, W3, self.offsets, self.dx_perm, self.ws)
-            moe_ffn_wgrad1_mx(s, self.xq_cols, self.xs_cols, self.dab, self.offsets, self.dW1, self.dW3, self.ws)
         else:
             moe_ffn_dgrad2(s, self.dy_perm, W2, self.ab, self.offsets, self.dab, self.ws)
             moe_ffn_wgrad2(s, self.h, self.dy_perm, self.offsets, self.dW2, self.ws)
             moe_ffn_dgrad1(s, self.dab, W1, W3, self.offsets, self.dx_perm, self.ws)
-            moe_ffn_wgrad1(s, self.x_perm, self.dab, self.offsets, self.dW1, self.dW3, self.ws)
         dx_r = None
         if self.learned:
             moe_route_bwd(s, self.dgates, g, self.topk_idx, self.dlogits)
@@ -194,6 +192,12 @@ class MoEExpertLayer:
             moe_ffn_wgrad1(ss, x, self.dab_s, off, self.dW1s, self.dW3s, self.ws_s)
             dx_add = self.dx_s
         moe_permute_bwd(s, self.dx_perm, self.slot_row, dx_r, dx_add, self.dx)
+        # wgrad1 goes last: its gradient writes, the largest output of the step, would
+        # otherwise push dx_perm out of the memory-side cache before the un-permute reads it
+        if self.mx_dispatch:
+            moe_ffn_wgrad1_mx(s, self.xq_cols, self.xs_cols, self.dab, self.offsets, self.dW1, self.dW3, self.ws)
+        else:
+            moe_ffn_wgrad1(s, self.x_perm, self.dab, self.offsets, self.dW1, self.dW3, self.ws)
         if self.recompute:
             self.ab = self.h = None
         return self.dx
