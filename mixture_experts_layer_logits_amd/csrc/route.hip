@@ -128,35 +128,37 @@ __global__ void __launch_bounds__(kThreads) route_chunk_kernel(int T, int E, int
 }
 
 // One workgroup: chunk bases (exclusive running sums over chunks, in place over the
-// histograms), counts and offsets.  Each expert's chunks are split into P contiguous runs
-// walked by P neighbouring lanes (P a power of two, P * E <= 1024): every lane sums its
-// run, the lanes scan the P sums, and each rewrites its run with the running bases.
+// histograms), counts and offsets.  The chunks are split into P contiguous runs (P a power
+// of two, P * E <= 1024); thread (part, expert) = (tid / E, tid % E) walks one run of one
+// expert, so a wave's loads read consecutive experts of one chunk row.  Every thread sums
+// its run, the sums meet in LDS, and each thread rewrites its run with the running bases.
 __global__ void __launch_bounds__(1024) route_scan_kernel(int E, int nchunks, int32_t* __restrict__ hist,
                                                            int32_t* __restrict__ counts, int32_t* __restrict__ offsets) {
   __shared__ int s_wave[16];
   __shared__ int s_cnt[kMaxExperts];
+  __shared__ int s_part[1024];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   int P = 1;
   while (P < kWave && 2 * P * E <= 1024) P *= 2;
-  const int ex = tid / P, part = tid % P;
-  if (ex < E) {  // uniform over each group of P lanes
-    const int c0 = (int)((int64_t)part * nchunks / P), c1 = (int)((int64_t)(part + 1) * nchunks / P);
-    int sum = 0;
+  const int part = tid / E, ex = tid - part * E;
+  const bool active = part < P;
+  const int c0 = active ? (int)((int64_t)part * nchunks / P) : 0;
+  const int c1 = active ? (int)((int64_t)(part + 1) * nchunks / P) : 0;
+  int sum = 0;
 #pragma unroll 8
-    for (int c = c0; c < c1; c++) sum += hist[(int64_t)c * E + ex];
-    int incl = sum;
-    for (int o = 1; o < P; o <<= 1) {
-      const int y = __shfl_up(incl, o, P);
-      if (part >= o) incl += y;
-    }
-    int run = incl - sum;
+  for (int c = c0; c < c1; c++) sum += hist[(int64_t)c * E + ex];
+  if (active) s_part[tid] = sum;
+  __syncthreads();
+  if (active) {
+    int run = 0;
+    for (int q = 0; q < part; q++) run += s_part[q * E + ex];
 #pragma unroll 8
     for (int c = c0; c < c1; c++) {
       const int h = hist[(int64_t)c * E + ex];
       hist[(int64_t)c * E + ex] = run;
       run += h;
     }
-    if (part == P - 1) s_cnt[ex] = incl;
+    if (part == P - 1) s_cnt[ex] = run;
   }
   __syncthreads();
   const int run = tid < E ? s_cnt[tid] : 0;
