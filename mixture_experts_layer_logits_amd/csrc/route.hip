@@ -189,17 +189,37 @@ __global__ void route_finalize_kernel(int T, int E, int k, const int32_t* __rest
   slot_row[s] = offsets[e] + hist[(int64_t)chunk * E + e] + local_rank[s];
 }
 
-// dlogits[t, e] = g_e (dg_e - sum_i g_i dg_i) on the chosen experts, else 0
+// dlogits[t, e] = g_e (dg_e - sum_i g_i dg_i) on the chosen experts, else 0.  A thread
+// writes four consecutive experts of one token (one 16-byte store when VEC: E % 4 == 0 and
+// dlogits 16-byte aligned), so each token's k gates, gate gradients and expert ids are
+// read by E / 4 threads instead of E.
+template <bool VEC>
 __global__ void route_bwd_kernel(int T, int E, int k, const float* __restrict__ dgates, const float* __restrict__ gates,
                                  const int32_t* __restrict__ idx, float* __restrict__ dlogits) {
+  const int E4 = (E + 3) / 4;
   const int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (q >= (int64_t)T * E) return;
-  const int t = (int)(q / E), e = (int)(q % E);
-  float inner = 0.f, out = 0.f;
-  for (int j = 0; j < k; j++) inner = fmaf(gates[(int64_t)t * k + j], dgates[(int64_t)t * k + j], inner);
-  for (int j = 0; j < k; j++)
-    if (idx[(int64_t)t * k + j] == e) out = gates[(int64_t)t * k + j] * (dgates[(int64_t)t * k + j] - inner);
-  dlogits[q] = out;
+  if (q >= (int64_t)T * E4) return;
+  const int t = (int)(q / E4), e0 = (int)(q % E4) * 4;
+  const float* g = gates + (int64_t)t * k;
+  const float* dg = dgates + (int64_t)t * k;
+  const int32_t* id = idx + (int64_t)t * k;
+  float inner = 0.f;
+  for (int j = 0; j < k; j++) inner = fmaf(g[j], dg[j], inner);
+  float out[4] = {0.f, 0.f, 0.f, 0.f};
+  for (int j = 0; j < k; j++) {
+    const int r = id[j] - e0;
+#pragma unroll
+    for (int c = 0; c < 4; c++)
+      if (r == c) out[c] = g[j] * (dg[j] - inner);
+  }
+  float* o = dlogits + (int64_t)t * E + e0;
+  if constexpr (VEC) {
+    *reinterpret_cast<float4*>(o) = make_float4(out[0], out[1], out[2], out[3]);
+  } else {
+#pragma unroll
+    for (int c = 0; c < 4; c++)
+      if (e0 + c < E) o[c] = out[c];
+  }
 }
 
 template <bool GIVEN>
@@ -261,9 +281,12 @@ hipError_t route_given(int T, int E, int k, const int32_t* idx, int32_t* counts,
 
 hipError_t route_backward(int T, int E, int k, const float* dgates, const float* gates, const int32_t* idx,
                           float* dlogits, hipStream_t st) {
-  const int64_t n = (int64_t)T * E;
-  hipLaunchKernelGGL(route_bwd_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, T, E, k, dgates, gates,
-                     idx, dlogits);
+  const int64_t n = (int64_t)T * ((E + 3) / 4);
+  const dim3 grid((unsigned)((n + 255) / 256));
+  if (E % 4 == 0 && (reinterpret_cast<uintptr_t>(dlogits) & 15) == 0)
+    hipLaunchKernelGGL(route_bwd_kernel<true>, grid, dim3(256), 0, st, T, E, k, dgates, gates, idx, dlogits);
+  else
+    hipLaunchKernelGGL(route_bwd_kernel<false>, grid, dim3(256), 0, st, T, E, k, dgates, gates, idx, dlogits);
   return hipGetLastError();
 }
 
