@@ -157,16 +157,35 @@ def dequantize_segment_cols(codes, scales, offsets, block: int = BLOCK) -> np.nd
 
 
 # ----------------------------------------------------------------------------- MXFP8 layer
-# The expert FFN with MXFP8 GEMMs: every GEMM operand is block-quantised along that
-# GEMM's reduction axis (forward: activations and weights along the model / hidden
-# width; data gradient: the upstream gradient along its width and the weights along the
-# other axis; weight gradient: both operands along the expert's rows), dequantised
-# exactly, and multiplied in fp64.  The GEMMs produce bf16 (round to nearest even at each
-# stored activation and gradient), and it is those bf16 values that the next GEMM
-# quantises: the E4M3 code of a value depends on its bf16 rounding, so the oracle takes
-# that decision on the same bf16 values as the device.  Everything else (routing,
-# dispatch, gates, combine, SwiGLU and its gradient) is the plain layer of moe_ref.
-# quant=False and bf16=False recover the unquantised, unrounded layer exactly.
+# The expert FFN with MXFP8 GEMMs.  A GEMM in the layer's MXFP8 scope takes both operands
+# block-quantised along that GEMM's reduction axis, dequantised exactly and multiplied in
+# fp64; a GEMM outside the scope multiplies its operands as stored.  The three kinds of
+# expert GEMM differ in where their reduction axis lies:
+#   forward        out_e = A_e W_e^T    K = columns of A and of W  (blocks along rows of both)
+#   data gradient  out_e = A_e W_e      K = columns of A, rows of W (blocks down W's columns)
+#   weight grad.   out_e = A_e^T B_e    K = the expert's rows       (blocks down the columns of
+#                                       A_e and B_e, restarting at the expert's first row)
+# The GEMMs produce bf16 (round to nearest even at each stored activation and gradient),
+# and it is those bf16 values that the next GEMM quantises: the E4M3 code of a value
+# depends on its bf16 rounding, so the oracle takes that decision on the same bf16 values
+# as the device.  Everything else (routing, dispatch, gates, combine, SwiGLU and its
+# gradient) is the plain layer of moe_ref.  quant=False and bf16=False recover the
+# unquantised, unrounded layer exactly.
+#
+# Which GEMMs are in the scope is a reading: the pages put MXFP8 on selected operations,
+# where it helped most, with most of the gain in the feed-forward compute and in moving
+# data between experts (bigchange.ai, "Olmo-core 3 открывает стек обучения MoE от Ai2…",
+# section "Главное изменение"; ettayeb.fr, "Olmo-core 3 ouvre l'entraînement des MoE…",
+# section "Trois parallélismes, trois optimisations de routage").  DEFAULT_SCOPE holds
+# the two GEMMs that reduce over the hidden width and produce the d-wide rows returned to
+# the tokens: GEMM2 (y_perm) and the input-gradient GEMM dgrad1 (dx_perm).  Every output
+# and gradient of the layer then passes through at most one quantised GEMM.
+
+# The six expert GEMMs by name.
+GEMMS = ("gemm1", "gemm2", "dgrad2", "wgrad2", "dgrad1", "wgrad1")
+ALL_GEMMS = frozenset(GEMMS)
+DEFAULT_SCOPE = frozenset(("gemm2", "dgrad1"))
+
 
 def bf16_round(v) -> np.ndarray:
     """Round to bfloat16 (nearest, ties to even) through fp32, returned as float64."""
@@ -178,67 +197,111 @@ def bf16_round(v) -> np.ndarray:
     return np.where(nan, np.nan, out)
 
 
-def _q_rows(v, quant=True):
-    if not quant:
-        return np.asarray(v, dtype=np.float64)
-    c, s = quantize_rows(v)
-    return dequantize_rows(c, s)
-
-
-def _q_cols(v, quant=True):
-    """Blocks down the columns of one segment (all rows of v)."""
-    if not quant:
-        return np.asarray(v, dtype=np.float64)
+def q_along_rows(v, on=True) -> np.ndarray:
+    """v dequantised after blocking along each row (32 consecutive columns)."""
     v = np.asarray(v, dtype=np.float64)
-    c, s = quantize_segment_cols(v, [0, v.shape[0]])
-    return dequantize_segment_cols(c, s, [0, v.shape[0]])
+    if not on:
+        return v
+    return dequantize_rows(*quantize_rows(v))
 
 
-def mx_expert_weights(W1e, W3e, W2e, quant=True) -> dict:
-    """The dequantised weight operands of one expert for the three GEMMs that read it:
-    forward (W1, W3 along d; W2 along f) and data gradient (W2 along d; W1, W3 along f)."""
-    W1e, W3e, W2e = (np.asarray(w, dtype=np.float64) for w in (W1e, W3e, W2e))
-    return {"W1": _q_rows(W1e, quant), "W3": _q_rows(W3e, quant), "W2": _q_rows(W2e, quant),
-            "W2t": _q_cols(W2e, quant),
-            "W13t": np.concatenate([_q_cols(W1e, quant), _q_cols(W3e, quant)], axis=0)}
+def q_down_cols(v, offsets=None, on=True) -> np.ndarray:
+    """v dequantised after blocking down each column (32 consecutive rows), the blocks
+    restarting at every offsets[e] (one segment spanning all rows if offsets is None)."""
+    v = np.asarray(v, dtype=np.float64)
+    if not on:
+        return v
+    off = [0, v.shape[0]] if offsets is None else offsets
+    c, s = quantize_segment_cols(v, off)
+    return dequantize_segment_cols(c, s, off)
 
 
-def mx_expert_fwd(X, Wq: dict, quant=True, bf16=True):
-    """One expert's rows X [n, d]: a = q(X) q(W1)^T, b likewise (stored bf16),
-    h = silu(a) b from the unrounded a, b (stored bf16), y = q(h) q(W2)^T (stored bf16)."""
+def _groups(offsets):
+    off = np.asarray(offsets).astype(np.int64)
+    return [(e, off[e], off[e + 1]) for e in range(len(off) - 1)]
+
+
+def mx_gemm_fwd(A, W, offsets, on=True) -> np.ndarray:
+    """Grouped forward GEMM: out[rows of e] = q(A_e) q(W_e)^T with A [R, K], W [E, N, K];
+    K (the columns of both) is the reduction axis."""
+    A = np.asarray(A, dtype=np.float64)
+    W = np.asarray(W, dtype=np.float64)
+    out = np.zeros((A.shape[0], W.shape[1]))
+    Aq = q_along_rows(A, on)
+    for e, lo, hi in _groups(offsets):
+        if hi > lo:
+            out[lo:hi] = Aq[lo:hi] @ q_along_rows(W[e], on).T
+    return out
+
+
+def mx_gemm_dgrad(A, W, offsets, on=True) -> np.ndarray:
+    """Grouped data-gradient GEMM: out[rows of e] = q(A_e) q(W_e) with A [R, K], W [E, K, N];
+    the reduction runs over A's columns and W's rows, so W is blocked down its columns."""
+    A = np.asarray(A, dtype=np.float64)
+    W = np.asarray(W, dtype=np.float64)
+    out = np.zeros((A.shape[0], W.shape[2]))
+    Aq = q_along_rows(A, on)
+    for e, lo, hi in _groups(offsets):
+        if hi > lo:
+            out[lo:hi] = Aq[lo:hi] @ q_down_cols(W[e], None, on)
+    return out
+
+
+def mx_gemm_wgrad(A, B, offsets, on=True) -> np.ndarray:
+    """Grouped weight-gradient GEMM: out[e] = q(A_e)^T q(B_e) with A [R, M], B [R, N]; the
+    reduction runs over the expert's rows, blocked down each column and restarting at
+    every offsets[e] so no block mixes two experts.  Experts with no rows get zeros."""
+    A = np.asarray(A, dtype=np.float64)
+    B = np.asarray(B, dtype=np.float64)
+    Aq = q_down_cols(A, offsets, on)
+    Bq = q_down_cols(B, offsets, on)
+    groups = _groups(offsets)
+    out = np.zeros((len(groups), A.shape[1], B.shape[1]))
+    for e, lo, hi in groups:
+        if hi > lo:
+            out[e] = Aq[lo:hi].T @ Bq[lo:hi]
+    return out
+
+
+def mx_ffn_fwd(xp, W1, W3, W2, offsets, quant=True, bf16=True, scope=DEFAULT_SCOPE):
+    """Grouped SwiGLU FFN on the packed rows xp [R, d]: a = X W1^T, b = X W3^T (GEMM1,
+    stored bf16), h = silu(a) b from the unrounded a, b (stored bf16), y_perm = h W2^T
+    (GEMM2, stored bf16).  Returns a, b, h, y_perm as stored."""
     from oracle import moe_ref as ref
     rnd = bf16_round if bf16 else (lambda z: z)
-    Xq = _q_rows(X, quant)
-    a = Xq @ Wq["W1"].T
-    b = Xq @ Wq["W3"].T
+    q = lambda name: quant and name in scope  # noqa: E731
+    a = mx_gemm_fwd(xp, W1, offsets, q("gemm1"))
+    b = mx_gemm_fwd(xp, W3, offsets, q("gemm1"))
     h = rnd(ref.silu(a) * b)
-    y = rnd(_q_rows(h, quant) @ Wq["W2"].T)
+    y = rnd(mx_gemm_fwd(h, W2, offsets, q("gemm2")))
     return rnd(a), rnd(b), h, y
 
 
-def mx_expert_bwd(dY, X, a, b, h, Wq: dict, quant=True, bf16=True):
-    """Backward of mx_expert_fwd for one expert's rows (a, b, h as stored): returns dX,
-    dW1, dW3, dW2.  dh = q(dY) q_d(W2); dW2 = q_r(dY)^T q_r(h); [da|db] from dh and the
-    stored a, b (stored bf16); dX = q([da|db]) q_f([W1; W3]); [dW1; dW3] =
-    q_r([da|db])^T q_r(X)  (q_r: blocks along the expert's rows)."""
+def mx_ffn_bwd(dyp, xp, a, b, h, W1, W3, W2, offsets, quant=True, bf16=True, scope=DEFAULT_SCOPE):
+    """Backward of mx_ffn_fwd from the stored a, b, h and the routed gradient dyp [R, d]:
+    dh = dY W2 (dgrad2); dW2 = dY^T h (wgrad2); [da | db] from dh and a, b (stored bf16);
+    dx_perm = [da | db] [W1; W3] (dgrad1, one reduction over 2f); [dW1; dW3] =
+    [da | db]^T X (wgrad1).  Returns dx_perm, dW1, dW3, dW2, dab as stored."""
     from oracle import moe_ref as ref
     rnd = bf16_round if bf16 else (lambda z: z)
-    f = Wq["W1"].shape[0]
-    dh = _q_rows(dY, quant) @ Wq["W2t"]
-    dW2 = rnd(_q_cols(dY, quant).T @ _q_cols(h, quant))
+    q = lambda name: quant and name in scope  # noqa: E731
+    f = np.asarray(W1).shape[1]
+    dh = mx_gemm_dgrad(dyp, W2, offsets, q("dgrad2"))
+    dW2 = rnd(mx_gemm_wgrad(dyp, h, offsets, q("wgrad2")))
     s = ref.sigmoid(a)
     dab = rnd(np.concatenate([dh * b * s * (1.0 + a * (1.0 - s)), dh * a * s], axis=1))
-    dX = rnd(_q_rows(dab, quant) @ Wq["W13t"])
-    dW13 = rnd(_q_cols(dab, quant).T @ _q_cols(X, quant))
-    return dX, dW13[:f], dW13[f:], dW2
+    W13 = np.concatenate([np.asarray(W1, dtype=np.float64), np.asarray(W3, dtype=np.float64)], axis=1)
+    dxp = rnd(mx_gemm_dgrad(dab, W13, offsets, q("dgrad1")))
+    dW13 = rnd(mx_gemm_wgrad(dab, xp, offsets, q("wgrad1")))
+    return dxp, dW13[:, :f], dW13[:, f:], dW2, dab
 
 
-def mx_layer(x, W1, W3, W2, k, topk_idx, gates, dy, quant=True, bf16=True, shared=None):
-    """Whole layer forward + backward with MXFP8 expert GEMMs, for tokens that arrive
-    routed (topk_idx, gates given).  Returns a dict like moe_ref's forward/backward.
-    shared: (W1s, W3s, W2s) of a shared expert run with the same MXFP8 GEMMs on every
-    token; its output (bf16, as stored) joins the combine and its input gradient the
-    un-permute sum."""
+def mx_layer(x, W1, W3, W2, k, topk_idx, gates, dy, quant=True, bf16=True, shared=None, scope=DEFAULT_SCOPE):
+    """Whole layer forward + backward with the expert GEMMs of `scope` in MXFP8, for tokens
+    that arrive routed (topk_idx, gates given).  Returns a dict like moe_ref's
+    forward/backward.  shared: (W1s, W3s, W2s) of a shared expert run with the same GEMMs
+    on every token (one group of T rows); its output (bf16, as stored) joins the combine
+    and its input gradient the un-permute sum."""
     from oracle import moe_ref as ref
     rnd = bf16_round if bf16 else (lambda z: z)
     W1, W3, W2 = ref.f64(W1), ref.f64(W3), ref.f64(W2)
@@ -247,37 +310,26 @@ def mx_layer(x, W1, W3, W2, k, topk_idx, gates, dy, quant=True, bf16=True, share
     g = ref.f64(gates)
     counts, offsets, slot_row, row_src = ref.dispatch(idx, E)
     xp = ref.permute(x, row_src)
-    R, d = xp.shape
-    f = W1.shape[1]
-    Wq = [mx_expert_weights(W1[e], W3[e], W2[e], quant) if counts[e] else None for e in range(E)]
-    a = np.zeros((R, f)); b = np.zeros((R, f)); h = np.zeros((R, f)); yp = np.zeros((R, d))
-    for e in range(E):
-        lo, hi = offsets[e], offsets[e + 1]
-        if hi > lo:
-            a[lo:hi], b[lo:hi], h[lo:hi], yp[lo:hi] = mx_expert_fwd(xp[lo:hi], Wq[e], quant, bf16)
+    a, b, h, yp = mx_ffn_fwd(xp, W1, W3, W2, offsets, quant, bf16, scope)
     ys = None
     if shared is not None:
-        Wq_s = mx_expert_weights(ref.f64(shared[0])[0], ref.f64(shared[1])[0], ref.f64(shared[2])[0], quant)
         xs = ref.f64(x)
-        a_s, b_s, h_s, ys = mx_expert_fwd(xs, Wq_s, quant, bf16)
+        Ws = [ref.f64(w) for w in shared]
+        off_s = [0, xs.shape[0]]
+        a_s, b_s, h_s, ys = mx_ffn_fwd(xs, *Ws, off_s, quant, bf16, scope)
     y = ref.combine(yp, g, slot_row)
     y = rnd(y if ys is None else ys + y)
     dyp, dgates = ref.combine_bwd(dy, yp, g, slot_row)
     dyp = rnd(dyp)
-    dxp = np.zeros((R, d)); dW1 = np.zeros_like(W1); dW3 = np.zeros_like(W3); dW2 = np.zeros_like(W2)
-    for e in range(E):
-        lo, hi = offsets[e], offsets[e + 1]
-        if hi > lo:
-            dxp[lo:hi], dW1[e], dW3[e], dW2[e] = mx_expert_bwd(dyp[lo:hi], xp[lo:hi], a[lo:hi], b[lo:hi], h[lo:hi],
-                                                               Wq[e], quant, bf16)
+    dxp, dW1, dW3, dW2, dab = mx_ffn_bwd(dyp, xp, a, b, h, W1, W3, W2, offsets, quant, bf16, scope)
     out = {}
     dx_add = None
     if shared is not None:
-        dx_s, dW1s, dW3s, dW2s = mx_expert_bwd(bf16_round(ref.f64(dy)) if bf16 else ref.f64(dy), xs, a_s, b_s, h_s,
-                                               Wq_s, quant, bf16)
-        dx_add = rnd(dx_s)
-        out.update(dW1s=dW1s[None], dW3s=dW3s[None], dW2s=dW2s[None], dx_s=dx_add, y_s=ys)
+        dys = bf16_round(ref.f64(dy)) if bf16 else ref.f64(dy)
+        dx_s, dW1s, dW3s, dW2s, _ = mx_ffn_bwd(dys, xs, a_s, b_s, h_s, *Ws, off_s, quant, bf16, scope)
+        dx_add = dx_s
+        out.update(dW1s=dW1s, dW3s=dW3s, dW2s=dW2s, dx_s=dx_add, y_s=ys)
     dx = rnd(ref.unpermute_sum(dxp, slot_row, dx_add))
     out.update(dict(counts=counts, offsets=offsets, slot_row=slot_row, x_perm=xp, a=a, b=b, h=h, y_perm=yp, y=y,
-                    dgates=dgates, dx_perm=dxp, dW1=dW1, dW3=dW3, dW2=dW2, dx=dx))
+                    dgates=dgates, dab=dab, dx_perm=dxp, dW1=dW1, dW3=dW3, dW2=dW2, dx=dx))
     return out

@@ -85,6 +85,27 @@ def test_gates_closed_forms():
     assert (np.diff(g4, axis=1) <= 0).all()          # value-descending order
 
 
+def test_router_bias_shifts_selection_and_gates():
+    """A per-expert bias adds to every token's score: +12 on expert 2 puts it first for
+    every token, -12 on expert 4 keeps it out, and the gates are the softmax of the
+    biased scores of the chosen experts (scipy's softmax over a torch matmul)."""
+    rng = np.random.default_rng(41)
+    x = rng.standard_normal((50, 16))
+    Wr = rng.standard_normal((6, 16)) * 0.05
+    bias = np.zeros(6)
+    bias[2], bias[4] = 12.0, -12.0
+    L = ref.router_logits(x, Wr, bias)
+    idx, g = ref.topk_gates(L, 3)
+    assert (idx[:, 0] == 2).all() and not (idx == 4).any()
+    raw = (torch.tensor(x) @ torch.tensor(Wr).T).numpy()
+    chosen = np.take_along_axis(raw, idx.astype(np.int64), axis=1) + bias[idx]
+    assert np.allclose(g, scipy.special.softmax(chosen, axis=1), rtol=1e-12, atol=0)
+    assert (g[:, 0] > 0.99).all()
+    fw = ref.layer_forward(x, rng.standard_normal((6, 8, 16)), rng.standard_normal((6, 8, 16)),
+                           rng.standard_normal((6, 16, 8)), 3, Wr=Wr, bias=bias)
+    assert (fw["counts"][2] == 50) and fw["counts"][4] == 0
+
+
 # ------------------------------------------------------------------ dispatch
 def _dispatch_loop(idx, E):
     T, k = idx.shape

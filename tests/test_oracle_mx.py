@@ -118,28 +118,137 @@ def test_mx_layer_without_quantisation_is_the_plain_layer():
         assert np.allclose(out[key], want, rtol=1e-12, atol=1e-12), key
 
 
-def test_mx_layer_on_grid_operands_forward_gemm_exact():
-    """Operands already on the MXFP8 grid quantise to themselves: the first forward GEMM
-    of the MXFP8 layer then equals the unquantised one exactly."""
-    x, W1, W3, W2, dy, idx, g = _mx_case(2)
-    # snap x and W1/W3 onto the grid (quantise once); a second quantisation is the identity
-    xg = mx.dequantize_rows(*mx.quantize_rows(x))
-    W1g = mx.dequantize_rows(*mx.quantize_rows(W1.reshape(-1, 64))).reshape(W1.shape)
-    W3g = mx.dequantize_rows(*mx.quantize_rows(W3.reshape(-1, 64))).reshape(W3.shape)
-    assert np.array_equal(mx.dequantize_rows(*mx.quantize_rows(xg)), xg)
-    Wq = mx.mx_expert_weights(W1g[0], W3g[0], W2[0])
-    a_q, b_q, _, _ = mx.mx_expert_fwd(xg[:10], Wq, quant=True, bf16=False)
-    assert np.array_equal(a_q, xg[:10] @ W1g[0].T) and np.array_equal(b_q, xg[:10] @ W3g[0].T)
+# ------------------------------------------------------------------ per-GEMM quantisation axes
+# Operands snapped onto the MXFP8 grid along one GEMM's reduction axis quantise to
+# themselves, so that GEMM must return the exact fp64 product.  Each operand also spans a
+# range of 2^+-12 across the other axis, so blocking it along the wrong axis pushes the
+# small entries of a block into E4M3's subnormal range, moves them off the grid and
+# changes the product; every test checks that the wrong axis does change it.
+
+def _wide(rng, shape, axis):
+    """Gaussian entries, each slice along `axis` scaled by its own power of two in 2^[-12, 12]."""
+    v = rng.standard_normal(shape)
+    sc_shape = [1] * len(shape)
+    sc_shape[axis] = shape[axis]
+    return v * np.exp2(rng.integers(-12, 13, size=sc_shape).astype(np.float64))
+
+
+def test_gemm_fwd_blocks_along_the_shared_width():
+    rng = np.random.default_rng(31)
+    off = [0, 40, 40, 97]                              # three experts, one empty, ragged
+    K, N = 96, 64
+    A = mx.q_along_rows(_wide(rng, (97, K), 0))        # rows of A: 2^+-12 apart
+    W = np.stack([mx.q_along_rows(_wide(rng, (N, K), 0)) for _ in range(3)])
+    exact = np.zeros((97, N))
+    for e in range(3):
+        exact[off[e]:off[e + 1]] = A[off[e]:off[e + 1]] @ W[e].T
+    assert np.array_equal(mx.mx_gemm_fwd(A, W, off), exact)
+    wrong = mx.q_down_cols(A[:40]) @ mx.q_down_cols(W[0]).T
+    assert not np.array_equal(wrong, exact[:40])
+
+
+def test_gemm_dgrad_blocks_weights_down_their_columns():
+    rng = np.random.default_rng(32)
+    off = [0, 33, 90]
+    K, N = 128, 64
+    A = mx.q_along_rows(_wide(rng, (90, K), 0))
+    W = np.stack([mx.q_down_cols(_wide(rng, (K, N), 1)) for _ in range(2)])   # [E, K, N]
+    exact = np.zeros((90, N))
+    for e in range(2):
+        exact[off[e]:off[e + 1]] = A[off[e]:off[e + 1]] @ W[e]
+    assert np.array_equal(mx.mx_gemm_dgrad(A, W, off), exact)
+    wrong = A[:33] @ mx.q_along_rows(W[0])              # weights blocked along their rows
+    assert not np.array_equal(wrong, exact[:33])
+    assert np.array_equal(mx.q_down_cols(W[0]), W[0])
+    assert not np.array_equal(mx.q_along_rows(W[0]), W[0])
+
+
+def test_gemm_wgrad_blocks_down_each_experts_rows():
+    """Blocks of 32 rows restart at every expert: experts of 45, 0, 70 and 13 rows whose
+    magnitudes differ by 2^20 are each on the grid in their own blocks; blocking the packed
+    rows across the expert boundaries (or along the columns) changes dW."""
+    rng = np.random.default_rng(33)
+    counts = [45, 0, 70, 13]
+    off = np.concatenate([[0], np.cumsum(counts)])
+    R, M, N = int(off[-1]), 64, 96
+    mag = np.exp2(np.array([10.0, 0.0, -10.0, 6.0]))
+    A = np.zeros((R, M)); B = np.zeros((R, N))
+    for e in range(4):
+        lo, hi = off[e], off[e + 1]
+        A[lo:hi] = _wide(rng, (hi - lo, M), 1) * mag[e]
+        B[lo:hi] = _wide(rng, (hi - lo, N), 1) / mag[e]
+    A = mx.q_down_cols(A, off)
+    B = mx.q_down_cols(B, off)
+    exact = np.zeros((4, M, N))
+    for e in range(4):
+        exact[e] = A[off[e]:off[e + 1]].T @ B[off[e]:off[e + 1]]
+    got = mx.mx_gemm_wgrad(A, B, off)
+    assert np.array_equal(got, exact)
+    assert not got[1].any()                                     # the empty expert
+    # the same operands blocked as one segment over all packed rows: the blocks that
+    # straddle an expert boundary take the larger expert's scale
+    A1, B1 = mx.q_down_cols(A), mx.q_down_cols(B)
+    across = [A1[off[e]:off[e + 1]].T @ B1[off[e]:off[e + 1]] for e in range(4)]
+    assert not all(np.array_equal(across[e], exact[e]) for e in range(4))
+    wrong = mx.q_along_rows(A[:45]).T @ mx.q_along_rows(B[:45])
+    assert not np.array_equal(wrong, exact[0])
+
+
+# ------------------------------------------------------------------ the layer's MXFP8 scope
+# Which outputs each GEMM reaches: a quantised GEMM may change exactly these, and must
+# leave every other output bit-identical with the layer that quantises nothing.
+_REACH = {
+    "gemm1": {"a", "b", "h", "y_perm", "y", "dgates", "dab", "dx_perm", "dx", "dW1", "dW3", "dW2"},
+    "gemm2": {"y_perm", "y", "dgates"},
+    "dgrad2": {"dab", "dx_perm", "dx", "dW1", "dW3"},
+    "wgrad2": {"dW2"},
+    "dgrad1": {"dx_perm", "dx"},
+    "wgrad1": {"dW1", "dW3"},
+}
+
+
+@pytest.mark.parametrize("gemm", mx.GEMMS)
+def test_scope_reaches_only_the_gemms_outputs(gemm):
+    x, W1, W3, W2, dy, idx, g = _mx_case(4, T=48, d=64, f=64, E=4, k=2)
+    base = mx.mx_layer(x, W1, W3, W2, 2, idx, g, dy, scope=frozenset())
+    one = mx.mx_layer(x, W1, W3, W2, 2, idx, g, dy, scope=frozenset([gemm]))
+    keys = set(_REACH["gemm1"])
+    changed = {k for k in keys if not np.array_equal(one[k], base[k])}
+    assert changed == _REACH[gemm], (gemm, changed ^ _REACH[gemm])
+
+
+def test_default_scope_passes_each_output_through_one_quantised_gemm():
+    reach = [_REACH[gm] for gm in mx.DEFAULT_SCOPE]
+    for i, r in enumerate(reach):
+        for r2 in reach[i + 1:]:
+            assert not (r & r2)
+
+
+@pytest.mark.parametrize("scope", [frozenset(), mx.DEFAULT_SCOPE, mx.ALL_GEMMS], ids=["none", "default", "all"])
+def test_stored_tensors_are_bf16(scope):
+    """Every activation and gradient the device stores in bf16 is a bf16 value in the
+    oracle too (the next GEMM quantises exactly those values)."""
+    x, W1, W3, W2, dy, idx, g = _mx_case(5, T=40, d=64, f=64, E=4, k=2)
+    out = mx.mx_layer(x, W1, W3, W2, 2, idx, g, dy, scope=scope)
+    for key in ("a", "b", "h", "y_perm", "y", "dab", "dx_perm", "dx", "dW1", "dW3", "dW2"):
+        assert np.array_equal(mx.bf16_round(out[key]), out[key]), key
+        assert np.abs(out[key]).max() > 0, key
 
 
 def test_mx_layer_error_is_the_formats():
-    """Quantisation changes the layer by a few percent (a 3-bit mantissa), not by more."""
+    """A quantised GEMM changes what it reaches by a few percent (a 3-bit mantissa): more
+    than bf16 rounding alone, far less than the values themselves."""
     x, W1, W3, W2, dy, idx, g = _mx_case(3, T=64, d=128, f=128)
-    q = mx.mx_layer(x, W1, W3, W2, 2, idx, g, dy, quant=True)
     p = mx.mx_layer(x, W1, W3, W2, 2, idx, g, dy, quant=False, bf16=False)
-    for key in ("y", "dx", "dW1", "dW3", "dW2"):
-        rel = np.abs(q[key] - p[key]).max() / np.abs(p[key]).max()
-        assert 1e-3 < rel < 0.25, (key, rel)
+    for scope in (mx.DEFAULT_SCOPE, mx.ALL_GEMMS):
+        q = mx.mx_layer(x, W1, W3, W2, 2, idx, g, dy, scope=scope)
+        reached = set().union(*(_REACH[gm] for gm in scope))
+        for key in ("y", "dx", "dW1", "dW3", "dW2"):
+            rel = np.abs(q[key] - p[key]).max() / np.abs(p[key]).max()
+            if key in reached:
+                assert 1e-2 < rel < 0.25, (key, rel)
+            else:
+                assert rel < 1e-2, (key, rel)
 
 
 def test_bf16_round_matches_torch():
