@@ -60,11 +60,32 @@ typedef enum {
 
 typedef enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_MXFP8 = 2 } moe_dtype;
 
+/* The six expert GEMMs, as bits of moe_shape.mx_scope. */
+#define MOE_MX_GEMM1 1   /* a, b = X W1^T, X W3^T (+ SwiGLU) */
+#define MOE_MX_GEMM2 2   /* y_perm = h W2^T */
+#define MOE_MX_DGRAD2 4  /* dh = dy_perm W2 (+ SwiGLU gradient) */
+#define MOE_MX_WGRAD2 8  /* dW2 = dy_perm^T h */
+#define MOE_MX_DGRAD1 16 /* dx_perm = [da | db] [W1; W3] */
+#define MOE_MX_WGRAD1 32 /* [dW1; dW3] = [da | db]^T X */
+#define MOE_MX_ALL 63
+/* The default MXFP8 scope: the two GEMMs that reduce over the hidden width and produce the
+ * d-wide rows returned to the tokens (y_perm and dx_perm).  Each output and gradient of the
+ * layer then passes through at most one E4M3-quantised GEMM, which keeps the layer within
+ * 6e-2 (normwise) of the unquantised result; with all six, two or three quantised GEMMs in
+ * series put it 6-14% away.  The pages enable MXFP8 on selected operations, where it helped
+ * most (bigchange.ai, "Olmo-core 3 открывает стек обучения MoE от Ai2…", section "Главное
+ * изменение"; ettayeb.fr, "Olmo-core 3 ouvre l'entraînement des MoE…", section "Trois
+ * parallélismes, trois optimisations de routage"). */
+#define MOE_MX_DEFAULT (MOE_MX_GEMM2 | MOE_MX_DGRAD1)
+
 /* All sizes are known on the host; nothing about the routing is. */
 typedef struct {
   int32_t T, d, f, E, k;
-  int32_t act;   /* MOE_F32 or MOE_BF16 */
-  int32_t gemm;  /* grouped-GEMM arithmetic: MOE_F32 (act F32), MOE_BF16 or MOE_MXFP8 (act BF16) */
+  int32_t act;       /* MOE_F32 or MOE_BF16 */
+  int32_t gemm;      /* grouped-GEMM arithmetic: MOE_F32 (act F32), MOE_BF16 or MOE_MXFP8 (act BF16) */
+  int32_t mx_scope;  /* with gemm = MOE_MXFP8: the MOE_MX_* bits of the expert GEMMs that take E4M3
+                        operands (0 means MOE_MX_DEFAULT); the other expert GEMMs run bf16.  Must be
+                        0 for other gemm values. */
 } moe_shape;
 
 /* Bits OR-ed into *dev_err by moe_route_given. */

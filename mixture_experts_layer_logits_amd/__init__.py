@@ -18,6 +18,12 @@ LIB_PATH = os.path.join(_HERE, "libmoe_mi355x.so")
 
 MOE_F32, MOE_BF16, MOE_MXFP8 = 0, 1, 2
 MOE_DEVERR_EXPERT_RANGE, MOE_DEVERR_DUPLICATE = 1, 2
+# expert GEMMs as bits of moe_shape.mx_scope (include/moe.h)
+MOE_MX_GEMM1, MOE_MX_GEMM2, MOE_MX_DGRAD2, MOE_MX_WGRAD2, MOE_MX_DGRAD1, MOE_MX_WGRAD1 = 1, 2, 4, 8, 16, 32
+MOE_MX_ALL = 63
+MOE_MX_DEFAULT = MOE_MX_GEMM2 | MOE_MX_DGRAD1
+MX_BITS = {"gemm1": MOE_MX_GEMM1, "gemm2": MOE_MX_GEMM2, "dgrad2": MOE_MX_DGRAD2, "wgrad2": MOE_MX_WGRAD2,
+           "dgrad1": MOE_MX_DGRAD1, "wgrad1": MOE_MX_WGRAD1}
 
 
 class MoeError(RuntimeError):
@@ -29,17 +35,26 @@ class MoeError(RuntimeError):
 class moe_shape(ctypes.Structure):
     _fields_ = [("T", ctypes.c_int32), ("d", ctypes.c_int32), ("f", ctypes.c_int32),
                 ("E", ctypes.c_int32), ("k", ctypes.c_int32), ("act", ctypes.c_int32),
-                ("gemm", ctypes.c_int32)]
+                ("gemm", ctypes.c_int32), ("mx_scope", ctypes.c_int32)]
 
     def __repr__(self):
         return (f"moe_shape(T={self.T}, d={self.d}, f={self.f}, E={self.E}, k={self.k}, "
-                f"act={self.act}, gemm={self.gemm})")
+                f"act={self.act}, gemm={self.gemm}, mx_scope={self.mx_scope})")
 
 
-def make_shape(T, d, f, E, k, act=MOE_BF16, gemm=None) -> moe_shape:
+def make_shape(T, d, f, E, k, act=MOE_BF16, gemm=None, mx_scope=0) -> moe_shape:
+    """mx_scope: MOE_MX_* bits of the expert GEMMs that run MXFP8 when gemm is MOE_MXFP8
+    (0: MOE_MX_DEFAULT); must be 0 otherwise."""
     if gemm is None:
         gemm = MOE_F32 if act == MOE_F32 else MOE_BF16
-    return moe_shape(T, d, f, E, k, act, gemm)
+    return moe_shape(T, d, f, E, k, act, gemm, mx_scope)
+
+
+def mx_scope_bits(shape: moe_shape) -> int:
+    """The expert GEMMs that run MXFP8 under `shape`, as MOE_MX_* bits (0 if none)."""
+    if shape.gemm != MOE_MXFP8:
+        return 0
+    return shape.mx_scope or MOE_MX_DEFAULT
 
 
 _VP = ctypes.c_void_p

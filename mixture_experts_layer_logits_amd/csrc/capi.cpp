@@ -50,7 +50,16 @@ moe_status check_shape(const moe_shape* s) {
   if ((s->gemm == MOE_BF16 || s->gemm == MOE_MXFP8) && s->act != MOE_BF16) return MOE_EUNSUPPORTED;
   if (s->gemm != MOE_F32 && s->gemm != MOE_BF16 && s->gemm != MOE_MXFP8) return MOE_EUNSUPPORTED;
   if (s->gemm == MOE_MXFP8 && (s->d % 128 != 0 || s->f % 128 != 0)) return MOE_EINVAL;
+  if (s->mx_scope < 0 || (s->mx_scope & ~MOE_MX_ALL) != 0) return MOE_EINVAL;
+  if (s->gemm != MOE_MXFP8 && s->mx_scope != 0) return MOE_EINVAL;
   return MOE_OK;
+}
+
+// Does the expert GEMM `bit` (MOE_MX_*) take MXFP8 operands under this shape?
+bool mx_on(const moe_shape* s, int bit) {
+  if (s->gemm != MOE_MXFP8) return false;
+  const int scope = s->mx_scope ? s->mx_scope : MOE_MX_DEFAULT;
+  return (scope & bit) != 0;
 }
 
 // every pointer non-null and 16-byte aligned
@@ -108,7 +117,7 @@ size_t moe_workspace_size(const moe_shape* s) {
     const size_t r = router_dw_workspace_bytes(s->T, s->d, s->E);
     if (r > b) b = r;
   }
-  if (s->gemm == MOE_BF16) {
+  if (s->gemm == MOE_BF16 || s->gemm == MOE_MXFP8) {  // bf16 weight gradients (any GEMM outside the MXFP8 scope)
     const size_t w = wgrad_split_workspace_bytes(gshape(s));
     if (w > b) b = w;
   }
@@ -163,11 +172,11 @@ moe_status moe_ffn_gemm1_fwd(const moe_shape* s, const void* x_perm, const void*
   MOE_TRY(check_rows(s, {x_perm, ab, h}));
   if (!offsets) return MOE_ENULL;
   const GemmShape g = gshape(s);
-  switch (s->gemm) {
-    case MOE_F32:
+  switch (s->gemm == MOE_F32 ? 0 : mx_on(s, MOE_MX_GEMM1) ? 2 : 1) {
+    case 0:
       return launched(gemm1_fwd_f32(g, offsets, (const float*)x_perm, (const float*)W1, (const float*)W3,
                                     (float*)ab, (float*)h, S(st)));
-    case MOE_BF16:
+    case 1:
       return launched(gemm1_fwd_bf16(g, offsets, (const bf16_t*)x_perm, (const bf16_t*)W1, (const bf16_t*)W3,
                                      (bf16_t*)ab, (bf16_t*)h, S(st)));
     default:
@@ -185,10 +194,10 @@ moe_status moe_ffn_gemm2_fwd(const moe_shape* s, const void* h, const void* W2, 
   MOE_TRY(check_rows(s, {h, y_perm}));
   if (!offsets) return MOE_ENULL;
   const GemmShape g = gshape(s);
-  switch (s->gemm) {
-    case MOE_F32:
+  switch (s->gemm == MOE_F32 ? 0 : mx_on(s, MOE_MX_GEMM2) ? 2 : 1) {
+    case 0:
       return launched(gemm2_fwd_f32(g, offsets, (const float*)h, (const float*)W2, (float*)y_perm, S(st)));
-    case MOE_BF16:
+    case 1:
       return launched(gemm2_fwd_bf16(g, offsets, (const bf16_t*)h, (const bf16_t*)W2, (bf16_t*)y_perm, S(st)));
     default:
       if (!ws) return MOE_ENULL;
@@ -229,11 +238,11 @@ moe_status moe_ffn_dgrad2(const moe_shape* s, const void* dy_perm, const void* W
   MOE_TRY(check_rows(s, {dy_perm, ab, dab}));
   if (!offsets) return MOE_ENULL;
   const GemmShape g = gshape(s);
-  switch (s->gemm) {
-    case MOE_F32:
+  switch (s->gemm == MOE_F32 ? 0 : mx_on(s, MOE_MX_DGRAD2) ? 2 : 1) {
+    case 0:
       return launched(dgrad2_f32(g, offsets, (const float*)dy_perm, (const float*)W2, (const float*)ab, (float*)dab,
                                  S(st)));
-    case MOE_BF16:
+    case 1:
       return launched(dgrad2_bf16(g, offsets, (const bf16_t*)dy_perm, (const bf16_t*)W2, (const bf16_t*)ab,
                                   (bf16_t*)dab, S(st)));
     default:
@@ -251,10 +260,10 @@ moe_status moe_ffn_wgrad2(const moe_shape* s, const void* h, const void* dy_perm
   MOE_TRY(check_rows(s, {h, dy_perm}));
   if (!offsets) return MOE_ENULL;
   const GemmShape g = gshape(s);
-  switch (s->gemm) {
-    case MOE_F32:
+  switch (s->gemm == MOE_F32 ? 0 : mx_on(s, MOE_MX_WGRAD2) ? 2 : 1) {
+    case 0:
       return launched(wgrad2_f32(g, offsets, (const float*)h, (const float*)dy_perm, (float*)dW2, S(st)));
-    case MOE_BF16:
+    case 1:
       if (g.E == 1 && ws_bytes < wgrad_split_workspace_bytes(g)) return MOE_EWORKSPACE;
       return launched(wgrad2_bf16(g, offsets, (const bf16_t*)h, (const bf16_t*)dy_perm, (bf16_t*)dW2, ws, S(st)));
     default:
@@ -271,11 +280,11 @@ moe_status moe_ffn_dgrad1(const moe_shape* s, const void* dab, const void* W1, c
   MOE_TRY(check_rows(s, {dab, dx_perm}));
   if (!offsets) return MOE_ENULL;
   const GemmShape g = gshape(s);
-  switch (s->gemm) {
-    case MOE_F32:
+  switch (s->gemm == MOE_F32 ? 0 : mx_on(s, MOE_MX_DGRAD1) ? 2 : 1) {
+    case 0:
       return launched(dgrad1_f32(g, offsets, (const float*)dab, (const float*)W1, (const float*)W3, (float*)dx_perm,
                                  S(st)));
-    case MOE_BF16:
+    case 1:
       return launched(dgrad1_bf16(g, offsets, (const bf16_t*)dab, (const bf16_t*)W1, (const bf16_t*)W3,
                                   (bf16_t*)dx_perm, S(st)));
     default:
@@ -293,11 +302,11 @@ moe_status moe_ffn_wgrad1(const moe_shape* s, const void* x_perm, const void* da
   MOE_TRY(check_rows(s, {x_perm, dab}));
   if (!offsets) return MOE_ENULL;
   const GemmShape g = gshape(s);
-  switch (s->gemm) {
-    case MOE_F32:
+  switch (s->gemm == MOE_F32 ? 0 : mx_on(s, MOE_MX_WGRAD1) ? 2 : 1) {
+    case 0:
       return launched(wgrad1_f32(g, offsets, (const float*)x_perm, (const float*)dab, (float*)dW1, (float*)dW3,
                                  S(st)));
-    case MOE_BF16:
+    case 1:
       if (g.E == 1 && ws_bytes < wgrad_split_workspace_bytes(g)) return MOE_EWORKSPACE;
       return launched(wgrad1_bf16(g, offsets, (const bf16_t*)x_perm, (const bf16_t*)dab, (bf16_t*)dW1,
                                   (bf16_t*)dW3, ws, S(st)));
@@ -403,7 +412,7 @@ moe_status moe_ffn_gemm1_fwd_mx(const moe_shape* s, const uint8_t* xq_rows, cons
                                 const void* W3, const int32_t* offsets, void* ab, void* h, void* ws, size_t ws_bytes,
                                 void* st) {
   MOE_TRY(check_shape(s));
-  if (s->gemm != MOE_MXFP8) return MOE_EUNSUPPORTED;
+  if (!mx_on(s, MOE_MX_GEMM1)) return MOE_EUNSUPPORTED;
   MOE_TRY(check_ptrs({W1, W3}));
   MOE_TRY(check_rows(s, {xq_rows, xs_rows, ab, h}));
   if (!offsets || !ws) return MOE_ENULL;
@@ -416,7 +425,7 @@ moe_status moe_ffn_gemm1_fwd_mx(const moe_shape* s, const uint8_t* xq_rows, cons
 moe_status moe_ffn_dgrad2_mx(const moe_shape* s, const uint8_t* dyq_rows, const uint8_t* dys_rows, const void* W2,
                              const void* ab, const int32_t* offsets, void* dab, void* ws, size_t ws_bytes, void* st) {
   MOE_TRY(check_shape(s));
-  if (s->gemm != MOE_MXFP8) return MOE_EUNSUPPORTED;
+  if (!mx_on(s, MOE_MX_DGRAD2)) return MOE_EUNSUPPORTED;
   MOE_TRY(check_ptrs({W2}));
   MOE_TRY(check_rows(s, {dyq_rows, dys_rows, ab, dab}));
   if (!offsets || !ws) return MOE_ENULL;
@@ -429,7 +438,7 @@ moe_status moe_ffn_dgrad2_mx(const moe_shape* s, const uint8_t* dyq_rows, const 
 moe_status moe_ffn_wgrad2_mx(const moe_shape* s, const void* h, const uint8_t* dyq_cols, const uint8_t* dys_cols,
                              const int32_t* offsets, void* dW2, void* ws, size_t ws_bytes, void* st) {
   MOE_TRY(check_shape(s));
-  if (s->gemm != MOE_MXFP8) return MOE_EUNSUPPORTED;
+  if (!mx_on(s, MOE_MX_WGRAD2)) return MOE_EUNSUPPORTED;
   MOE_TRY(check_ptrs({dW2, dyq_cols, dys_cols}));
   MOE_TRY(check_rows(s, {h}));
   if (!offsets || !ws) return MOE_ENULL;
@@ -441,7 +450,7 @@ moe_status moe_ffn_wgrad2_mx(const moe_shape* s, const void* h, const uint8_t* d
 moe_status moe_ffn_wgrad1_mx(const moe_shape* s, const uint8_t* xq_cols, const uint8_t* xs_cols, const void* dab,
                              const int32_t* offsets, void* dW1, void* dW3, void* ws, size_t ws_bytes, void* st) {
   MOE_TRY(check_shape(s));
-  if (s->gemm != MOE_MXFP8) return MOE_EUNSUPPORTED;
+  if (!mx_on(s, MOE_MX_WGRAD1)) return MOE_EUNSUPPORTED;
   MOE_TRY(check_ptrs({dW1, dW3, xq_cols, xs_cols}));
   MOE_TRY(check_rows(s, {dab}));
   if (!offsets || !ws) return MOE_ENULL;

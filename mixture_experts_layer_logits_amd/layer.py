@@ -23,13 +23,17 @@ one shared expert).  It runs as a one-group call of the same grouped GEMMs over 
 token rows (E = 1, k = 1, offsets [0, T]); its output enters through moe_combine's
 ``y_add`` and its input gradient through moe_permute_bwd's ``dx_add``.
 
-MXFP8 dispatch (``mx_dispatch``, on by default for MXFP8 expert GEMMs): moe_permute_mx
-and moe_combine_bwd_mx write the routed rows of x and of the output gradient only as
-E4M3 codes with their block scales, in the row layout (forward / data-gradient GEMMs)
-and the per-expert column layout (weight-gradient GEMMs), so no bf16 x_perm or dy_perm
-exists and the GEMMs quantise neither (MXFP8 for the data moved to the experts: unite.ai,
-section "Παραλληλισμός, Ακρίβεια και Τεχνικές Μνήμης").  The results are bit-identical
-with the bf16 dispatch.
+MXFP8 scope (``mx_scope``, MOE_MX_* bits; MOE_MX_DEFAULT = GEMM2 and dgrad1): the expert
+GEMMs that take E4M3 operands when ``gemm`` is MOE_MXFP8; the others run bf16.
+
+MXFP8 dispatch (``mx_dispatch``; on by default when the scope holds all four GEMMs that
+read the dispatched rows: GEMM1 and wgrad1 read x's, dgrad2 and wgrad2 the output
+gradient's): moe_permute_mx and moe_combine_bwd_mx write the routed rows of x and of the
+output gradient only as E4M3 codes with their block scales, in the row layout (forward /
+data-gradient GEMMs) and the per-expert column layout (weight-gradient GEMMs), so no bf16
+x_perm or dy_perm exists and the GEMMs quantise neither (MXFP8 for the data moved to the
+experts: unite.ai, section "Παραλληλισμός, Ακρίβεια και Τεχνικές Μνήμης").  The results
+are bit-identical with the bf16 dispatch.
 
 Activation recompute (``recompute=True``): the forward keeps only ``x_perm`` of the
 expert FFN; ``ab = [a | b]`` and ``h`` live in buffers allocated for the forward's GEMM1 /
@@ -43,22 +47,27 @@ from __future__ import annotations
 
 import torch
 
-from . import (MOE_BF16, MOE_F32, MOE_MXFP8, make_shape, moe_combine, moe_combine_bwd, moe_combine_bwd_mx,
+from . import (MOE_BF16, MOE_F32, MOE_MX_DGRAD2, MOE_MX_GEMM1, MOE_MX_WGRAD1, MOE_MX_WGRAD2, MOE_MXFP8,
+               make_shape, moe_combine, moe_combine_bwd, moe_combine_bwd_mx,
                moe_ffn_dgrad1, moe_ffn_dgrad2, moe_ffn_dgrad2_mx, moe_ffn_gemm1_fwd, moe_ffn_gemm1_fwd_mx,
                moe_ffn_gemm2_fwd, moe_ffn_wgrad1, moe_ffn_wgrad1_mx, moe_ffn_wgrad2, moe_ffn_wgrad2_mx, moe_mx_cols_ld,
                moe_permute, moe_permute_bwd, moe_permute_mx, moe_route, moe_route_bwd, moe_route_given, moe_router_bwd,
-               moe_router_fwd, moe_workspace_size)
+               moe_router_fwd, moe_workspace_size, mx_scope_bits)
+
+# the GEMMs that read the dispatched rows: all four must run MXFP8 for the MXFP8 dispatch
+_DISPATCH_READERS = MOE_MX_GEMM1 | MOE_MX_WGRAD1 | MOE_MX_DGRAD2 | MOE_MX_WGRAD2
 
 
 class MoEExpertLayer:
     def __init__(self, T, d, f, E, k, act=MOE_BF16, gemm=None, device="cuda", recompute=False, shared_f=0,
-                 mx_dispatch=None):
-        self.shape = make_shape(T, d, f, E, k, act, gemm)
+                 mx_dispatch=None, mx_scope=0):
+        self.shape = make_shape(T, d, f, E, k, act, gemm, mx_scope)
         self.recompute = recompute
-        is_mx = self.shape.gemm == MOE_MXFP8
-        self.mx_dispatch = is_mx if mx_dispatch is None else bool(mx_dispatch)
-        if self.mx_dispatch and not is_mx:
-            raise ValueError("the MXFP8 dispatch needs MXFP8 expert GEMMs")
+        covers = (mx_scope_bits(self.shape) & _DISPATCH_READERS) == _DISPATCH_READERS
+        self.mx_dispatch = covers if mx_dispatch is None else bool(mx_dispatch)
+        if self.mx_dispatch and not covers:
+            raise ValueError("the MXFP8 dispatch needs GEMM1, wgrad1, dgrad2 and wgrad2 in the MXFP8 scope")
+        self.steps = 0   # forwards run so far: the autograd wrapper checks its backward sees its own
         self.shared_f = shared_f
         self.T, self.d, self.f, self.E, self.k = T, d, f, E, k
         self.R = T * k
@@ -110,7 +119,7 @@ class MoEExpertLayer:
         self._shared = None
         if shared_f:
             fs = shared_f
-            self.shape_s = make_shape(T, d, fs, 1, 1, act, gemm)
+            self.shape_s = make_shape(T, d, fs, 1, 1, act, gemm, mx_scope)
             self.offsets_s = torch.tensor([0, T], dtype=i32, device=dev)
             self.ab_s, self.h_s, self.y_s = e(T, 2 * fs), e(T, fs), e(T, d)
             self.dab_s, self.dx_s = e(T, 2 * fs), e(T, d)
@@ -124,14 +133,14 @@ class MoEExpertLayer:
             self.learned = True
             moe_router_fwd(s, x, Wr, bias, self.logits)
             moe_route(s, self.logits, self.topk_idx, self.gates, self.counts, self.offsets, self.slot_row, self.ws)
-        else:
+        else:  # the caller's ids are only read; the layer's own topk_idx buffer is left alone
             self.learned = False
-            self.topk_idx = topk_idx
             moe_route_given(s, topk_idx, self.counts, self.offsets, self.slot_row, self.dev_err, self.ws)
 
     def forward(self, x, W1, W3, W2, Wr=None, bias=None, topk_idx=None, gates=None, shared=None):
         """shared: (W1s [1, fs, d], W3s [1, fs, d], W2s [1, d, fs]) of the shared expert."""
         s = self.shape
+        self.steps += 1
         self.route(x, Wr, bias, topk_idx)
         g = self.gates if topk_idx is None else gates
         self._params = (x, W1, W3, W2, Wr, g)
@@ -225,16 +234,25 @@ class MoEExpertLayer:
 
 
 class MoEExpertFunction(torch.autograd.Function):
-    """y = MoE(x) with learned routing; gradients for x, Wr, W1, W3, W2."""
+    """y = MoE(x) with learned routing (optional constant per-expert router bias);
+    gradients for x, Wr, W1, W3, W2.  The layer's buffers hold one forward at a time, so
+    each backward must follow its own forward: a second forward through the same layer
+    before the first one's backward makes that backward raise instead of returning the
+    second forward's gradients."""
 
     @staticmethod
-    def forward(ctx, x, Wr, W1, W3, W2, layer: MoEExpertLayer):
-        y = layer.forward(x.contiguous(), W1.contiguous(), W3.contiguous(), W2.contiguous(), Wr=Wr.contiguous())
+    def forward(ctx, x, Wr, W1, W3, W2, layer: MoEExpertLayer, bias=None):
+        y = layer.forward(x.contiguous(), W1.contiguous(), W3.contiguous(), W2.contiguous(), Wr=Wr.contiguous(),
+                          bias=None if bias is None else bias.contiguous())
         ctx.layer = layer
+        ctx.step = layer.steps
         return y.clone()
 
     @staticmethod
     def backward(ctx, dy):
         L = ctx.layer
+        if L.steps != ctx.step:
+            raise RuntimeError("MoEExpertFunction: the layer ran another forward since this one; its saved "
+                               "activations are gone (one layer object per in-flight forward)")
         L.backward(dy.contiguous())
-        return L.dx.clone(), L.dWr.to(L.dtype), L.dW1.clone(), L.dW3.clone(), L.dW2.clone(), None
+        return L.dx.clone(), L.dWr.to(L.dtype), L.dW1.clone(), L.dW3.clone(), L.dW2.clone(), None, None

@@ -15,7 +15,12 @@ MOE_OK, MOE_EINVAL, MOE_ENULL, MOE_EALIGN, MOE_EWORKSPACE, MOE_EUNSUPPORTED = 0,
 
 
 class Shape(ctypes.Structure):
-    _fields_ = [(n, ctypes.c_int32) for n in ("T", "d", "f", "E", "k", "act", "gemm")]
+    _fields_ = [(n, ctypes.c_int32) for n in ("T", "d", "f", "E", "k", "act", "gemm", "mx_scope")]
+
+
+def header_defines():
+    return {m.group(1): m.group(2) for m in re.finditer(r"#define\s+(MOE_\w+)\s+(.+?)\s*(?:/\*.*)?$",
+                                                          open(HEADER).read(), flags=re.M)}
 
 
 def declared_functions():
@@ -76,6 +81,9 @@ def _route(lib, s, ptr=0x1000, ws_bytes=1 << 30):
     ((64, 128, 128, 8, 2, 1, 0), MOE_EUNSUPPORTED),  # bf16 activations with fp32 GEMMs
     ((64, 128, 128, 8, 2, 0, 1), MOE_EUNSUPPORTED),  # fp32 activations with bf16 GEMMs
     ((64, 192, 128, 8, 2, 1, 2), MOE_EINVAL),       # MXFP8 needs multiples of 128
+    ((64, 128, 128, 8, 2, 1, 2, 64), MOE_EINVAL),   # MXFP8 scope bit beyond the six GEMMs
+    ((64, 128, 128, 8, 2, 1, 2, -1), MOE_EINVAL),   # negative scope
+    ((64, 128, 128, 8, 2, 1, 1, 2), MOE_EINVAL),    # a scope on bf16 GEMMs
 ])
 def test_bad_shapes_rejected_before_launch(lib, shape, code):
     assert _route(lib, Shape(*shape)) == code
@@ -94,3 +102,28 @@ def test_null_misaligned_and_workspace(lib):
     assert lib.moe_mx_quantize(4, 33, 0, P(0), 0, P(0x1000), P(0x1000), P(0x1000), P(0)) == MOE_EINVAL
     lib.moe_status_str.restype = ctypes.c_char_p
     assert lib.moe_status_str(MOE_EWORKSPACE) == b"workspace too small"
+
+
+def test_mx_scope_constants_agree():
+    """The scope bits of the header, the binding's copies and the oracle's default scope
+    name the same GEMMs."""
+    import mixture_experts_layer_logits_amd as m
+    from oracle import mx_ref
+    h = header_defines()
+    names = {"gemm1": "MOE_MX_GEMM1", "gemm2": "MOE_MX_GEMM2", "dgrad2": "MOE_MX_DGRAD2",
+             "wgrad2": "MOE_MX_WGRAD2", "dgrad1": "MOE_MX_DGRAD1", "wgrad1": "MOE_MX_WGRAD1"}
+    for n, c in names.items():
+        assert int(h[c]) == m.MX_BITS[n] == getattr(m, c)
+    assert set(names) == set(mx_ref.GEMMS)
+    assert {n for n, b in m.MX_BITS.items() if b & m.MOE_MX_DEFAULT} == set(mx_ref.DEFAULT_SCOPE)
+    assert int(h["MOE_MX_ALL"]) == m.MOE_MX_ALL == sum(m.MX_BITS.values())
+
+
+def test_mx_scope_gates_the_mx_operand_entry_points(lib):
+    """An entry point that takes dispatched E4M3 rows refuses a shape whose scope leaves
+    its GEMM in bf16 (before touching any pointer)."""
+    P = ctypes.c_void_p
+    s = Shape(64, 128, 128, 8, 2, 1, 2, 0)          # default scope: GEMM2 and dgrad1
+    st = lib.moe_ffn_gemm1_fwd_mx(ctypes.byref(s), P(0x1000), P(0x1000), P(0x1000), P(0x1000), P(0x1000), P(0x1000),
+                                  P(0x1000), P(0x1000), ctypes.c_size_t(1 << 30), P(0))
+    assert st == MOE_EUNSUPPORTED

@@ -22,7 +22,8 @@ ROUTER = ("logits", "dlogits", "dWr", "gates", "topk_idx")  # absent or caller i
 @pytest.mark.parametrize("wname,over", [
     ("e128_k4_t8192", dict(T=512, d=256, f=192)),
     ("e32_k4_t16384_d4096_mxfp8", dict(T=300, d=256, f=256, E=8, k=4)),
-], ids=["bf16_learned", "mxfp8_given"])
+    ("e32_k4_t16384_d4096_mxfp8_all", dict(T=300, d=256, f=256, E=8, k=4)),
+], ids=["bf16_learned", "mxfp8_given", "mxfp8_all_six_dispatch"])
 def test_layer_step_graph_replays_match_eager(wname, over):
     w = workloads.scaled(workloads.WORKLOADS[wname], **over)
     inp = workloads.make_inputs(w)

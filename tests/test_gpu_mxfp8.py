@@ -1,14 +1,14 @@
 """MXFP8 path on the GPU: quantiser bytes bit-exact against the oracle; each MXFP8
-grouped GEMM against fp64 GEMMs of its dequantised operands; and the MXFP8 layer (all six
-grouped GEMMs on E4M3 operands with E8M0 block scales) within 6e-2 normwise of the fp64
-oracle of the MXFP8 method, with the format's own error against the unquantised layer
-reported beside it."""
+grouped GEMM against fp64 GEMMs of its dequantised operands; the MXFP8 layer with its
+default scope (GEMM2 and dgrad1 on E4M3 operands with E8M0 block scales) within 6e-2
+normwise of the unquantised fp64 oracle, and every scope (all six GEMMs included) against
+the emulated fp64 oracle of the MXFP8 method as a diagnostic."""
 import numpy as np
 import pytest
 import torch
 
 import workloads
-from gpu_common import TOL, host, normwise_err, oracle_for, run_layer, say
+from gpu_common import TOL, host, normwise_err, oracle_for, run_layer, say, tol_mx_emulated
 
 pytestmark = pytest.mark.gpu
 
@@ -104,6 +104,9 @@ def test_mx_quantize_segment_cols_bit_exact():
             P += npad
 
 
+MX = workloads.WORKLOADS["e32_k4_t16384_d4096_mxfp8"]          # default scope: GEMM2, dgrad1
+MX_ALL = workloads.WORKLOADS["e32_k4_t16384_d4096_mxfp8_all"]  # all six GEMMs, MXFP8 dispatch
+
 MX_CASES = [
     dict(T=256, d=256, f=256, E=8, k=4, name="mx_small"),
     dict(T=300, d=384, f=256, E=32, k=4, name="mx_ragged_e32"),
@@ -111,34 +114,57 @@ MX_CASES = [
     dict(T=260, d=256, f=256, E=8, k=4, shared_f=256, name="mx_shared_expert"),
     # >= 1024 rows per expert: 256 x 256 tiles in two stages for the M-grouped GEMMs
     dict(T=1100, d=256, f=384, E=2, k=2, name="mx_long_segments"),
+    dict(T=150, d=256, f=128, E=64, k=2, name="mx_sparse_e64"),    # many tiny and empty experts
 ]
+
+
+def _layer_errors(w, inp, L):
+    keys = ["h", "y", "dgates", "dx", "dW1", "dW3", "dW2"] + (["dW1s", "dW3s", "dW2s"] if w.shared_f else [])
+    plain = oracle_for(w, inp)                         # the unquantised fp64 layer: the gate
+    emu = oracle_for(w, inp, emulate_mx=True)          # the emulated MXFP8 method: a diagnostic
+    def pick(fb, k):
+        fw, bw = fb
+        return fw[k] if k in fw else bw[k]
+    got = {k: host(getattr(L, k)) for k in keys}
+    e_plain = {k: normwise_err(got[k], pick(plain, k)) for k in keys}
+    e_emu = {k: normwise_err(got[k], pick(emu, k)) for k in keys}
+    print(w.name, "| vs unquantised", {k: f"{v:.2e}" for k, v in e_plain.items()},
+          "| vs emulated MXFP8", {k: f"{v:.2e}" for k, v in e_emu.items()})
+    return plain, e_plain, e_emu
 
 
 @pytest.mark.parametrize("over", MX_CASES, ids=[c["name"] for c in MX_CASES])
 def test_mxfp8_layer_parity(over):
-    from oracle import mx_ref
-    w = workloads.scaled(workloads.WORKLOADS["e32_k4_t16384_d4096_mxfp8"], **over)
+    """The default-scope MXFP8 layer against the unquantised fp64 oracle at 6e-2."""
+    w = workloads.scaled(MX, **over)
     inp = workloads.make_inputs(w)
     say(f"[gpu] mxfp8 layer {w}")
     L = run_layer(w, inp)
-    fw, bw = oracle_for(w, inp)        # fp64 oracle of the MXFP8 method
+    assert not L.mx_dispatch
+    (fw, bw), e_plain, e_emu = _layer_errors(w, inp, L)
     assert np.array_equal(host(L.slot_row), fw["slot_row"])
-    keys = {"h": (L.h, fw["h"]), "y": (L.y, fw["y"]), "dgates": (L.dgates, bw["dgates"]),
-            "dx": (L.dx, bw["dx"]), "dW1": (L.dW1, bw["dW1"]), "dW3": (L.dW3, bw["dW3"]), "dW2": (L.dW2, bw["dW2"])}
-    if w.shared_f:
-        keys.update(dW1s=(L.dW1s, bw["dW1s"]), dW3s=(L.dW3s, bw["dW3s"]), dW2s=(L.dW2s, bw["dW2s"]))
-    errs = {k: normwise_err(host(g), r) for k, (g, r) in keys.items()}
-    # the format's own error: the same layer without quantisation (reported, bounded loosely)
-    plain = mx_ref.mx_layer(inp["x"], inp["W1"], inp["W3"], inp["W2"], w.k, inp["topk_idx"].numpy(), inp["gates"],
-                            inp["dy"], quant=False, bf16=False, shared=inp.get("shared"))
-    fmt = {k: normwise_err(host(keys[k][0]), plain[k]) for k in ("y", "dx", "dW1", "dW3", "dW2")}
-    print(w.name, "vs MXFP8 oracle", {k: f"{v:.2e}" for k, v in errs.items()},
-          "| vs unquantised", {k: f"{v:.2e}" for k, v in fmt.items()})
-    bad = {k: v for k, v in errs.items() if v > TOL["mxfp8"]}
+    bad = {k: v for k, v in e_plain.items() if v > TOL["mxfp8"]}
     assert not bad, (w.name, bad)
-    assert max(fmt.values()) < 0.25
+    bad = {k: v for k, v in e_emu.items() if v > tol_mx_emulated(k)}
+    assert not bad, (w.name, "emulated", bad)
     for e in np.nonzero(fw["counts"] == 0)[0]:
         assert not host(L.dW1[e]).any() and not host(L.dW2[e]).any()
+
+
+@pytest.mark.parametrize("over", MX_CASES[:4], ids=[c["name"] + "_all6" for c in MX_CASES[:4]])
+def test_mxfp8_all_six_against_the_emulated_method(over):
+    """All six expert GEMMs in MXFP8 with the MXFP8 dispatch: outside the 6e-2 bound (two
+    or three quantised GEMMs in series), so checked against the emulated MXFP8 oracle only;
+    the unquantised error is printed."""
+    w = workloads.scaled(MX_ALL, **over)
+    inp = workloads.make_inputs(w)
+    say(f"[gpu] mxfp8 layer, all six GEMMs {w}")
+    L = run_layer(w, inp)
+    assert L.mx_dispatch
+    _, e_plain, e_emu = _layer_errors(w, inp, L)
+    bad = {k: v for k, v in e_emu.items() if v > tol_mx_emulated(k)}
+    assert not bad, (w.name, "emulated", bad)
+    assert max(e_plain.values()) < 0.25
 
 
 def check_mx_layouts(q_rows, s_rows, q_cols, s_cols, vrows, offsets, rows=None, experts=None):
@@ -192,7 +218,7 @@ def test_mx_dispatch_bytes_bit_exact(over):
     gated output gradient, exactly the E4M3 codes and E8M0 scales the oracle's quantisers
     give for those rows, in both layouts."""
     from oracle import moe_ref as ref
-    w = workloads.scaled(workloads.WORKLOADS["e32_k4_t16384_d4096_mxfp8"], **over)
+    w = workloads.scaled(MX_ALL, **over)
     inp = workloads.make_inputs(w)
     say(f"[gpu] mxfp8 dispatch bytes {w}")
     L = run_layer(w, inp, mx_dispatch=True)
@@ -205,12 +231,12 @@ def test_mx_dispatch_bytes_bit_exact(over):
                      lambda i: routed_dy_rows(inp, slot_row, row_src, i), offsets)
 
 
-@pytest.mark.parametrize("over", MX_CASES[:2] + MX_CASES[3:], ids=[c["name"] for c in MX_CASES[:2] + MX_CASES[3:]])
+@pytest.mark.parametrize("over", MX_CASES[:2] + MX_CASES[3:5], ids=[c["name"] for c in MX_CASES[:2] + MX_CASES[3:5]])
 def test_mx_dispatch_equals_bf16_dispatch_bitwise(over):
     """The layer with the MXFP8 dispatch gives bit for bit the outputs of the layer that
     dispatches bf16 rows and quantises them inside each GEMM (the same bytes reach the
     same GEMM kernels; dgates keeps its summation order)."""
-    w = workloads.scaled(workloads.WORKLOADS["e32_k4_t16384_d4096_mxfp8"], **over)
+    w = workloads.scaled(MX_ALL, **over)
     inp = workloads.make_inputs(w)
     say(f"[gpu] mxfp8 dispatch vs bf16 dispatch {w}")
     A = run_layer(w, inp, mx_dispatch=True)
@@ -228,8 +254,7 @@ def test_mx_gemms_match_dequantized_operands():
     rounding of the outputs: a check of the scaled-MFMA operand and scale layouts."""
     from oracle import moe_ref as ref
     from oracle import mx_ref as mx
-    w = workloads.scaled(workloads.WORKLOADS["e32_k4_t16384_d4096_mxfp8"], T=300, d=256, f=384, E=8, k=4,
-                         name="mx_emulated")
+    w = workloads.scaled(MX_ALL, T=300, d=256, f=384, E=8, k=4, name="mx_emulated")
     inp = workloads.make_inputs(w)
     say(f"[gpu] mxfp8 GEMMs vs dequantised operands {w}")
     L = run_layer(w, inp, mx_dispatch=False)  # keeps bf16 x_perm and dy_perm to quantise here

@@ -52,7 +52,8 @@ def _check_layer(w, inp, layer):
     if learned:
         errs["logits"] = normwise_err(gl, fw["logits"])
         errs["gates"] = normwise_err(host(layer.gates), fw["gates"])
-    errs["h"] = normwise_err(host(layer.h), fw["h"])
+    if layer.h is not None:  # a recompute layer drops a, b and h after the backward
+        errs["h"] = normwise_err(host(layer.h), fw["h"])
     errs["y_perm"] = normwise_err(host(layer.y_perm), fw["y_perm"])
     errs["y"] = normwise_err(host(layer.y), fw["y"])
     errs["dgates"] = normwise_err(host(layer.dgates), bw["dgates"])
@@ -84,6 +85,77 @@ def test_layer_parity(name, over):
     say(f"[gpu] layer parity {w}")
     layer = run_layer(w, inp)
     _check_layer(w, inp, layer)
+
+
+RECOMPUTE_CASES = [("e128_k4_t8192", dict(T=512, d=256, f=192)),
+                   ("e128_k4_t8192_shared", dict(T=300, d=256, f=192, shared_f=128, name="shared_expert")),
+                   ("e128_k4_t16384_random", dict(T=333, d=192, f=128))]
+
+
+@pytest.mark.parametrize("name,over", RECOMPUTE_CASES, ids=[c[1].get("name", c[0]) + "_recompute"
+                                                            for c in RECOMPUTE_CASES])
+def test_recompute_layer_parity(name, over):
+    """The layer that recomputes GEMM1 in the backward, against the oracle."""
+    w = _case(name, over)
+    inp = workloads.make_inputs(w)
+    say(f"[gpu] recompute layer parity {w}")
+    layer = run_layer(w, inp, recompute=True)
+    assert layer.ab is None and layer.h is None
+    _check_layer(w, inp, layer)
+
+
+def test_autograd_function_against_the_oracle():
+    """MoEExpertFunction (learned routing with a router bias): torch autograd gradients of
+    x, Wr, W1, W3, W2 against the oracle's; a second forward through the same layer before
+    the first one's backward makes that backward raise."""
+    import mixture_experts_layer_logits_amd as m
+    from mixture_experts_layer_logits_amd.layer import MoEExpertFunction
+    from oracle import moe_ref as ref
+    w = workloads.scaled(W["e128_k4_t16384_zipf"], T=256, d=128, f=128, E=16, name="autograd")
+    inp = workloads.make_inputs(w)
+    say(f"[gpu] autograd function {w}")
+    d = to_dev(inp)
+    layer = m.MoEExpertLayer(w.T, w.d, w.f, w.E, w.k)
+    leaves = {k: d[k].clone().requires_grad_(True) for k in ("x", "Wr", "W1", "W3", "W2")}
+    y = MoEExpertFunction.apply(leaves["x"], leaves["Wr"], leaves["W1"], leaves["W3"], leaves["W2"], layer,
+                                d["router_bias"])
+    y.backward(d["dy"])
+    torch.cuda.synchronize()
+    fw = ref.layer_forward(inp["x"], inp["W1"], inp["W3"], inp["W2"], w.k, Wr=inp["Wr"], bias=inp["router_bias"],
+                           select_logits=host(layer.logits))
+    bw = ref.layer_backward(fw, inp["dy"], inp["x"], inp["W1"], inp["W3"], inp["W2"], Wr=inp["Wr"])
+    errs = {"y": normwise_err(host(y), fw["y"]), "dx": normwise_err(host(leaves["x"].grad), bw["dx"]),
+            "dWr": normwise_err(host(leaves["Wr"].grad), bw["dWr"]),
+            "dW1": normwise_err(host(leaves["W1"].grad), bw["dW1"]),
+            "dW3": normwise_err(host(leaves["W3"].grad), bw["dW3"]),
+            "dW2": normwise_err(host(leaves["W2"].grad), bw["dW2"])}
+    print("autograd", {k: f"{v:.2e}" for k, v in errs.items()})
+    assert max(errs.values()) < TOL["bf16"], errs
+    # two forwards, then the first one's backward: refused
+    y1 = MoEExpertFunction.apply(leaves["x"], leaves["Wr"], leaves["W1"], leaves["W3"], leaves["W2"], layer)
+    y2 = MoEExpertFunction.apply(leaves["x"], leaves["Wr"], leaves["W1"], leaves["W3"], leaves["W2"], layer)
+    with pytest.raises(RuntimeError, match="another forward"):
+        y1.backward(d["dy"])
+    y2.backward(d["dy"])
+    torch.cuda.synchronize()
+
+
+def test_given_routing_leaves_the_layer_ids_alone():
+    """A forward with caller-given expert ids only reads them: a later learned-routing
+    forward writes its ids into the layer's own buffer, never into the caller's tensor."""
+    import mixture_experts_layer_logits_amd as m
+    w = workloads.scaled(W["e128_k4_t16384_random"], T=64, d=128, f=128, E=8, name="given_then_learned")
+    inp = workloads.make_inputs(w)
+    say("[gpu] given routing then learned routing")
+    d = to_dev(inp)
+    layer = m.MoEExpertLayer(w.T, w.d, w.f, w.E, w.k)
+    given = d["topk_idx"].clone()
+    layer.forward(d["x"], d["W1"], d["W3"], d["W2"], topk_idx=given, gates=d["gates"])
+    Wr = (torch.randn(w.E, w.d, generator=torch.Generator().manual_seed(3)) * 0.02).to(torch.bfloat16).cuda()
+    layer.forward(d["x"], d["W1"], d["W3"], d["W2"], Wr=Wr)
+    torch.cuda.synchronize()
+    assert torch.equal(given, d["topk_idx"])
+    assert layer.topk_idx.data_ptr() != given.data_ptr()
 
 
 def test_layer_deterministic():

@@ -35,10 +35,14 @@ import torch
 # is stored here so that input generation itself never routes anything.
 ZIPF_S = 1.1
 
-# beta calibrated per (seed, T, d, E, k); see oracle/calibrate_zipf.py
+# beta calibrated per (seed, T, d, E, k); see oracle/calibrate_zipf.py.  With one scale for
+# the whole rank profile the two halves of the load-imbalance description do not meet:
+# hottest/mean = 10 leaves every expert some rows, and the first beta on a 0.05 grid that
+# empties an expert (0.8) makes the hottest 27x the mean.  Both are workloads.
 _ZIPF_BETA_TABLE = {
     (1004, 16384, 2048, 128, 4): 0.3241,   # hottest/mean = 9.996, no empty expert
 }
+ZIPF_BETA_STEEP = 0.8                      # hottest/mean = 26.8, three empty experts (seed 1004)
 
 
 @dataclasses.dataclass(frozen=True)
@@ -55,6 +59,8 @@ class Workload:
     routing: str          # "learned", "learned_zipf" or "given_uniform"
     note: str = ""
     shared_f: int = 0     # width of an always-on shared expert (0: none)
+    zipf_beta: Optional[float] = None      # learned_zipf: bias scale (None: the calibrated table)
+    mx_scope: Optional[tuple] = None       # mxfp8: names of the expert GEMMs run in MXFP8 (None: the default)
 
     @property
     def R(self) -> int:
@@ -77,11 +83,18 @@ WORKLOADS = {
                  "the E=128 k=4 layer plus one always-on shared expert of width f (production rows' layout)",
                  shared_f=1024),
         Workload("e128_k4_t16384_zipf", 1004, 16384, 2048, 1024, 128, 4, "bf16", "bf16", "learned_zipf",
-                 "router logits get a Zipf(1.1) per-expert bias: hottest expert ~10x mean, some empty"),
+                 "router logits get a Zipf(1.1) per-expert bias: hottest expert 10x the mean, none empty"),
+        Workload("e128_k4_t16384_zipf_steep", 1004, 16384, 2048, 1024, 128, 4, "bf16", "bf16", "learned_zipf",
+                 "the Zipf(1.1) bias at beta 0.8: three experts receive no rows, the hottest 27x the mean",
+                 zipf_beta=ZIPF_BETA_STEEP),
         Workload("e128_k4_t16384_random", 1005, 16384, 2048, 1024, 128, 4, "bf16", "bf16", "given_uniform",
                  "top-4 sampled uniformly without replacement, gates Dirichlet(1)"),
         Workload("e32_k4_t16384_d4096_mxfp8", 1006, 16384, 4096, 1536, 32, 4, "bf16", "mxfp8", "given_uniform",
-                 "one GPU's resident share: 32 local experts, tokens arrive routed; MXFP8 GEMMs"),
+                 "one GPU's resident share: 32 local experts, tokens arrive routed; GEMM2 and dgrad1 in MXFP8"),
+        Workload("e32_k4_t16384_d4096_mxfp8_all", 1006, 16384, 4096, 1536, 32, 4, "bf16", "mxfp8", "given_uniform",
+                 "the same inputs with all six expert GEMMs in MXFP8 and the MXFP8 dispatch (outside the 6e-2 "
+                 "error bound; for the throughput comparison)",
+                 mx_scope=("gemm1", "gemm2", "dgrad2", "wgrad2", "dgrad1", "wgrad1")),
         Workload("e32_k4_t16384_d4096_bf16", 1006, 16384, 4096, 1536, 32, 4, "bf16", "bf16", "given_uniform",
                  "same inputs as the MXFP8 run, bf16 GEMMs, for the throughput/error comparison"),
     ]
@@ -90,12 +103,13 @@ WORKLOADS = {
 
 def scaled(w: Workload, T: Optional[int] = None, d: Optional[int] = None, f: Optional[int] = None,
            E: Optional[int] = None, k: Optional[int] = None, seed: Optional[int] = None,
-           name: Optional[str] = None, shared_f: Optional[int] = None) -> Workload:
+           name: Optional[str] = None, shared_f: Optional[int] = None, mx_scope: Optional[tuple] = None) -> Workload:
     """A smaller copy of a workload (same routing mode and dtype) for oracle-sized tests."""
     return dataclasses.replace(
-        w, T=T or w.T, d=d or w.d, f=f or w.f, E=E or w.E, k=k or w.k,
+        w, T=T if T is not None else w.T, d=d or w.d, f=f or w.f, E=E or w.E, k=k or w.k,
         seed=w.seed if seed is None else seed, name=name or (w.name + "_scaled"),
-        shared_f=w.shared_f if shared_f is None else shared_f)
+        shared_f=w.shared_f if shared_f is None else shared_f,
+        mx_scope=w.mx_scope if mx_scope is None else tuple(mx_scope))
 
 
 def _round(t: torch.Tensor, dtype) -> torch.Tensor:
@@ -113,6 +127,8 @@ def zipf_bias(w: Workload, gen: torch.Generator, beta: float) -> torch.Tensor:
 
 
 def zipf_beta(w: Workload) -> float:
+    if w.zipf_beta is not None:
+        return w.zipf_beta
     key = (w.seed, w.T, w.d, w.E, w.k)
     if key in _ZIPF_BETA_TABLE:
         return _ZIPF_BETA_TABLE[key]
