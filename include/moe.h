@@ -55,7 +55,8 @@ typedef enum {
   MOE_EALIGN = -3,        /* a pointer is not aligned as required */
   MOE_EWORKSPACE = -4,    /* workspace smaller than moe_workspace_size() */
   MOE_EUNSUPPORTED = -5,  /* dtype combination not implemented */
-  MOE_ELAUNCH = -6        /* a kernel launch failed */
+  MOE_ELAUNCH = -6,       /* a kernel launch failed */
+  MOE_ESCRATCH = -7       /* shape too large for moe_route_noalloc's fixed scratch */
 } moe_status;
 
 typedef enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_MXFP8 = 2 } moe_dtype;
@@ -121,6 +122,21 @@ moe_status moe_router_fwd(const moe_shape* s, const void* x, const void* Wr, con
 moe_status moe_route(const moe_shape* s, const float* logits, int32_t* topk_idx, float* gates,
                      int32_t* counts, int32_t* offsets, int32_t* slot_row, void* ws, size_t ws_bytes,
                      void* stream);
+
+/* moe_route for callers that cannot allocate device memory: code under HIP graph capture
+ * that must not call hipMalloc, tight serving loops, harnesses that forbid allocation.  Same
+ * arguments, kernels and results (bit for bit) as moe_route, without the workspace: the
+ * per-chunk histograms and ranks live in a fixed array of 2^20 int32 (4 MiB) in the
+ * library's own device memory, one per GPU, held until the process ends.  The first call on
+ * a device takes that array's address on the current device (hipGetSymbolAddress, no
+ * allocation); no call allocates or frees anything.  Shapes needing more than 4 MiB
+ * (ceil(T/32)*E + T*k int32 values; e.g. T up to 131072 at E = 128, k = 4) return
+ * MOE_ESCRATCH before anything is enqueued.  Every call on one GPU shares that GPU's array,
+ * so calls that may overlap on one GPU (other streams, other host threads) race and must be
+ * ordered by the caller.  No clearing is needed: every histogram entry and rank a launch reads
+ * is written earlier in the same call. */
+moe_status moe_route_noalloc(const moe_shape* s, const float* logits, int32_t* topk_idx, float* gates,
+                             int32_t* counts, int32_t* offsets, int32_t* slot_row, void* stream);
 
 /* Dispatch metadata for tokens that arrive already routed (random routing of the large
  * benchmark rows: bigchange.ai, section "Три числа, три знаменателя"; unite.ai, section

@@ -66,6 +66,7 @@ _SIGS = {
     "moe_router_fwd": [_VP, _VP, _VP, _VP, _VP],
     "moe_route": [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _SZ, _VP],
     "moe_route_given": [_VP, _VP, _VP, _VP, _VP, _VP, _SZ, _VP],
+    "moe_route_noalloc": [_VP, _VP, _VP, _VP, _VP, _VP, _VP],
     "moe_permute": [_VP, _VP, _VP, _VP, _VP],
     "moe_grouped_ffn_fwd": [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _SZ, _VP],
     "moe_ffn_gemm1_fwd": [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _SZ, _VP],
@@ -167,6 +168,10 @@ def moe_router_fwd(shape, x, Wr, bias, logits, stream=None):
 
 def moe_route(shape, logits, topk_idx, gates, counts, offsets, slot_row, ws, stream=None):
     _call("moe_route", shape, logits, topk_idx, gates, counts, offsets, slot_row, ws, _ws(ws), stream=stream)
+
+
+def moe_route_noalloc(shape, logits, topk_idx, gates, counts, offsets, slot_row, stream=None):
+    _call("moe_route_noalloc", shape, logits, topk_idx, gates, counts, offsets, slot_row, stream=stream)
 
 
 def moe_route_given(shape, topk_idx, counts, offsets, slot_row, dev_err, ws, stream=None):

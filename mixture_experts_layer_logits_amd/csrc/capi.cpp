@@ -106,6 +106,7 @@ const char* moe_status_str(int status) {
     case MOE_EWORKSPACE: return "workspace too small";
     case MOE_EUNSUPPORTED: return "unsupported dtype combination";
     case MOE_ELAUNCH: return "kernel launch failed";
+    case MOE_ESCRATCH: return "shape too large for the allocation-free entry point's fixed scratch (4 MiB)";
     default: return "unknown status";
   }
 }
@@ -146,6 +147,17 @@ moe_status moe_route(const moe_shape* s, const float* logits, int32_t* topk_idx,
   if (!counts || !offsets || !ws) return MOE_ENULL;
   if (ws_bytes < route_workspace_bytes(s->T, s->E, s->k)) return MOE_EWORKSPACE;
   return launched(route_topk(s->T, s->E, s->k, logits, topk_idx, gates, counts, offsets, slot_row, ws, S(st)));
+}
+
+moe_status moe_route_noalloc(const moe_shape* s, const float* logits, int32_t* topk_idx, float* gates,
+                             int32_t* counts, int32_t* offsets, int32_t* slot_row, void* st) {
+  MOE_TRY(check_shape(s));
+  if (!rows_ok(s, logits) || !rows_ok(s, topk_idx) || !rows_ok(s, gates) || !rows_ok(s, slot_row)) return MOE_ENULL;
+  if (!counts || !offsets) return MOE_ENULL;
+  if (route_workspace_bytes(s->T, s->E, s->k) > kRouteScratchInts * sizeof(int32_t)) return MOE_ESCRATCH;
+  int32_t* scr = nullptr;
+  if (route_scratch_ptr(&scr) != hipSuccess) return MOE_ELAUNCH;
+  return launched(route_topk(s->T, s->E, s->k, logits, topk_idx, gates, counts, offsets, slot_row, scr, S(st)));
 }
 
 moe_status moe_route_given(const moe_shape* s, const int32_t* topk_idx, int32_t* counts, int32_t* offsets,

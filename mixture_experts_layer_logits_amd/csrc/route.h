@@ -13,6 +13,11 @@ constexpr int MOE_DEVERR_EXPERT_RANGE_BIT = 1;
 constexpr int MOE_DEVERR_DUPLICATE_BIT = 2;
 
 size_t route_workspace_bytes(int T, int E, int k);
+// The allocation-free routing entry point's fixed device scratch: 2^20 int32 (4 MiB) per
+// device; shapes whose route_workspace_bytes exceed it are refused.
+constexpr size_t kRouteScratchInts = size_t(1) << 20;
+// Device address of that scratch on the current device (taken once per device).
+hipError_t route_scratch_ptr(int32_t** out);
 hipError_t route_topk(int T, int E, int k, const float* logits, int32_t* idx, float* gates, int32_t* counts,
                       int32_t* offsets, int32_t* slot_row, void* ws, hipStream_t st);
 hipError_t route_given(int T, int E, int k, const int32_t* idx, int32_t* counts, int32_t* offsets,

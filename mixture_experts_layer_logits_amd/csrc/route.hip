@@ -15,12 +15,26 @@
 //      exclusive prefix sum over experts (offsets);
 //   3. per slot: slot_row = offsets[e] + chunk base + in-chunk rank.
 // The result is the stable counting sort of slots t*k + j by expert, bit for bit.
+#include <mutex>
+
 #include "common.h"
 #include "gemm.h"
 #include "route.h"
 
+// Fixed scratch of the allocation-free routing entry point: the per-chunk expert histograms
+// and in-chunk ranks that route_topk otherwise keeps in the caller's workspace.  Each GPU the
+// library runs on holds its own copy for the life of the process.  Host code never names it
+// directly (the name is a host-side stand-in, not a device address): it uses the per-device
+// address that route_scratch_ptr() takes with hipGetSymbolAddress.
+static __device__ __align__(256) int32_t scratch[moe::kRouteScratchInts];
+
 namespace moe {
 namespace {
+
+constexpr int kMaxDevices = 64;
+std::once_flag g_scratch_once[kMaxDevices];
+int32_t* g_scratch_ptr[kMaxDevices];
+hipError_t g_scratch_err[kMaxDevices];
 
 // 16 waves per chunk, two tokens each: the per-token top-k is a chain of dependent
 // cross-lane reductions, so many waves per compute unit keep it fed
@@ -243,6 +257,23 @@ hipError_t launch_chunk(int T, int E, int k, const float* logits, const int32_t*
 size_t route_workspace_bytes(int T, int E, int k) {
   const size_t nchunks = (size_t)(T + kRouteChunk - 1) / kRouteChunk;
   return (nchunks * E + (size_t)T * k) * sizeof(int32_t);
+}
+
+// Device address of `scratch` on the current device, taken once per device (with that
+// device current) and kept.
+hipError_t route_scratch_ptr(int32_t** out) {
+  int dev = 0;
+  hipError_t err = hipGetDevice(&dev);
+  if (err != hipSuccess) return err;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::call_once(g_scratch_once[dev], [dev]() {
+    void* p = nullptr;
+    g_scratch_err[dev] = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    g_scratch_ptr[dev] = static_cast<int32_t*>(p);
+  });
+  if (g_scratch_err[dev] != hipSuccess) return g_scratch_err[dev];
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
 }
 
 hipError_t route_topk(int T, int E, int k, const float* logits, int32_t* idx, float* gates, int32_t* counts,

@@ -127,3 +127,14 @@ def test_mx_scope_gates_the_mx_operand_entry_points(lib):
     st = lib.moe_ffn_gemm1_fwd_mx(ctypes.byref(s), P(0x1000), P(0x1000), P(0x1000), P(0x1000), P(0x1000), P(0x1000),
                                   P(0x1000), P(0x1000), ctypes.c_size_t(1 << 30), P(0))
     assert st == MOE_EUNSUPPORTED
+
+
+def test_route_noalloc_refuses_oversized_shapes_on_the_host(lib):
+    """The allocation-free routing call refuses a shape whose histograms and ranks exceed its
+    fixed 4 MiB scratch, before any HIP call (so this runs without a GPU)."""
+    P = ctypes.c_void_p
+    s = Shape(200000, 64, 64, 128, 4, 1, 1, 0)      # 6250 * 128 + 800000 int32 > 2^20
+    st = lib.moe_route_noalloc(ctypes.byref(s), P(0x1000), P(0x1000), P(0x1000), P(0x1000), P(0x1000), P(0x1000), P(0))
+    assert st == -7
+    lib.moe_status_str.restype = ctypes.c_char_p
+    assert b"scratch" in lib.moe_status_str(-7)
