@@ -3,6 +3,8 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
     python bench.py --profile-kernel NAME [--steps K] [--workload NAME]   # one call, K times
     python bench.py --copy-mib N [--steps K]                              # plain copy, K times
+    python bench.py --profile-steps K [--workload NAME]                   # K eager steps, nothing else
+    python bench.py --pmc-summary CSV [CSV ...]                           # counter medians per call
 
 The last two forms run under rocprofv3 counter passes: one layer call (after one full
 step to set up its inputs) or a plain device copy of N MiB (the reference against which
@@ -37,7 +39,10 @@ sys.path.insert(0, ROOT)
 METRIC = "MoE layer tokens/s fwd+bwd at E=128,k=4 on 1 GPU; grouped-GEMM MFMA % of peak"
 PEAK_TFLOPS = {"bf16": 2500.0, "mxfp8": 5000.0, "f32": 157.3}
 PEAK_HBM_GBS = 8000.0
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.json")
+COUNTERS_FILE = os.path.join(ROOT, "profiles", "counters.json")
+SQ_PASS = ("SQ_VALU_MFMA_BUSY_CYCLES SQ_BUSY_CU_CYCLES SQ_INSTS_VALU_MFMA_MOPS_BF16 SQ_INSTS_VALU_MFMA_MOPS_F8 "
+           "SQ_WAIT_INST_ANY SQ_WAVE_CYCLES SQ_INSTS_LDS SQ_LDS_BANK_CONFLICT GRBM_GUI_ACTIVE GRBM_COUNT")
+N_XCC, N_SIMD = 8, 1024          # MI355X: 8 XCDs, 256 CUs x 4 SIMDs
 
 
 def parse():
@@ -51,6 +56,13 @@ def parse():
                     help="tokens in the oracle's timed sample (0: sized for about 12 s of CPU work)")
     ap.add_argument("--profile-kernel", default=None, help="run only this call of the step, --steps times")
     ap.add_argument("--copy-mib", type=int, default=0, help="run a plain device copy of this many MiB, --steps times")
+    ap.add_argument("--profile-steps", type=int, default=0,
+                    help="run this many eager steps of the whole layer and nothing else (for counter passes)")
+    ap.add_argument("--pmc-summary", nargs="+", default=None,
+                    help="rocprofv3 counter_collection.csv files: print per-call medians of each counter as JSON")
+    ap.add_argument("--pmc-record", default=None, metavar="DIR",
+                    help="record the counter passes under DIR (pmc_sq_W, pmc_fetch_W, pmc_write_W for --workload W, "
+                         "pmc_fetch_copy, pmc_write_copy) into profiles/counters.json; prints the summary table")
     ap.add_argument("--recompute", action="store_true",
                     help="activation recompute: keep only x_perm and run GEMM1 again in the backward")
     ap.add_argument("--seed-offset", type=int, default=0,
@@ -229,8 +241,130 @@ def cpu_baseline(w, inp, ntok=0, target_s=12.0):
             "sample": f"{what}, all {w.E} experts' weights, fwd+bwd in fp64 NumPy ({dt:.1f} s)"}
 
 
+# kernel-name fragments -> the layer call that launches them (every bf16 GEMM call is one
+# launch of the pipelined kernel with its problem type; MXFP8 GEMM calls add quantiser launches)
+KERNEL_CALLS = [("ProbGemm1", "gemm1_fwd"), ("ProbGemm2", "gemm2_fwd"), ("ProbDgrad2", "dgrad2"),
+                ("ProbWgrad2", "wgrad2"), ("ProbDgrad1", "dgrad1"), ("ProbWgrad1", "wgrad1"),
+                ("MxGemm1", "gemm1_fwd"), ("MxDgrad2", "dgrad2"), ("ProbRouterFwd", "router_fwd"),
+                ("ProbRouterDx", "router_bwd"), ("ProbRouterDw", "router_bwd"), ("route_chunk", "route"),
+                ("route_scan", "route"), ("route_finalize", "route"), ("route_bwd", "route_bwd"),
+                ("permute_kernel", "permute"), ("combine_kernel", "combine"), ("combine_bwd_kernel", "combine_bwd"),
+                ("unpermute_sum", "permute_bwd"), ("mx_dispatch", "mx_dispatch"), ("dgates_kernel", "combine_bwd"),
+                ("row_src_kernel", "permute"), ("copyBuffer", "copy"), ("elementwise_kernel", "copy")]
+
+
+def pmc_summary(paths):
+    """Median over dispatches of every counter, per kernel (rocprofv3 --pmc csv output)."""
+    import csv
+    import statistics
+    vals = {}
+    for path in paths:
+        with open(path) as fh:
+            for row in csv.DictReader(fh):
+                name = row["Kernel_Name"]
+                key = (name, row["Counter_Name"])
+                vals.setdefault(key, {}).setdefault(row.get("Dispatch_Id", len(vals)), 0.0)
+                vals[key][row.get("Dispatch_Id")] += float(row["Counter_Value"])
+    out = {}
+    for (name, ctr), per in vals.items():
+        call = next((c for frag, c in KERNEL_CALLS if frag in name), None)
+        short = name if len(name) < 110 else name[:107] + "..."
+        e = out.setdefault(short, {"call": call, "dispatches": len(per)})
+        e[ctr] = statistics.median(per.values())
+    return out
+
+
+def _csv(d, name):
+    return os.path.join(d, "pmc_" + name, "p_counter_collection.csv")
+
+
+def pmc_record(wname, d):
+    """Per call of the step: MFMA utilisation (rocprofv3's MfmaUtil: MFMA-busy cycles over
+    GUI-active cycles of one XCD times the SIMD count; GRBM_GUI_ACTIVE comes summed over the
+    8 XCDs), MFMA flops counted, and HBM-side traffic from FETCH_SIZE / WRITE_SIZE scaled by
+    what the same counters read for a plain 256 MiB device copy.  Writes the entries into
+    COUNTERS_FILE (with the kernel-source digest) and returns the markdown summary."""
+    import workloads
+    w = workloads.WORKLOADS[wname]
+    sq = pmc_summary([_csv(d, f"sq_{wname}")])
+    fe = pmc_summary([_csv(d, f"fetch_{wname}")])
+    wr = pmc_summary([_csv(d, f"write_{wname}")])
+    cf = pmc_summary([_csv(d, "fetch_copy")])
+    cw = pmc_summary([_csv(d, "write_copy")])
+    copy_bytes = 256 << 20
+    fetch_f = next(v["FETCH_SIZE"] for k, v in cf.items() if "copyBuffer" in k) * 1024 / copy_bytes
+    write_f = next(v["WRITE_SIZE"] for k, v in cw.items() if "copyBuffer" in k) * 1024 / copy_bytes
+    eb = 4 if w.dtype == "f32" else 2
+    mx_dispatch = w.gemm == "mxfp8" and bool(w.mx_scope) and len(w.mx_scope) == 6
+    gem, byt = algorithmic_work(w, eb, mx_dispatch)
+    calls = {}
+    for table, keys in ((sq, ("GRBM_GUI_ACTIVE", "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_INSTS_VALU_MFMA_MOPS_BF16",
+                              "SQ_INSTS_VALU_MFMA_MOPS_F8", "SQ_LDS_BANK_CONFLICT", "SQ_INSTS_LDS")),
+                        (fe, ("FETCH_SIZE",)), (wr, ("WRITE_SIZE",))):
+        for kname, v in table.items():
+            c = v.get("call")
+            if not c or c == "copy":
+                continue
+            e = calls.setdefault(c, {"kernels": set()})
+            e["kernels"].add(kname)
+            for key in keys:
+                e[key] = e.get(key, 0.0) + v.get(key, 0.0)
+    digest = kernel_sources_digest()
+    rec = json.load(open(COUNTERS_FILE)) if os.path.exists(COUNTERS_FILE) else {}
+    rows = []
+    for c, e in calls.items():
+        gui = e.get("GRBM_GUI_ACTIVE", 0.0) / N_XCC
+        util = 100.0 * e.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0) / (gui * N_SIMD) if gui else 0.0
+        flops = 512.0 * (e.get("SQ_INSTS_VALU_MFMA_MOPS_BF16", 0.0) + e.get("SQ_INSTS_VALU_MFMA_MOPS_F8", 0.0))
+        reads = e.get("FETCH_SIZE", 0.0) * 1024 / fetch_f
+        writes = e.get("WRITE_SIZE", 0.0) * 1024 / write_f
+        entry = {"source_digest": digest, "kernels": sorted(e["kernels"]), "gui_cycles_per_xcd": round(gui),
+                 "mfma_util_pct": round(util, 2), "mfma_flops_counted": flops,
+                 "algorithmic_flops_per_launch": gem.get(c), "read_bytes": round(reads), "write_bytes": round(writes),
+                 "bytes_per_launch": round(reads + writes), "algorithmic_bytes_per_launch": byt.get(c),
+                 "copy_fetch_factor": round(fetch_f, 5), "copy_write_factor": round(write_f, 5),
+                 "lds_bank_conflicts": e.get("SQ_LDS_BANK_CONFLICT", 0.0)}
+        rec[f"{wname}:{c}"] = entry
+        rows.append((c, entry))
+    with open(COUNTERS_FILE, "w") as fh:
+        json.dump(rec, fh, indent=1, sort_keys=True)
+    order = ["router_fwd", "route", "permute", "gemm1_fwd", "gemm2_fwd", "combine", "combine_bwd", "dgrad2", "wgrad2",
+             "dgrad1", "route_bwd", "router_bwd", "permute_bwd", "wgrad1", "mx_dispatch"]
+    rows.sort(key=lambda r: order.index(r[0]) if r[0] in order else 99)
+    md = [f"| call | GUI cycles / XCD | MFMA util % | MFMA flops counted / algorithmic | HBM reads | HBM writes | "
+          f"traffic / algorithmic bytes |", "|---|---|---|---|---|---|---|"]
+    for c, e in rows:
+        fl = (f"{e['mfma_flops_counted'] / e['algorithmic_flops_per_launch']:.3f}"
+              if e["algorithmic_flops_per_launch"] and e["mfma_flops_counted"] else "")
+        tb = (f"{e['bytes_per_launch'] / e['algorithmic_bytes_per_launch']:.2f}"
+              if e["algorithmic_bytes_per_launch"] else "")
+        md.append(f"| {c} | {e['gui_cycles_per_xcd']:,} | {e['mfma_util_pct'] if fl else ''} | {fl} | "
+                  f"{e['read_bytes']:,} | {e['write_bytes']:,} | {tb} |")
+    md.append("")
+    md.append(f"Copy calibration: FETCH_SIZE reads {fetch_f:.4f} and WRITE_SIZE {write_f:.4f} of a 256 MiB copy's "
+              f"bytes; kernel sources digest {digest}.")
+    return "\n".join(md)
+
+
+def counter_entry(wname, call):
+    """The recorded counters of one call, if they were taken on the current kernel sources."""
+    if not os.path.exists(COUNTERS_FILE):
+        return None
+    try:
+        e = json.load(open(COUNTERS_FILE)).get(f"{wname}:{call}")
+    except Exception:
+        return None
+    return e if e and e.get("source_digest") == kernel_sources_digest() else None
+
+
 def main():
     args = parse()
+    if args.pmc_summary:
+        print(json.dumps(pmc_summary(args.pmc_summary), indent=1))
+        return
+    if args.pmc_record:
+        print(pmc_record(args.workload, args.pmc_record))
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: the layer runs on one GPU's resident experts and this build has no "
               f"multi-GPU path (asked for --gpus {args.gpus})", file=sys.stderr)
@@ -274,6 +408,14 @@ def main():
     L.forward(d_inp["x"], d_inp["W1"], d_inp["W3"], d_inp["W2"], Wr=d_inp["Wr"], bias=d_inp["router_bias"],
               topk_idx=d_inp["topk_idx"], gates=d_inp["gates"], shared=d_inp["shared"])
     calls = step_calls(m, L, d_inp, learned, args.recompute)
+
+    if args.profile_steps:
+        for _ in range(args.profile_steps):
+            for _, fn in calls:
+                fn()
+        torch.cuda.synchronize()
+        print(json.dumps({"workload": w.name, "profile_steps": args.profile_steps}), flush=True)
+        return
 
     if args.profile_kernel:
         for _, fn in calls:  # one whole step sets up every call's inputs
@@ -389,15 +531,17 @@ def main():
     t_mfma = gem[dom] / (peak * 1e12)
     t_hbm = byt[dom] / (PEAK_HBM_GBS * 1e9)
     sec = per_call_ms[dom] * 1e-3
-    traffic = None
-    digest = kernel_sources_digest()
-    if os.path.exists(TRAFFIC_FILE):
-        try:
-            rec = json.load(open(TRAFFIC_FILE)).get(f"{w.name}:{dom}")
-            if rec and rec.get("source_digest") == digest:
-                traffic = rec["bytes_per_launch"]
-        except Exception:
-            traffic = None
+    # counter evidence (rocprofv3 passes recorded in profiles/counters.json on these kernel
+    # sources): HBM-side traffic and MFMA utilisation per call, next to the algorithmic figures
+    for name, e in kernels.items():
+        ce = counter_entry(w.name, name)
+        if ce:
+            e["counter_traffic_bytes"] = ce["bytes_per_launch"]
+            e["counter_gbs"] = round(ce["bytes_per_launch"] / (e["ms"] * 1e-3) / 1e9, 1)
+            if ce.get("algorithmic_flops_per_launch"):
+                e["counter_mfma_util_pct"] = ce["mfma_util_pct"]
+    ce = counter_entry(w.name, dom)
+    traffic = ce["bytes_per_launch"] if ce else None
     if t_hbm >= t_mfma:
         achieved = byt[dom] / sec / 1e9
         roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
