@@ -60,6 +60,9 @@ def parse():
                     help="run this many eager steps of the whole layer and nothing else (for counter passes)")
     ap.add_argument("--pmc-summary", nargs="+", default=None,
                     help="rocprofv3 counter_collection.csv files: print per-call medians of each counter as JSON")
+    ap.add_argument("--vendor-calibration", action="store_true",
+                    help="time torch.bmm (the vendor BLAS) on uniform batched GEMMs of the workload's six expert "
+                         "GEMM shapes and a dense 8192^3 GEMM: the practical MFMA ceiling of this box, for reference")
     ap.add_argument("--pmc-record", default=None, metavar="DIR",
                     help="record the counter passes under DIR (pmc_sq_W, pmc_fetch_W, pmc_write_W for --workload W, "
                          "pmc_fetch_copy, pmc_write_copy) into profiles/counters.json; prints the summary table")
@@ -357,8 +360,45 @@ def counter_entry(wname, call):
     return e if e and e.get("source_digest") == kernel_sources_digest() else None
 
 
+def vendor_calibration(w):
+    """The vendor BLAS (torch.bmm, bf16, contiguous operands) on batched GEMMs with the shapes
+    of the workload's six expert GEMMs, every expert given the mean row count R/E: what a
+    tuned library reaches on these shapes without ragged experts or fused epilogues.  A
+    reference point for the MFMA fractions; nothing of the layer runs through it."""
+    import torch
+    n = w.T * w.k // w.E
+    d, f, E = w.d, w.f, w.E
+    shapes = {"gemm1_fwd": (E, n, d, 2 * f), "gemm2_fwd": (E, n, f, d), "dgrad2": (E, n, d, f),
+              "wgrad2": (E, d, n, f), "dgrad1": (E, n, 2 * f, d), "wgrad1": (E, 2 * f, n, d),
+              "dense_8192": (1, 8192, 8192, 8192)}
+    out = {}
+    g = torch.Generator(device="cuda").manual_seed(0)
+    for name, (B, M, K, N) in shapes.items():
+        a = torch.randn(B, M, K, device="cuda", generator=g).to(torch.bfloat16).contiguous()
+        b = torch.randn(B, K, N, device="cuda", generator=g).to(torch.bfloat16).contiguous()
+        for _ in range(3):
+            torch.bmm(a, b)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(20):
+            torch.bmm(a, b)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / 20
+        fl = 2.0 * B * M * K * N
+        out[name] = {"batch_m_k_n": [B, M, K, N], "ms": round(ms, 4), "tflops": round(fl / ms / 1e9, 1),
+                     "frac_of_2.5pf": round(fl / ms / 1e9 / PEAK_TFLOPS["bf16"], 4)}
+        del a, b
+    return {"workload": w.name, "rows_per_expert": n, "vendor_bmm": out}
+
+
 def main():
     args = parse()
+    if args.vendor_calibration:
+        import workloads
+        print(json.dumps(vendor_calibration(workloads.WORKLOADS[args.workload])), flush=True)
+        return
     if args.pmc_summary:
         print(json.dumps(pmc_summary(args.pmc_summary), indent=1))
         return

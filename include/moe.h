@@ -33,8 +33,18 @@
  *    expert id) are reported by OR-ing bits into a caller-provided device word.
  *  - Determinism: every output is bitwise reproducible run to run (no float atomics,
  *    fixed reduction orders).
- *  - Re-entrancy: the library holds no state; calls on different streams with disjoint
- *    buffers may run concurrently.  Calls that share a workspace must be ordered.
+ *  - Re-entrancy: calls on different streams, or from different host threads, with disjoint
+ *    buffers may run concurrently; calls that share a workspace must be ordered.  The only
+ *    state the library keeps is host-side and filled once: each device's compute-unit count,
+ *    the occupancy of each kernel at each dynamic-LDS size (it sizes the persistent GEMM
+ *    grids), and the tuning overrides below; all three are read and filled under a lock or
+ *    atomically.  moe_route_noalloc adds one fixed device array per GPU (see there).
+ *  - Tuning overrides: MOE_TILE_<GEMM> / MOE_TILE, MOE_GEMM_BK, MOE_GEMM_STAGES,
+ *    MOE_GEMM_LOADERS and MOE_MX_TILE select other GEMM tile shapes, k-depths, stage counts
+ *    and loader waves than the measured defaults.  Each is read from the environment once,
+ *    at the first launch that consults it, and kept for the life of the process.  They
+ *    change only how the work is tiled and scheduled: every output element is still one fp32
+ *    reduction over the same values in ascending order of the reduction index.
  *  - Limits: 1 <= k <= E <= 1024, T*k < 2^31, d and f multiples of 64; with MOE_MXFP8
  *    GEMMs d and f must be multiples of 128.  bf16 buffers need 16-byte alignment.
  */
@@ -109,7 +119,13 @@ size_t moe_workspace_size(const moe_shape* s);
 moe_status moe_router_fwd(const moe_shape* s, const void* x, const void* Wr, const float* bias,
                           float* logits, void* stream);
 
-/* Top-k gating and dispatch metadata, all on the device.
+/* Top-k gating and dispatch metadata, all on the device: each token picks k of the E
+ * experts (top-four routing in the production rows: bigchange.ai, "Olmo-core 3 открывает
+ * стек обучения MoE от Ai2…", section "Что инженер может попробовать на практике"), and the
+ * counts and offsets stay in device memory so the host never waits for them (unite.ai,
+ * "Ai2 κυκλοφορεί το Olmo-Core 3…", section "Παραλληλισμός, Ακρίβεια και Τεχνικές
+ * Μνήμης").  The gate function is not on the pages; the softmax over the chosen k scores
+ * is the reading taken.
  * In:  logits [T, E] float (finite).
  * Out: topk_idx [T, k] int32, the k largest scores per token in value-descending order,
  *      equal scores broken toward the lower expert index;
@@ -149,7 +165,10 @@ moe_status moe_route_given(const moe_shape* s, const int32_t* topk_idx, int32_t*
                            size_t ws_bytes, void* stream);
 
 /* Rowwise dispatch into per-expert input buffers: x_perm[slot_row[t, j]] = x[t] and
- * row_src[slot_row[t, j]] = t.  x [T, d] act, slot_row [T, k], row_src [R] int32 (written,
+ * row_src[slot_row[t, j]] = t.  Routed rows are written straight into the experts' input
+ * buffers (unite.ai, section "Παραλληλισμός, Ακρίβεια και Τεχνικές Μνήμης"; ettayeb.fr,
+ * "Olmo-core 3 ouvre l'entraînement des MoE…", section "Trois parallélismes, trois
+ * optimisations de routage").  x [T, d] act, slot_row [T, k], row_src [R] int32 (written,
  * may be NULL), x_perm [R, d] act (written). */
 moe_status moe_permute(const moe_shape* s, const void* x, const int32_t* slot_row, int32_t* row_src,
                        void* x_perm, void* stream);
@@ -159,9 +178,9 @@ moe_status moe_permute(const moe_shape* s, const void* x, const int32_t* slot_ro
  * y_e = h W2_e^T.  Equivalent to moe_ffn_gemm1_fwd followed by moe_ffn_gemm2_fwd.
  * x_perm [R, d] act; ab [R, 2f] act written (a in columns [0, f), b in [f, 2f), kept for
  * the backward); h [R, f] act written; y_perm [R, d] act written.  Accumulation is
- * float; with MOE_MXFP8 both GEMMs take E4M3 operands with one E8M0 scale per 32
- * elements along K (MXFP8 for the expert FFN: unite.ai, section "Παραλληλισμός,
- * Ακρίβεια και Τεχνικές Μνήμης"). */
+ * float; with MOE_MXFP8 the GEMMs in moe_shape.mx_scope take E4M3 operands with one E8M0
+ * scale per 32 elements along K (MXFP8 for the expert FFN: unite.ai, section
+ * "Παραλληλισμός, Ακρίβεια και Τεχνικές Μνήμης"). */
 moe_status moe_grouped_ffn_fwd(const moe_shape* s, const void* x_perm, const void* W1, const void* W3,
                                const void* W2, const int32_t* offsets, void* ab, void* h, void* y_perm,
                                void* ws, size_t ws_bytes, void* stream);
@@ -186,14 +205,21 @@ moe_status moe_combine(const moe_shape* s, const void* y_perm, const float* gate
 
 /* ---------------------------------------------------------------- backward */
 
-/* dy_perm[slot_row[t, j]] = gates[t, j] * dy[t];  dgates[t, j] = <dy[t], y_perm[slot_row[t, j]]>.
+/* Backward of moe_combine: dy_perm[slot_row[t, j]] = gates[t, j] * dy[t] and
+ * dgates[t, j] = <dy[t], y_perm[slot_row[t, j]]>.  The pages train the layer (forward and
+ * backward) and route every token through its experts, whose outputs it gets back
+ * (bigchange.ai, section "Главное изменение", where moving tokens to the experts is named
+ * as a cost of its own); the gate-weighted sum differentiated here is the reading taken for
+ * the combine.
  * dy [T, d] act, y_perm [R, d] act, gates [T, k] float; dy_perm [R, d] act and
  * dgates [T, k] float written. */
 moe_status moe_combine_bwd(const moe_shape* s, const void* dy, const void* y_perm, const float* gates,
                            const int32_t* slot_row, void* dy_perm, float* dgates, void* stream);
 
 /* Backward of the grouped FFN (equivalent to moe_ffn_dgrad2, moe_ffn_wgrad2,
- * moe_ffn_dgrad1, moe_ffn_wgrad1 in that order).
+ * moe_ffn_dgrad1, moe_ffn_wgrad1 in that order): the grouped expert GEMMs of the training
+ * step (unite.ai, section "Παραλληλισμός, Ακρίβεια και Τεχνικές Μνήμης"), differentiated for
+ * the SwiGLU reading of the expert FFN.
  *   dh = dy_e W2_e;  da = dh * b * s * (1 + a (1 - s)), db = dh * silu(a), s = sigmoid(a)
  *   dW2_e = dy_e^T h_e;  dx_e = da W1_e + db W3_e;  dW1_e = da^T X_e;  dW3_e = db^T X_e
  * dy_perm [R, d], x_perm [R, d], ab [R, 2f], h [R, f]: act inputs.  dab [R, 2f] act written
@@ -220,18 +246,23 @@ moe_status moe_ffn_wgrad1(const moe_shape* s, const void* x_perm, const void* da
                           void* dW1, void* dW3, void* ws, size_t ws_bytes, void* stream);
 
 /* Gradient of the gates w.r.t. the scores: dlogits[t, e] = g_e (dg_e - sum_i g_i dg_i) for
- * the k chosen experts, 0 for the others.  dgates, gates [T, k] float, topk_idx [T, k],
+ * the k chosen experts, 0 for the others (the derivative of the softmax gate of moe_route).
+ * The router is trained in the learned-routing rows (bigchange.ai, section "Что инженер
+ * может попробовать на практике").  dgates, gates [T, k] float, topk_idx [T, k],
  * dlogits [T, E] float (written in full). */
 moe_status moe_route_bwd(const moe_shape* s, const float* dgates, const float* gates,
                          const int32_t* topk_idx, float* dlogits, void* stream);
 
 /* Router backward: dx_r = dlogits Wr ([T, d] act, written), dWr = dlogits^T x ([E, d]
- * float, written).  The reduction over T is split into partial sums held in ws and added
+ * float, written), the gradients of the learned router's scores (bigchange.ai, section
+ * "Что инженер может попробовать на практике").  The reduction over T is split into partial sums held in ws and added
  * in a fixed order (deterministic). */
 moe_status moe_router_bwd(const moe_shape* s, const void* x, const void* Wr, const float* dlogits,
                           void* dx_r, float* dWr, void* ws, size_t ws_bytes, void* stream);
 
-/* Un-permute and sum: dx[t] = dx_r[t] + dx_add[t] + sum_j dx_perm[slot_row[t, j]] (float
+/* Un-permute and sum, the backward of the rowwise dispatch (unite.ai, section
+ * "Παραλληλισμός, Ακρίβεια και Τεχνικές Μνήμης"): each token gathers the input gradients of
+ * its k routed rows.  dx[t] = dx_r[t] + dx_add[t] + sum_j dx_perm[slot_row[t, j]] (float
  * accumulation in that order; dx_r, the router's input gradient, and dx_add, the shared
  * expert's, may each be NULL).  dx_perm [R, d], dx_r / dx_add [T, d], dx [T, d] act. */
 moe_status moe_permute_bwd(const moe_shape* s, const void* dx_perm, const int32_t* slot_row,
@@ -305,7 +336,8 @@ moe_status moe_combine_bwd_mx(const moe_shape* s, const void* dy, const void* y_
  *   dgrad2_mx:    dy rows (q_rows, s_rows of moe_combine_bwd_mx)
  *   wgrad2_mx:    dy columns (q_cols, s_cols of moe_combine_bwd_mx)
  *   wgrad1_mx:    x columns (q_cols, s_cols of moe_permute_mx)
- * Other arguments, workspace and errors as the bf16-operand calls. */
+ * Each needs its GEMM in moe_shape.mx_scope (MOE_EUNSUPPORTED otherwise, before anything is
+ * enqueued).  Other arguments, workspace and errors as the bf16-operand calls. */
 moe_status moe_ffn_gemm1_fwd_mx(const moe_shape* s, const uint8_t* xq_rows, const uint8_t* xs_rows,
                                 const void* W1, const void* W3, const int32_t* offsets, void* ab, void* h,
                                 void* ws, size_t ws_bytes, void* stream);

@@ -3,8 +3,14 @@
 // device memory; every routing quantity stays on the device.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cstddef>
 #include <cstdint>
+#include <cstdlib>
+#include <map>
+#include <mutex>
+#include <string>
+#include <tuple>
 
 #include "../../include/moe.h"
 #include "gemm.h"
@@ -13,16 +19,51 @@
 
 namespace moe {
 
-int device_cu_count() {
-  static int cached[64] = {0};
+namespace {
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_cu_count[kMaxDevices];  // 0: not yet read
+std::mutex g_state_mu;                     // guards the two maps below
+std::map<std::tuple<int, const void*, int, size_t>, int> g_occupancy;
+std::map<std::string, std::string> g_env;  // names read so far; "\x01" marks an unset name
+
+int current_device() {
   int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
-  if (cached[dev] == 0) {
-    int n = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) dev = 0;
+  return dev;
+}
+}  // namespace
+
+int device_cu_count() {
+  const int dev = current_device();
+  int n = g_cu_count[dev].load(std::memory_order_relaxed);
+  if (n == 0) {  // every thread that races here reads the same attribute
     if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
-    cached[dev] = n;
+    g_cu_count[dev].store(n, std::memory_order_relaxed);
   }
-  return cached[dev];
+  return n;
+}
+
+int kernel_occupancy(const void* kern, int threads, size_t dyn_lds) {
+  const auto key = std::make_tuple(current_device(), kern, threads, dyn_lds);
+  {
+    std::lock_guard<std::mutex> lk(g_state_mu);
+    auto it = g_occupancy.find(key);
+    if (it != g_occupancy.end()) return it->second;
+  }
+  int o = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&o, kern, threads, dyn_lds) != hipSuccess || o < 1) o = 1;
+  std::lock_guard<std::mutex> lk(g_state_mu);
+  return g_occupancy.emplace(key, o).first->second;
+}
+
+const char* tuning_env(const char* name) {
+  std::lock_guard<std::mutex> lk(g_state_mu);
+  auto it = g_env.find(name);
+  if (it == g_env.end()) {
+    const char* v = std::getenv(name);
+    it = g_env.emplace(name, v ? std::string(v) : std::string("\x01")).first;
+  }
+  return it->second == "\x01" ? nullptr : it->second.c_str();  // map nodes never move
 }
 
 }  // namespace moe

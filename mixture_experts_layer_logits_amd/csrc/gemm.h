@@ -18,8 +18,16 @@ struct TileCfg {
   static constexpr int WTM = BM / WAVES_M / 32, WTN = BN / WAVES_N / 32;
 };
 
-// Compute units of the current device (cached per device; host only).
+// Host-side launch state (capi.cpp).  Every cache is filled once and safe to read and fill
+// from several host threads at once.
+// Compute units of the current device (cached per device).
 int device_cu_count();
+// Resident workgroups per compute unit of `kern` at `threads` threads and `dyn_lds` bytes of
+// dynamic LDS on the current device (at least 1; cached per device, kernel and sizes).
+int kernel_occupancy(const void* kern, int threads, size_t dyn_lds);
+// A tuning override from the environment (MOE_TILE_*, MOE_GEMM_*, MOE_MX_TILE), read at the
+// first request of each name and kept for the life of the process; nullptr when unset.
+const char* tuning_env(const char* name);
 
 // Expert-GEMM sizes: R routed rows, d model width, f hidden width, E experts.
 struct GemmShape {

@@ -701,12 +701,12 @@ static TileChoice tile_for(const char* name, Tile dflt, int dflt_bk, int dflt_st
   char key[64];
   snprintf(key, sizeof key, "MOE_TILE_%s", name);
   Tile t = dflt;
-  if (!parse_tile(getenv(key), &t)) parse_tile(getenv("MOE_TILE"), &t);
-  const char* bk = getenv("MOE_GEMM_BK");
+  if (!parse_tile(tuning_env(key), &t)) parse_tile(tuning_env("MOE_TILE"), &t);
+  const char* bk = tuning_env("MOE_GEMM_BK");
   const int b = bk ? atoi(bk) : dflt_bk;
-  const char* ns = getenv("MOE_GEMM_STAGES");
+  const char* ns = tuning_env("MOE_GEMM_STAGES");
   const int n = ns ? atoi(ns) : dflt_stages;
-  const char* nl = getenv("MOE_GEMM_LOADERS");
+  const char* nl = tuning_env("MOE_GEMM_LOADERS");
   const int l = nl ? atoi(nl) : dflt_loaders;
   return TileChoice{t, b == 64 ? 64 : 32, n == 4 ? 4 : (n == 2 ? 2 : 3), l == 4 ? 4 : 0};
 }
@@ -714,12 +714,8 @@ static TileChoice tile_for(const char* name, Tile dflt, int dflt_bk, int dflt_st
 // Persistent grid: resident workgroups per CU x CUs, capped by the tile bound known on the
 // host, rounded to a multiple of the 8 XCDs.
 template <class Cfg, class Prob, class Kern>
-static hipError_t launch_kernel(Kern kern, const Prob& p, hipStream_t st, int& occ, size_t dyn_lds, int threads) {
-  if (occ == 0) {
-    int o = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&o, kern, threads, dyn_lds) != hipSuccess || o < 1) o = 1;
-    occ = o;
-  }
+static hipError_t launch_kernel(Kern kern, const Prob& p, hipStream_t st, size_t dyn_lds, int threads) {
+  const int occ = kernel_occupancy(reinterpret_cast<const void*>(kern), threads, dyn_lds);
   int64_t bound;
   const int64_t ntn = (p.N + Cfg::BN - 1) / Cfg::BN;
   if constexpr (Prob::GROUP == Group::M) bound = ((int64_t)p.M / Cfg::BM + p.E) * ntn;
@@ -734,10 +730,8 @@ static hipError_t launch_kernel(Kern kern, const Prob& p, hipStream_t st, int& o
 
 template <class Cfg, class Prob, int TK, int NS, int NL = 0>
 static hipError_t launch_pipe(const Prob& p, hipStream_t st) {
-  // occupancy depends on the dynamic LDS, i.e. on the expert count: cache it per count
-  static int occ_e = -1, occ = 0;
-  if (occ_e != p.E) { occ_e = p.E; occ = 0; }
-  return launch_kernel<Cfg>(grouped_gemm_pipe_kernel<Cfg, Prob, TK, NS, NL>, p, st, occ, pipe_dyn_lds_bytes(p.E),
+  // occupancy depends on the dynamic LDS, i.e. on the expert count (cached per size)
+  return launch_kernel<Cfg>(grouped_gemm_pipe_kernel<Cfg, Prob, TK, NS, NL>, p, st, pipe_dyn_lds_bytes(p.E),
                             Cfg::NT + 64 * NL);
 }
 

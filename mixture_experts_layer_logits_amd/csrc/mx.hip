@@ -895,13 +895,8 @@ template <class Cfg, int NS, class Prob>
 static hipError_t launch_mx_cfg(const Prob& p, hipStream_t st) {
   const auto kern = mx_gemm_kernel<Cfg, Prob, 128, NS>;
   const size_t dyn = mx_dyn_lds_bytes(p.E);
-  static int occ_e = -1, occ = 0;  // occupancy depends on the dynamic LDS, i.e. on E
-  if (occ_e != p.E) { occ_e = p.E; occ = 0; }
-  if (occ == 0) {
-    int o = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&o, kern, Cfg::NT, dyn) != hipSuccess || o < 1) o = 1;
-    occ = o;
-  }
+  // occupancy depends on the dynamic LDS, i.e. on E (cached per size)
+  const int occ = kernel_occupancy(reinterpret_cast<const void*>(kern), Cfg::NT, dyn);
   int64_t bound;
   const int64_t ntn = (p.N + Cfg::BN - 1) / Cfg::BN;
   if constexpr (Prob::GROUP == Group::M) bound = ((int64_t)p.M / Cfg::BM + p.E) * ntn;
@@ -923,7 +918,7 @@ template <class Prob>
 static hipError_t launch_mx(const Prob& p, hipStream_t st) {
   const int64_t rows = Prob::GROUP == Group::M ? p.M : p.K;
   bool big = rows >= (int64_t)1024 * p.E;
-  if (const char* v = getenv("MOE_MX_TILE")) big = strcmp(v, "256x256") == 0;
+  if (const char* v = tuning_env("MOE_MX_TILE")) big = strcmp(v, "256x256") == 0;
   if (big) return launch_mx_cfg<TileCfg<256, 256, 2, 4>, 2>(p, st);
   return launch_mx_cfg<TileCfg<128, 256, 2, 4>, 3>(p, st);
 }

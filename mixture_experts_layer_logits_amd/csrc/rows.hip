@@ -39,10 +39,10 @@ __global__ void __launch_bounds__(kThreads) permute_kernel(int ntok, int d, int 
 }
 
 // Gathers (combine, un-permute) read k rows per token: a wave takes its token's slot rows
-// and gates into lanes once (broadcast with shuffles), then issues the loads of two
-// 16-byte chunks of all k rows before any arithmetic, so up to 2k loads per lane are in
-// flight.  k > kGatherK falls back to one row at a time.
-constexpr int kGatherK = 8;
+// and gates into lanes once (broadcast with shuffles), then issues the loads of U 16-byte
+// chunks of all k rows before any arithmetic.  k <= 4 runs four chunks per lane and pass
+// (a whole 2048-wide row per wave pass; cold at T = 8192, d = 2048, E = 128 that was 8-9%
+// faster than two for combine and un-permute), k <= 8 two, larger k one row at a time.
 
 template <typename T>
 __device__ __forceinline__ void widen8(const uint4& q, float (&v)[8]);
@@ -56,8 +56,9 @@ __device__ __forceinline__ void widen8<bf16_t>(const uint4& q, float (&v)[8]) {
   }
 }
 
-// y[t] = y_add[t] + sum_j gates[t, j] * y_perm[slot_row[t, j]]   (y_add may be null)
-template <typename T>
+// y[t] = y_add[t] + sum_j gates[t, j] * y_perm[slot_row[t, j]]   (y_add may be null).
+// KG > 0 (bf16, k <= KG): U chunks per lane and pass, all k rows' loads issued first.
+template <typename T, int KG, int U>
 __global__ void __launch_bounds__(kThreads) combine_kernel(int ntok, int d, int k, const T* __restrict__ y_perm,
                                                            const float* __restrict__ gates,
                                                            const int32_t* __restrict__ slot_row,
@@ -66,43 +67,41 @@ __global__ void __launch_bounds__(kThreads) combine_kernel(int ntok, int d, int 
   const int lane = threadIdx.x & 63;
   if (t >= ntok) return;
   const int nchunk = d / 8;
-  if constexpr (sizeof(T) == 2) {
-    if (k <= kGatherK) {
-      const int my_r = lane < k ? slot_row[(int64_t)t * k + lane] : 0;
-      const float my_g = lane < k ? gates[(int64_t)t * k + lane] : 0.f;
-      for (int c0 = lane; c0 < nchunk; c0 += 2 * kWave) {
-        uint4 q[2][kGatherK + 1];
+  if constexpr (KG > 0) {
+    const int my_r = lane < k ? slot_row[(int64_t)t * k + lane] : 0;
+    const float my_g = lane < k ? gates[(int64_t)t * k + lane] : 0.f;
+    for (int c0 = lane; c0 < nchunk; c0 += U * kWave) {
+      uint4 q[U][KG + 1];
 #pragma unroll
-        for (int u = 0; u < 2; u++) {
-          const int c = c0 + u * kWave;
-          q[u][kGatherK] = make_uint4(0, 0, 0, 0);
-          if (y_add && c < nchunk) q[u][kGatherK] = *reinterpret_cast<const uint4*>(y_add + (int64_t)t * d + c * 8);
+      for (int u = 0; u < U; u++) {
+        const int c = c0 + u * kWave;
+        q[u][KG] = make_uint4(0, 0, 0, 0);
+        if (y_add && c < nchunk) q[u][KG] = *reinterpret_cast<const uint4*>(y_add + (int64_t)t * d + c * 8);
 #pragma unroll
-          for (int j = 0; j < kGatherK; j++) {
-            const int r = __shfl(my_r, j, kWave);
-            if (j < k && c < nchunk) q[u][j] = *reinterpret_cast<const uint4*>(y_perm + (int64_t)r * d + c * 8);
-          }
-        }
-#pragma unroll
-        for (int u = 0; u < 2; u++) {
-          const int c = c0 + u * kWave;
-          if (c >= nchunk) break;
-          float acc[8];
-          widen8<T>(q[u][kGatherK], acc);
-#pragma unroll
-          for (int j = 0; j < kGatherK; j++) {
-            if (j >= k) break;
-            const float g = __shfl(my_g, j, kWave);
-            float v[8];
-            widen8<T>(q[u][j], v);
-#pragma unroll
-            for (int i = 0; i < 8; i++) acc[i] = fmaf(g, v[i], acc[i]);
-          }
-          store8<T>(y + (int64_t)t * d + c * 8, acc);
+        for (int j = 0; j < KG; j++) {
+          const int r = __shfl(my_r, j, kWave);
+          if (j < k && c < nchunk) q[u][j] = *reinterpret_cast<const uint4*>(y_perm + (int64_t)r * d + c * 8);
         }
       }
-      return;
+#pragma unroll
+      for (int u = 0; u < U; u++) {
+        const int c = c0 + u * kWave;
+        if (c >= nchunk) break;
+        float acc[8];
+        widen8<T>(q[u][KG], acc);
+#pragma unroll
+        for (int j = 0; j < KG; j++) {
+          if (j >= k) break;
+          const float g = __shfl(my_g, j, kWave);
+          float v[8];
+          widen8<T>(q[u][j], v);
+#pragma unroll
+          for (int i = 0; i < 8; i++) acc[i] = fmaf(g, v[i], acc[i]);
+        }
+        store8<T>(y + (int64_t)t * d + c * 8, acc);
+      }
     }
+    return;
   }
   for (int c = lane; c < nchunk; c += kWave) {
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
@@ -119,8 +118,10 @@ __global__ void __launch_bounds__(kThreads) combine_kernel(int ntok, int d, int 
   }
 }
 
-// dy_perm[slot_row[t, j]] = gates[t, j] * dy[t];  dgates[t, j] = <dy[t], y_perm[slot_row[t, j]]>
-template <typename T>
+// dy_perm[slot_row[t, j]] = gates[t, j] * dy[t];  dgates[t, j] = <dy[t], y_perm[slot_row[t, j]]>.
+// KG > 0 (bf16, k <= KG): dy read once per chunk, U chunks per lane and pass with all k
+// rows' loads issued first.  Each lane sums its chunks in ascending order whatever U is.
+template <typename T, int KG, int U>
 __global__ void __launch_bounds__(kThreads) combine_bwd_kernel(int ntok, int d, int k, const T* __restrict__ dy,
                                                                const T* __restrict__ y_perm,
                                                                const float* __restrict__ gates,
@@ -130,55 +131,53 @@ __global__ void __launch_bounds__(kThreads) combine_bwd_kernel(int ntok, int d, 
   const int lane = threadIdx.x & 63;
   if (t >= ntok) return;
   const int nchunk = d / 8;
-  if constexpr (sizeof(T) == 2) {
-    if (k <= kGatherK) {  // dy read once per chunk, the k rows' loads of two chunks issued together
-      const int my_r = lane < k ? slot_row[(int64_t)t * k + lane] : 0;
-      const float my_g = lane < k ? gates[(int64_t)t * k + lane] : 0.f;
-      float dot[kGatherK];
+  if constexpr (KG > 0) {
+    const int my_r = lane < k ? slot_row[(int64_t)t * k + lane] : 0;
+    const float my_g = lane < k ? gates[(int64_t)t * k + lane] : 0.f;
+    float dot[KG];
 #pragma unroll
-      for (int j = 0; j < kGatherK; j++) dot[j] = 0.f;
-      for (int c0 = lane; c0 < nchunk; c0 += 2 * kWave) {
-        uint4 q[2][kGatherK + 1];
+    for (int j = 0; j < KG; j++) dot[j] = 0.f;
+    for (int c0 = lane; c0 < nchunk; c0 += U * kWave) {
+      uint4 q[U][KG + 1];
 #pragma unroll
-        for (int u = 0; u < 2; u++) {
-          const int c = c0 + u * kWave;
-          if (c < nchunk) q[u][kGatherK] = *reinterpret_cast<const uint4*>(dy + (int64_t)t * d + c * 8);
+      for (int u = 0; u < U; u++) {
+        const int c = c0 + u * kWave;
+        if (c < nchunk) q[u][KG] = *reinterpret_cast<const uint4*>(dy + (int64_t)t * d + c * 8);
 #pragma unroll
-          for (int j = 0; j < kGatherK; j++) {
-            const int r = __shfl(my_r, j, kWave);
-            if (j < k && c < nchunk) q[u][j] = *reinterpret_cast<const uint4*>(y_perm + (int64_t)r * d + c * 8);
-          }
-        }
-#pragma unroll
-        for (int u = 0; u < 2; u++) {
-          const int c = c0 + u * kWave;
-          if (c >= nchunk) break;
-          float du[8];
-          widen8<T>(q[u][kGatherK], du);
-#pragma unroll
-          for (int j = 0; j < kGatherK; j++) {
-            if (j >= k) break;
-            const int r = __shfl(my_r, j, kWave);
-            const float g = __shfl(my_g, j, kWave);
-            float v[8], o[8];
-            widen8<T>(q[u][j], v);
-#pragma unroll
-            for (int i = 0; i < 8; i++) {
-              dot[j] = fmaf(du[i], v[i], dot[j]);
-              o[i] = g * du[i];
-            }
-            store8<T>(dy_perm + (int64_t)r * d + c * 8, o);
-          }
+        for (int j = 0; j < KG; j++) {
+          const int r = __shfl(my_r, j, kWave);
+          if (j < k && c < nchunk) q[u][j] = *reinterpret_cast<const uint4*>(y_perm + (int64_t)r * d + c * 8);
         }
       }
 #pragma unroll
-      for (int j = 0; j < kGatherK; j++) {
-        if (j >= k) break;
-        const float sj = wave_sum(dot[j]);
-        if (lane == 0) dgates[(int64_t)t * k + j] = sj;
+      for (int u = 0; u < U; u++) {
+        const int c = c0 + u * kWave;
+        if (c >= nchunk) break;
+        float du[8];
+        widen8<T>(q[u][KG], du);
+#pragma unroll
+        for (int j = 0; j < KG; j++) {
+          if (j >= k) break;
+          const int r = __shfl(my_r, j, kWave);
+          const float g = __shfl(my_g, j, kWave);
+          float v[8], o[8];
+          widen8<T>(q[u][j], v);
+#pragma unroll
+          for (int i = 0; i < 8; i++) {
+            dot[j] = fmaf(du[i], v[i], dot[j]);
+            o[i] = g * du[i];
+          }
+          store8<T>(dy_perm + (int64_t)r * d + c * 8, o);
+        }
       }
-      return;
     }
+#pragma unroll
+    for (int j = 0; j < KG; j++) {
+      if (j >= k) break;
+      const float sj = wave_sum(dot[j]);
+      if (lane == 0) dgates[(int64_t)t * k + j] = sj;
+    }
+    return;
   }
   for (int j = 0; j < k; j++) {
     const int r = slot_row[(int64_t)t * k + j];
@@ -203,7 +202,8 @@ __global__ void __launch_bounds__(kThreads) combine_bwd_kernel(int ntok, int d, 
 // dgates[t, j] = <dy[t], y_perm[slot_row[t, j]]> alone (the routed gradient rows are
 // written elsewhere).  Same per-lane order as combine_bwd_kernel (chunks ascending, the 8
 // elements of a chunk in order, then a butterfly over the wave), so the two agree bit for
-// bit; the k rows' loads of two chunks are issued before any arithmetic, as there.
+// bit; U chunks per lane and pass, the k rows' loads issued before any arithmetic.
+template <int KG, int U>
 __global__ void __launch_bounds__(kThreads) dgates_kernel(int ntok, int d, int k, const bf16_t* __restrict__ dy,
                                                           const bf16_t* __restrict__ y_perm,
                                                           const int32_t* __restrict__ slot_row,
@@ -212,7 +212,7 @@ __global__ void __launch_bounds__(kThreads) dgates_kernel(int ntok, int d, int k
   const int lane = threadIdx.x & 63;
   if (t >= ntok) return;
   const int nchunk = d / 8;
-  if (k > kGatherK) {  // one row at a time
+  if constexpr (KG == 0) {  // one row at a time
     for (int j = 0; j < k; j++) {
       const int r = slot_row[(int64_t)t * k + j];
       float dot = 0.f;
@@ -227,43 +227,44 @@ __global__ void __launch_bounds__(kThreads) dgates_kernel(int ntok, int d, int k
       if (lane == 0) dgates[(int64_t)t * k + j] = dot;
     }
     return;
-  }
-  const int my_r = lane < k ? slot_row[(int64_t)t * k + lane] : 0;
-  float dot[kGatherK];
+  } else {
+    const int my_r = lane < k ? slot_row[(int64_t)t * k + lane] : 0;
+    float dot[KG];
 #pragma unroll
-  for (int j = 0; j < kGatherK; j++) dot[j] = 0.f;
-  for (int c0 = lane; c0 < nchunk; c0 += 2 * kWave) {
-    uint4 q[2][kGatherK + 1];
+    for (int j = 0; j < KG; j++) dot[j] = 0.f;
+    for (int c0 = lane; c0 < nchunk; c0 += U * kWave) {
+      uint4 q[U][KG + 1];
 #pragma unroll
-    for (int u = 0; u < 2; u++) {
-      const int c = c0 + u * kWave;
-      if (c < nchunk) q[u][kGatherK] = *reinterpret_cast<const uint4*>(dy + (int64_t)t * d + c * 8);
+      for (int u = 0; u < U; u++) {
+        const int c = c0 + u * kWave;
+        if (c < nchunk) q[u][KG] = *reinterpret_cast<const uint4*>(dy + (int64_t)t * d + c * 8);
 #pragma unroll
-      for (int j = 0; j < kGatherK; j++) {
-        const int r = __shfl(my_r, j, kWave);
-        if (j < k && c < nchunk) q[u][j] = *reinterpret_cast<const uint4*>(y_perm + (int64_t)r * d + c * 8);
+        for (int j = 0; j < KG; j++) {
+          const int r = __shfl(my_r, j, kWave);
+          if (j < k && c < nchunk) q[u][j] = *reinterpret_cast<const uint4*>(y_perm + (int64_t)r * d + c * 8);
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < U; u++) {
+        if (c0 + u * kWave >= nchunk) break;
+        float du[8];
+        widen8<bf16_t>(q[u][KG], du);
+#pragma unroll
+        for (int j = 0; j < KG; j++) {
+          if (j >= k) break;
+          float v[8];
+          widen8<bf16_t>(q[u][j], v);
+#pragma unroll
+          for (int i = 0; i < 8; i++) dot[j] = fmaf(du[i], v[i], dot[j]);
+        }
       }
     }
 #pragma unroll
-    for (int u = 0; u < 2; u++) {
-      if (c0 + u * kWave >= nchunk) break;
-      float du[8];
-      widen8<bf16_t>(q[u][kGatherK], du);
-#pragma unroll
-      for (int j = 0; j < kGatherK; j++) {
-        if (j >= k) break;
-        float v[8];
-        widen8<bf16_t>(q[u][j], v);
-#pragma unroll
-        for (int i = 0; i < 8; i++) dot[j] = fmaf(du[i], v[i], dot[j]);
-      }
+    for (int j = 0; j < KG; j++) {
+      if (j >= k) break;
+      const float sm = wave_sum(dot[j]);
+      if (lane == 0) dgates[(int64_t)t * k + j] = sm;
     }
-  }
-#pragma unroll
-  for (int j = 0; j < kGatherK; j++) {
-    if (j >= k) break;
-    const float s = wave_sum(dot[j]);
-    if (lane == 0) dgates[(int64_t)t * k + j] = s;
   }
 }
 
@@ -273,8 +274,9 @@ __global__ void row_src_kernel(int nslot, int k, const int32_t* __restrict__ slo
   if (i < nslot) row_src[slot_row[i]] = i / k;
 }
 
-// dx[t] = dx_r[t] + dx_add[t] + sum_j dx_perm[slot_row[t, j]]   (dx_r, dx_add may be null)
-template <typename T>
+// dx[t] = dx_r[t] + dx_add[t] + sum_j dx_perm[slot_row[t, j]]   (dx_r, dx_add may be null).
+// KG > 0 (bf16, k <= KG): U chunks per lane and pass, all loads issued first.
+template <typename T, int KG, int U>
 __global__ void __launch_bounds__(kThreads) unpermute_sum_kernel(int ntok, int d, int k, const T* __restrict__ dx_perm,
                                                                  const int32_t* __restrict__ slot_row,
                                                                  const T* __restrict__ dx_r,
@@ -283,47 +285,44 @@ __global__ void __launch_bounds__(kThreads) unpermute_sum_kernel(int ntok, int d
   const int lane = threadIdx.x & 63;
   if (t >= ntok) return;
   const int nchunk = d / 8;
-  if constexpr (sizeof(T) == 2) {
-    if (k <= kGatherK) {
-      const int my_r = lane < k ? slot_row[(int64_t)t * k + lane] : 0;
-      for (int c0 = lane; c0 < nchunk; c0 += 2 * kWave) {
-        uint4 q[2][kGatherK + 2];
+  if constexpr (KG > 0) {
+    const int my_r = lane < k ? slot_row[(int64_t)t * k + lane] : 0;
+    for (int c0 = lane; c0 < nchunk; c0 += U * kWave) {
+      uint4 q[U][KG + 2];
 #pragma unroll
-        for (int u = 0; u < 2; u++) {
-          const int c = c0 + u * kWave;
-          q[u][kGatherK] = make_uint4(0, 0, 0, 0);
-          q[u][kGatherK + 1] = make_uint4(0, 0, 0, 0);
-          if (dx_r && c < nchunk) q[u][kGatherK] = *reinterpret_cast<const uint4*>(dx_r + (int64_t)t * d + c * 8);
-          if (dx_add && c < nchunk)
-            q[u][kGatherK + 1] = *reinterpret_cast<const uint4*>(dx_add + (int64_t)t * d + c * 8);
+      for (int u = 0; u < U; u++) {
+        const int c = c0 + u * kWave;
+        q[u][KG] = make_uint4(0, 0, 0, 0);
+        q[u][KG + 1] = make_uint4(0, 0, 0, 0);
+        if (dx_r && c < nchunk) q[u][KG] = *reinterpret_cast<const uint4*>(dx_r + (int64_t)t * d + c * 8);
+        if (dx_add && c < nchunk) q[u][KG + 1] = *reinterpret_cast<const uint4*>(dx_add + (int64_t)t * d + c * 8);
 #pragma unroll
-          for (int j = 0; j < kGatherK; j++) {
-            const int r = __shfl(my_r, j, kWave);
-            if (j < k && c < nchunk) q[u][j] = *reinterpret_cast<const uint4*>(dx_perm + (int64_t)r * d + c * 8);
-          }
-        }
-#pragma unroll
-        for (int u = 0; u < 2; u++) {
-          const int c = c0 + u * kWave;
-          if (c >= nchunk) break;
-          float acc[8], w[8];
-          widen8<T>(q[u][kGatherK], acc);
-          widen8<T>(q[u][kGatherK + 1], w);
-#pragma unroll
-          for (int i = 0; i < 8; i++) acc[i] += w[i];
-#pragma unroll
-          for (int j = 0; j < kGatherK; j++) {
-            if (j >= k) break;
-            float v[8];
-            widen8<T>(q[u][j], v);
-#pragma unroll
-            for (int i = 0; i < 8; i++) acc[i] += v[i];
-          }
-          store8<T>(dx + (int64_t)t * d + c * 8, acc);
+        for (int j = 0; j < KG; j++) {
+          const int r = __shfl(my_r, j, kWave);
+          if (j < k && c < nchunk) q[u][j] = *reinterpret_cast<const uint4*>(dx_perm + (int64_t)r * d + c * 8);
         }
       }
-      return;
+#pragma unroll
+      for (int u = 0; u < U; u++) {
+        const int c = c0 + u * kWave;
+        if (c >= nchunk) break;
+        float acc[8], w[8];
+        widen8<T>(q[u][KG], acc);
+        widen8<T>(q[u][KG + 1], w);
+#pragma unroll
+        for (int i = 0; i < 8; i++) acc[i] += w[i];
+#pragma unroll
+        for (int j = 0; j < KG; j++) {
+          if (j >= k) break;
+          float v[8];
+          widen8<T>(q[u][j], v);
+#pragma unroll
+          for (int i = 0; i < 8; i++) acc[i] += v[i];
+        }
+        store8<T>(dx + (int64_t)t * d + c * 8, acc);
+      }
     }
+    return;
   }
   for (int c = lane; c < nchunk; c += kWave) {
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
@@ -361,34 +360,57 @@ hipError_t permute_rows(int eb, int T, int d, int k, const void* x, const int32_
   return hipGetLastError();
 }
 
+// bf16 gather kernels by the token's expert count: <KG, U> = <4, 4> for k <= 4, <8, 2> for
+// k <= 8, one row at a time beyond.  fp32 rows always take the row-at-a-time loop.
 hipError_t combine_rows(int eb, int T, int d, int k, const void* y_perm, const float* gates, const int32_t* slot_row,
                         const void* y_add, void* y, hipStream_t st) {
   if (T == 0) return hipSuccess;
-  if (eb == 2)
-    hipLaunchKernelGGL(combine_kernel<bf16_t>, tok_grid(T), dim3(kThreads), 0, st, T, d, k, (const bf16_t*)y_perm,
-                       gates, slot_row, (const bf16_t*)y_add, (bf16_t*)y);
-  else
-    hipLaunchKernelGGL(combine_kernel<float>, tok_grid(T), dim3(kThreads), 0, st, T, d, k, (const float*)y_perm, gates,
-                       slot_row, (const float*)y_add, (float*)y);
+  if (eb == 2) {
+    if (k <= 4)
+      hipLaunchKernelGGL((combine_kernel<bf16_t, 4, 4>), tok_grid(T), dim3(kThreads), 0, st, T, d, k,
+                         (const bf16_t*)y_perm, gates, slot_row, (const bf16_t*)y_add, (bf16_t*)y);
+    else if (k <= 8)
+      hipLaunchKernelGGL((combine_kernel<bf16_t, 8, 2>), tok_grid(T), dim3(kThreads), 0, st, T, d, k,
+                         (const bf16_t*)y_perm, gates, slot_row, (const bf16_t*)y_add, (bf16_t*)y);
+    else
+      hipLaunchKernelGGL((combine_kernel<bf16_t, 0, 1>), tok_grid(T), dim3(kThreads), 0, st, T, d, k,
+                         (const bf16_t*)y_perm, gates, slot_row, (const bf16_t*)y_add, (bf16_t*)y);
+  } else {
+    hipLaunchKernelGGL((combine_kernel<float, 0, 1>), tok_grid(T), dim3(kThreads), 0, st, T, d, k, (const float*)y_perm,
+                       gates, slot_row, (const float*)y_add, (float*)y);
+  }
   return hipGetLastError();
 }
 
 hipError_t combine_rows_bwd(int eb, int T, int d, int k, const void* dy, const void* y_perm, const float* gates,
                             const int32_t* slot_row, void* dy_perm, float* dgates, hipStream_t st) {
   if (T == 0) return hipSuccess;
-  if (eb == 2)
-    hipLaunchKernelGGL(combine_bwd_kernel<bf16_t>, tok_grid(T), dim3(kThreads), 0, st, T, d, k, (const bf16_t*)dy,
-                       (const bf16_t*)y_perm, gates, slot_row, (bf16_t*)dy_perm, dgates);
-  else
-    hipLaunchKernelGGL(combine_bwd_kernel<float>, tok_grid(T), dim3(kThreads), 0, st, T, d, k, (const float*)dy,
-                       (const float*)y_perm, gates, slot_row, (float*)dy_perm, dgates);
+  if (eb == 2) {
+    if (k <= 4)
+      hipLaunchKernelGGL((combine_bwd_kernel<bf16_t, 4, 4>), tok_grid(T), dim3(kThreads), 0, st, T, d, k,
+                         (const bf16_t*)dy, (const bf16_t*)y_perm, gates, slot_row, (bf16_t*)dy_perm, dgates);
+    else if (k <= 8)
+      hipLaunchKernelGGL((combine_bwd_kernel<bf16_t, 8, 2>), tok_grid(T), dim3(kThreads), 0, st, T, d, k,
+                         (const bf16_t*)dy, (const bf16_t*)y_perm, gates, slot_row, (bf16_t*)dy_perm, dgates);
+    else
+      hipLaunchKernelGGL((combine_bwd_kernel<bf16_t, 0, 1>), tok_grid(T), dim3(kThreads), 0, st, T, d, k,
+                         (const bf16_t*)dy, (const bf16_t*)y_perm, gates, slot_row, (bf16_t*)dy_perm, dgates);
+  } else {
+    hipLaunchKernelGGL((combine_bwd_kernel<float, 0, 1>), tok_grid(T), dim3(kThreads), 0, st, T, d, k,
+                       (const float*)dy, (const float*)y_perm, gates, slot_row, (float*)dy_perm, dgates);
+  }
   return hipGetLastError();
 }
 
 hipError_t dgates_rows(int T, int d, int k, const bf16_t* dy, const bf16_t* y_perm, const int32_t* slot_row,
                        float* dgates, hipStream_t st) {
   if (T == 0) return hipSuccess;
-  hipLaunchKernelGGL(dgates_kernel, tok_grid(T), dim3(kThreads), 0, st, T, d, k, dy, y_perm, slot_row, dgates);
+  if (k <= 4)
+    hipLaunchKernelGGL((dgates_kernel<4, 4>), tok_grid(T), dim3(kThreads), 0, st, T, d, k, dy, y_perm, slot_row, dgates);
+  else if (k <= 8)
+    hipLaunchKernelGGL((dgates_kernel<8, 2>), tok_grid(T), dim3(kThreads), 0, st, T, d, k, dy, y_perm, slot_row, dgates);
+  else
+    hipLaunchKernelGGL((dgates_kernel<0, 1>), tok_grid(T), dim3(kThreads), 0, st, T, d, k, dy, y_perm, slot_row, dgates);
   return hipGetLastError();
 }
 
@@ -402,12 +424,20 @@ hipError_t row_src_rows(int T, int k, const int32_t* slot_row, int32_t* row_src,
 hipError_t unpermute_sum_rows(int eb, int T, int d, int k, const void* dx_perm, const int32_t* slot_row,
                               const void* dx_r, const void* dx_add, void* dx, hipStream_t st) {
   if (T == 0) return hipSuccess;
-  if (eb == 2)
-    hipLaunchKernelGGL(unpermute_sum_kernel<bf16_t>, tok_grid(T), dim3(kThreads), 0, st, T, d, k,
-                       (const bf16_t*)dx_perm, slot_row, (const bf16_t*)dx_r, (const bf16_t*)dx_add, (bf16_t*)dx);
-  else
-    hipLaunchKernelGGL(unpermute_sum_kernel<float>, tok_grid(T), dim3(kThreads), 0, st, T, d, k,
+  if (eb == 2) {
+    if (k <= 4)
+      hipLaunchKernelGGL((unpermute_sum_kernel<bf16_t, 4, 4>), tok_grid(T), dim3(kThreads), 0, st, T, d, k,
+                         (const bf16_t*)dx_perm, slot_row, (const bf16_t*)dx_r, (const bf16_t*)dx_add, (bf16_t*)dx);
+    else if (k <= 8)
+      hipLaunchKernelGGL((unpermute_sum_kernel<bf16_t, 8, 2>), tok_grid(T), dim3(kThreads), 0, st, T, d, k,
+                         (const bf16_t*)dx_perm, slot_row, (const bf16_t*)dx_r, (const bf16_t*)dx_add, (bf16_t*)dx);
+    else
+      hipLaunchKernelGGL((unpermute_sum_kernel<bf16_t, 0, 1>), tok_grid(T), dim3(kThreads), 0, st, T, d, k,
+                         (const bf16_t*)dx_perm, slot_row, (const bf16_t*)dx_r, (const bf16_t*)dx_add, (bf16_t*)dx);
+  } else {
+    hipLaunchKernelGGL((unpermute_sum_kernel<float, 0, 1>), tok_grid(T), dim3(kThreads), 0, st, T, d, k,
                        (const float*)dx_perm, slot_row, (const float*)dx_r, (const float*)dx_add, (float*)dx);
+  }
   return hipGetLastError();
 }
 
