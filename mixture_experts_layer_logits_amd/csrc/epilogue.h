@@ -8,8 +8,13 @@
 //
 // Problem interface (all columns n are multiples of 4; rows m < m_end, n < N are checked
 // here, partial column groups are the problem's business):
-//   Epi::Store, Epi::DSwiGLU   p.epilogue4(e, m, n, v[4])          columns n .. n+3
+//   Epi::Store                 p.epilogue4(e, m, n, v[4])          columns n .. n+3
 //   Epi::SwiGLU                p.epilogue_swiglu4(m, hcol, a[4], b[4])
+//   Epi::DSwiGLU               p.prefetch4(m, n) -> AbPair, then p.epilogue4_pre(e, m, n, v[4], pair)
+// The SwiGLU gradient reads the saved a, b of every output position.  Those loads are issued
+// for a whole 32-row block of the wave before any of its stores: memory operations complete
+// in order on one counter, so a load issued after a store (or after the operand loads still
+// in flight for the next steps) would wait for all of them.
 #pragma once
 #include "common.h"
 #include "gemm.h"
@@ -60,6 +65,32 @@ __device__ __forceinline__ void load_bf16x4(const bf16_t* p, float (&v)[4]) {
   v[3] = __uint_as_float(q.y & 0xffff0000u);
 }
 
+// Saved a and b of four consecutive hidden columns of one row, packed bf16.
+struct AbPair {
+  uint2 a, b;
+};
+// ab [rows][2N] (a in columns [0, N), b in [N, 2N)): row m, columns n .. n+3
+__device__ __forceinline__ AbPair load_ab4(const bf16_t* ab, int N, int m, int n) {
+  const bf16_t* abr = ab + (int64_t)m * 2 * N;
+  return AbPair{*reinterpret_cast<const uint2*>(abr + n), *reinterpret_cast<const uint2*>(abr + N + n)};
+}
+// da = dh b s (1 + a (1 - s)), db = dh silu(a), s = sigmoid(a); stored bf16 to dab [rows][2N]
+__device__ __forceinline__ void dswiglu_store4(bf16_t* dab, int N, int m, int n, const float (&dh)[4],
+                                               const AbPair& pr) {
+  float a[4], b[4], da[4], db[4];
+  load_bf16x4(reinterpret_cast<const bf16_t*>(&pr.a), a);
+  load_bf16x4(reinterpret_cast<const bf16_t*>(&pr.b), b);
+#pragma unroll
+  for (int c = 0; c < 4; c++) {
+    const float s = sigmoidf_(a[c]);
+    da[c] = dh[c] * b[c] * s * (1.f + a[c] * (1.f - s));
+    db[c] = dh[c] * a[c] * s;
+  }
+  bf16_t* o = dab + (int64_t)m * 2 * N;
+  store_bf16x4(o + n, da);
+  store_bf16x4(o + N + n, db);
+}
+
 // Writes the tile of wave (wave_m, wave_n) whose accumulators are acc.
 template <class Prob, int WTM, int WTN>
 __device__ __forceinline__ void tile_epilogue(const Prob& p, const f32x16 (&acc)[WTM][WTN], const TileRange& tr,
@@ -67,25 +98,24 @@ __device__ __forceinline__ void tile_epilogue(const Prob& p, const f32x16 (&acc)
   const int sub = lane & 3, quad = (lane & 31) >> 2, half = lane >> 5;
 #pragma unroll
   for (int i = 0; i < WTM; i++) {
+    if constexpr (Prob::EPI == Epi::DSwiGLU) {
+      // every saved (a, b) of the block first (rows and columns clamped into the tile, so no
+      // load is out of range or under a branch), then the gradients and their stores
+      AbPair pre[4][WTN];
 #pragma unroll
-    for (int q = 0; q < 4; q++) {
-      const int m = tr.m0 + (wave_m * WTM + i) * 32 + 8 * q + 4 * half + sub;
-      if constexpr (Prob::EPI == Epi::SwiGLU) {
-        // 32-column blocks alternate a (even j) and b (odd j) of the same h columns
+      for (int q = 0; q < 4; q++) {
+        int m = tr.m0 + (wave_m * WTM + i) * 32 + 8 * q + 4 * half + sub;
+        m = m < tr.m_end ? m : tr.m_end - 1;
 #pragma unroll
-        for (int j = 0; j < WTN; j += 2) {
-          float a[4], b[4];
-#pragma unroll
-          for (int c = 0; c < 4; c++) {
-            a[c] = acc[i][j][4 * q + c];
-            b[c] = acc[i][j + 1][4 * q + c];
-          }
-          quad_transpose(a, lane);
-          quad_transpose(b, lane);
-          const int hcol = tr.n0 / 2 + ((wave_n * WTN + j) >> 1) * 32 + 4 * quad;
-          if (m < tr.m_end && hcol < p.N / 2) p.epilogue_swiglu4(m, hcol, a, b);
+        for (int j = 0; j < WTN; j++) {
+          int n = tr.n0 + (wave_n * WTN + j) * 32 + 4 * quad;
+          n = n < p.N ? n : p.N - 4;
+          pre[q][j] = p.prefetch4(m, n);
         }
-      } else {
+      }
+#pragma unroll
+      for (int q = 0; q < 4; q++) {
+        const int m = tr.m0 + (wave_m * WTM + i) * 32 + 8 * q + 4 * half + sub;
 #pragma unroll
         for (int j = 0; j < WTN; j++) {
           float v[4];
@@ -93,7 +123,38 @@ __device__ __forceinline__ void tile_epilogue(const Prob& p, const f32x16 (&acc)
           for (int c = 0; c < 4; c++) v[c] = acc[i][j][4 * q + c];
           quad_transpose(v, lane);
           const int n = tr.n0 + (wave_n * WTN + j) * 32 + 4 * quad;
-          if (m < tr.m_end && n < p.N) p.epilogue4(tr.e, m, n, v);
+          if (m < tr.m_end && n < p.N) p.epilogue4_pre(tr.e, m, n, v, pre[q][j]);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int q = 0; q < 4; q++) {
+        const int m = tr.m0 + (wave_m * WTM + i) * 32 + 8 * q + 4 * half + sub;
+        if constexpr (Prob::EPI == Epi::SwiGLU) {
+          // 32-column blocks alternate a (even j) and b (odd j) of the same h columns
+#pragma unroll
+          for (int j = 0; j < WTN; j += 2) {
+            float a[4], b[4];
+#pragma unroll
+            for (int c = 0; c < 4; c++) {
+              a[c] = acc[i][j][4 * q + c];
+              b[c] = acc[i][j + 1][4 * q + c];
+            }
+            quad_transpose(a, lane);
+            quad_transpose(b, lane);
+            const int hcol = tr.n0 / 2 + ((wave_n * WTN + j) >> 1) * 32 + 4 * quad;
+            if (m < tr.m_end && hcol < p.N / 2) p.epilogue_swiglu4(m, hcol, a, b);
+          }
+        } else {
+#pragma unroll
+          for (int j = 0; j < WTN; j++) {
+            float v[4];
+#pragma unroll
+            for (int c = 0; c < 4; c++) v[c] = acc[i][j][4 * q + c];
+            quad_transpose(v, lane);
+            const int n = tr.n0 + (wave_n * WTN + j) * 32 + 4 * quad;
+            if (m < tr.m_end && n < p.N) p.epilogue4(tr.e, m, n, v);
+          }
         }
       }
     }

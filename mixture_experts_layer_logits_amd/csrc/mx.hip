@@ -857,20 +857,9 @@ struct MxDgrad2 : MxPlain {  // dh = dy W2_e, then the SwiGLU gradient from the 
   static constexpr Epi EPI = Epi::DSwiGLU;
   const bf16_t* ab = nullptr;
   bf16_t* dab = nullptr;
-  __device__ void epilogue4(int, int m, int n, const float (&dh)[4]) const {
-    const bf16_t* abr = ab + (int64_t)m * 2 * N;
-    float a[4], b[4], da[4], db[4];
-    load_bf16x4(abr + n, a);
-    load_bf16x4(abr + N + n, b);
-#pragma unroll
-    for (int c = 0; c < 4; c++) {
-      const float s = sigmoidf_(a[c]);
-      da[c] = dh[c] * b[c] * s * (1.f + a[c] * (1.f - s));
-      db[c] = dh[c] * a[c] * s;
-    }
-    bf16_t* o = dab + (int64_t)m * 2 * N;
-    store_bf16x4(o + n, da);
-    store_bf16x4(o + N + n, db);
+  __device__ AbPair prefetch4(int m, int n) const { return load_ab4(ab, N, m, n); }
+  __device__ void epilogue4_pre(int, int m, int n, const float (&dh)[4], const AbPair& pr) const {
+    dswiglu_store4(dab, N, m, n, dh, pr);
   }
 };
 
