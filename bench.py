@@ -75,6 +75,9 @@ def parse():
     ap.add_argument("--bf16-dispatch", action="store_true",
                     help="MXFP8 workloads: dispatch bf16 rows and let each GEMM quantise them (default: the "
                          "MXFP8 dispatch writes E4M3 rows)")
+    ap.add_argument("--unfused-quant", action="store_true",
+                    help="MXFP8 workloads: GEMM2 / dgrad1 quantise their bf16 operand themselves (default: GEMM1 / "
+                         "dgrad2 write it as MXFP8 rows from their epilogues)")
     return ap.parse_args()
 
 
@@ -109,8 +112,13 @@ def step_calls(m, L, d_inp, learned, recompute=False):
     if sh is not None:  # the shared expert: one-group GEMMs over the T token rows
         ss, so = L.shape_s, L.offsets_s
         W1s, W3s, W2s = sh
-        calls += [("shared_gemm1", lambda: m.moe_ffn_gemm1_fwd(ss, x, W1s, W3s, so, L.ab_s, L.h_s, L.ws_s)),
-                  ("shared_gemm2", lambda: m.moe_ffn_gemm2_fwd(ss, L.h_s, W2s, so, L.y_s, L.ws_s))]
+        if L.fq_h:  # h's MXFP8 rows from GEMM1's epilogue feed the MXFP8 GEMM2
+            calls += [("shared_gemm1", lambda: m.moe_ffn_gemm1_fwd_q(ss, x, W1s, W3s, so, L.ab_s, L.h_s, L.hq_s,
+                                                                      L.hs_s)),
+                      ("shared_gemm2", lambda: m.moe_ffn_gemm2_fwd_mx(ss, L.hq_s, L.hs_s, W2s, so, L.y_s, L.ws_s))]
+        else:
+            calls += [("shared_gemm1", lambda: m.moe_ffn_gemm1_fwd(ss, x, W1s, W3s, so, L.ab_s, L.h_s, L.ws_s)),
+                      ("shared_gemm2", lambda: m.moe_ffn_gemm2_fwd(ss, L.h_s, W2s, so, L.y_s, L.ws_s))]
     y_add = L.y_s if sh is not None else None
     if L.mx_dispatch:  # routed rows of x and dy exist only as E4M3 codes (row and column layouts)
         gemm1 = lambda: m.moe_ffn_gemm1_fwd_mx(s, L.xq_rows, L.xs_rows, W1, W3, L.offsets, L.ab, L.h, L.ws)  # noqa: E731
@@ -133,30 +141,52 @@ def step_calls(m, L, d_inp, learned, recompute=False):
         wgrad1 = ("wgrad1", lambda: m.moe_ffn_wgrad1_mx(s, L.xq_cols, L.xs_cols, L.dab, L.offsets, L.dW1, L.dW3,
                                                           L.ws))
     else:
+        calls += [("permute", lambda: m.moe_permute(s, x, L.slot_row, L.row_src, L.x_perm))]
+        if L.fq_h:
+            calls += [
+                ("gemm1_fwd", lambda: m.moe_ffn_gemm1_fwd_q(s, L.x_perm, W1, W3, L.offsets, L.ab, L.h, L.hq_rows,
+                                                            L.hs_rows)),
+                ("gemm2_fwd", lambda: m.moe_ffn_gemm2_fwd_mx(s, L.hq_rows, L.hs_rows, W2, L.offsets, L.y_perm,
+                                                             L.ws))]
+        else:
+            calls += [
+                ("gemm1_fwd", lambda: m.moe_ffn_gemm1_fwd(s, L.x_perm, W1, W3, L.offsets, L.ab, L.h, L.ws)),
+                ("gemm2_fwd", lambda: m.moe_ffn_gemm2_fwd(s, L.h, W2, L.offsets, L.y_perm, L.ws))]
         calls += [
-            ("permute", lambda: m.moe_permute(s, x, L.slot_row, L.row_src, L.x_perm)),
-            ("gemm1_fwd", lambda: m.moe_ffn_gemm1_fwd(s, L.x_perm, W1, W3, L.offsets, L.ab, L.h, L.ws)),
-            ("gemm2_fwd", lambda: m.moe_ffn_gemm2_fwd(s, L.h, W2, L.offsets, L.y_perm, L.ws)),
             ("combine", lambda: m.moe_combine(s, L.y_perm, g, L.slot_row, y_add, L.y)),
             ("combine_bwd", lambda: m.moe_combine_bwd(s, dy, L.y_perm, g, L.slot_row, L.dy_perm, L.dgates)),
         ]
         if recompute:
             calls += [("gemm1_recompute",
                        lambda: m.moe_ffn_gemm1_fwd(s, L.x_perm, W1, W3, L.offsets, L.ab, L.h, L.ws))]
-        calls += [
-            ("dgrad2", lambda: m.moe_ffn_dgrad2(s, L.dy_perm, W2, L.ab, L.offsets, L.dab, L.ws)),
-            ("wgrad2", lambda: m.moe_ffn_wgrad2(s, L.h, L.dy_perm, L.offsets, L.dW2, L.ws)),
-            ("dgrad1", lambda: m.moe_ffn_dgrad1(s, L.dab, W1, W3, L.offsets, L.dx_perm, L.ws)),
-        ]
+        if L.fq_dab:  # [da | db]'s MXFP8 rows from dgrad2's epilogue feed the MXFP8 dgrad1
+            calls += [
+                ("dgrad2", lambda: m.moe_ffn_dgrad2_q(s, L.dy_perm, W2, L.ab, L.offsets, L.dab, L.dabq_rows,
+                                                      L.dabs_rows)),
+                ("wgrad2", lambda: m.moe_ffn_wgrad2(s, L.h, L.dy_perm, L.offsets, L.dW2, L.ws)),
+                ("dgrad1", lambda: m.moe_ffn_dgrad1_mx(s, L.dabq_rows, L.dabs_rows, W1, W3, L.offsets, L.dx_perm,
+                                                       L.ws))]
+        else:
+            calls += [
+                ("dgrad2", lambda: m.moe_ffn_dgrad2(s, L.dy_perm, W2, L.ab, L.offsets, L.dab, L.ws)),
+                ("wgrad2", lambda: m.moe_ffn_wgrad2(s, L.h, L.dy_perm, L.offsets, L.dW2, L.ws)),
+                ("dgrad1", lambda: m.moe_ffn_dgrad1(s, L.dab, W1, W3, L.offsets, L.dx_perm, L.ws))]
         wgrad1 = ("wgrad1", lambda: m.moe_ffn_wgrad1(s, L.x_perm, L.dab, L.offsets, L.dW1, L.dW3, L.ws))
     if learned:
         calls += [("route_bwd", lambda: m.moe_route_bwd(s, L.dgates, g, L.topk_idx, L.dlogits)),
                   ("router_bwd", lambda: m.moe_router_bwd(s, x, Wr, L.dlogits, L.dx_r, L.dWr, L.ws))]
     if sh is not None:
-        calls += [("shared_dgrad2", lambda: m.moe_ffn_dgrad2(ss, dy, W2s, L.ab_s, so, L.dab_s, L.ws_s)),
-                  ("shared_wgrad2", lambda: m.moe_ffn_wgrad2(ss, L.h_s, dy, so, L.dW2s, L.ws_s)),
-                  ("shared_dgrad1", lambda: m.moe_ffn_dgrad1(ss, L.dab_s, W1s, W3s, so, L.dx_s, L.ws_s)),
-                  ("shared_wgrad1", lambda: m.moe_ffn_wgrad1(ss, x, L.dab_s, so, L.dW1s, L.dW3s, L.ws_s))]
+        if L.fq_dab:
+            calls += [("shared_dgrad2", lambda: m.moe_ffn_dgrad2_q(ss, dy, W2s, L.ab_s, so, L.dab_s, L.dabq_s,
+                                                                    L.dabs_s)),
+                      ("shared_wgrad2", lambda: m.moe_ffn_wgrad2(ss, L.h_s, dy, so, L.dW2s, L.ws_s)),
+                      ("shared_dgrad1", lambda: m.moe_ffn_dgrad1_mx(ss, L.dabq_s, L.dabs_s, W1s, W3s, so, L.dx_s,
+                                                                     L.ws_s))]
+        else:
+            calls += [("shared_dgrad2", lambda: m.moe_ffn_dgrad2(ss, dy, W2s, L.ab_s, so, L.dab_s, L.ws_s)),
+                      ("shared_wgrad2", lambda: m.moe_ffn_wgrad2(ss, L.h_s, dy, so, L.dW2s, L.ws_s)),
+                      ("shared_dgrad1", lambda: m.moe_ffn_dgrad1(ss, L.dab_s, W1s, W3s, so, L.dx_s, L.ws_s))]
+        calls += [("shared_wgrad1", lambda: m.moe_ffn_wgrad1(ss, x, L.dab_s, so, L.dW1s, L.dW3s, L.ws_s))]
     dx_add = L.dx_s if sh is not None else None
     calls += [("permute_bwd", lambda: m.moe_permute_bwd(s, L.dx_perm, L.slot_row, L.dx_r if learned else None,
                                                         dx_add, L.dx))]
@@ -166,10 +196,21 @@ def step_calls(m, L, d_inp, learned, recompute=False):
     return calls
 
 
-def algorithmic_work(w, eb, mx_dispatch=False):
+def fused_quant_flags(w):
+    """(fq_h, fq_dab) of a workload as the layer sets them by default: GEMM1 / dgrad2 write
+    MXFP8 rows when their consumer GEMM runs MXFP8 and they do not."""
+    if w.gemm != "mxfp8":
+        return False, False
+    sc = set(w.mx_scope) if w.mx_scope else {"gemm2", "dgrad1"}
+    return ("gemm2" in sc and "gemm1" not in sc), ("dgrad1" in sc and "dgrad2" not in sc)
+
+
+def algorithmic_work(w, eb, mx_dispatch=False, fq_h=False, fq_dab=False):
     """Per-launch algorithmic flops (GEMMs) and HBM bytes (everything) of each call.  With
     the MXFP8 dispatch the routed rows of x and dy are written once in each of two E4M3
-    layouts (1 + 1/32 bytes per element with the scales) and read in that form."""
+    layouts (1 + 1/32 bytes per element with the scales) and read in that form.  fq_h /
+    fq_dab: GEMM1 / dgrad2 also write h / [da | db] as MXFP8 rows, which GEMM2 / dgrad1 read
+    in place of the bf16 copy."""
     T, d, f, E, k = w.T, w.d, w.f, w.E, w.k
     R = T * k
     gem = {"gemm1_fwd": 2.0 * R * d * 2 * f, "gemm2_fwd": 2.0 * R * f * d, "dgrad2": 2.0 * R * d * f,
@@ -192,6 +233,14 @@ def algorithmic_work(w, eb, mx_dispatch=False):
         "router_bwd": 2 * T * E * 4 + E * d * eb + 2 * T * d * eb + E * d * 4,
         "permute_bwd": R * d * eb + 2 * T * d * eb + R * 4,
     }
+    if fq_h:
+        qh = R * f * 33 // 32
+        byt["gemm1_fwd"] += qh
+        byt["gemm2_fwd"] = qh + wbytes + R * d * eb
+    if fq_dab:
+        qd = R * 2 * f * 33 // 32
+        byt["dgrad2"] += qd
+        byt["dgrad1"] = qd + 2 * wbytes + R * d * eb
     if mx_dispatch:
         q = R * d * 33 // 32  # one E4M3 layout of the routed rows with its scales
         byt.update({
@@ -299,7 +348,7 @@ def pmc_record(wname, d):
     write_f = next(v["WRITE_SIZE"] for k, v in cw.items() if "copyBuffer" in k) * 1024 / copy_bytes
     eb = 4 if w.dtype == "f32" else 2
     mx_dispatch = w.gemm == "mxfp8" and bool(w.mx_scope) and len(w.mx_scope) == 6
-    gem, byt = algorithmic_work(w, eb, mx_dispatch)
+    gem, byt = algorithmic_work(w, eb, mx_dispatch, *fused_quant_flags(w))
     calls = {}
     for table, keys in ((sq, ("GRBM_GUI_ACTIVE", "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_INSTS_VALU_MFMA_MOPS_BF16",
                               "SQ_INSTS_VALU_MFMA_MOPS_F8", "SQ_LDS_BANK_CONFLICT", "SQ_INSTS_LDS")),
@@ -435,7 +484,7 @@ def main():
     mx_scope = sum(m.MX_BITS[n] for n in w.mx_scope) if (gemm == m.MOE_MXFP8 and w.mx_scope) else 0
     mx_dispatch = False if args.bf16_dispatch else None   # None: on when the scope covers the dispatch readers
     L = m.MoEExpertLayer(w.T, w.d, w.f, w.E, w.k, act=act, gemm=gemm, shared_f=w.shared_f, mx_dispatch=mx_dispatch,
-                         mx_scope=mx_scope)
+                         mx_scope=mx_scope, mx_fused_quant=not args.unfused_quant)
     mx_bits = m.mx_scope_bits(L.shape)
     gemm_peak = {n: (PEAK_TFLOPS["mxfp8"] if mx_bits & b else PEAK_TFLOPS["bf16" if w.gemm == "mxfp8" else w.gemm])
                  for n, b in (("gemm1_fwd", m.MOE_MX_GEMM1), ("gemm2_fwd", m.MOE_MX_GEMM2),
@@ -545,10 +594,10 @@ def main():
     tokens_per_s = w.T * args.steps / elapsed
 
     eb = 4 if w.dtype == "f32" else 2
-    gem, byt = algorithmic_work(w, eb, L.mx_dispatch)
+    gem, byt = algorithmic_work(w, eb, L.mx_dispatch, L.fq_h, L.fq_dab)
     if w.shared_f:  # the shared expert's GEMMs: the routed ones with R = T, f = fs, one expert
         ws_ = dataclasses.replace(w, k=1, E=1, f=w.shared_f)
-        gs, bs = algorithmic_work(ws_, eb)
+        gs, bs = algorithmic_work(ws_, eb, False, L.fq_h, L.fq_dab)
         for n in ("gemm1_fwd", "gemm2_fwd", "dgrad2", "wgrad2", "dgrad1", "wgrad1"):
             key = "shared_" + n.replace("_fwd", "")
             gem[key], byt[key] = gs[n], bs[n]

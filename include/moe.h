@@ -351,6 +351,37 @@ moe_status moe_ffn_wgrad1_mx(const moe_shape* s, const uint8_t* xq_cols, const u
                              const void* dab, const int32_t* offsets, void* dW1, void* dW3, void* ws,
                              size_t ws_bytes, void* stream);
 
+/* ---------------------------------------------------------------------------------------
+ * MXFP8 operands written by the producing GEMM's epilogue (the default scope: GEMM1 and
+ * dgrad2 in bf16, GEMM2 and dgrad1 in MXFP8).  GEMM1 writes h and dgrad2 writes [da | db]
+ * also as MXFP8 row blocks (blocks of 32 along the row, the layout of moe_mx_quantize with
+ * axis 0), bit for bit the bytes the row quantiser writes for the stored bf16 values, so the
+ * MXFP8 GEMM that reads them quantises nothing itself and its results are unchanged.  This
+ * keeps the quantisation inside the expert FFN compute that MXFP8 serves (unite.ai,
+ * section "Παραλληλισμός, Ακρίβεια και Τεχνικές Μνήμης").
+ *
+ * moe_ffn_gemm1_fwd_q: moe_ffn_gemm1_fwd (bf16), plus hq_rows [R, f] u8 codes and
+ *   hs_rows [R, f/32] u8 scales of h.  Needs GEMM2 in the MXFP8 scope and GEMM1 outside it.
+ * moe_ffn_gemm2_fwd_mx: moe_ffn_gemm2_fwd with h given as those rows.  Needs GEMM2 in scope.
+ * moe_ffn_dgrad2_q: moe_ffn_dgrad2 (bf16), plus dabq_rows [R, 2f] codes and dabs_rows
+ *   [R, 2f/32] scales of [da | db].  Needs dgrad1 in the MXFP8 scope and dgrad2 outside it.
+ * moe_ffn_dgrad1_mx: moe_ffn_dgrad1 with [da | db] given as those rows.  Needs dgrad1 in scope.
+ * A call whose scope condition fails returns MOE_EUNSUPPORTED before anything is enqueued;
+ * buffers are caller-owned device memory, 16-byte aligned; other arguments and errors as the
+ * plain calls.
+ * --------------------------------------------------------------------------------------- */
+moe_status moe_ffn_gemm1_fwd_q(const moe_shape* s, const void* x_perm, const void* W1, const void* W3,
+                               const int32_t* offsets, void* ab, void* h, uint8_t* hq_rows, uint8_t* hs_rows,
+                               void* stream);
+moe_status moe_ffn_gemm2_fwd_mx(const moe_shape* s, const uint8_t* hq_rows, const uint8_t* hs_rows, const void* W2,
+                                const int32_t* offsets, void* y_perm, void* ws, size_t ws_bytes, void* stream);
+moe_status moe_ffn_dgrad2_q(const moe_shape* s, const void* dy_perm, const void* W2, const void* ab,
+                            const int32_t* offsets, void* dab, uint8_t* dabq_rows, uint8_t* dabs_rows,
+                            void* stream);
+moe_status moe_ffn_dgrad1_mx(const moe_shape* s, const uint8_t* dabq_rows, const uint8_t* dabs_rows, const void* W1,
+                             const void* W3, const int32_t* offsets, void* dx_perm, void* ws, size_t ws_bytes,
+                             void* stream);
+
 #ifdef __cplusplus
 }
 #endif

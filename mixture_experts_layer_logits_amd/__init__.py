@@ -88,6 +88,11 @@ _SIGS = {
     "moe_ffn_dgrad2_mx": [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _SZ, _VP],
     "moe_ffn_wgrad2_mx": [_VP, _VP, _VP, _VP, _VP, _VP, _SZ, _VP],
     "moe_ffn_wgrad1_mx": [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _SZ, _VP],
+    # MXFP8 operands written by the producing bf16 GEMM's epilogue
+    "moe_ffn_gemm1_fwd_q": [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP],
+    "moe_ffn_gemm2_fwd_mx": [_VP, _VP, _VP, _VP, _VP, _VP, _SZ, _VP],
+    "moe_ffn_dgrad2_q": [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP],
+    "moe_ffn_dgrad1_mx": [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _SZ, _VP],
 }
 EXPORTED = sorted(list(_SIGS) + ["moe_mx_quantize", "moe_workspace_size", "moe_mx_cols_ld", "moe_status_str"])
 
@@ -269,6 +274,22 @@ def moe_ffn_wgrad2_mx(shape, h, dyq_cols, dys_cols, offsets, dW2, ws, stream=Non
 
 def moe_ffn_wgrad1_mx(shape, xq_cols, xs_cols, dab, offsets, dW1, dW3, ws, stream=None):
     _call("moe_ffn_wgrad1_mx", shape, xq_cols, xs_cols, dab, offsets, dW1, dW3, ws, _ws(ws), stream=stream)
+
+
+def moe_ffn_gemm1_fwd_q(shape, x_perm, W1, W3, offsets, ab, h, hq_rows, hs_rows, stream=None):
+    _call("moe_ffn_gemm1_fwd_q", shape, x_perm, W1, W3, offsets, ab, h, hq_rows, hs_rows, stream=stream)
+
+
+def moe_ffn_gemm2_fwd_mx(shape, hq_rows, hs_rows, W2, offsets, y_perm, ws, stream=None):
+    _call("moe_ffn_gemm2_fwd_mx", shape, hq_rows, hs_rows, W2, offsets, y_perm, ws, _ws(ws), stream=stream)
+
+
+def moe_ffn_dgrad2_q(shape, dy_perm, W2, ab, offsets, dab, dabq_rows, dabs_rows, stream=None):
+    _call("moe_ffn_dgrad2_q", shape, dy_perm, W2, ab, offsets, dab, dabq_rows, dabs_rows, stream=stream)
+
+
+def moe_ffn_dgrad1_mx(shape, dabq_rows, dabs_rows, W1, W3, offsets, dx_perm, ws, stream=None):
+    _call("moe_ffn_dgrad1_mx", shape, dabq_rows, dabs_rows, W1, W3, offsets, dx_perm, ws, _ws(ws), stream=stream)
 
 
 from .layer import MoEExpertLayer  # noqa: E402  (re-export)

@@ -513,4 +513,53 @@ moe_status moe_ffn_wgrad1_mx(const moe_shape* s, const uint8_t* xq_cols, const u
                             MxIn{xq_cols, xs_cols}));
 }
 
+moe_status moe_ffn_gemm1_fwd_q(const moe_shape* s, const void* x_perm, const void* W1, const void* W3,
+                               const int32_t* offsets, void* ab, void* h, uint8_t* hq_rows, uint8_t* hs_rows, void* st) {
+  MOE_TRY(check_shape(s));
+  if (!mx_on(s, MOE_MX_GEMM2) || mx_on(s, MOE_MX_GEMM1)) return MOE_EUNSUPPORTED;
+  MOE_TRY(check_ptrs({W1, W3}));
+  MOE_TRY(check_rows(s, {x_perm, ab, h, hq_rows, hs_rows}));
+  if (!offsets) return MOE_ENULL;
+  return launched(gemm1_fwd_bf16(gshape(s), offsets, (const bf16_t*)x_perm, (const bf16_t*)W1, (const bf16_t*)W3,
+                                 (bf16_t*)ab, (bf16_t*)h, S(st), hq_rows, hs_rows));
+}
+
+moe_status moe_ffn_gemm2_fwd_mx(const moe_shape* s, const uint8_t* hq_rows, const uint8_t* hs_rows, const void* W2,
+                                const int32_t* offsets, void* y_perm, void* ws, size_t ws_bytes, void* st) {
+  MOE_TRY(check_shape(s));
+  if (!mx_on(s, MOE_MX_GEMM2)) return MOE_EUNSUPPORTED;
+  MOE_TRY(check_ptrs({W2}));
+  MOE_TRY(check_rows(s, {hq_rows, hs_rows, y_perm}));
+  if (!offsets || !ws) return MOE_ENULL;
+  const GemmShape g = gshape(s);
+  if (ws_bytes < mx_workspace_bytes(g.R, g.d, g.f, g.E)) return MOE_EWORKSPACE;
+  return launched(gemm2_fwd_mx(g, offsets, nullptr, (const bf16_t*)W2, (bf16_t*)y_perm, ws, S(st),
+                               MxIn{hq_rows, hs_rows}));
+}
+
+moe_status moe_ffn_dgrad2_q(const moe_shape* s, const void* dy_perm, const void* W2, const void* ab,
+                            const int32_t* offsets, void* dab, uint8_t* dabq_rows, uint8_t* dabs_rows, void* st) {
+  MOE_TRY(check_shape(s));
+  if (!mx_on(s, MOE_MX_DGRAD1) || mx_on(s, MOE_MX_DGRAD2)) return MOE_EUNSUPPORTED;
+  MOE_TRY(check_ptrs({W2}));
+  MOE_TRY(check_rows(s, {dy_perm, ab, dab, dabq_rows, dabs_rows}));
+  if (!offsets) return MOE_ENULL;
+  return launched(dgrad2_bf16(gshape(s), offsets, (const bf16_t*)dy_perm, (const bf16_t*)W2, (const bf16_t*)ab,
+                              (bf16_t*)dab, S(st), dabq_rows, dabs_rows));
+}
+
+moe_status moe_ffn_dgrad1_mx(const moe_shape* s, const uint8_t* dabq_rows, const uint8_t* dabs_rows, const void* W1,
+                             const void* W3, const int32_t* offsets, void* dx_perm, void* ws, size_t ws_bytes,
+                             void* st) {
+  MOE_TRY(check_shape(s));
+  if (!mx_on(s, MOE_MX_DGRAD1)) return MOE_EUNSUPPORTED;
+  MOE_TRY(check_ptrs({W1, W3}));
+  MOE_TRY(check_rows(s, {dabq_rows, dabs_rows, dx_perm}));
+  if (!offsets || !ws) return MOE_ENULL;
+  const GemmShape g = gshape(s);
+  if (ws_bytes < mx_workspace_bytes(g.R, g.d, g.f, g.E)) return MOE_EWORKSPACE;
+  return launched(dgrad1_mx(g, offsets, nullptr, (const bf16_t*)W1, (const bf16_t*)W3, (bf16_t*)dx_perm, ws, S(st),
+                            MxIn{dabq_rows, dabs_rows}));
+}
+
 }  // extern "C"

@@ -11,6 +11,11 @@
 //   Epi::Store                 p.epilogue4(e, m, n, v[4])          columns n .. n+3
 //   Epi::SwiGLU                p.epilogue_swiglu4(m, hcol, a[4], b[4])
 //   Epi::DSwiGLU               p.prefetch4(m, n) -> AbPair, then p.epilogue4_pre(e, m, n, v[4], pair)
+// A problem with MXQ = true also writes its SwiGLU (h) or SwiGLU-gradient (da | db) output as
+// MXFP8 row blocks; its _q epilogue is called by every lane (the block maximum is a shuffle
+// over the 8 lanes of the block) with `valid` gating the stores:
+//   Epi::SwiGLU                p.epilogue_swiglu4_q(m, hcol, a[4], b[4], valid, quad)
+//   Epi::DSwiGLU               p.epilogue4_pre_q(e, m, n, v[4], pair, valid, quad)
 // The SwiGLU gradient reads the saved a, b of every output position.  Those loads are issued
 // for a whole 32-row block of the wave before any of its stores: memory operations complete
 // in order on one counter, so a load issued after a store (or after the operand loads still
@@ -18,6 +23,7 @@
 #pragma once
 #include "common.h"
 #include "gemm.h"
+#include "mxcode.h"
 #include "tilemap.h"
 
 namespace moe {
@@ -74,10 +80,9 @@ __device__ __forceinline__ AbPair load_ab4(const bf16_t* ab, int N, int m, int n
   const bf16_t* abr = ab + (int64_t)m * 2 * N;
   return AbPair{*reinterpret_cast<const uint2*>(abr + n), *reinterpret_cast<const uint2*>(abr + N + n)};
 }
-// da = dh b s (1 + a (1 - s)), db = dh silu(a), s = sigmoid(a); stored bf16 to dab [rows][2N]
-__device__ __forceinline__ void dswiglu_store4(bf16_t* dab, int N, int m, int n, const float (&dh)[4],
-                                               const AbPair& pr) {
-  float a[4], b[4], da[4], db[4];
+// da = dh b s (1 + a (1 - s)), db = dh silu(a), s = sigmoid(a)
+__device__ __forceinline__ void dswiglu4(const float (&dh)[4], const AbPair& pr, float (&da)[4], float (&db)[4]) {
+  float a[4], b[4];
   load_bf16x4(reinterpret_cast<const bf16_t*>(&pr.a), a);
   load_bf16x4(reinterpret_cast<const bf16_t*>(&pr.b), b);
 #pragma unroll
@@ -86,9 +91,41 @@ __device__ __forceinline__ void dswiglu_store4(bf16_t* dab, int N, int m, int n,
     da[c] = dh[c] * b[c] * s * (1.f + a[c] * (1.f - s));
     db[c] = dh[c] * a[c] * s;
   }
+}
+// ... stored bf16 to dab [rows][2N]
+__device__ __forceinline__ void dswiglu_store4(bf16_t* dab, int N, int m, int n, const float (&dh)[4],
+                                               const AbPair& pr) {
+  float da[4], db[4];
+  dswiglu4(dh, pr, da, db);
   bf16_t* o = dab + (int64_t)m * 2 * N;
   store_bf16x4(o + n, da);
   store_bf16x4(o + N + n, db);
+}
+
+// One MXFP8 row block of 32 consecutive outputs, held 4 per lane by the 8 lanes that share
+// (lane & 3, lane >> 5) (quad = (lane & 31) >> 2 = 0..7): the values are rounded to bf16 as
+// the bf16 copy stores them, their block maximum is taken over the 8 lanes (butterfly over
+// lane bits 2-4), and each lane encodes its 4 values under the block's scale.  Bit for bit
+// what the row quantiser writes for the stored bf16 row.  Every lane must call it; `valid`
+// (uniform over the block's lanes) gates the stores of the 4 codes at q and, from quad 0,
+// the scale byte at sc.
+__device__ __forceinline__ void mx_block_store4(const float (&v)[4], bool valid, uint8_t* q, uint8_t* sc, int quad) {
+  float r[4], amax = 0.f;
+#pragma unroll
+  for (int c = 0; c < 4; c++) {
+    r[c] = bf2f(f2bf(v[c]));
+    amax = fmaxf(amax, fabsf(r[c]));
+  }
+  amax = fmaxf(amax, __shfl_xor(amax, 4, kWave));
+  amax = fmaxf(amax, __shfl_xor(amax, 8, kWave));
+  amax = fmaxf(amax, __shfl_xor(amax, 16, kWave));
+  const int s = mx_scale_exp(amax);
+  const float inv = mx_inv_scale(s);
+  const uint32_t codes = e4m3x4(r[0] * inv, r[1] * inv, r[2] * inv, r[3] * inv);
+  if (valid) {
+    *reinterpret_cast<uint32_t*>(q) = codes;
+    if (quad == 0) *sc = (uint8_t)(s + 127);
+  }
 }
 
 // Writes the tile of wave (wave_m, wave_n) whose accumulators are acc.
@@ -123,7 +160,9 @@ __device__ __forceinline__ void tile_epilogue(const Prob& p, const f32x16 (&acc)
           for (int c = 0; c < 4; c++) v[c] = acc[i][j][4 * q + c];
           quad_transpose(v, lane);
           const int n = tr.n0 + (wave_n * WTN + j) * 32 + 4 * quad;
-          if (m < tr.m_end && n < p.N) p.epilogue4_pre(tr.e, m, n, v, pre[q][j]);
+          const bool valid = m < tr.m_end && n < p.N;
+          if constexpr (Prob::MXQ) p.epilogue4_pre_q(tr.e, m, n, v, pre[q][j], valid, quad);
+          else if (valid) p.epilogue4_pre(tr.e, m, n, v, pre[q][j]);
         }
       }
     } else {
@@ -143,7 +182,9 @@ __device__ __forceinline__ void tile_epilogue(const Prob& p, const f32x16 (&acc)
             quad_transpose(a, lane);
             quad_transpose(b, lane);
             const int hcol = tr.n0 / 2 + ((wave_n * WTN + j) >> 1) * 32 + 4 * quad;
-            if (m < tr.m_end && hcol < p.N / 2) p.epilogue_swiglu4(m, hcol, a, b);
+            const bool valid = m < tr.m_end && hcol < p.N / 2;
+            if constexpr (Prob::MXQ) p.epilogue_swiglu4_q(m, hcol, a, b, valid, quad);
+            else if (valid) p.epilogue_swiglu4(m, hcol, a, b);
           }
         } else {
 #pragma unroll

@@ -35,12 +35,16 @@ struct GemmShape {
 };
 
 // bf16 grouped GEMMs (offsets: device [E+1] segment starts)
+// hq, hs (optional): h also written as MXFP8 row blocks (codes [R][f], scales [R][f/32])
 hipError_t gemm1_fwd_bf16(const GemmShape& s, const int* offsets, const bf16_t* X, const bf16_t* W1,
-                          const bf16_t* W3, bf16_t* ab, bf16_t* h, hipStream_t st);
+                          const bf16_t* W3, bf16_t* ab, bf16_t* h, hipStream_t st, uint8_t* hq = nullptr,
+                          uint8_t* hs = nullptr);
 hipError_t gemm2_fwd_bf16(const GemmShape& s, const int* offsets, const bf16_t* H, const bf16_t* W2, bf16_t* Y,
                           hipStream_t st);
+// dq, ds (optional): [da | db] also written as MXFP8 row blocks (codes [R][2f], scales [R][2f/32])
 hipError_t dgrad2_bf16(const GemmShape& s, const int* offsets, const bf16_t* dY, const bf16_t* W2,
-                       const bf16_t* ab, bf16_t* dab, hipStream_t st);
+                       const bf16_t* ab, bf16_t* dab, hipStream_t st, uint8_t* dq = nullptr,
+                       uint8_t* ds = nullptr);
 // weight gradients; with a single group (E == 1) and ws of wgrad_split_workspace_bytes
 // the reduction over the rows is split (ws may be null: no split)
 hipError_t wgrad2_bf16(const GemmShape& s, const int* offsets, const bf16_t* H, const bf16_t* dY, bf16_t* dW2,

@@ -38,6 +38,7 @@ typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 // seg_len rows (single-group GEMMs and split reductions).
 // ---------------------------------------------------------------------------------------
 struct ProbBase {
+  static constexpr bool MXQ = false;  // no MXFP8 copy of the output
   int M = 0, N = 0, K = 0, E = 1;
   const int* offsets = nullptr;
   int seg_len = 0, seg_total = 0;
@@ -54,30 +55,51 @@ struct ProbBase {
 
 // Forward GEMM1 with the SwiGLU epilogue: [a | b] = X_e [W1_e | W3_e]^T, the B tile's
 // 32-column blocks alternate W1 / W3 rows so each wave holds a and b of the same column.
-struct ProbGemm1 : ProbBase {
+// Q: h is also written as MXFP8 row blocks (codes hq [R][f], scales hs [R][f/32]), the
+// operand of an MXFP8 GEMM2.
+template <bool Q>
+struct ProbGemm1T : ProbBase {
   using TA = bf16_t;
   static constexpr Group GROUP = Group::M;
   static constexpr bool A_KC = true, B_KC = true;
   static constexpr Epi EPI = Epi::SwiGLU;
+  static constexpr bool MXQ = Q;
   int f = 0;
   const bf16_t* X = nullptr; const bf16_t* W1 = nullptr; const bf16_t* W3 = nullptr;
   bf16_t* ab = nullptr; bf16_t* h = nullptr;
+  uint8_t* hq = nullptr; uint8_t* hs = nullptr;
   __device__ const bf16_t* a_row(int, int m) const { return X + (int64_t)m * K; }
   __device__ const bf16_t* b_row(int e, int n) const {
     const int blk = n >> 5, col = (blk >> 1) * 32 + (n & 31);
     const bf16_t* W = (blk & 1) ? W3 : W1;
     return W + ((int64_t)e * f + col) * K;
   }
+  __device__ void swiglu4(const float (&a)[4], const float (&b)[4], float (&hv)[4]) const {
+#pragma unroll
+    for (int c = 0; c < 4; c++) hv[c] = a[c] * sigmoidf_(a[c]) * b[c];
+  }
   __device__ void epilogue_swiglu4(int m, int hcol, const float (&a)[4], const float (&b)[4]) const {
     bf16_t* abr = ab + (int64_t)m * 2 * f;
     store_bf16x4(abr + hcol, a);
     store_bf16x4(abr + f + hcol, b);
     float hv[4];
-#pragma unroll
-    for (int c = 0; c < 4; c++) hv[c] = a[c] * sigmoidf_(a[c]) * b[c];
+    swiglu4(a, b, hv);
     store_bf16x4(h + (int64_t)m * f + hcol, hv);
   }
+  __device__ void epilogue_swiglu4_q(int m, int hcol, const float (&a)[4], const float (&b)[4], bool valid,
+                                     int quad) const {
+    float hv[4];
+    swiglu4(a, b, hv);
+    if (valid) {
+      bf16_t* abr = ab + (int64_t)m * 2 * f;
+      store_bf16x4(abr + hcol, a);
+      store_bf16x4(abr + f + hcol, b);
+      store_bf16x4(h + (int64_t)m * f + hcol, hv);
+    }
+    mx_block_store4(hv, valid, hq + (int64_t)m * f + hcol, hs + (int64_t)m * (f / 32) + hcol / 32, quad);
+  }
 };
+using ProbGemm1 = ProbGemm1T<false>;
 
 // y_perm = h W2_e^T
 struct ProbGemm2 : ProbBase {
@@ -92,21 +114,41 @@ struct ProbGemm2 : ProbBase {
   __device__ void epilogue4(int, int m, int n, const float (&v)[4]) const { store_bf16x4(Y + (int64_t)m * N + n, v); }
 };
 
-// dh = dy_e W2_e (B = W2_e read [k=d][n=f]) with the SwiGLU-gradient epilogue
-struct ProbDgrad2 : ProbBase {
+// dh = dy_e W2_e (B = W2_e read [k=d][n=f]) with the SwiGLU-gradient epilogue.  Q: [da | db]
+// is also written as MXFP8 row blocks (codes dq [R][2f], scales ds [R][2f/32]), the operand
+// of an MXFP8 dgrad1.
+template <bool Q>
+struct ProbDgrad2T : ProbBase {
   using TA = bf16_t;
   static constexpr Group GROUP = Group::M;
   static constexpr bool A_KC = true, B_KC = false;
   static constexpr Epi EPI = Epi::DSwiGLU;
+  static constexpr bool MXQ = Q;
   const bf16_t* dY = nullptr; const bf16_t* W2 = nullptr; const bf16_t* ab = nullptr;
   bf16_t* dab = nullptr;
+  uint8_t* dq = nullptr; uint8_t* ds = nullptr;
   __device__ const bf16_t* a_row(int, int m) const { return dY + (int64_t)m * K; }
   __device__ const bf16_t* b_row(int e, int k) const { return W2 + ((int64_t)e * K + k) * N; }
   __device__ AbPair prefetch4(int m, int n) const { return load_ab4(ab, N, m, n); }
   __device__ void epilogue4_pre(int, int m, int n, const float (&dh)[4], const AbPair& pr) const {
     dswiglu_store4(dab, N, m, n, dh, pr);
   }
+  __device__ void epilogue4_pre_q(int, int m, int n, const float (&dh)[4], const AbPair& pr, bool valid,
+                                  int quad) const {
+    float da[4], db[4];
+    dswiglu4(dh, pr, da, db);
+    if (valid) {
+      bf16_t* o = dab + (int64_t)m * 2 * N;
+      store_bf16x4(o + n, da);
+      store_bf16x4(o + N + n, db);
+    }
+    uint8_t* q = dq + (int64_t)m * 2 * N;
+    uint8_t* sc = ds + (int64_t)m * (2 * N / 32);
+    mx_block_store4(da, valid, q + n, sc + n / 32, quad);
+    mx_block_store4(db, valid, q + N + n, sc + (N + n) / 32, quad);
+  }
 };
+using ProbDgrad2 = ProbDgrad2T<false>;
 
 // dW2_e[d, f] = dy_e^T h_e: A[m=d][k=r] = dy[r][d], B[k=r][n=f] = h[r][f]
 struct ProbWgrad2 : ProbBase {
@@ -794,12 +836,18 @@ static TileChoice m_grouped_tile(const char* name, const GemmShape& s, int short
   return tile_for(name, Tile::t128x256w8, short_bk, 3, short_bk == 64 ? 4 : 0);
 }
 
-hipError_t gemm1_fwd_bf16(const GemmShape& s, const int* offsets, const bf16_t* X, const bf16_t* W1,
-                          const bf16_t* W3, bf16_t* ab, bf16_t* h, hipStream_t st) {
-  ProbGemm1 p;
+template <bool Q>
+static hipError_t gemm1_launch(const GemmShape& s, const int* offsets, const bf16_t* X, const bf16_t* W1,
+                               const bf16_t* W3, bf16_t* ab, bf16_t* h, uint8_t* hq, uint8_t* hs, hipStream_t st) {
+  ProbGemm1T<Q> p;
   p.M = s.R; p.N = 2 * s.f; p.K = s.d; p.E = s.E; p.offsets = offsets; p.f = s.f;
-  p.X = X; p.W1 = W1; p.W3 = W3; p.ab = ab; p.h = h;
+  p.X = X; p.W1 = W1; p.W3 = W3; p.ab = ab; p.h = h; p.hq = hq; p.hs = hs;
   return launch(m_grouped_tile("GEMM1", s, 64), p, st);
+}
+hipError_t gemm1_fwd_bf16(const GemmShape& s, const int* offsets, const bf16_t* X, const bf16_t* W1,
+                          const bf16_t* W3, bf16_t* ab, bf16_t* h, hipStream_t st, uint8_t* hq, uint8_t* hs) {
+  if (hq) return gemm1_launch<true>(s, offsets, X, W1, W3, ab, h, hq, hs, st);
+  return gemm1_launch<false>(s, offsets, X, W1, W3, ab, h, nullptr, nullptr, st);
 }
 hipError_t gemm2_fwd_bf16(const GemmShape& s, const int* offsets, const bf16_t* H, const bf16_t* W2, bf16_t* Y,
                           hipStream_t st) {
@@ -813,12 +861,18 @@ hipError_t gemm2_fwd_bf16(const GemmShape& s, const int* offsets, const bf16_t* 
 // operand loads those reads wait only on each other.  At 4096 and 2048 rows per expert
 // that is 14% and 9% faster than the 256 x 256 two-stage tiles (E = 8, T = 8192, d = 2048;
 // E = 32, T = 16384, d = 4096).
-hipError_t dgrad2_bf16(const GemmShape& s, const int* offsets, const bf16_t* dY, const bf16_t* W2,
-                       const bf16_t* ab, bf16_t* dab, hipStream_t st) {
-  ProbDgrad2 p;
+template <bool Q>
+static hipError_t dgrad2_launch(const GemmShape& s, const int* offsets, const bf16_t* dY, const bf16_t* W2,
+                                const bf16_t* ab, bf16_t* dab, uint8_t* dq, uint8_t* ds, hipStream_t st) {
+  ProbDgrad2T<Q> p;
   p.M = s.R; p.N = s.f; p.K = s.d; p.E = s.E; p.offsets = offsets;
-  p.dY = dY; p.W2 = W2; p.ab = ab; p.dab = dab;
+  p.dY = dY; p.W2 = W2; p.ab = ab; p.dab = dab; p.dq = dq; p.ds = ds;
   return launch(tile_for("DGRAD2", Tile::t128x256w8, 64, 3, 4), p, st);
+}
+hipError_t dgrad2_bf16(const GemmShape& s, const int* offsets, const bf16_t* dY, const bf16_t* W2,
+                       const bf16_t* ab, bf16_t* dab, hipStream_t st, uint8_t* dq, uint8_t* ds) {
+  if (dq) return dgrad2_launch<true>(s, offsets, dY, W2, ab, dab, dq, ds, st);
+  return dgrad2_launch<false>(s, offsets, dY, W2, ab, dab, nullptr, nullptr, st);
 }
 // Single-group weight gradients: with one expert the output has few tiles (64 for
 // 2048 x 2048 at 256 x 256), so the reduction over the R rows is split to give about two

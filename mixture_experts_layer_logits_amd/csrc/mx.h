@@ -26,8 +26,9 @@ hipError_t mx_dispatch(int R, int cols, int E, int k, const bf16_t* src, const i
                        const int32_t* offsets, const float* gates, const int32_t* slot_row, uint8_t* q_rows,
                        uint8_t* s_rows, uint8_t* q_cols, uint8_t* s_cols, hipStream_t st);
 
-// An activation operand the caller has already quantised (from the MXFP8 dispatch), in the
-// layout the GEMM reads; q == nullptr: the GEMM quantises its bf16 source itself.
+// An activation operand the caller has already quantised (by the MXFP8 dispatch, or by the
+// epilogue of the bf16 GEMM that produced it), in the layout the GEMM reads; q == nullptr:
+// the GEMM quantises its bf16 source itself.
 struct MxIn {
   const uint8_t* q = nullptr;
   const uint8_t* s = nullptr;
@@ -36,13 +37,13 @@ struct MxIn {
 hipError_t gemm1_fwd_mx(const GemmShape& s, const int* offsets, const bf16_t* X, const bf16_t* W1, const bf16_t* W3,
                         bf16_t* ab, bf16_t* h, void* ws, hipStream_t st, MxIn x_rows = {});
 hipError_t gemm2_fwd_mx(const GemmShape& s, const int* offsets, const bf16_t* H, const bf16_t* W2, bf16_t* Y,
-                        void* ws, hipStream_t st);
+                        void* ws, hipStream_t st, MxIn h_rows = {});
 hipError_t dgrad2_mx(const GemmShape& s, const int* offsets, const bf16_t* dY, const bf16_t* W2, const bf16_t* ab,
                      bf16_t* dab, void* ws, hipStream_t st, MxIn dy_rows = {});
 hipError_t wgrad2_mx(const GemmShape& s, const int* offsets, const bf16_t* H, const bf16_t* dY, bf16_t* dW2,
                      void* ws, hipStream_t st, MxIn dy_cols = {});
 hipError_t dgrad1_mx(const GemmShape& s, const int* offsets, const bf16_t* dab, const bf16_t* W1, const bf16_t* W3,
-                     bf16_t* dX, void* ws, hipStream_t st);
+                     bf16_t* dX, void* ws, hipStream_t st, MxIn dab_rows = {});
 hipError_t wgrad1_mx(const GemmShape& s, const int* offsets, const bf16_t* X, const bf16_t* dab, bf16_t* dW1,
                      bf16_t* dW3, void* ws, hipStream_t st, MxIn x_cols = {});
 

@@ -15,31 +15,11 @@
 
 #include "common.h"
 #include "mx.h"
+#include "mxcode.h"
 #include "tilemap.h"
 #include "epilogue.h"
 
 namespace moe {
-
-__device__ __forceinline__ int mx_scale_exp(float amax) {
-  const uint32_t u = __float_as_uint(amax);
-  const int eb = (int)((u >> 23) & 0xff);
-  if (eb == 0) return -127;
-  int s = eb - 127 - 8 + ((u & 0x7fffffu) > 0x600000u ? 1 : 0);  // mantissa above 1.75 -> next power
-  return s < -127 ? -127 : (s > 127 ? 127 : s);
-}
-
-// Four values of magnitude <= 448 -> four E4M3 codes (bytes 0..3), round to nearest even.
-__device__ __forceinline__ uint32_t e4m3x4(float a, float b, float c, float d) {
-  const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
-  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(c, d, lo, true);
-}
-
-__device__ __forceinline__ float exp2i(int s) { return __uint_as_float((uint32_t)(s + 127) << 23); }  // 2^s, s in [-126,127]
-
-// 2^-s as one fp32 factor.  Finite bf16 input has amax < 2^128, so s <= 120 and the factor
-// is a normal number; v * 2^-s is exact unless it falls below 2^-126, where its code is
-// zero either way.
-__device__ __forceinline__ float mx_inv_scale(int s) { return exp2i(-s); }
 
 namespace {
 
@@ -814,6 +794,7 @@ mx_gemm_kernel(const Prob p) {
 // Problems.  Codes q* [rows][K] and scales s* [rows][K/32] (K-contiguous).
 // ---------------------------------------------------------------------------------------
 struct MxBase {
+  static constexpr bool MXQ = false;  // no MXFP8 copy of the output
   int M = 0, N = 0, K = 0, E = 1;
   const int* offsets = nullptr;
   const uint8_t *qa = nullptr, *sa = nullptr;  // A codes / scales, row length K (padded for Group::K)
@@ -965,13 +946,18 @@ hipError_t gemm1_fwd_mx(const GemmShape& s, const int* offsets, const bf16_t* X,
 }
 
 hipError_t gemm2_fwd_mx(const GemmShape& s, const int* offsets, const bf16_t* H, const bf16_t* W2, bf16_t* Y,
-                        void* ws, hipStream_t st) {
+                        void* ws, hipStream_t st, MxIn h_rows) {
   Carve c{static_cast<char*>(ws)};
   const int64_t Ed = (int64_t)s.E * s.d;
   uint8_t *hq = c.take((size_t)s.R * s.f), *hs = c.take((size_t)s.R * s.f / kMxBlock);
   uint8_t *wq = c.take((size_t)Ed * s.f), *wsc = c.take((size_t)Ed * s.f / kMxBlock);
   hipError_t err;
-  if ((err = mx_quantize_rows(s.R, s.f, H, hq, hs, st)) != hipSuccess) return err;
+  if (h_rows.q) {
+    hq = const_cast<uint8_t*>(h_rows.q);
+    hs = const_cast<uint8_t*>(h_rows.s);
+  } else if ((err = mx_quantize_rows(s.R, s.f, H, hq, hs, st)) != hipSuccess) {
+    return err;
+  }
   if ((err = mx_quantize_rows((int)Ed, s.f, W2, wq, wsc, st)) != hipSuccess) return err;
   MxPlain p;
   p.M = s.R; p.N = s.d; p.K = s.f; p.E = s.E; p.offsets = offsets; p.qa = hq; p.sa = hs;
@@ -1009,13 +995,18 @@ hipError_t dgrad2_mx(const GemmShape& s, const int* offsets, const bf16_t* dY, c
 }
 
 hipError_t dgrad1_mx(const GemmShape& s, const int* offsets, const bf16_t* dab, const bf16_t* W1, const bf16_t* W3,
-                     bf16_t* dX, void* ws, hipStream_t st) {
+                     bf16_t* dX, void* ws, hipStream_t st, MxIn dab_rows) {
   Carve c{static_cast<char*>(ws)};
   const int64_t Ed = (int64_t)s.E * s.d;
   uint8_t *gq = c.take((size_t)s.R * 2 * s.f), *gs = c.take((size_t)s.R * 2 * s.f / kMxBlock);
   uint8_t *wq = c.take((size_t)Ed * 2 * s.f), *wsc = c.take((size_t)Ed * 2 * s.f / kMxBlock);
   hipError_t err;
-  if ((err = mx_quantize_rows(s.R, 2 * s.f, dab, gq, gs, st)) != hipSuccess) return err;
+  if (dab_rows.q) {
+    gq = const_cast<uint8_t*>(dab_rows.q);
+    gs = const_cast<uint8_t*>(dab_rows.s);
+  } else if ((err = mx_quantize_rows(s.R, 2 * s.f, dab, gq, gs, st)) != hipSuccess) {
+    return err;
+  }
   // [W1_e ; W3_e]^T = [d][2f]: W1_e^T in columns [0, f), W3_e^T in [f, 2f)
   if ((err = quantize_weight_t(s.E, s.f, s.d, W1, wq, wsc, 2 * s.f, 0, st)) != hipSuccess) return err;
   if ((err = quantize_weight_t(s.E, s.f, s.d, W3, wq, wsc, 2 * s.f, s.f, st)) != hipSuccess) return err;

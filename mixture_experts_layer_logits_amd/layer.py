@@ -26,6 +26,12 @@ token rows (E = 1, k = 1, offsets [0, T]); its output enters through moe_combine
 MXFP8 scope (``mx_scope``, MOE_MX_* bits; MOE_MX_DEFAULT = GEMM2 and dgrad1): the expert
 GEMMs that take E4M3 operands when ``gemm`` is MOE_MXFP8; the others run bf16.
 
+MXFP8 operands from the producing epilogue (``mx_fused_quant``, on by default where it
+applies): when GEMM2 runs MXFP8 and GEMM1 bf16 (the default scope), GEMM1's epilogue also
+writes h as MXFP8 row blocks and GEMM2 reads those; likewise dgrad2's epilogue writes
+[da | db] for an MXFP8 dgrad1.  The bytes are the ones the GEMM would quantise itself, so the
+results are bit-identical and two standalone quantiser passes over h and [da | db] go away.
+
 MXFP8 dispatch (``mx_dispatch``; on by default when the scope holds all four GEMMs that
 read the dispatched rows: GEMM1 and wgrad1 read x's, dgrad2 and wgrad2 the output
 gradient's): moe_permute_mx and moe_combine_bwd_mx write the routed rows of x and of the
@@ -47,8 +53,9 @@ from __future__ import annotations
 
 import torch
 
-from . import (MOE_BF16, MOE_F32, MOE_MX_DGRAD2, MOE_MX_GEMM1, MOE_MX_WGRAD1, MOE_MX_WGRAD2, MOE_MXFP8,
-               make_shape, moe_combine, moe_combine_bwd, moe_combine_bwd_mx,
+from . import (MOE_BF16, MOE_F32, MOE_MX_DGRAD1, MOE_MX_DGRAD2, MOE_MX_GEMM1, MOE_MX_GEMM2, MOE_MX_WGRAD1,
+               MOE_MX_WGRAD2, MOE_MXFP8, make_shape, moe_combine, moe_ffn_dgrad1_mx, moe_ffn_dgrad2_q,
+               moe_ffn_gemm1_fwd_q, moe_ffn_gemm2_fwd_mx, moe_combine_bwd, moe_combine_bwd_mx,
                moe_ffn_dgrad1, moe_ffn_dgrad2, moe_ffn_dgrad2_mx, moe_ffn_gemm1_fwd, moe_ffn_gemm1_fwd_mx,
                moe_ffn_gemm2_fwd, moe_ffn_wgrad1, moe_ffn_wgrad1_mx, moe_ffn_wgrad2, moe_ffn_wgrad2_mx, moe_mx_cols_ld,
                moe_permute, moe_permute_bwd, moe_permute_mx, moe_route, moe_route_bwd, moe_route_given, moe_router_bwd,
@@ -60,10 +67,14 @@ _DISPATCH_READERS = MOE_MX_GEMM1 | MOE_MX_WGRAD1 | MOE_MX_DGRAD2 | MOE_MX_WGRAD2
 
 class MoEExpertLayer:
     def __init__(self, T, d, f, E, k, act=MOE_BF16, gemm=None, device="cuda", recompute=False, shared_f=0,
-                 mx_dispatch=None, mx_scope=0):
+                 mx_dispatch=None, mx_scope=0, mx_fused_quant=True):
         self.shape = make_shape(T, d, f, E, k, act, gemm, mx_scope)
         self.recompute = recompute
-        covers = (mx_scope_bits(self.shape) & _DISPATCH_READERS) == _DISPATCH_READERS
+        bits = mx_scope_bits(self.shape)
+        # MXFP8 operands written by the producing bf16 GEMM's epilogue
+        self.fq_h = bool(mx_fused_quant) and bool(bits & MOE_MX_GEMM2) and not bits & MOE_MX_GEMM1
+        self.fq_dab = bool(mx_fused_quant) and bool(bits & MOE_MX_DGRAD1) and not bits & MOE_MX_DGRAD2
+        covers = (bits & _DISPATCH_READERS) == _DISPATCH_READERS
         self.mx_dispatch = covers if mx_dispatch is None else bool(mx_dispatch)
         if self.mx_dispatch and not covers:
             raise ValueError("the MXFP8 dispatch needs GEMM1, wgrad1, dgrad2 and wgrad2 in the MXFP8 scope")
@@ -100,6 +111,11 @@ class MoEExpertLayer:
             self.dy_perm = e(R, d)
         self.ab = None if recompute else e(R, 2 * f)
         self.h = None if recompute else e(R, f)
+        self.hq_rows = self.hs_rows = self.dabq_rows = self.dabs_rows = None
+        if self.fq_h:
+            self.hq_rows, self.hs_rows = e(R, f, dtype=u8), e(R, f // 32, dtype=u8)
+        if self.fq_dab:
+            self.dabq_rows, self.dabs_rows = e(R, 2 * f, dtype=u8), e(R, 2 * f // 32, dtype=u8)
         self.y_perm = e(R, d)
         self.y = e(T, d)
         # backward buffers
@@ -123,6 +139,10 @@ class MoEExpertLayer:
             self.offsets_s = torch.tensor([0, T], dtype=i32, device=dev)
             self.ab_s, self.h_s, self.y_s = e(T, 2 * fs), e(T, fs), e(T, d)
             self.dab_s, self.dx_s = e(T, 2 * fs), e(T, d)
+            if self.fq_h:
+                self.hq_s, self.hs_s = e(T, fs, dtype=u8), e(T, fs // 32, dtype=u8)
+            if self.fq_dab:
+                self.dabq_s, self.dabs_s = e(T, 2 * fs, dtype=u8), e(T, 2 * fs // 32, dtype=u8)
             self.dW1s, self.dW3s, self.dW2s = e(1, fs, d), e(1, fs, d), e(1, d, fs)
             self.ws_s = torch.empty(moe_workspace_size(self.shape_s), dtype=torch.uint8, device=dev)
 
@@ -149,8 +169,12 @@ class MoEExpertLayer:
         if shared is not None:
             W1s, W3s, W2s = shared
             ss = self.shape_s
-            moe_ffn_gemm1_fwd(ss, x, W1s, W3s, self.offsets_s, self.ab_s, self.h_s, self.ws_s)
-            moe_ffn_gemm2_fwd(ss, self.h_s, W2s, self.offsets_s, self.y_s, self.ws_s)
+            if self.fq_h:
+                moe_ffn_gemm1_fwd_q(ss, x, W1s, W3s, self.offsets_s, self.ab_s, self.h_s, self.hq_s, self.hs_s)
+                moe_ffn_gemm2_fwd_mx(ss, self.hq_s, self.hs_s, W2s, self.offsets_s, self.y_s, self.ws_s)
+            else:
+                moe_ffn_gemm1_fwd(ss, x, W1s, W3s, self.offsets_s, self.ab_s, self.h_s, self.ws_s)
+                moe_ffn_gemm2_fwd(ss, self.h_s, W2s, self.offsets_s, self.y_s, self.ws_s)
             y_add = self.y_s
         if self.mx_dispatch:
             moe_permute_mx(s, x, self.slot_row, self.offsets, self.row_src, self.xq_rows, self.xs_rows, self.xq_cols,
@@ -159,8 +183,11 @@ class MoEExpertLayer:
             moe_permute(s, x, self.slot_row, self.row_src, self.x_perm)
         if self.recompute:
             self.ab, self.h = self._e(self.R, 2 * self.f), self._e(self.R, self.f)
-        self._gemm1(W1, W3)
-        moe_ffn_gemm2_fwd(s, self.h, W2, self.offsets, self.y_perm, self.ws)
+        self._gemm1(W1, W3, with_q=True)
+        if self.fq_h:
+            moe_ffn_gemm2_fwd_mx(s, self.hq_rows, self.hs_rows, W2, self.offsets, self.y_perm, self.ws)
+        else:
+            moe_ffn_gemm2_fwd(s, self.h, W2, self.offsets, self.y_perm, self.ws)
         if self.recompute:  # the SwiGLU activations are not kept for the backward
             self.ab = self.h = None
         moe_combine(s, self.y_perm, g, self.slot_row, y_add, self.y)
@@ -183,9 +210,16 @@ class MoEExpertLayer:
             moe_ffn_wgrad2_mx(s, self.h, self.dyq_cols, self.dys_cols, self.offsets, self.dW2, self.ws)
             moe_ffn_dgrad1(s, self.dab, W1, W3, self.offsets, self.dx_perm, self.ws)
         else:
-            moe_ffn_dgrad2(s, self.dy_perm, W2, self.ab, self.offsets, self.dab, self.ws)
+            if self.fq_dab:
+                moe_ffn_dgrad2_q(s, self.dy_perm, W2, self.ab, self.offsets, self.dab, self.dabq_rows,
+                                 self.dabs_rows)
+            else:
+                moe_ffn_dgrad2(s, self.dy_perm, W2, self.ab, self.offsets, self.dab, self.ws)
             moe_ffn_wgrad2(s, self.h, self.dy_perm, self.offsets, self.dW2, self.ws)
-            moe_ffn_dgrad1(s, self.dab, W1, W3, self.offsets, self.dx_perm, self.ws)
+            if self.fq_dab:
+                moe_ffn_dgrad1_mx(s, self.dabq_rows, self.dabs_rows, W1, W3, self.offsets, self.dx_perm, self.ws)
+            else:
+                moe_ffn_dgrad1(s, self.dab, W1, W3, self.offsets, self.dx_perm, self.ws)
         dx_r = None
         if self.learned:
             moe_route_bwd(s, self.dgates, g, self.topk_idx, self.dlogits)
@@ -195,9 +229,15 @@ class MoEExpertLayer:
         if self._shared is not None:
             W1s, W3s, W2s = self._shared
             ss, off = self.shape_s, self.offsets_s
-            moe_ffn_dgrad2(ss, dy, W2s, self.ab_s, off, self.dab_s, self.ws_s)
+            if self.fq_dab:
+                moe_ffn_dgrad2_q(ss, dy, W2s, self.ab_s, off, self.dab_s, self.dabq_s, self.dabs_s)
+            else:
+                moe_ffn_dgrad2(ss, dy, W2s, self.ab_s, off, self.dab_s, self.ws_s)
             moe_ffn_wgrad2(ss, self.h_s, dy, off, self.dW2s, self.ws_s)
-            moe_ffn_dgrad1(ss, self.dab_s, W1s, W3s, off, self.dx_s, self.ws_s)
+            if self.fq_dab:
+                moe_ffn_dgrad1_mx(ss, self.dabq_s, self.dabs_s, W1s, W3s, off, self.dx_s, self.ws_s)
+            else:
+                moe_ffn_dgrad1(ss, self.dab_s, W1s, W3s, off, self.dx_s, self.ws_s)
             moe_ffn_wgrad1(ss, x, self.dab_s, off, self.dW1s, self.dW3s, self.ws_s)
             dx_add = self.dx_s
         moe_permute_bwd(s, self.dx_perm, self.slot_row, dx_r, dx_add, self.dx)
@@ -211,9 +251,12 @@ class MoEExpertLayer:
             self.ab = self.h = None
         return self.dx
 
-    def _gemm1(self, W1, W3):
+    def _gemm1(self, W1, W3, with_q=False):
+        """GEMM1 (with_q: also h's MXFP8 rows, for the forward's MXFP8 GEMM2)."""
         s = self.shape
-        if self.mx_dispatch:
+        if with_q and self.fq_h:
+            moe_ffn_gemm1_fwd_q(s, self.x_perm, W1, W3, self.offsets, self.ab, self.h, self.hq_rows, self.hs_rows)
+        elif self.mx_dispatch:
             moe_ffn_gemm1_fwd_mx(s, self.xq_rows, self.xs_rows, W1, W3, self.offsets, self.ab, self.h, self.ws)
         else:
             moe_ffn_gemm1_fwd(s, self.x_perm, W1, W3, self.offsets, self.ab, self.h, self.ws)

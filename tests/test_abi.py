@@ -129,6 +129,33 @@ def test_mx_scope_gates_the_mx_operand_entry_points(lib):
     assert st == MOE_EUNSUPPORTED
 
 
+def test_mx_scope_gates_the_fused_quantisation_entry_points(lib):
+    """The calls that write MXFP8 rows from a bf16 GEMM's epilogue need the consumer GEMM in
+    the scope and the producer outside it; the calls that read them need the consumer in the
+    scope.  Every refusal comes before any pointer is touched."""
+    P = ctypes.c_void_p
+    a = P(0x1000)
+    ws = ctypes.c_size_t(1 << 30)
+    calls = {
+        "moe_ffn_gemm1_fwd_q": lambda s: lib.moe_ffn_gemm1_fwd_q(ctypes.byref(s), a, a, a, a, a, a, a, a, P(0)),
+        "moe_ffn_gemm2_fwd_mx": lambda s: lib.moe_ffn_gemm2_fwd_mx(ctypes.byref(s), a, a, a, a, a, a, ws, P(0)),
+        "moe_ffn_dgrad2_q": lambda s: lib.moe_ffn_dgrad2_q(ctypes.byref(s), a, a, a, a, a, a, a, P(0)),
+        "moe_ffn_dgrad1_mx": lambda s: lib.moe_ffn_dgrad1_mx(ctypes.byref(s), a, a, a, a, a, a, a, ws, P(0)),
+    }
+    bf16 = Shape(64, 128, 128, 8, 2, 1, 1, 0)
+    all6 = Shape(64, 128, 128, 8, 2, 1, 2, 63)      # producers in scope: nothing to fuse
+    producers = Shape(64, 128, 128, 8, 2, 1, 2, 1 | 4)  # GEMM1 and dgrad2 only: no consumer in scope
+    for name, call in calls.items():
+        assert call(bf16) == MOE_EUNSUPPORTED, name
+        assert call(producers) == MOE_EUNSUPPORTED, name
+    assert calls["moe_ffn_gemm1_fwd_q"](all6) == MOE_EUNSUPPORTED
+    assert calls["moe_ffn_dgrad2_q"](all6) == MOE_EUNSUPPORTED
+    # the default scope passes the scope check and fails on the missing offsets (no launch)
+    dflt = Shape(64, 128, 128, 8, 2, 1, 2, 0)
+    assert lib.moe_ffn_gemm1_fwd_q(ctypes.byref(dflt), a, a, a, P(0), a, a, a, a, P(0)) == MOE_ENULL
+    assert lib.moe_ffn_dgrad2_q(ctypes.byref(dflt), a, a, a, P(0), a, a, a, P(0)) == MOE_ENULL
+
+
 def test_route_noalloc_refuses_oversized_shapes_on_the_host(lib):
     """The allocation-free routing call refuses a shape whose histograms and ranks exceed its
     fixed 4 MiB scratch, before any HIP call (so this runs without a GPU)."""

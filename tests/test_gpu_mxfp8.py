@@ -248,6 +248,40 @@ def test_mx_dispatch_equals_bf16_dispatch_bitwise(over):
     assert not diff, diff
 
 
+@pytest.mark.parametrize("over,recompute", [(c, False) for c in MX_CASES] + [(MX_CASES[1], True)],
+                         ids=[c["name"] for c in MX_CASES] + [MX_CASES[1]["name"] + "_recompute"])
+def test_fused_quantisation_bytes_and_layer_bitwise(over, recompute):
+    """With the default scope, GEMM1's epilogue writes h and dgrad2's writes [da | db] also as
+    MXFP8 row blocks: those bytes equal the oracle's row quantiser applied to the bf16 h and
+    [da | db] the same kernels store, and the layer's outputs equal, bit for bit, those of the
+    layer whose MXFP8 GEMM2 and dgrad1 quantise their bf16 operands themselves."""
+    from oracle import mx_ref
+    w = workloads.scaled(MX, **over)
+    inp = workloads.make_inputs(w)
+    say(f"[gpu] fused MXFP8 quantisation {w} recompute={recompute}")
+    A = run_layer(w, inp, recompute=recompute, mx_fused_quant=True)
+    assert A.fq_h and A.fq_dab and not A.mx_dispatch
+    if not recompute:
+        for q, sc, v in ((A.hq_rows, A.hs_rows, A.h), (A.dabq_rows, A.dabs_rows, A.dab)):
+            codes, scales = mx_ref.quantize_rows(host(v).astype(np.float64))
+            assert np.array_equal(host(q), codes)
+            assert np.array_equal(host(sc), scales)
+        if w.shared_f:
+            for q, sc, v in ((A.hq_s, A.hs_s, A.h_s), (A.dabq_s, A.dabs_s, A.dab_s)):
+                codes, scales = mx_ref.quantize_rows(host(v).astype(np.float64))
+                assert np.array_equal(host(q), codes) and np.array_equal(host(sc), scales)
+    say(f"[gpu] unfused MXFP8 layer {w} recompute={recompute}")
+    B = run_layer(w, inp, recompute=recompute, mx_fused_quant=False)
+    assert not B.fq_h and not B.fq_dab
+    names = ["y_perm", "y", "dgates", "dab", "dx_perm", "dW1", "dW3", "dW2", "dx"]
+    if not recompute:
+        names += ["ab", "h"]
+    if w.shared_f:
+        names += ["y_s", "dW1s", "dW3s", "dW2s"]
+    diff = [n for n in names if not torch.equal(getattr(A, n), getattr(B, n))]
+    assert not diff, diff
+
+
 def test_mx_gemms_match_dequantized_operands():
     """Each MXFP8 grouped GEMM equals the fp64 GEMM of its dequantised operands (the
     oracle's quantiser is bit-exact with the GPU's), up to fp32 accumulation and the bf16
