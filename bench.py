@@ -66,6 +66,9 @@ def parse():
     ap.add_argument("--pmc-record", default=None, metavar="DIR",
                     help="record the counter passes under DIR (pmc_sq_W, pmc_fetch_W, pmc_write_W for --workload W, "
                          "pmc_fetch_copy, pmc_write_copy) into profiles/counters.json; prints the summary table")
+    ap.add_argument("--trace-summary", default=None, metavar="DIR",
+                    help="turn a rocprofv3 --kernel-trace csv run under DIR into a markdown table per kernel "
+                         "(calls, mean, median, min, max, share of kernel time)")
     ap.add_argument("--recompute", action="store_true",
                     help="activation recompute: keep only x_perm and run GEMM1 again in the backward")
     ap.add_argument("--seed-offset", type=int, default=0,
@@ -305,6 +308,29 @@ KERNEL_CALLS = [("ProbGemm1", "gemm1_fwd"), ("ProbGemm2", "gemm2_fwd"), ("ProbDg
                 ("row_src_kernel", "permute"), ("copyBuffer", "copy"), ("elementwise_kernel", "copy")]
 
 
+def trace_summary(d, workload):
+    """Per-kernel statistics of a rocprofv3 --kernel-trace csv run under d, durations in us:
+    calls, mean, median, min, max and share of the summed kernel time."""
+    import csv
+    import glob
+    path = sorted(glob.glob(os.path.join(d, "**", "*kernel_trace.csv"), recursive=True))
+    if not path:
+        raise SystemExit(f"no *kernel_trace.csv under {d}")
+    per = {}
+    for r in csv.DictReader(open(path[0])):
+        per.setdefault(r["Kernel_Name"], []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    total = sum(sum(v) for v in per.values())
+    rows = sorted(((sum(v), name, sorted(v)) for name, v in per.items()), reverse=True)
+    out = [f"# rocprofv3 kernel trace: {workload}", "",
+           "Per-kernel statistics over every dispatch of the run (durations in microseconds).", "",
+           "| kernel | calls | mean us | median us | min us | max us | share % |", "|---|---|---|---|---|---|---|"]
+    for tot, name, v in rows:
+        nm = name if len(name) <= 110 else name[:107] + "..."
+        out.append(f"| `{nm}` | {len(v)} | {tot / len(v):.1f} | {v[len(v) // 2]:.1f} | {v[0]:.1f} | {v[-1]:.1f} | "
+                   f"{100 * tot / total:.2f} |")
+    return "\n".join(out)
+
+
 def pmc_summary(paths):
     """Median over dispatches of every counter, per kernel (rocprofv3 --pmc csv output)."""
     import csv
@@ -450,6 +476,9 @@ def main():
         return
     if args.pmc_summary:
         print(json.dumps(pmc_summary(args.pmc_summary), indent=1))
+        return
+    if args.trace_summary:
+        print(trace_summary(args.trace_summary, args.workload))
         return
     if args.pmc_record:
         print(pmc_record(args.workload, args.pmc_record))

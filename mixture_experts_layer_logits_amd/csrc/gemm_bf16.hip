@@ -39,6 +39,7 @@ typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 // ---------------------------------------------------------------------------------------
 struct ProbBase {
   static constexpr bool MXQ = false;  // no MXFP8 copy of the output
+  static constexpr bool N_MAJOR = true;  // Group::M tile order within an expert
   int M = 0, N = 0, K = 0, E = 1;
   const int* offsets = nullptr;
   int seg_len = 0, seg_total = 0;
@@ -124,6 +125,9 @@ struct ProbDgrad2T : ProbBase {
   static constexpr bool A_KC = true, B_KC = false;
   static constexpr Epi EPI = Epi::DSwiGLU;
   static constexpr bool MXQ = Q;
+  // M-tile major: N-tile major measured 6% slower here at E = 128, T = 8192 (its epilogue
+  // reads the saved a, b of the tile's rows)
+  static constexpr bool N_MAJOR = false;
   const bf16_t* dY = nullptr; const bf16_t* W2 = nullptr; const bf16_t* ab = nullptr;
   bf16_t* dab = nullptr;
   uint8_t* dq = nullptr; uint8_t* ds = nullptr;
@@ -495,7 +499,7 @@ __global__ void __launch_bounds__(Cfg::NT + 64 * NL)
   if (wg >= total_tiles) return;  // uniform over the workgroup
   // tile ranges are workgroup-uniform: keep them in scalar registers
   auto tile = [&](int t) {
-    TileRange r = tile_at<Prob::GROUP, BM, BN>(t, s_map, seg, E, p.M, p.N, p.K);
+    TileRange r = tile_at<Prob::GROUP, BM, BN, Prob::N_MAJOR>(t, s_map, seg, E, p.M, p.N, p.K);
     r.e = __builtin_amdgcn_readfirstlane(r.e);
     r.m0 = __builtin_amdgcn_readfirstlane(r.m0);
     r.m_end = __builtin_amdgcn_readfirstlane(r.m_end);

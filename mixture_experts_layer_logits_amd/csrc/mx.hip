@@ -637,7 +637,7 @@ mx_gemm_kernel(const Prob p) {
   if (wg >= total_tiles) return;  // uniform over the workgroup
 
   auto tile = [&](int t) {
-    TileRange r = tile_at<Prob::GROUP, BM, BN>(t, s_map, seg, E, p.M, p.N, p.K);
+    TileRange r = tile_at<Prob::GROUP, BM, BN, Prob::N_MAJOR>(t, s_map, seg, E, p.M, p.N, p.K);
     r.e = __builtin_amdgcn_readfirstlane(r.e);
     r.m0 = __builtin_amdgcn_readfirstlane(r.m0);
     r.m_end = __builtin_amdgcn_readfirstlane(r.m_end);
@@ -795,6 +795,7 @@ mx_gemm_kernel(const Prob p) {
 // ---------------------------------------------------------------------------------------
 struct MxBase {
   static constexpr bool MXQ = false;  // no MXFP8 copy of the output
+  static constexpr bool N_MAJOR = true;  // Group::M tile order within an expert
   int M = 0, N = 0, K = 0, E = 1;
   const int* offsets = nullptr;
   const uint8_t *qa = nullptr, *sa = nullptr;  // A codes / scales, row length K (padded for Group::K)
@@ -836,6 +837,7 @@ struct MxPlain : MxBase {  // C[m][n] = sum_k A[m][k] B_e[n][k], bf16 out (Group
 
 struct MxDgrad2 : MxPlain {  // dh = dy W2_e, then the SwiGLU gradient from the saved a, b
   static constexpr Epi EPI = Epi::DSwiGLU;
+  static constexpr bool N_MAJOR = false;  // as the bf16 dgrad2
   const bf16_t* ab = nullptr;
   bf16_t* dab = nullptr;
   __device__ AbPair prefetch4(int m, int n) const { return load_ab4(ab, N, m, n); }

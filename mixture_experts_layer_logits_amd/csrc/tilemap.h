@@ -3,8 +3,9 @@
 // and walks a persistent, XCD-aware schedule over it.
 //
 //   Group::M  rows grouped by expert: the M-tiles of expert e are numbered from
-//             s_map[e] = sum_{e' < e} ceil(rows_e' / BM); tile t -> (M-tile t / ntn,
-//             N-tile t % ntn), so consecutive tiles of one expert share its weights.
+//             s_map[e] = sum_{e' < e} ceil(rows_e' / BM); its tiles are numbered N-tile
+//             major (consecutive tiles read the same weight block) or, for problems that
+//             set N_MAJOR = false, M-tile major (consecutive tiles read the same rows).
 //   Group::K  reduction grouped by expert: one output tile set per expert, experts
 //             ordered by descending row count (ties: lower id) so the longest reductions
 //             start first.
@@ -58,20 +59,33 @@ __device__ __forceinline__ int build_tile_map(int* s_map, Seg seg, int E, int M,
 }
 
 // Tile t of the map.  Group::M: K range [0, K); Group::K: K range = the expert's rows.
-template <Group GROUP, int BM, int BN, class Seg>
+// NMAJOR (Group::M): an expert's tiles are numbered N-tile major, else M-tile major.
+template <Group GROUP, int BM, int BN, bool NMAJOR, class Seg>
 __device__ __forceinline__ TileRange tile_at(int t, const int* s_map, Seg seg, int E, int M, int N, int K) {
   const int ntn = (N + BN - 1) / BN;
   TileRange r;
   if constexpr (GROUP == Group::M) {
+    // expert e owns tiles [s_map[e] * ntn, s_map[e + 1] * ntn).  N-tile major: the M-tiles
+    // that read the same weight block are consecutive, so a run of tiles that ends inside
+    // an expert splits it between N-tiles (each weight block still read by one run) rather
+    // than between M-tiles (every weight block read by both runs).
     const int mt = t / ntn;
-    r.n0 = (t % ntn) * BN;
     int lo = 0, hi = E;  // largest e with s_map[e] <= mt
     while (hi - lo > 1) {
       const int mid = (lo + hi) >> 1;
       if (s_map[mid] <= mt) lo = mid; else hi = mid;
     }
     r.e = lo;
-    r.m0 = seg(lo) + (mt - s_map[lo]) * BM;
+    if constexpr (NMAJOR) {
+      const int me = s_map[lo + 1] - s_map[lo];  // M-tiles of expert lo (>= 1 here)
+      const int local = t - s_map[lo] * ntn;
+      const int nt = local / me;
+      r.n0 = nt * BN;
+      r.m0 = seg(lo) + (local - nt * me) * BM;
+    } else {
+      r.n0 = (t % ntn) * BN;
+      r.m0 = seg(lo) + (mt - s_map[lo]) * BM;
+    }
     r.m_end = seg(lo + 1);
     r.k_beg = 0;
     r.k_end = K;
