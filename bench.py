@@ -208,7 +208,7 @@ def fused_quant_flags(w):
     return ("gemm2" in sc and "gemm1" not in sc), ("dgrad1" in sc and "dgrad2" not in sc)
 
 
-def algorithmic_work(w, eb, mx_dispatch=False, fq_h=False, fq_dab=False):
+def algorithmic_work(w, eb, mx_dispatch=False, fq_h=False, fq_dab=False):  # noqa: C901
     """Per-launch algorithmic flops (GEMMs) and HBM bytes (everything) of each call.  With
     the MXFP8 dispatch the routed rows of x and dy are written once in each of two E4M3
     layouts (1 + 1/32 bytes per element with the scales) and read in that form.  fq_h /
@@ -234,7 +234,8 @@ def algorithmic_work(w, eb, mx_dispatch=False, fq_h=False, fq_dab=False):
         "wgrad1": R * 2 * f * eb + R * d * eb + 2 * wbytes,
         "route_bwd": R * 12 + T * E * 4,
         "router_bwd": 2 * T * E * 4 + E * d * eb + 2 * T * d * eb + E * d * 4,
-        "permute_bwd": R * d * eb + 2 * T * d * eb + R * 4,
+        # dx_perm rows in, dx out, and with learned routing the router's dx_r in
+        "permute_bwd": R * d * eb + (2 if w.routing != "given_uniform" else 1) * T * d * eb + R * 4,
     }
     if fq_h:
         qh = R * f * 33 // 32
@@ -383,6 +384,8 @@ def pmc_record(wname, d):
             c = v.get("call")
             if not c or c == "copy":
                 continue
+            if c == "route" and w.routing == "given_uniform":  # the same kernels read the given ids
+                c = "route_given"
             e = calls.setdefault(c, {"kernels": set()})
             e["kernels"].add(kname)
             for key in keys:
