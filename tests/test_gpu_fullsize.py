@@ -153,6 +153,14 @@ def test_full_size_layer(name, recompute):
     else:
         assert torch.equal(L.x_perm[torch.from_numpy(rows).cuda()].cpu(),
                            inp["x"][torch.from_numpy(row_src[rows]).long()])
+    # MXFP8 rows written by the bf16 producer GEMMs' epilogues: on sampled rows, the oracle's
+    # row quantiser applied to the bf16 values the same kernels stored, byte for byte
+    from oracle import mx_ref
+    sel = torch.from_numpy(rows).cuda()
+    for on, q, sc, v in ((L.fq_h, L.hq_rows, L.hs_rows, L.h), (L.fq_dab, L.dabq_rows, L.dabs_rows, L.dab)):
+        if on:
+            codes, scales = mx_ref.quantize_rows(host(v[sel]).astype(np.float64))
+            assert np.array_equal(host(q[sel]), codes) and np.array_equal(host(sc[sel]), scales)
 
     # sampled tokens: forward output and gradients
     toks = rng.choice(w.T, 8 if w.d >= 4096 else 24, replace=False)
