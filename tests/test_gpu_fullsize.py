@@ -10,8 +10,9 @@ The oracle cannot run whole layers of these sizes in seconds, so:
   * values are checked on sampled tokens (forward output, input gradient, gate and score
     gradients) and on sampled experts (weight gradients, which sum over all of an
     expert's rows), each recomputed by the oracle from that token's or expert's inputs;
-  * the router weight gradient is checked in full against fp64 dlogits^T x taken from
-    the GPU's own dlogits (its per-token inputs are checked separately).
+  * the gate gradient of the scores (dlogits) and the router weight gradient are checked in
+    full against the oracle's fp64 route and router backward applied to the GPU's dgates
+    (which are checked against the oracle on the sampled tokens).
 Tolerance: 2e-2 normwise against the fp64 oracle for bf16, 6e-2 for the MXFP8 layer (its
 default scope), both against the unquantised layer, as for the small cases.
 """
@@ -191,8 +192,12 @@ def test_full_size_layer(name, recompute):
         errs[f"dW3[{e}]"] = normwise_err(host(L.dW3[e]), dW3)
         errs[f"dW2[{e}]"] = normwise_err(host(L.dW2[e]), dW2)
     if learned:
-        dWr_ref = host(L.dlogits).astype(np.float64).T @ _f64(inp["x"])
-        errs["dWr"] = normwise_err(host(L.dWr), dWr_ref)
+        # the oracle's gate gradient (fp64, its own gates) from the GPU's dgates, which are
+        # checked against the oracle on the sampled tokens above, then the oracle's router
+        # backward over every token
+        dL64 = ref.route_bwd(host(L.dgates), gates64, idx, w.E)
+        errs["dlogits_all"] = normwise_err(host(L.dlogits), dL64)
+        errs["dWr"] = normwise_err(host(L.dWr), ref.router_bwd(inp["x"], inp["Wr"], dL64)[1])
     if inp.get("shared") is not None:  # shared expert weight gradients over all T tokens
         sh = [_f64(u) for u in inp["shared"]]
         X = _f64(inp["x"])
