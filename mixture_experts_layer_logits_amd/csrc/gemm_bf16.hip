@@ -40,6 +40,7 @@ typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 struct ProbBase {
   static constexpr bool MXQ = false;  // no MXFP8 copy of the output
   static constexpr bool N_MAJOR = true;  // Group::M tile order within an expert
+  static constexpr bool STORE16 = false;  // bf16 output rows through out_row (Epi::Store)
   int M = 0, N = 0, K = 0, E = 1;
   const int* offsets = nullptr;
   int seg_len = 0, seg_total = 0;
@@ -112,6 +113,8 @@ struct ProbGemm2 : ProbBase {
   bf16_t* Y = nullptr;
   __device__ const bf16_t* a_row(int, int m) const { return Hm + (int64_t)m * K; }
   __device__ const bf16_t* b_row(int e, int n) const { return W2 + ((int64_t)e * N + n) * K; }
+  static constexpr bool STORE16 = true;
+  __device__ bf16_t* out_row(int, int m) const { return Y + (int64_t)m * N; }
   __device__ void epilogue4(int, int m, int n, const float (&v)[4]) const { store_bf16x4(Y + (int64_t)m * N + n, v); }
 };
 
@@ -164,6 +167,8 @@ struct ProbWgrad2 : ProbBase {
   bf16_t* dW2 = nullptr;
   __device__ const bf16_t* a_row(int, int r) const { return dY + (int64_t)r * M; }
   __device__ const bf16_t* b_row(int, int r) const { return Hm + (int64_t)r * N; }
+  static constexpr bool STORE16 = true;
+  __device__ bf16_t* out_row(int e, int m) const { return dW2 + ((int64_t)e * M + m) * N; }
   __device__ void epilogue4(int e, int m, int n, const float (&v)[4]) const {
     store_bf16x4(dW2 + ((int64_t)e * M + m) * N + n, v);
   }
@@ -184,6 +189,8 @@ struct ProbDgrad1 : ProbBase {
   }
   static constexpr bool K_SPLIT = true;
   __device__ int k_split() const { return f; }
+  static constexpr bool STORE16 = true;
+  __device__ bf16_t* out_row(int, int m) const { return dX + (int64_t)m * N; }
   __device__ void epilogue4(int, int m, int n, const float (&v)[4]) const { store_bf16x4(dX + (int64_t)m * N + n, v); }
 };
 
@@ -198,10 +205,11 @@ struct ProbWgrad1 : ProbBase {
   bf16_t* dW1 = nullptr; bf16_t* dW3 = nullptr;
   __device__ const bf16_t* a_row(int, int r) const { return dab + (int64_t)r * M; }
   __device__ const bf16_t* b_row(int, int r) const { return X + (int64_t)r * N; }
-  __device__ void epilogue4(int e, int m, int n, const float (&v)[4]) const {
-    bf16_t* W = m < f ? dW1 + ((int64_t)e * f + m) * N : dW3 + ((int64_t)e * f + (m - f)) * N;
-    store_bf16x4(W + n, v);
+  static constexpr bool STORE16 = true;
+  __device__ bf16_t* out_row(int e, int m) const {
+    return m < f ? dW1 + ((int64_t)e * f + m) * N : dW3 + ((int64_t)e * f + (m - f)) * N;
   }
+  __device__ void epilogue4(int e, int m, int n, const float (&v)[4]) const { store_bf16x4(out_row(e, m) + n, v); }
 };
 
 // Router scores: logits[t, e] = x[t] . Wr[e] + bias[e]  (single group over T rows)
@@ -233,6 +241,8 @@ struct ProbRouterDx : ProbBase {
   bf16_t* dX = nullptr;
   __device__ const bf16_t* a_row(int, int m) const { return dL + (int64_t)m * lda; }
   __device__ const bf16_t* b_row(int, int k) const { return Wr + (int64_t)k * N; }
+  static constexpr bool STORE16 = true;
+  __device__ bf16_t* out_row(int, int m) const { return dX + (int64_t)m * N; }
   __device__ void epilogue4(int, int m, int n, const float (&v)[4]) const { store_bf16x4(dX + (int64_t)m * N + n, v); }
 };
 

@@ -796,6 +796,7 @@ mx_gemm_kernel(const Prob p) {
 struct MxBase {
   static constexpr bool MXQ = false;  // no MXFP8 copy of the output
   static constexpr bool N_MAJOR = true;  // Group::M tile order within an expert
+  static constexpr bool STORE16 = false;  // bf16 output rows through out_row (Epi::Store)
   int M = 0, N = 0, K = 0, E = 1;
   const int* offsets = nullptr;
   const uint8_t *qa = nullptr, *sa = nullptr;  // A codes / scales, row length K (padded for Group::K)
@@ -832,6 +833,8 @@ struct MxPlain : MxBase {  // C[m][n] = sum_k A[m][k] B_e[n][k], bf16 out (Group
   __device__ const uint8_t* a_scale_row(int, int m) const { return sa + (int64_t)m * (K / kMxBlock); }
   __device__ const uint8_t* b_row(int e, int n) const { return qb + ((int64_t)e * N + n) * K; }
   __device__ const uint8_t* b_scale_row(int e, int n) const { return sb + ((int64_t)e * N + n) * (K / kMxBlock); }
+  static constexpr bool STORE16 = true;
+  __device__ bf16_t* out_row(int, int m) const { return C + (int64_t)m * N; }
   __device__ void epilogue4(int, int m, int n, const float (&v)[4]) const { store_bf16x4(C + (int64_t)m * N + n, v); }
 };
 
@@ -857,10 +860,11 @@ struct MxWgrad : MxBase {  // C_e[m][n] = sum over expert e's (padded) rows of A
   __device__ const uint8_t* a_scale_row(int, int m) const { return sa + (int64_t)m * (K / kMxBlock); }
   __device__ const uint8_t* b_row(int, int n) const { return qb + (int64_t)n * K; }
   __device__ const uint8_t* b_scale_row(int, int n) const { return sb + (int64_t)n * (K / kMxBlock); }
-  __device__ void epilogue4(int e, int m, int n, const float (&v)[4]) const {
-    bf16_t* W = m < split ? C0 + ((int64_t)e * split + m) * N : C1 + ((int64_t)e * (M - split) + (m - split)) * N;
-    store_bf16x4(W + n, v);
+  static constexpr bool STORE16 = true;
+  __device__ bf16_t* out_row(int e, int m) const {
+    return m < split ? C0 + ((int64_t)e * split + m) * N : C1 + ((int64_t)e * (M - split) + (m - split)) * N;
   }
+  __device__ void epilogue4(int e, int m, int n, const float (&v)[4]) const { store_bf16x4(out_row(e, m) + n, v); }
 };
 
 template <class Cfg, int NS, class Prob>
