@@ -17,6 +17,11 @@
 //   Epi::Store                 p.epilogue4(e, m, n, v[4])          columns n .. n+3
 //   Epi::Store, STORE16        p.out_row(e, m) -> bf16 row; 16-byte stores at columns
 //                              n .. n+7 (N a multiple of 8)
+//   Epi::SwiGLU, STORE16       p.swiglu4(a[4], b[4], h[4]), then p.store_swiglu16(m, hcol,
+//                              a, b, h) with 8 packed bf16 columns each (and, MXQ,
+//                              p.store_swiglu16_q(m, hcol, h, valid, first) from every lane)
+//   Epi::DSwiGLU, STORE16      p.prefetch4 as above, then p.store_dswiglu16(m, n, da, db)
+//                              (and, MXQ, p.store_dswiglu16_q(m, n, da, db, valid, first))
 //   Epi::SwiGLU                p.epilogue_swiglu4(m, hcol, a[4], b[4])
 //   Epi::DSwiGLU               p.prefetch4(m, n) -> AbPair, then p.epilogue4_pre(e, m, n, v[4], pair)
 // A problem with MXQ = true also writes its SwiGLU (h) or SwiGLU-gradient (da | db) output as
@@ -136,6 +141,43 @@ __device__ __forceinline__ void mx_block_store4(const float (&v)[4], bool valid,
   }
 }
 
+// Lanes of quads 2c and 2c + 1 after the quad transpose: w[h] is the packed bf16 of row group
+// 2 pq + h at the lane's 4 columns.  Returns the 8 consecutive columns of the lane's own row
+// group (2 pq for the even quad, 2 pq + 1 for the odd one): each lane sends its partner (lane
+// ^ 4) the partner's row group.
+__device__ __forceinline__ uint4 pair_row16(const uint32_t (&w)[2][2], bool odd) {
+  const uint32_t r0 = __shfl_xor(odd ? w[0][0] : w[1][0], 4, kWave);
+  const uint32_t r1 = __shfl_xor(odd ? w[0][1] : w[1][1], 4, kWave);
+  return odd ? make_uint4(r0, r1, w[1][0], w[1][1]) : make_uint4(w[0][0], w[0][1], r0, r1);
+}
+
+// The MXFP8 row block of 32 columns held 8 per lane (packed bf16, the stored values) by the
+// 4 lanes that differ only in lane bits 3 and 4: block maximum over those lanes, then each
+// lane encodes its 8 values.  Bit for bit what the row quantiser writes for the stored row.
+// Every lane must call it; `valid` gates the 8-byte code store at q and, from the block's
+// first lane, the scale byte at sc.
+__device__ __forceinline__ void mx_block_store8(const uint4& pk, bool valid, uint8_t* q, uint8_t* sc, bool first) {
+  const uint32_t w[4] = {pk.x, pk.y, pk.z, pk.w};
+  float r[8], amax = 0.f;
+#pragma unroll
+  for (int u = 0; u < 4; u++) {
+    r[2 * u] = __uint_as_float(w[u] << 16);
+    r[2 * u + 1] = __uint_as_float(w[u] & 0xffff0000u);
+  }
+#pragma unroll
+  for (int c = 0; c < 8; c++) amax = fmaxf(amax, fabsf(r[c]));
+  amax = fmaxf(amax, __shfl_xor(amax, 8, kWave));
+  amax = fmaxf(amax, __shfl_xor(amax, 16, kWave));
+  const int s = mx_scale_exp(amax);
+  const float inv = mx_inv_scale(s);
+  const uint2 codes = make_uint2(e4m3x4(r[0] * inv, r[1] * inv, r[2] * inv, r[3] * inv),
+                                 e4m3x4(r[4] * inv, r[5] * inv, r[6] * inv, r[7] * inv));
+  if (valid) {
+    *reinterpret_cast<uint2*>(q) = codes;
+    if (first) *sc = (uint8_t)(s + 127);
+  }
+}
+
 // Writes the tile of wave (wave_m, wave_n) whose accumulators are acc.
 template <class Prob, int WTM, int WTN>
 __device__ __forceinline__ void tile_epilogue(const Prob& p, const f32x16 (&acc)[WTM][WTN], const TileRange& tr,
@@ -158,19 +200,85 @@ __device__ __forceinline__ void tile_epilogue(const Prob& p, const f32x16 (&acc)
           pre[q][j] = p.prefetch4(m, n);
         }
       }
+      if constexpr (Prob::STORE16) {
+        // the gradients of the lane's own 4 columns in fp32, rounded, then completed to 8
+        // columns of one row by the quad-pair exchange: 16-byte stores
+        const bool odd = quad & 1;
 #pragma unroll
-      for (int q = 0; q < 4; q++) {
-        const int m = tr.m0 + (wave_m * WTM + i) * 32 + 8 * q + 4 * half + sub;
+        for (int pq = 0; pq < 2; pq++) {
+          const int m = tr.m0 + (wave_m * WTM + i) * 32 + 8 * (2 * pq + (odd ? 1 : 0)) + 4 * half + sub;
 #pragma unroll
-        for (int j = 0; j < WTN; j++) {
-          float v[4];
+          for (int j = 0; j < WTN; j++) {
+            uint32_t wa[2][2], wb[2][2];
 #pragma unroll
-          for (int c = 0; c < 4; c++) v[c] = acc[i][j][4 * q + c];
-          quad_transpose(v, lane);
-          const int n = tr.n0 + (wave_n * WTN + j) * 32 + 4 * quad;
-          const bool valid = m < tr.m_end && n < p.N;
-          if constexpr (Prob::MXQ) p.epilogue4_pre_q(tr.e, m, n, v, pre[q][j], valid, quad);
-          else if (valid) p.epilogue4_pre(tr.e, m, n, v, pre[q][j]);
+            for (int h = 0; h < 2; h++) {
+              float v[4], da[4], db[4];
+#pragma unroll
+              for (int c = 0; c < 4; c++) v[c] = acc[i][j][4 * (2 * pq + h) + c];
+              quad_transpose(v, lane);
+              dswiglu4(v, pre[2 * pq + h][j], da, db);
+              wa[h][0] = pack_bf16x2(da[0], da[1]);
+              wa[h][1] = pack_bf16x2(da[2], da[3]);
+              wb[h][0] = pack_bf16x2(db[0], db[1]);
+              wb[h][1] = pack_bf16x2(db[2], db[3]);
+            }
+            const uint4 ua = pair_row16(wa, odd), ub = pair_row16(wb, odd);
+            const int n = tr.n0 + (wave_n * WTN + j) * 32 + 8 * (quad >> 1);
+            const bool valid = m < tr.m_end && n < p.N;
+            if (valid) p.store_dswiglu16(m, n, ua, ub);
+            if constexpr (Prob::MXQ) p.store_dswiglu16_q(m, n, ua, ub, valid, (quad >> 1) == 0);
+          }
+        }
+      } else {
+#pragma unroll
+        for (int q = 0; q < 4; q++) {
+          const int m = tr.m0 + (wave_m * WTM + i) * 32 + 8 * q + 4 * half + sub;
+#pragma unroll
+          for (int j = 0; j < WTN; j++) {
+            float v[4];
+#pragma unroll
+            for (int c = 0; c < 4; c++) v[c] = acc[i][j][4 * q + c];
+            quad_transpose(v, lane);
+            const int n = tr.n0 + (wave_n * WTN + j) * 32 + 4 * quad;
+            const bool valid = m < tr.m_end && n < p.N;
+            if constexpr (Prob::MXQ) p.epilogue4_pre_q(tr.e, m, n, v, pre[q][j], valid, quad);
+            else if (valid) p.epilogue4_pre(tr.e, m, n, v, pre[q][j]);
+          }
+        }
+      }
+    } else if constexpr (Prob::EPI == Epi::SwiGLU && Prob::STORE16) {
+      // a and b of the lane's own 4 columns, h from them in fp32, all three rounded and
+      // completed to 8 columns of one row by the quad-pair exchange: 16-byte stores
+      const bool odd = quad & 1;
+#pragma unroll
+      for (int pq = 0; pq < 2; pq++) {
+        const int m = tr.m0 + (wave_m * WTM + i) * 32 + 8 * (2 * pq + (odd ? 1 : 0)) + 4 * half + sub;
+#pragma unroll
+        for (int j = 0; j < WTN; j += 2) {
+          uint32_t wa[2][2], wb[2][2], wh[2][2];
+#pragma unroll
+          for (int h = 0; h < 2; h++) {
+            float a[4], b[4], hv[4];
+#pragma unroll
+            for (int c = 0; c < 4; c++) {
+              a[c] = acc[i][j][4 * (2 * pq + h) + c];
+              b[c] = acc[i][j + 1][4 * (2 * pq + h) + c];
+            }
+            quad_transpose(a, lane);
+            quad_transpose(b, lane);
+            p.swiglu4(a, b, hv);
+            wa[h][0] = pack_bf16x2(a[0], a[1]);
+            wa[h][1] = pack_bf16x2(a[2], a[3]);
+            wb[h][0] = pack_bf16x2(b[0], b[1]);
+            wb[h][1] = pack_bf16x2(b[2], b[3]);
+            wh[h][0] = pack_bf16x2(hv[0], hv[1]);
+            wh[h][1] = pack_bf16x2(hv[2], hv[3]);
+          }
+          const uint4 ua = pair_row16(wa, odd), ub = pair_row16(wb, odd), uh = pair_row16(wh, odd);
+          const int hcol = tr.n0 / 2 + ((wave_n * WTN + j) >> 1) * 32 + 8 * (quad >> 1);
+          const bool valid = m < tr.m_end && hcol < p.N / 2;
+          if (valid) p.store_swiglu16(m, hcol, ua, ub, uh);
+          if constexpr (Prob::MXQ) p.store_swiglu16_q(m, hcol, uh, valid, (quad >> 1) == 0);
         }
       }
     } else if constexpr (Prob::EPI == Epi::Store && Prob::STORE16) {
@@ -192,9 +300,7 @@ __device__ __forceinline__ void tile_epilogue(const Prob& p, const f32x16 (&acc)
             w[h][0] = pack_bf16x2(v[0], v[1]);
             w[h][1] = pack_bf16x2(v[2], v[3]);
           }
-          const uint32_t r0 = __shfl_xor(odd ? w[0][0] : w[1][0], 4, kWave);
-          const uint32_t r1 = __shfl_xor(odd ? w[0][1] : w[1][1], 4, kWave);
-          const uint4 o = odd ? make_uint4(r0, r1, w[1][0], w[1][1]) : make_uint4(w[0][0], w[0][1], r0, r1);
+          const uint4 o = pair_row16(w, odd);
           const int n = tr.n0 + (wave_n * WTN + j) * 32 + 8 * (quad >> 1);
           if (m < tr.m_end && n < p.N) *reinterpret_cast<uint4*>(p.out_row(tr.e, m) + n) = o;
         }

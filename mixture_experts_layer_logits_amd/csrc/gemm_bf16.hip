@@ -88,6 +88,17 @@ struct ProbGemm1T : ProbBase {
     swiglu4(a, b, hv);
     store_bf16x4(h + (int64_t)m * f + hcol, hv);
   }
+  static constexpr bool STORE16 = true;
+  // 8 columns hcol .. hcol+7 of row m, packed bf16: a, b into ab, h into h
+  __device__ void store_swiglu16(int m, int hcol, const uint4& a, const uint4& b, const uint4& hv) const {
+    bf16_t* abr = ab + (int64_t)m * 2 * f;
+    *reinterpret_cast<uint4*>(abr + hcol) = a;
+    *reinterpret_cast<uint4*>(abr + f + hcol) = b;
+    *reinterpret_cast<uint4*>(h + (int64_t)m * f + hcol) = hv;
+  }
+  __device__ void store_swiglu16_q(int m, int hcol, const uint4& hv, bool valid, bool first) const {
+    mx_block_store8(hv, valid, hq + (int64_t)m * f + hcol, hs + (int64_t)m * (f / 32) + hcol / 32, first);
+  }
   __device__ void epilogue_swiglu4_q(int m, int hcol, const float (&a)[4], const float (&b)[4], bool valid,
                                      int quad) const {
     float hv[4];
@@ -139,6 +150,19 @@ struct ProbDgrad2T : ProbBase {
   __device__ AbPair prefetch4(int m, int n) const { return load_ab4(ab, N, m, n); }
   __device__ void epilogue4_pre(int, int m, int n, const float (&dh)[4], const AbPair& pr) const {
     dswiglu_store4(dab, N, m, n, dh, pr);
+  }
+  static constexpr bool STORE16 = true;
+  // 8 columns n .. n+7 of row m, packed bf16: da into dab[m][n], db into dab[m][N + n]
+  __device__ void store_dswiglu16(int m, int n, const uint4& da, const uint4& db) const {
+    bf16_t* o = dab + (int64_t)m * 2 * N;
+    *reinterpret_cast<uint4*>(o + n) = da;
+    *reinterpret_cast<uint4*>(o + N + n) = db;
+  }
+  __device__ void store_dswiglu16_q(int m, int n, const uint4& da, const uint4& db, bool valid, bool first) const {
+    uint8_t* q = dq + (int64_t)m * 2 * N;
+    uint8_t* sc = ds + (int64_t)m * (2 * N / 32);
+    mx_block_store8(da, valid, q + n, sc + n / 32, first);
+    mx_block_store8(db, valid, q + N + n, sc + (N + n) / 32, first);
   }
   __device__ void epilogue4_pre_q(int, int m, int n, const float (&dh)[4], const AbPair& pr, bool valid,
                                   int quad) const {

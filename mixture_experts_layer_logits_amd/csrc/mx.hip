@@ -841,6 +841,7 @@ struct MxPlain : MxBase {  // C[m][n] = sum_k A[m][k] B_e[n][k], bf16 out (Group
 struct MxDgrad2 : MxPlain {  // dh = dy W2_e, then the SwiGLU gradient from the saved a, b
   static constexpr Epi EPI = Epi::DSwiGLU;
   static constexpr bool N_MAJOR = false;  // as the bf16 dgrad2
+  static constexpr bool STORE16 = false;  // 8-byte SwiGLU-gradient stores (epilogue4_pre)
   const bf16_t* ab = nullptr;
   bf16_t* dab = nullptr;
   __device__ AbPair prefetch4(int m, int n) const { return load_ab4(ab, N, m, n); }
