@@ -808,6 +808,11 @@ static hipError_t launch_pipe(const Prob& p, hipStream_t st) {
 template <class Cfg, class Prob>
 static hipError_t launch_cfg(const Prob& p, hipStream_t st, int bk, int stages, int loaders) {
   static_assert(std::is_same<typename Prob::TA, bf16_t>::value, "bf16 operands");
+  // the SwiGLU epilogue pairs each wave's 32-column blocks (a, b): a tile override whose
+  // waves hold an odd number of them runs the default tile instead
+  if constexpr (Prob::EPI == Epi::SwiGLU && Cfg::WTN % 2 != 0) {
+    return launch_cfg<TileCfg<128, 256, 2, 4>>(p, st, bk, stages, loaders);
+  } else {
   // the stage buffers must fit the 160 KB of LDS with room for the tile map
   constexpr bool fits64 = 3 * (Cfg::BM + Cfg::BN) * 64 * 2 <= 152 * 1024;
   constexpr bool fits32x4 = 4 * (Cfg::BM + Cfg::BN) * 32 * 2 <= 152 * 1024;
@@ -839,6 +844,7 @@ static hipError_t launch_cfg(const Prob& p, hipStream_t st, int bk, int stages, 
   }
   if constexpr (fits64) return launch_pipe<Cfg, Prob, 64, 3>(p, st);
   return hipErrorInvalidConfiguration;
+  }
 }
 
 // The default build compiles the tile shapes the defaults use; -DMOE_ALL_TILES adds the
