@@ -197,6 +197,10 @@ __global__ void __launch_bounds__(kTransThreads) mx_trans_kernel(TransQ a) {
 // bf16 values in LDS; each lane then quantises one column's 32-row block from LDS, and the
 // codes leave through an LDS tile as full 128-byte lines of the column layout.  The row
 // layout gets 64-byte halves of its lines from consecutive column tiles of one workgroup.
+// The kernel is bound by its vector-memory instruction count, so its stores are few and
+// wide: row codes leave 16 bytes per lane (lane pairs swap one row's 8 codes), each lane
+// stores at most one row-scale pair, and one wave stores a tile's four column-scale bytes
+// of each column as one word.
 // ---------------------------------------------------------------------------------------
 struct DispatchQ {
   const bf16_t* src;  // [T][cols]
@@ -226,6 +230,7 @@ static_assert((kMaxExperts + 1) * 4 <= kDispRows * kDispInPitch, "segment scan r
 static_assert(kDispCols == kWave && kDispRows == 32 * (kDispThreads / kWave), "one column per lane, one block per wave");
 
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 template <int CTRL>
 __device__ __forceinline__ float quad_max(float v) {
@@ -246,6 +251,7 @@ __global__ void __launch_bounds__(kDispThreads) mx_dispatch_kernel(DispatchQ a) 
   __shared__ int s_tok[kDispRows];
   __shared__ float s_gate[kDispRows];
   __shared__ int s_wsum[kDispThreads / kWave];
+  __shared__ uint32_t s_csc[kDispCols];  // the tile's column scale bytes, 4 per column
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
 
   // --- padded tile starts of the experts (exclusive scan of roundup(n_e, 128) / 128),
@@ -338,6 +344,8 @@ __global__ void __launch_bounds__(kDispThreads) mx_dispatch_kernel(DispatchQ a) 
     const int c0 = ct * kDispCols;
     load(nxt, min(ct + 1, ct_end - 1));  // the next tile's rows are in flight during this one
     // --- row blocks, straight from registers
+    uint2 codes[kDispChunks];
+    uint32_t sw[kDispChunks];
 #pragma unroll
     for (int i = 0; i < kDispChunks; i++) {
       const int row = row_base + kDispRowStep * i;
@@ -361,16 +369,38 @@ __global__ void __launch_bounds__(kDispThreads) mx_dispatch_kernel(DispatchQ a) 
       const float r = mx_inv_scale(sexp);
       const uint32_t w0 = e4m3x4(v[0] * r, v[1] * r, v[2] * r, v[3] * r);
       const uint32_t w1 = e4m3x4(v[4] * r, v[5] * r, v[6] * r, v[7] * r);
-      // the scale bytes of the row's two blocks, gathered into the lane of chunk 0 (the
-      // other lanes' stores are aimed past the buffer and dropped)
+      // the scale bytes of the row's two blocks, gathered into the lane of chunk 0
       const uint32_t sb = (uint32_t)(sexp + 127);
-      const uint32_t sw = sb | (__shfl_down(sb, 4, kDispRowChunks) << 8);
-      const uint2 codes = make_uint2(w0, w1);
-      __builtin_amdgcn_raw_buffer_store_b64(*reinterpret_cast<const u32x2*>(&codes), rq,
-                                            row * a.cols + c0 + chunk * 8, 0, 0);
-      __builtin_amdgcn_raw_buffer_store_b16((uint16_t)sw, rs, chunk == 0 ? row * nbc + c0 / kMxBlock : 0x7ffffff0,
-                                            0, 0);
+      sw[i] = sb | (__shfl_down(sb, 4, kDispRowChunks) << 8);
+      codes[i] = make_uint2(w0, w1);
       *reinterpret_cast<uint4*>(s_buf + row * kDispInPitch + chunk * 16) = cur[i];
+    }
+    // row codes as 16-byte stores: the lanes of chunks 2c and 2c + 1 (lane ^ 1) pair up, the
+    // even one storing both chunks of row i, the odd one of row i + 1 (i = 0, 2)
+    {
+      const bool odd = chunk & 1;
+#pragma unroll
+      for (int i = 0; i < kDispChunks; i += 2) {
+        const uint2 give = odd ? codes[i] : codes[i + 1];  // the partner's row
+        const uint32_t g0 = __shfl_xor(give.x, 1, kWave), g1 = __shfl_xor(give.y, 1, kWave);
+        const int row = row_base + kDispRowStep * (i + (odd ? 1 : 0));
+        const u32x4 v = odd ? u32x4{g0, g1, codes[i + 1].x, codes[i + 1].y} : u32x4{codes[i].x, codes[i].y, g0, g1};
+        __builtin_amdgcn_raw_buffer_store_b128(v, rq, row * a.cols + c0 + (chunk & ~1) * 8, 0, 0);
+      }
+    }
+    // row scales, one store per lane: the lane of chunk c < 4 stores the two scale bytes of
+    // row row_base + 32 c (held by the chunk-0 lane of its row group); the other lanes'
+    // stores are aimed past the buffer and dropped
+    {
+      uint32_t mine = 0;
+#pragma unroll
+      for (int i = 0; i < kDispChunks; i++) {
+        const uint32_t v = __shfl(sw[i], lane & ~(kDispRowChunks - 1), kWave);
+        if (chunk == i) mine = v;
+      }
+      __builtin_amdgcn_raw_buffer_store_b16(
+          (uint16_t)mine, rs, chunk < kDispChunks ? (row_base + kDispRowStep * chunk) * nbc + c0 / kMxBlock : 0x7ffffff0,
+          0, 0);
     }
     __syncthreads();
     // --- column blocks: wave w takes rows [32 w, 32 w + 32) of column `lane`; two passes
@@ -387,7 +417,7 @@ __global__ void __launch_bounds__(kDispThreads) mx_dispatch_kernel(DispatchQ a) 
       auto at = [&](int i) { return bf2f(*reinterpret_cast<const bf16_t*>(col + i * kDispInPitch)) * r; };
 #pragma unroll
       for (int i = 0; i < 8; i++) q[i] = e4m3x4(at(4 * i), at(4 * i + 1), at(4 * i + 2), at(4 * i + 3));
-      a.s_cols[(int64_t)(c0 + lane) * (a.ld / kMxBlock) + prow / kMxBlock + wave] = (uint8_t)(sexp + 127);
+      reinterpret_cast<uint8_t*>(s_csc)[lane * 4 + wave] = (uint8_t)(sexp + 127);
     }
     __syncthreads();  // every wave is done reading the bf16 tile
     {
@@ -396,6 +426,20 @@ __global__ void __launch_bounds__(kDispThreads) mx_dispatch_kernel(DispatchQ a) 
       o[1] = make_uint4(q[4], q[5], q[6], q[7]);
     }
     __syncthreads();
+    // the column scales of this tile: the four 32-row blocks of column c0 + lane are four
+    // consecutive bytes, stored by wave 0 as one word (or as bytes when the rows per column
+    // leave the word unaligned)
+    if (wave == 0) {
+      const int64_t sld = a.ld / kMxBlock;
+      uint8_t* dst = a.s_cols + (int64_t)(c0 + lane) * sld + prow / kMxBlock;
+      const uint32_t w = s_csc[lane];
+      if (sld % 4 == 0) {
+        *reinterpret_cast<uint32_t*>(dst) = w;
+      } else {
+#pragma unroll
+        for (int b = 0; b < 4; b++) dst[b] = (uint8_t)(w >> (8 * b));
+      }
+    }
     // 64 columns x 128 bytes, 8 lanes per line
 #pragma unroll
     for (int u = 0; u < kDispCols * kDispRows / 16 / kDispThreads; u++) {
