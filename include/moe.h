@@ -42,7 +42,7 @@
  *  - Tuning overrides: MOE_TILE_<GEMM> / MOE_TILE, MOE_GEMM_BK, MOE_GEMM_STAGES,
  *    MOE_GEMM_LOADERS and MOE_MX_TILE select other GEMM tile shapes, k-depths, stage counts
  *    and loader waves than the measured defaults.  Each is read from the environment once,
- *    at the first launch that consults it, and kept for the life of the process.  They
+ *    at the first launch that consults it, and kept until moe_tuning_reload.  They
  *    change only how the work is tiled and scheduled: every output element is still one fp32
  *    reduction over the same values in ascending order of the reduction index.
  *  - Limits: 1 <= k <= E <= 1024, T*k < 2^31, d and f multiples of 64; with MOE_MXFP8
@@ -381,6 +381,14 @@ moe_status moe_ffn_dgrad2_q(const moe_shape* s, const void* dy_perm, const void*
 moe_status moe_ffn_dgrad1_mx(const moe_shape* s, const uint8_t* dabq_rows, const uint8_t* dabs_rows, const void* W1,
                              const void* W3, const int32_t* offsets, void* dx_perm, void* ws, size_t ws_bytes,
                              void* stream);
+
+/* ---------------------------------------------------------------------------------------
+ * moe_tuning_reload: forget the tuning overrides read so far (see the file header), so each
+ * is read from the environment again at its next use.  For tuning sweeps and tests that
+ * change them within one process; it must not run while another host thread launches
+ * through the library.
+ * --------------------------------------------------------------------------------------- */
+void moe_tuning_reload(void);
 
 #ifdef __cplusplus
 }

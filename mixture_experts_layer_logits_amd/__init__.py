@@ -94,7 +94,8 @@ _SIGS = {
     "moe_ffn_dgrad2_q": [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP],
     "moe_ffn_dgrad1_mx": [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _SZ, _VP],
 }
-EXPORTED = sorted(list(_SIGS) + ["moe_mx_quantize", "moe_workspace_size", "moe_mx_cols_ld", "moe_status_str"])
+EXPORTED = sorted(list(_SIGS) + ["moe_mx_quantize", "moe_workspace_size", "moe_mx_cols_ld", "moe_status_str",
+                                  "moe_tuning_reload"])
 
 _lib = None
 
@@ -120,6 +121,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.moe_mx_cols_ld.restype = ctypes.c_size_t
     lib.moe_status_str.argtypes = [ctypes.c_int]
     lib.moe_status_str.restype = ctypes.c_char_p
+    lib.moe_tuning_reload.argtypes = []
+    lib.moe_tuning_reload.restype = None
     _lib = lib
     return lib
 
@@ -240,6 +243,12 @@ def moe_router_bwd(shape, x, Wr, dlogits, dx_r, dWr, ws, stream=None):
 
 def moe_permute_bwd(shape, dx_perm, slot_row, dx_r, dx_add, dx, stream=None):
     _call("moe_permute_bwd", shape, dx_perm, slot_row, dx_r, dx_add, dx, stream=stream)
+
+
+def moe_tuning_reload():
+    """Forget the MOE_TILE_* / MOE_GEMM_* / MOE_MX_TILE overrides read so far; each is read
+    from the environment again at its next use."""
+    load_library().moe_tuning_reload()
 
 
 # ------------------------------------------------------------------ MXFP8

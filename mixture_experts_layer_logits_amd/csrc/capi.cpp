@@ -513,6 +513,11 @@ moe_status moe_ffn_wgrad1_mx(const moe_shape* s, const uint8_t* xq_cols, const u
                             MxIn{xq_cols, xs_cols}));
 }
 
+void moe_tuning_reload(void) {
+  std::lock_guard<std::mutex> lk(g_state_mu);
+  g_env.clear();  // the next tuning_env call of each name reads the environment again
+}
+
 moe_status moe_ffn_gemm1_fwd_q(const moe_shape* s, const void* x_perm, const void* W1, const void* W3,
                                const int32_t* offsets, void* ab, void* h, uint8_t* hq_rows, uint8_t* hs_rows, void* st) {
   MOE_TRY(check_shape(s));

@@ -624,8 +624,34 @@ __global__ void __launch_bounds__(Cfg::NT + 64 * NL)
   };
   // MFMAs of one k-step.  Fragments are double-buffered: slice kk+1 is read from LDS
   // before slice kk's MFMAs issue, so its latency runs under them.
+  // With loader waves beside 4 x 2 accumulator blocks per wave, the fragments are read one
+  // slice at a time (single-buffered) so the workgroup fits three waves per SIMD.
+  constexpr bool FRAG1 = NL > 0 && WTM * WTN >= 8;
   auto compute = [&](const char* st) {
     constexpr int KS = TK / 16;
+    constexpr int NREAD = (Prob::A_KC ? 1 : 2) * WTM + (Prob::B_KC ? 1 : 2) * WTN;
+    if constexpr (FRAG1) {
+      bf16x8 af1[WTM], bf1[WTN];
+#pragma unroll
+      for (int kk = 0; kk < KS; kk++) {
+#pragma unroll
+        for (int i = 0; i < WTM; i++) af1[i] = OA::frag(st, kk, (wave_m * WTM + i) * 32, lane);
+#pragma unroll
+        for (int j = 0; j < WTN; j++) bf1[j] = OB::frag(st + OA::TILE_BYTES, kk, (wave_n * WTN + j) * 32, lane);
+#pragma unroll
+        for (int i = 0; i < WTM; i++)
+#pragma unroll
+          for (int j = 0; j < WTN; j++)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af1[i], bf1[j], acc[i][j], 0, 0, 0);
+      }
+#pragma unroll
+      for (int kk = 0; kk < KS; kk++) {
+        __builtin_amdgcn_sched_group_barrier(0x100, NREAD, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, WTM * WTN, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      return;
+    }
     bf16x8 af[2][WTM], bfr[2][WTN];
     auto read = [&](int kk, int b) {
 #pragma unroll
@@ -645,7 +671,6 @@ __global__ void __launch_bounds__(Cfg::NT + 64 * NL)
     }
     // issue order: slice 0's reads, then per slice the next slice's reads ahead of this
     // slice's MFMAs (LDS reads: mask 0x100, MFMA: mask 0x8)
-    constexpr int NREAD = (Prob::A_KC ? 1 : 2) * WTM + (Prob::B_KC ? 1 : 2) * WTN;
     __builtin_amdgcn_sched_group_barrier(0x100, NREAD, 0);
 #pragma unroll
     for (int kk = 0; kk < KS; kk++) {
@@ -760,7 +785,7 @@ struct TileChoice {
   Tile tile;
   int bk;
   int stages;   // LDS stage buffers: 3, or 4 at a k-depth of 32, or 2 at a k-depth of 64 (where they fit)
-  int loaders;  // extra waves that issue every operand load (0, or 4 for 8-wave 128 x 256 tiles)
+  int loaders;  // extra waves that issue every operand load (0, or 4 for 8-wave 128 x 256 and 256 x 256 tiles)
 };
 
 // Tile shape, k-depth, stage count and loader waves of one GEMM: MOE_TILE_<NAME> /
@@ -824,6 +849,11 @@ static hipError_t launch_cfg(const Prob& p, hipStream_t st, int bk, int stages, 
       if (bk == 64) return launch_pipe<Cfg, Prob, 64, 3, 4>(p, st);
       return launch_pipe<Cfg, Prob, 32, 3, 4>(p, st);
     }
+  }
+  // loader waves for the 256 x 256 weight-gradient tiles, 32 deep in four stages: the
+  // compute waves then issue only their epilogue stores, which no operand load waits behind
+  if constexpr (Prob::GROUP == Group::K && Cfg::BM == 256 && Cfg::BN == 256 && Cfg::NT == 512) {
+    if (loaders == 4 && bk == 32 && stages == 4) return launch_pipe<Cfg, Prob, 32, 4, 4>(p, st);
   }
   if constexpr (Cfg::BM >= 64 && Cfg::BN >= 64 && fits64x2) {
     if (bk == 64 && stages == 2) return launch_pipe<Cfg, Prob, 64, 2>(p, st);
@@ -950,6 +980,14 @@ static hipError_t wgrad_split(int R, int M, int N, int nsplit, const bf16_t* A, 
   return hipGetLastError();
 }
 
+// Weight-gradient tiles: 256 x 256, 32 deep, four stage buffers.  With 512 or more rows per
+// expert on average, four loader waves issue every operand load, so the compute waves' gradient
+// stores hold back no load wait: 8-10% faster on both weight gradients at 512, 2048 and 4096
+// rows per expert (E = 128, T = 16384; E = 32, d = 4096; E = 8); at 256 rows they gain nothing.
+static TileChoice wgrad_tile(const char* name, const GemmShape& s) {
+  return tile_for(name, Tile::t256x256w8, 32, 4, (int64_t)s.R >= (int64_t)512 * s.E ? 4 : 0);
+}
+
 hipError_t wgrad2_bf16(const GemmShape& s, const int* offsets, const bf16_t* H, const bf16_t* dY, bf16_t* dW2,
                        void* ws, hipStream_t st) {
   if (s.E == 1 && ws) {
@@ -959,7 +997,7 @@ hipError_t wgrad2_bf16(const GemmShape& s, const int* offsets, const bf16_t* H, 
   ProbWgrad2 p;
   p.M = s.d; p.N = s.f; p.K = s.R; p.E = s.E; p.offsets = offsets;
   p.dY = dY; p.Hm = H; p.dW2 = dW2;
-  return launch(tile_for("WGRAD2", Tile::t256x256w8, 32, 4), p, st);
+  return launch(wgrad_tile("WGRAD2", s), p, st);
 }
 hipError_t dgrad1_bf16(const GemmShape& s, const int* offsets, const bf16_t* dab, const bf16_t* W1,
                        const bf16_t* W3, bf16_t* dX, hipStream_t st) {
@@ -977,7 +1015,7 @@ hipError_t wgrad1_bf16(const GemmShape& s, const int* offsets, const bf16_t* X, 
   ProbWgrad1 p;
   p.M = 2 * s.f; p.N = s.d; p.K = s.R; p.E = s.E; p.offsets = offsets; p.f = s.f;
   p.dab = dab; p.X = X; p.dW1 = dW1; p.dW3 = dW3;
-  return launch(tile_for("WGRAD1", Tile::t256x256w8, 32, 4), p, st);
+  return launch(wgrad_tile("WGRAD1", s), p, st);
 }
 hipError_t router_fwd_bf16(int T, int d, int E, const bf16_t* X, const bf16_t* Wr, const float* bias, float* L,
                            hipStream_t st) {
