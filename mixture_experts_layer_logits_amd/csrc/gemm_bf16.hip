@@ -840,12 +840,12 @@ static hipError_t launch_cfg(const Prob& p, hipStream_t st, int bk, int stages, 
     return launch_cfg<TileCfg<128, 256, 2, 4>>(p, st, bk, stages, loaders);
   } else if constexpr (Cfg::BM == 192) {
     // 192-row tiles (GEMMs grouped along M): 64 deep in two stages, or with loader waves
-    // 32 deep in three or four.  The default build compiles them for dgrad1 only (its
-    // default tile); another GEMM asking for them runs its default tile.
+    // 32 deep in three or four.  The default build compiles them for dgrad1 and dgrad2 (whose
+    // defaults use them); another GEMM asking for them runs its default tile.
 #ifdef MOE_ALL_TILES
     constexpr bool built = true;
 #else
-    constexpr bool built = std::is_same<Prob, ProbDgrad1>::value;
+    constexpr bool built = std::is_same<Prob, ProbDgrad1>::value || std::is_same<Prob, ProbDgrad2>::value;
 #endif
     if constexpr (!built) {
       return launch_cfg<TileCfg<128, 256, 2, 4>>(p, st, bk, stages, loaders);
@@ -953,17 +953,24 @@ hipError_t gemm2_fwd_bf16(const GemmShape& s, const int* offsets, const bf16_t* 
   p.Hm = H; p.W2 = W2; p.Y = Y;
   return launch(m_grouped_tile("GEMM2", s, 64), p, st);
 }
-// dgrad2 keeps the 128 x 256 tiles with loader waves over long expert segments too: its
-// epilogue reads the saved a, b of every output, and with the compute waves issuing no
-// operand loads those reads wait only on each other.  At 4096 and 2048 rows per expert
-// that is 14% and 9% faster than the 256 x 256 two-stage tiles (E = 8, T = 8192, d = 2048;
-// E = 32, T = 16384, d = 4096).
+// dgrad2 runs with loader waves at every segment length: its epilogue reads the saved a, b
+// of every output, and with the compute waves issuing no operand loads those reads wait
+// only on each other (at 4096 and 2048 rows per expert 14% and 9% faster than the 256 x 256
+// two-stage tiles without them).  Short segments keep 128 x 256 tiles, 64 deep.  Long ones
+// (1024 rows per expert or more on average) take 192 x 256 tiles, 32 deep in three stages,
+// so each weight block is read by fewer tiles of an expert: alternating runs on one MI355X,
+// 0.215 -> 0.192 ms at E = 8, T = 8192 and 0.934 -> 0.907 ms at E = 32, T = 16384, d = 4096;
+// at 512 and 256 rows per expert they measured 3% slower and even.  The variant that also
+// writes MXFP8 rows of [da | db] keeps the 128 x 256 tiles (on 192 x 256 its epilogue took
+// 1.74 ms against 1.02 at E = 32, T = 16384, d = 4096).
 template <bool Q>
 static hipError_t dgrad2_launch(const GemmShape& s, const int* offsets, const bf16_t* dY, const bf16_t* W2,
                                 const bf16_t* ab, bf16_t* dab, uint8_t* dq, uint8_t* ds, hipStream_t st) {
   ProbDgrad2T<Q> p;
   p.M = s.R; p.N = s.f; p.K = s.d; p.E = s.E; p.offsets = offsets;
   p.dY = dY; p.W2 = W2; p.ab = ab; p.dab = dab; p.dq = dq; p.ds = ds;
+  if (!Q && (int64_t)s.R >= (int64_t)1024 * s.E)
+    return launch(tile_for("DGRAD2", Tile::t192x256w8, 32, 3, 4), p, st);
   return launch(tile_for("DGRAD2", Tile::t128x256w8, 64, 3, 4), p, st);
 }
 hipError_t dgrad2_bf16(const GemmShape& s, const int* offsets, const bf16_t* dY, const bf16_t* W2,
