@@ -191,8 +191,12 @@ def step_calls(m, L, d_inp, learned, recompute=False):
                       ("shared_dgrad1", lambda: m.moe_ffn_dgrad1(ss, L.dab_s, W1s, W3s, so, L.dx_s, L.ws_s))]
         calls += [("shared_wgrad1", lambda: m.moe_ffn_wgrad1(ss, x, L.dab_s, so, L.dW1s, L.dW3s, L.ws_s))]
     dx_add = L.dx_s if sh is not None else None
-    calls += [("permute_bwd", lambda: m.moe_permute_bwd(s, L.dx_perm, L.slot_row, L.dx_r if learned else None,
-                                                        dx_add, L.dx))]
+    if learned and L.router_dx_fused:  # the router's dx_r folded into the un-permute
+        calls += [("permute_bwd", lambda: m.moe_permute_bwd_router(s, L.dx_perm, L.slot_row, L.topk_idx, L.dlogits,
+                                                                   Wr, dx_add, L.dx))]
+    else:
+        calls += [("permute_bwd", lambda: m.moe_permute_bwd(s, L.dx_perm, L.slot_row, L.dx_r if learned else None,
+                                                            dx_add, L.dx))]
     # wgrad1 last, as in the layer's backward: its gradient writes would otherwise push
     # dx_perm out of the memory-side cache before the un-permute reads it
     calls += [wgrad1]
@@ -233,9 +237,11 @@ def algorithmic_work(w, eb, mx_dispatch=False, fq_h=False, fq_dab=False):  # noq
         "dgrad1": R * 2 * f * eb + 2 * wbytes + R * d * eb,
         "wgrad1": R * 2 * f * eb + R * d * eb + 2 * wbytes,
         "route_bwd": R * 12 + T * E * 4,
-        "router_bwd": 2 * T * E * 4 + E * d * eb + 2 * T * d * eb + E * d * 4,
-        # dx_perm rows in, dx out, and with learned routing the router's dx_r in
-        "permute_bwd": R * d * eb + (2 if w.routing != "given_uniform" else 1) * T * d * eb + R * 4,
+        # dlogits in, x in, dWr out (the router's dx_r is folded into the un-permute)
+        "router_bwd": T * E * 4 + T * d * eb + E * d * 4,
+        # dx_perm rows in, dx out; with learned routing also the k ids and dlogits of each
+        # token and Wr (read once; its rows are gathered from L2)
+        "permute_bwd": R * d * eb + T * d * eb + R * 4 + (R * 8 + E * d * eb if w.routing != "given_uniform" else 0),
     }
     if fq_h:
         qh = R * f * 33 // 32

@@ -256,7 +256,8 @@ moe_status moe_route_bwd(const moe_shape* s, const float* dgates, const float* g
 /* Router backward: dx_r = dlogits Wr ([T, d] act, written), dWr = dlogits^T x ([E, d]
  * float, written), the gradients of the learned router's scores (bigchange.ai, section
  * "Что инженер может попробовать на практике").  The reduction over T is split into partial sums held in ws and added
- * in a fixed order (deterministic). */
+ * in a fixed order (deterministic).  dx_r may be NULL: then only dWr is computed (the caller
+ * folds dx_r into moe_permute_bwd_router). */
 moe_status moe_router_bwd(const moe_shape* s, const void* x, const void* Wr, const float* dlogits,
                           void* dx_r, float* dWr, void* ws, size_t ws_bytes, void* stream);
 
@@ -267,6 +268,19 @@ moe_status moe_router_bwd(const moe_shape* s, const void* x, const void* Wr, con
  * expert's, may each be NULL).  dx_perm [R, d], dx_r / dx_add [T, d], dx [T, d] act. */
 moe_status moe_permute_bwd(const moe_shape* s, const void* dx_perm, const int32_t* slot_row,
                            const void* dx_r, const void* dx_add, void* dx, void* stream);
+
+/* Un-permute with the router's input gradient folded in (the same dispatch backward as
+ * moe_permute_bwd, plus the gradient through the learned router's scores: bigchange.ai,
+ * section "Что инженер может попробовать на практике").  The gates are a softmax over each
+ * token's k chosen scores, so dlogits is zero outside them and dx_r[t] = sum_e dlogits[t, e]
+ * Wr[e] has k terms: dx[t] = dx_add[t] + sum_j (dx_perm[slot_row[t, j]] + dlogits[t, e_j]
+ * Wr[e_j]), e_j = topk_idx[t, j] (float accumulation in that order, one rounding to act;
+ * dx_add may be NULL).  dlogits [T, E] float as written by moe_route_bwd, topk_idx [T, k]
+ * from moe_route (ids outside [0, E) are clamped, never read out of range), Wr [E, d] act,
+ * dx_perm [R, d], dx [T, d] act.  Replaces moe_router_bwd's dx_r and its read here. */
+moe_status moe_permute_bwd_router(const moe_shape* s, const void* dx_perm, const int32_t* slot_row,
+                                  const int32_t* topk_idx, const float* dlogits, const void* Wr,
+                                  const void* dx_add, void* dx, void* stream);
 
 /* ---------------------------------------------------------------- MXFP8 */
 

@@ -81,6 +81,7 @@ _SIGS = {
     "moe_route_bwd": [_VP, _VP, _VP, _VP, _VP],
     "moe_router_bwd": [_VP, _VP, _VP, _VP, _VP, _VP, _SZ, _VP],
     "moe_permute_bwd": [_VP, _VP, _VP, _VP, _VP, _VP],
+    "moe_permute_bwd_router": [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP],
     # MXFP8 dispatch and the GEMMs that read its quantised rows
     "moe_permute_mx": [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP],
     "moe_combine_bwd_mx": [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP],
@@ -243,6 +244,10 @@ def moe_router_bwd(shape, x, Wr, dlogits, dx_r, dWr, ws, stream=None):
 
 def moe_permute_bwd(shape, dx_perm, slot_row, dx_r, dx_add, dx, stream=None):
     _call("moe_permute_bwd", shape, dx_perm, slot_row, dx_r, dx_add, dx, stream=stream)
+
+
+def moe_permute_bwd_router(shape, dx_perm, slot_row, topk_idx, dlogits, Wr, dx_add, dx, stream=None):
+    _call("moe_permute_bwd_router", shape, dx_perm, slot_row, topk_idx, dlogits, Wr, dx_add, dx, stream=stream)
 
 
 def moe_tuning_reload():

@@ -393,10 +393,12 @@ moe_status moe_router_bwd(const moe_shape* s, const void* x, const void* Wr, con
                           float* dWr, void* ws, size_t ws_bytes, void* st) {
   MOE_TRY(check_shape(s));
   MOE_TRY(check_ptrs({Wr, dWr}));
-  MOE_TRY(check_rows(s, {x, dx_r}));
+  MOE_TRY(check_rows(s, {x}));
+  if (dx_r && !aligned16(dx_r)) return MOE_EALIGN;
   if (!rows_ok(s, dlogits)) return MOE_ENULL;
   if (s->act == MOE_F32) {
-    if (s->T > 0 && router_dx_f32(s->T, s->d, s->E, dlogits, (const float*)Wr, (float*)dx_r, S(st)) != hipSuccess)
+    if (dx_r && s->T > 0 &&
+        router_dx_f32(s->T, s->d, s->E, dlogits, (const float*)Wr, (float*)dx_r, S(st)) != hipSuccess)
       return MOE_ELAUNCH;
     return launched(router_dw_f32(s->T, s->d, s->E, dlogits, (const float*)x, dWr, S(st)));
   }
@@ -414,6 +416,18 @@ moe_status moe_permute_bwd(const moe_shape* s, const void* dx_perm, const int32_
   if ((dx_r && !aligned16(dx_r)) || (dx_add && !aligned16(dx_add))) return MOE_EALIGN;
   return launched(
       unpermute_sum_rows(elem_bytes(s), s->T, s->d, s->k, dx_perm, slot_row, dx_r, dx_add, dx, S(st)));
+}
+
+moe_status moe_permute_bwd_router(const moe_shape* s, const void* dx_perm, const int32_t* slot_row,
+                                  const int32_t* topk_idx, const float* dlogits, const void* Wr, const void* dx_add,
+                                  void* dx, void* st) {
+  MOE_TRY(check_shape(s));
+  MOE_TRY(check_ptrs({Wr}));
+  MOE_TRY(check_rows(s, {dx_perm, dx}));
+  if (!rows_ok(s, slot_row) || !rows_ok(s, topk_idx) || !rows_ok(s, dlogits)) return MOE_ENULL;
+  if (!aligned16(Wr) || (dx_add && !aligned16(dx_add))) return MOE_EALIGN;
+  return launched(unpermute_router_rows(elem_bytes(s), s->T, s->d, s->k, s->E, dx_perm, slot_row, topk_idx, dlogits,
+                                        Wr, dx_add, dx, S(st)));
 }
 
 moe_status moe_mx_quantize(int32_t rows, int32_t cols, int32_t axis, const int32_t* seg_offsets, int32_t nseg,

@@ -1077,8 +1077,8 @@ static size_t al256(size_t b) { return (b + 255) / 256 * 256; }
 size_t router_dw_workspace_bytes(int T, int d, int E) {
   return al256((size_t)T * router_lda(E) * sizeof(bf16_t)) + (size_t)router_dw_splits(T, d, E) * E * d * sizeof(float);
 }
-// dx_r = dlogits Wr and dWr = dlogits^T x through the bf16 copy of dlogits at the start of
-// ws (split partials of dWr after it)
+// dx_r = dlogits Wr (skipped when dX is null) and dWr = dlogits^T x through the bf16 copy of
+// dlogits at the start of ws (split partials of dWr after it)
 hipError_t router_bwd_bf16(int T, int d, int E, const float* dL, const bf16_t* Wr, const bf16_t* X, bf16_t* dX,
                            float* dW, void* ws, hipStream_t st) {
   const int lda = router_lda(E);
@@ -1089,10 +1089,12 @@ hipError_t router_bwd_bf16(int T, int d, int E, const float* dL, const bf16_t* W
     const int64_t n = (int64_t)T * lda;
     hipLaunchKernelGGL(dlogits_bf16_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, T, E, lda, dL, dLb);
     if ((err = hipGetLastError()) != hipSuccess) return err;
-    ProbRouterDx p;
-    p.M = T; p.N = d; p.K = E; p.E = 1; p.seg_len = T; p.seg_total = T;
-    p.lda = lda; p.dL = dLb; p.Wr = Wr; p.dX = dX;
-    if ((err = launch(tile_for("ROUTER_DX", Tile::t128x256w8, 64), p, st)) != hipSuccess) return err;
+    if (dX) {  // null: the caller folds dx_r into the un-permute (unpermute_router_rows)
+      ProbRouterDx p;
+      p.M = T; p.N = d; p.K = E; p.E = 1; p.seg_len = T; p.seg_total = T;
+      p.lda = lda; p.dL = dLb; p.Wr = Wr; p.dX = dX;
+      if ((err = launch(tile_for("ROUTER_DX", Tile::t128x256w8, 64), p, st)) != hipSuccess) return err;
+    }
   }
   int ns = router_dw_splits(T, d, E);
   const int seg_len = ((T + ns - 1) / ns + 63) / 64 * 64;

@@ -40,5 +40,9 @@ hipError_t dgates_rows(int T, int d, int k, const bf16_t* dy, const bf16_t* y_pe
 hipError_t row_src_rows(int T, int k, const int32_t* slot_row, int32_t* row_src, hipStream_t st);
 hipError_t unpermute_sum_rows(int elem_bytes, int T, int d, int k, const void* dx_perm, const int32_t* slot_row,
                               const void* dx_r, const void* dx_add, void* dx, hipStream_t st);
+// un-permute with the router's input gradient folded in (k rows of Wr per token)
+hipError_t unpermute_router_rows(int elem_bytes, int T, int d, int k, int E, const void* dx_perm,
+                                 const int32_t* slot_row, const int32_t* topk_idx, const float* dlogits,
+                                 const void* Wr, const void* dx_add, void* dx, hipStream_t st);
 
 }  // namespace moe

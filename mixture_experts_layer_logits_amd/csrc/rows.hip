@@ -344,6 +344,87 @@ __global__ void __launch_bounds__(kThreads) unpermute_sum_kernel(int ntok, int d
   }
 }
 
+// dx[t] = dx_add[t] + sum_j (dx_perm[slot_row[t, j]] + dL[t, e_j] Wr[e_j]), e_j = topk_idx[t, j]:
+// the un-permute with the router's input gradient dx_r = dL Wr folded in.  The gates are a
+// softmax over the token's k chosen scores, so dL is zero outside those k experts and
+// dx_r[t] has k terms, each a row of Wr (E rows of d, which stay in L2).  Float accumulation
+// in the order dx_add, then per j the routed row and the fma of its router term; one
+// rounding to the output type.  Expert ids are clamped into [0, E) before any Wr access.
+// KG > 0 (bf16, k <= KG): U chunks per lane and pass, all 2k + 1 loads issued first.
+template <typename T, int KG, int U>
+__global__ void __launch_bounds__(kThreads) unpermute_router_kernel(int ntok, int d, int k, int E,
+                                                                    const T* __restrict__ dx_perm,
+                                                                    const int32_t* __restrict__ slot_row,
+                                                                    const int32_t* __restrict__ topk_idx,
+                                                                    const float* __restrict__ dL,
+                                                                    const T* __restrict__ Wr,
+                                                                    const T* __restrict__ dx_add, T* __restrict__ dx) {
+  const int t = blockIdx.x * kTokPerBlock + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (t >= ntok) return;
+  const int nchunk = d / 8;
+  auto expert = [&](int j) {
+    const int e = topk_idx[(int64_t)t * k + j];
+    return e < 0 ? 0 : (e >= E ? E - 1 : e);
+  };
+  if constexpr (KG > 0) {
+    const int my_r = lane < k ? slot_row[(int64_t)t * k + lane] : 0;
+    const int my_e = lane < k ? expert(lane) : 0;
+    const float my_g = lane < k ? dL[(int64_t)t * E + my_e] : 0.f;
+    for (int c0 = lane; c0 < nchunk; c0 += U * kWave) {
+      uint4 q[U][2 * KG + 1];
+#pragma unroll
+      for (int u = 0; u < U; u++) {
+        const int c = c0 + u * kWave;
+        q[u][2 * KG] = make_uint4(0, 0, 0, 0);
+        if (dx_add && c < nchunk) q[u][2 * KG] = *reinterpret_cast<const uint4*>(dx_add + (int64_t)t * d + c * 8);
+#pragma unroll
+        for (int j = 0; j < KG; j++) {
+          const int r = __shfl(my_r, j, kWave), e = __shfl(my_e, j, kWave);
+          if (j < k && c < nchunk) {
+            q[u][j] = *reinterpret_cast<const uint4*>(dx_perm + (int64_t)r * d + c * 8);
+            q[u][KG + j] = *reinterpret_cast<const uint4*>(Wr + (int64_t)e * d + c * 8);
+          }
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < U; u++) {
+        const int c = c0 + u * kWave;
+        if (c >= nchunk) break;
+        float acc[8];
+        widen8<T>(q[u][2 * KG], acc);
+#pragma unroll
+        for (int j = 0; j < KG; j++) {
+          if (j >= k) break;
+          const float g = __shfl(my_g, j, kWave);
+          float v[8], w[8];
+          widen8<T>(q[u][j], v);
+          widen8<T>(q[u][KG + j], w);
+#pragma unroll
+          for (int i = 0; i < 8; i++) acc[i] = fmaf(g, w[i], acc[i] + v[i]);
+        }
+        store8<T>(dx + (int64_t)t * d + c * 8, acc);
+      }
+    }
+    return;
+  }
+  for (int c = lane; c < nchunk; c += kWave) {
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    if (dx_add) load8<T>(dx_add + (int64_t)t * d + c * 8, acc);
+    for (int j = 0; j < k; j++) {
+      const int r = slot_row[(int64_t)t * k + j];
+      const int e = expert(j);
+      const float g = dL[(int64_t)t * E + e];
+      float v[8], w[8];
+      load8<T>(dx_perm + (int64_t)r * d + c * 8, v);
+      load8<T>(Wr + (int64_t)e * d + c * 8, w);
+#pragma unroll
+      for (int i = 0; i < 8; i++) acc[i] = fmaf(g, w[i], acc[i] + v[i]);
+    }
+    store8<T>(dx + (int64_t)t * d + c * 8, acc);
+  }
+}
+
 inline dim3 tok_grid(int T) { return dim3((unsigned)((T + kTokPerBlock - 1) / kTokPerBlock)); }
 
 }  // namespace
@@ -437,6 +518,27 @@ hipError_t unpermute_sum_rows(int eb, int T, int d, int k, const void* dx_perm, 
   } else {
     hipLaunchKernelGGL((unpermute_sum_kernel<float, 0, 1>), tok_grid(T), dim3(kThreads), 0, st, T, d, k,
                        (const float*)dx_perm, slot_row, (const float*)dx_r, (const float*)dx_add, (float*)dx);
+  }
+  return hipGetLastError();
+}
+
+hipError_t unpermute_router_rows(int eb, int T, int d, int k, int E, const void* dx_perm, const int32_t* slot_row,
+                                 const int32_t* topk_idx, const float* dL, const void* Wr, const void* dx_add,
+                                 void* dx, hipStream_t st) {
+  if (T == 0) return hipSuccess;
+  if (eb == 2) {
+    if (k <= 4)
+      hipLaunchKernelGGL((unpermute_router_kernel<bf16_t, 4, 2>), tok_grid(T), dim3(kThreads), 0, st, T, d, k, E,
+                         (const bf16_t*)dx_perm, slot_row, topk_idx, dL, (const bf16_t*)Wr, (const bf16_t*)dx_add,
+                         (bf16_t*)dx);
+    else
+      hipLaunchKernelGGL((unpermute_router_kernel<bf16_t, 0, 1>), tok_grid(T), dim3(kThreads), 0, st, T, d, k, E,
+                         (const bf16_t*)dx_perm, slot_row, topk_idx, dL, (const bf16_t*)Wr, (const bf16_t*)dx_add,
+                         (bf16_t*)dx);
+  } else {
+    hipLaunchKernelGGL((unpermute_router_kernel<float, 0, 1>), tok_grid(T), dim3(kThreads), 0, st, T, d, k, E,
+                       (const float*)dx_perm, slot_row, topk_idx, dL, (const float*)Wr, (const float*)dx_add,
+                       (float*)dx);
   }
   return hipGetLastError();
 }

@@ -58,7 +58,8 @@ from . import (MOE_BF16, MOE_F32, MOE_MX_DGRAD1, MOE_MX_DGRAD2, MOE_MX_GEMM1, MO
                moe_ffn_gemm1_fwd_q, moe_ffn_gemm2_fwd_mx, moe_combine_bwd, moe_combine_bwd_mx,
                moe_ffn_dgrad1, moe_ffn_dgrad2, moe_ffn_dgrad2_mx, moe_ffn_gemm1_fwd, moe_ffn_gemm1_fwd_mx,
                moe_ffn_gemm2_fwd, moe_ffn_wgrad1, moe_ffn_wgrad1_mx, moe_ffn_wgrad2, moe_ffn_wgrad2_mx, moe_mx_cols_ld,
-               moe_permute, moe_permute_bwd, moe_permute_mx, moe_route, moe_route_bwd, moe_route_given, moe_router_bwd,
+               moe_permute, moe_permute_bwd, moe_permute_bwd_router, moe_permute_mx, moe_route, moe_route_bwd,
+               moe_route_given, moe_router_bwd,
                moe_router_fwd, moe_workspace_size, mx_scope_bits)
 
 # the GEMMs that read the dispatched rows: all four must run MXFP8 for the MXFP8 dispatch
@@ -67,9 +68,12 @@ _DISPATCH_READERS = MOE_MX_GEMM1 | MOE_MX_WGRAD1 | MOE_MX_DGRAD2 | MOE_MX_WGRAD2
 
 class MoEExpertLayer:
     def __init__(self, T, d, f, E, k, act=MOE_BF16, gemm=None, device="cuda", recompute=False, shared_f=0,
-                 mx_dispatch=None, mx_scope=0, mx_fused_quant=True):
+                 mx_dispatch=None, mx_scope=0, mx_fused_quant=True, router_dx_fused=True):
         self.shape = make_shape(T, d, f, E, k, act, gemm, mx_scope)
         self.recompute = recompute
+        # the router's input gradient folded into the un-permute (k rows of Wr per token)
+        # instead of a dense dlogits Wr GEMM written to dx_r and read back
+        self.router_dx_fused = bool(router_dx_fused)
         bits = mx_scope_bits(self.shape)
         # MXFP8 operands written by the producing bf16 GEMM's epilogue
         self.fq_h = bool(mx_fused_quant) and bool(bits & MOE_MX_GEMM2) and not bits & MOE_MX_GEMM1
@@ -126,7 +130,7 @@ class MoEExpertLayer:
         self.dW3 = e(E, f, d)
         self.dW2 = e(E, d, f)
         self.dlogits = e(T, E, dtype=f32)
-        self.dx_r = e(T, d)
+        self.dx_r = None if self.router_dx_fused else e(T, d)
         self.dWr = e(E, d, dtype=f32)
         self.dx = e(T, d)
         self.ws = torch.empty(moe_workspace_size(self.shape), dtype=torch.uint8, device=dev)
@@ -240,7 +244,10 @@ class MoEExpertLayer:
                 moe_ffn_dgrad1(ss, self.dab_s, W1s, W3s, off, self.dx_s, self.ws_s)
             moe_ffn_wgrad1(ss, x, self.dab_s, off, self.dW1s, self.dW3s, self.ws_s)
             dx_add = self.dx_s
-        moe_permute_bwd(s, self.dx_perm, self.slot_row, dx_r, dx_add, self.dx)
+        if self.learned and self.router_dx_fused:
+            moe_permute_bwd_router(s, self.dx_perm, self.slot_row, self.topk_idx, self.dlogits, Wr, dx_add, self.dx)
+        else:
+            moe_permute_bwd(s, self.dx_perm, self.slot_row, dx_r, dx_add, self.dx)
         # wgrad1 goes last: its gradient writes, the largest output of the step, would
         # otherwise push dx_perm out of the memory-side cache before the un-permute reads it
         if self.mx_dispatch:

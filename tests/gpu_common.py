@@ -83,22 +83,24 @@ def say(msg: str):
     sys.stdout.flush()
 
 
-def make_layer(w, mx_dispatch=None, recompute=False, mx_fused_quant=True):
+def make_layer(w, mx_dispatch=None, recompute=False, mx_fused_quant=True, router_dx_fused=True):
     import mixture_experts_layer_logits_amd as m
     act = m.MOE_F32 if w.dtype == "f32" else m.MOE_BF16
     gemm = {"f32": m.MOE_F32, "bf16": m.MOE_BF16, "mxfp8": m.MOE_MXFP8}[w.gemm]
     return m.MoEExpertLayer(w.T, w.d, w.f, w.E, w.k, act=act, gemm=gemm, shared_f=w.shared_f,
                             mx_dispatch=mx_dispatch, mx_scope=mx_scope_bits(w), recompute=recompute,
-                            mx_fused_quant=mx_fused_quant)
+                            mx_fused_quant=mx_fused_quant, router_dx_fused=router_dx_fused)
 
 
-def run_layer(w, inp: dict, layer=None, mx_dispatch=None, recompute=False, mx_fused_quant=True):
+def run_layer(w, inp: dict, layer=None, mx_dispatch=None, recompute=False, mx_fused_quant=True,
+              router_dx_fused=True):
     """Forward + backward of the whole layer on the GPU; returns the layer object
     (mx_dispatch: None = the layer's default, on when the MXFP8 scope covers every GEMM
     that reads the dispatched rows; mx_fused_quant: MXFP8 operands written by the
-    producing bf16 GEMM's epilogue where the scope allows)."""
+    producing bf16 GEMM's epilogue where the scope allows; router_dx_fused: the router's input
+    gradient folded into the un-permute rather than a dense GEMM into dx_r)."""
     if layer is None:
-        layer = make_layer(w, mx_dispatch, recompute, mx_fused_quant)
+        layer = make_layer(w, mx_dispatch, recompute, mx_fused_quant, router_dx_fused)
     d = to_dev(inp)
     sh = d.get("shared")
     if w.routing == "given_uniform":

@@ -33,8 +33,11 @@ def test_algorithmic_work_counts_each_operand_once(bench):
     assert byt["permute"] == T * d * eb + R * d * eb + R * 8
     # wgrad1: dab and x_perm read once, dW1 and dW3 written once
     assert byt["wgrad1"] == R * 2 * f * eb + R * d * eb + 2 * E * f * d * eb
-    # learned routing: the un-permute also reads the router's dx_r; given routing does not
-    assert byt["permute_bwd"] == R * d * eb + 2 * T * d * eb + R * 4
+    # learned routing: the un-permute also folds in the router's dx_r, reading each token's k
+    # ids and dlogits and Wr once; given routing does not
+    assert byt["permute_bwd"] == R * d * eb + T * d * eb + R * 4 + R * 8 + E * d * eb
+    # the router backward then reads dlogits and x and writes dWr only
+    assert byt["router_bwd"] == T * E * 4 + T * d * eb + E * d * 4
     wg = workloads.WORKLOADS["e128_k4_t16384_random"]
     _, bg = bench.algorithmic_work(wg, eb)
     assert bg["permute_bwd"] == wg.R * wg.d * eb + wg.T * wg.d * eb + wg.R * 4

@@ -104,6 +104,31 @@ def test_recompute_layer_parity(name, over):
     _check_layer(w, inp, layer)
 
 
+ROUTER_DX_CASES = [("e128_k4_t8192", dict(T=300, d=256, f=128, E=16, k=4)),
+                   ("e128_k4_t8192", dict(T=200, d=192, f=128, E=16, k=6, name="k6")),
+                   ("tiny_fp32", {})]
+
+
+@pytest.mark.parametrize("name,over", ROUTER_DX_CASES, ids=[c[1].get("name", c[0]) for c in ROUTER_DX_CASES])
+def test_router_dx_folded_into_unpermute(name, over):
+    """The un-permute with the router's input gradient folded in (k rows of Wr per token,
+    the layer's default) and the dense dlogits Wr GEMM into dx_r followed by the plain
+    un-permute: both against the oracle, the same dlogits and dWr bit for bit, and dx of
+    the two within the tolerance of each other."""
+    w = _case(name, over)
+    inp = workloads.make_inputs(w)
+    say(f"[gpu] router dx folded {w}")
+    A = run_layer(w, inp, router_dx_fused=True)
+    assert A.dx_r is None
+    _check_layer(w, inp, A)
+    keep = {n: getattr(A, n).clone() for n in ("dlogits", "dWr", "dx")}
+    say(f"[gpu] router dx as a GEMM {w}")
+    B = run_layer(w, inp, router_dx_fused=False)
+    _check_layer(w, inp, B)
+    assert torch.equal(B.dlogits, keep["dlogits"]) and torch.equal(B.dWr, keep["dWr"])
+    assert normwise_err(host(B.dx), host(keep["dx"])) < TOL[w.gemm]
+
+
 def test_autograd_function_against_the_oracle():
     """MoEExpertFunction (learned routing with a router bias): torch autograd gradients of
     x, Wr, W1, W3, W2 against the oracle's; a second forward through the same layer before
