@@ -93,6 +93,7 @@ __global__ void __launch_bounds__(kTransThreads) mx_trans_kernel(TransQ a) {
   __shared__ int s_pstart[kMaxExperts + 1];
   __shared__ __attribute__((aligned(16))) bf16_t s_in[kTransRows][kTransCols];
   __shared__ __attribute__((aligned(16))) uint8_t s_out[kTransCols][kTransOutPitch];
+  __shared__ uint32_t s_csc[kTransCols];  // the tile's four 32-row block scales of each column
   const int tid = threadIdx.x;
   const bool padded = a.seg != nullptr;
   if (padded) {
@@ -162,9 +163,20 @@ __global__ void __launch_bounds__(kTransThreads) mx_trans_kernel(TransQ a) {
       uint4* o = reinterpret_cast<uint4*>(&s_out[c][b * 32]);
       o[0] = make_uint4(w[0], w[1], w[2], w[3]);
       o[1] = make_uint4(w[4], w[5], w[6], w[7]);
-      if (b < nblk && c0 + c < a.cols) a.s[srow0 + (int64_t)(c0 + c) * a.lds + b] = (uint8_t)(sexp + 127);
+      reinterpret_cast<uint8_t*>(s_csc)[c * 4 + b] = (uint8_t)(sexp + 127);
     }
     __syncthreads();
+    // the scales of column c0 + c are nblk consecutive bytes: one 4-byte store per column
+    // when all four blocks are stored and the word is aligned, else byte by byte
+    if (tid < kTransCols && c0 + tid < a.cols) {
+      uint8_t* dst = a.s + srow0 + (int64_t)(c0 + tid) * a.lds;
+      const uint32_t w = s_csc[tid];
+      if (nblk == 4 && (reinterpret_cast<uintptr_t>(dst) & 3) == 0) {
+        *reinterpret_cast<uint32_t*>(dst) = w;
+      } else {
+        for (int b = 0; b < nblk; b++) dst[b] = (uint8_t)(w >> (8 * b));
+      }
+    }
     // 64 output rows x (32 * nblk) bytes, 8 lanes per 128-byte row
 #pragma unroll
     for (int i = 0; i < kTransCols * kTransRows / 16 / kTransThreads; i++) {
