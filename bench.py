@@ -311,7 +311,7 @@ KERNEL_CALLS = [("ProbGemm1", "gemm1_fwd"), ("ProbGemm2", "gemm2_fwd"), ("ProbDg
                 ("ProbRouterDx", "router_bwd"), ("ProbRouterDw", "router_bwd"), ("route_chunk", "route"),
                 ("route_scan", "route"), ("route_finalize", "route"), ("route_bwd", "route_bwd"),
                 ("permute_kernel", "permute"), ("combine_kernel", "combine"), ("combine_bwd_kernel", "combine_bwd"),
-                ("unpermute_sum", "permute_bwd"), ("mx_dispatch", "mx_dispatch"), ("dgates_kernel", "combine_bwd"),
+                ("unpermute_sum", "permute_bwd"), ("unpermute_router", "permute_bwd"), ("mx_dispatch", "mx_dispatch"), ("dgates_kernel", "combine_bwd"),
                 ("row_src_kernel", "permute"), ("copyBuffer", "copy"), ("elementwise_kernel", "copy")]
 
 
