@@ -129,6 +129,46 @@ def test_router_dx_folded_into_unpermute(name, over):
     assert normwise_err(host(B.dx), host(keep["dx"])) < TOL[w.gemm]
 
 
+def test_folded_router_dx_clamps_expert_ids():
+    """moe_permute_bwd_router reads a row of Wr per routed slot; an expert id outside [0, E)
+    is clamped into it, never used as an address.  Against the oracle's un-permute and
+    router backward with those clamped ids (each token's ids stay distinct after clamping)."""
+    import mixture_experts_layer_logits_amd as m
+    from oracle import moe_ref as ref
+    T, E, k, d = 24, 8, 2, 64
+    g = torch.Generator().manual_seed(5)
+    idx = torch.stack([torch.randperm(E, generator=g)[:k] for _ in range(T)]).int()
+    s = m.make_shape(T, d, 64, E, k)
+    counts = torch.empty(E, dtype=torch.int32, device="cuda")
+    offsets = torch.empty(E + 1, dtype=torch.int32, device="cuda")
+    slot = torch.empty(T, k, dtype=torch.int32, device="cuda")
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    ws = torch.empty(m.moe_workspace_size(s), dtype=torch.uint8, device="cuda")
+    m.moe_route_given(s, idx.cuda(), counts, offsets, slot, err, ws)
+    bad = idx.clone()
+    # ids that clamp to 0 or E - 1, on tokens that do not already hold that expert
+    for t in range(T):
+        if t % 3 == 0 and 0 not in idx[t].tolist():
+            bad[t, 0] = -3
+        elif t % 3 == 1 and E - 1 not in idx[t].tolist():
+            bad[t, 1] = E + 5
+    assert (bad < 0).any() and (bad >= E).any()
+    dx_perm = torch.randn(T * k, d, generator=g).to(torch.bfloat16)
+    dL = torch.randn(T, E, generator=g)
+    Wr = (0.02 * torch.randn(E, d, generator=g)).to(torch.bfloat16)
+    dx = torch.empty(T, d, dtype=torch.bfloat16, device="cuda")
+    say("[gpu] folded router dx with clamped ids")
+    m.moe_permute_bwd_router(s, dx_perm.cuda(), slot, bad.cuda(), dL.cuda(), Wr.cuda(), None, dx)
+    torch.cuda.synchronize()
+    used = bad.clamp(0, E - 1).numpy()
+    dLs = np.zeros((T, E))
+    for t in range(T):
+        dLs[t, used[t]] = dL[t, used[t]].numpy()
+    dx_r, _ = ref.router_bwd(np.zeros((T, d)), Wr.float().numpy(), dLs)
+    want = ref.unpermute_sum(dx_perm.float().numpy(), host(slot), dx_r)
+    assert normwise_err(host(dx), want) < 1e-2
+
+
 def test_autograd_function_against_the_oracle():
     """MoEExpertFunction (learned routing with a router bias): torch autograd gradients of
     x, Wr, W1, W3, W2 against the oracle's; a second forward through the same layer before
