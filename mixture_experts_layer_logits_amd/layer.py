@@ -8,8 +8,17 @@ backward passes as the library's calls, in order, on the current stream:
             or moe_route_given                 (tokens arrive routed)
             -> moe_permute -> moe_grouped_ffn_fwd -> moe_combine
   backward  moe_combine_bwd -> the expert GEMMs' dgrad2, wgrad2, dgrad1
-            -> moe_route_bwd -> moe_router_bwd (learned routing)
-            -> moe_permute_bwd -> wgrad1 (last, after the un-permute has read dx_perm)
+            -> moe_route_bwd -> moe_router_bwd (learned routing; dWr only)
+            -> moe_permute_bwd_router (learned routing) or moe_permute_bwd
+            -> wgrad1 (last, after the un-permute has read dx_perm)
+
+Router input gradient (``router_dx_fused``, on by default): the gates are a softmax over
+each token's k chosen scores, so dlogits is zero outside them and dx_r = dlogits Wr is k
+rows of Wr per token.  moe_permute_bwd_router adds those rows while it gathers the token's
+routed rows of dx_perm, so no dense dlogits Wr GEMM runs and no dx_r is written or read
+(bigchange.ai, section "Что инженер может попробовать на практике", for the learned
+router).  ``router_dx_fused=False`` keeps the dense GEMM into ``dx_r`` and the plain
+un-permute.
 
 Nothing is copied back to the host between calls; routing counts and offsets stay on
 the GPU (unite.ai, "Ai2 κυκλοφορεί το Olmo-Core 3…", section "Παραλληλισμός, Ακρίβεια
