@@ -158,19 +158,40 @@ __global__ void __launch_bounds__(1024) route_scan_kernel(int E, int nchunks, in
   const bool active = part < P;
   const int c0 = active ? (int)((int64_t)part * nchunks / P) : 0;
   const int c1 = active ? (int)((int64_t)(part + 1) * nchunks / P) : 0;
+  // a run of at most kScanHeld chunks is loaded once, every load issued before the first
+  // add, and kept in registers for the rewrite; longer runs are read twice
+  constexpr int kScanHeld = 64;
+  const int n = c1 - c0;
+  const bool held = n <= kScanHeld;
+  int v[kScanHeld];
   int sum = 0;
+  if (held) {
+#pragma unroll
+    for (int i = 0; i < kScanHeld; i++) v[i] = i < n ? hist[(int64_t)(c0 + i) * E + ex] : 0;
+#pragma unroll
+    for (int i = 0; i < kScanHeld; i++) sum += v[i];
+  } else {
 #pragma unroll 8
-  for (int c = c0; c < c1; c++) sum += hist[(int64_t)c * E + ex];
+    for (int c = c0; c < c1; c++) sum += hist[(int64_t)c * E + ex];
+  }
   if (active) s_part[tid] = sum;
   __syncthreads();
   if (active) {
     int run = 0;
     for (int q = 0; q < part; q++) run += s_part[q * E + ex];
+    if (held) {
+#pragma unroll
+      for (int i = 0; i < kScanHeld; i++) {
+        if (i < n) hist[(int64_t)(c0 + i) * E + ex] = run;
+        run += v[i];
+      }
+    } else {
 #pragma unroll 8
-    for (int c = c0; c < c1; c++) {
-      const int h = hist[(int64_t)c * E + ex];
-      hist[(int64_t)c * E + ex] = run;
-      run += h;
+      for (int c = c0; c < c1; c++) {
+        const int h = hist[(int64_t)c * E + ex];
+        hist[(int64_t)c * E + ex] = run;
+        run += h;
+      }
     }
     if (part == P - 1) s_cnt[ex] = run;
   }
