@@ -211,6 +211,39 @@ def _loss(params, dy, k, learned=True, idx=None):
     return float((fw["y"] * dy).sum()), fw["topk_idx"]
 
 
+def test_score_gradient_is_zero_outside_the_chosen_experts():
+    """dlogits against central differences of the loss in every single score, with the
+    selection held (the gates are a softmax over the k chosen scores): each token's
+    gradient has exactly its k chosen experts' entries, zero elsewhere.  The un-permute
+    that folds in the router's input gradient reads only those k entries per token."""
+    T, d, f, E, k = 6, 8, 8, 5, 2
+    x, Wr, W1, W3, W2, dy = _rand_case(21, T, d, f, E, k, scale_w=0.5)
+    L = ref.router_logits(x, Wr)
+    srt = np.sort(L, axis=1)[:, ::-1]
+    assert (srt[:, k - 1] - srt[:, k]).min() > 1e-3          # the selection stays put under +-h
+    fw = ref.layer_forward(x, W1, W3, W2, k, Wr=Wr)
+    bw = ref.layer_backward(fw, dy, x, W1, W3, W2, Wr=Wr)
+
+    def loss(Lp):
+        idx, gates = ref.topk_gates(Lp, k)
+        assert np.array_equal(idx, fw["topk_idx"])
+        return float((ref.layer_forward(x, W1, W3, W2, k, topk_idx=idx, gates=gates)["y"] * dy).sum())
+
+    h = 1e-6
+    fd = np.zeros((T, E))
+    for t in range(T):
+        for e in range(E):
+            Lp, Lm = L.copy(), L.copy()
+            Lp[t, e] += h
+            Lm[t, e] -= h
+            fd[t, e] = (loss(Lp) - loss(Lm)) / (2 * h)
+    chosen = np.zeros((T, E), dtype=bool)
+    np.put_along_axis(chosen, fw["topk_idx"].astype(np.int64), True, axis=1)
+    assert np.abs(fd[~chosen]).max() < 1e-8
+    assert np.abs(bw["dlogits"][~chosen]).max() == 0.0
+    assert np.allclose(bw["dlogits"][chosen], fd[chosen], rtol=1e-5, atol=1e-7)
+
+
 @pytest.mark.parametrize("learned", [True, False])
 def test_backward_finite_differences(learned):
     T, d, f, E, k = 24, 10, 12, 5, 2
